@@ -1,0 +1,266 @@
+"""CPU oracle of the Qwen Sparse Attention (QSA) forward path.
+
+TEST INFRASTRUCTURE ONLY. This is the plain, slow, obviously correct fp64 numpy
+statement of what the path computes, used to check the HIP library. Only the test
+suite, the smoke check and the benchmark's CPU-baseline leg may import it; the
+product path never calls it. It shares no code with the HIP library.
+
+Sources (the pages describing QSA; cited by title and section):
+
+* [DR] "On the Design of Qwen3.8-Next Architecture" (summary page), section
+  "four architecture components", item 2 "Qwen Sparse Attention (QSA)": the
+  indexer scores micro-blocks of r=4 tokens; keys are first mean-pooled, then a
+  positional encoding is added; the indexer has 4 MQA query heads; the token
+  budget is K=2048; the route follows DeepSeek DSA's light indexer + top-k.
+* [MR] "Qwen3.8-Flash-Next" (Miles RL recipe page), section 1 "Model
+  Introduction": each full-attention layer projects its own indexer queries and
+  compressed keys, scores them, keeps ``indexer_budget`` key tokens per query and
+  attention reads only those; 24 heads, 2 query groups, kv-channels 256.
+* [RA] Release article "Qwen3.8-Flash-Next开源", section "GDN+QSA": the light
+  indexer aggregates the sequence into micro-blocks, rates importance per block,
+  then attends only over the most relevant regions.
+
+Readings where the pages leave a step open (each is stated where it is used):
+
+* Score (DSA reading): s[t,b] = sum_h w[t,h] * max(0, qI[t,h] . kbar[b]); no extra
+  global scale (a positive scale cannot change a ranking).
+* Pooling is the mean over the r keys of a complete block, rounded once to bf16;
+  a trailing partial block is never pooled. No positional encoding is added inside
+  the path (the caller may add one to the pooled keys before scoring).
+* Only complete blocks strictly before the query's own block b(t) = t // r are
+  scored; the own block is always kept and counts toward the budget, so
+  n_sel = K // r blocks are kept in all. Ties go to the lower block index; -0.0
+  equals +0.0. With fewer causal blocks than n_sel - 1 every block is kept.
+* One selection per query token, shared by all heads; head h uses KV group
+  h // (Hq // Hkv). Inside the kept blocks, keys after the query are masked.
+* lse is the natural-log sum of exp of the scaled logits.
+
+Parity pins: every function here is checked against something other than itself
+in tests/test_oracle_pins.py (library routines, brute force, closed forms,
+hand-derived selections in tests/golden/).
+"""
+from __future__ import annotations
+
+from typing import Callable, Optional, Sequence
+
+import numpy as np
+
+# --------------------------------------------------------------------------------------
+# bf16 encoding (inputs arrive as raw bf16 bit patterns, uint16)
+# --------------------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode raw bf16 bit patterns: a bf16 value is the top half of an IEEE fp32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 (round to nearest, ties to even), return bit patterns.
+
+    bf16 keeps 8 significant bits and fp32's exponent range; its spacing in
+    [2^e', 2^(e'+1)) is 2^(e'-7), and 2^-133 below the smallest normal 2^-126.
+    The rounding is done once, directly from fp64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)  # x = m * 2**e with 0.5 <= |m| < 1
+    q_exp = np.maximum(e - 8, -133)  # exponent of the bf16 spacing at x
+    y = np.ldexp(np.rint(np.ldexp(x, -q_exp)), q_exp)  # rint: ties to even
+    return (y.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------------------
+# Stage 1: micro-block mean pooling of the indexer keys  [DR]
+# --------------------------------------------------------------------------------------
+
+
+def pool_keys(k_idx_bits: np.ndarray, r: int) -> np.ndarray:
+    """Mean-pool r consecutive indexer keys per complete block, rounded to bf16.
+
+    k_idx_bits: [n_tokens, d_I] bf16 bits. Returns [n_tokens // r, d_I] bf16 bits.
+    """
+    x = bf16_to_f64(k_idx_bits)
+    nb = x.shape[0] // r
+    blocks = x[: nb * r].reshape(nb, r, x.shape[1])
+    return f64_to_bf16(blocks.sum(axis=1) / r)
+
+
+# --------------------------------------------------------------------------------------
+# Stage 2: light MQA indexer scores at block granularity  [DR], [RA]
+# --------------------------------------------------------------------------------------
+
+
+def index_scores(q_idx: np.ndarray, w: np.ndarray, k_pooled: np.ndarray,
+                 positions: np.ndarray, r: int) -> np.ndarray:
+    """Block scores for query rows at absolute ``positions``.
+
+    q_idx [n, H_I, d_I] and w [n, H_I] as fp64, k_pooled [nblk, d_I] fp64.
+    Returns [n, nblk] fp64 with s[i, b] = sum_h w[i,h] * max(0, q_idx[i,h] . k_pooled[b])
+    for b < positions[i] // r, and NaN where the block is not scored.
+    """
+    n, n_heads, _ = q_idx.shape
+    s = np.zeros((n, k_pooled.shape[0]), dtype=np.float64)
+    for h in range(n_heads):
+        dots = q_idx[:, h, :] @ k_pooled.T  # one plain matmul per indexer head
+        s += w[:, h : h + 1] * np.maximum(dots, 0.0)
+    own = np.asarray(positions) // r
+    cols = np.arange(k_pooled.shape[0])
+    s[cols[None, :] >= own[:, None]] = np.nan
+    return s
+
+
+# --------------------------------------------------------------------------------------
+# Stage 3: block top-k under the token budget  [MR], [DR]
+# --------------------------------------------------------------------------------------
+
+
+def select_blocks(scores_row: np.ndarray, own_block: int, n_sel: int) -> np.ndarray:
+    """Kept blocks of one query row: ascending block ids, padded with -1.
+
+    scores_row holds the scores of blocks 0..own_block-1. The own block is always
+    kept; of the earlier blocks the n_sel - 1 best are kept, ranked by score
+    (descending) then block id (ascending).
+    """
+    cand = np.asarray(scores_row[:own_block], dtype=np.float64)
+    m = min(n_sel - 1, own_block)
+    ids = np.arange(own_block)
+    order = np.lexsort((ids, -cand))  # primary key: -score ascending; then id ascending
+    sel = np.full(n_sel, -1, dtype=np.int64)
+    sel[:m] = np.sort(order[:m])
+    sel[m] = own_block
+    return sel
+
+
+def ranked_threshold_gap(scores_row: np.ndarray, own_block: int, n_sel: int):
+    """(m-th best score, (m+1)-th best score) of the candidates, or None if all are kept."""
+    cand = np.asarray(scores_row[:own_block], dtype=np.float64)
+    m = min(n_sel - 1, own_block)
+    if m >= own_block or m == 0:
+        return None
+    srt = np.sort(cand)[::-1]
+    return float(srt[m - 1]), float(srt[m])
+
+
+# --------------------------------------------------------------------------------------
+# Stage 4: exact softmax attention over the kept tokens  [MR]
+# --------------------------------------------------------------------------------------
+
+
+def kept_tokens(sel_row: np.ndarray, t: int, r: int, n_keys: int) -> np.ndarray:
+    """Token ids read by query position t: every token of a kept block, j <= t."""
+    blocks = np.asarray(sel_row)[np.asarray(sel_row) >= 0]
+    toks = (blocks[:, None] * r + np.arange(r)[None, :]).reshape(-1)
+    return toks[(toks <= t) & (toks < n_keys)]
+
+
+def attend(q_t: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float):
+    """Softmax attention of one query token over given key/value rows.
+
+    q_t [Hq, d], k_rows/v_rows [n, Hkv, d] fp64; head h reads KV group h // (Hq//Hkv).
+    Returns (o [Hq, d], lse [Hq]), lse the natural-log normaliser of the scaled logits.
+    """
+    hq, d = q_t.shape
+    hkv = k_rows.shape[1]
+    grp = hq // hkv
+    o = np.zeros((hq, d), dtype=np.float64)
+    lse = np.zeros(hq, dtype=np.float64)
+    for h in range(hq):
+        g = h // grp
+        z = scale * (k_rows[:, g, :] @ q_t[h])
+        mx = z.max()
+        p = np.exp(z - mx)
+        den = p.sum()
+        o[h] = (p @ v_rows[:, g, :]) / den
+        lse[h] = mx + np.log(den)
+    return o, lse
+
+
+# --------------------------------------------------------------------------------------
+# Whole path
+# --------------------------------------------------------------------------------------
+
+
+def _rows_fetcher(k_bits: np.ndarray, v_bits: np.ndarray):
+    def fetch(tokens: np.ndarray):
+        return bf16_to_f64(k_bits[tokens]), bf16_to_f64(v_bits[tokens])
+    return fetch
+
+
+def forward_prefill(q_bits, k_bits, v_bits, q_idx_bits, w, k_idx_bits, *, r: int, budget: int,
+                    q_pos0: int = 0, scale: Optional[float] = None,
+                    k_pooled_prefix_bits: Optional[np.ndarray] = None,
+                    rows: Optional[Sequence[int]] = None, n_keys: Optional[int] = None,
+                    fetch_kv: Optional[Callable] = None, row_chunk: int = 2048) -> dict:
+    """QSA prefill for query rows ``rows`` (default: all).
+
+    q_bits [Lq, Hq, d]; k_bits/v_bits [Lk, Hkv, d] (or ``fetch_kv(tokens)`` returning
+    fp64 rows, with ``n_keys`` = Lk); q_idx_bits [Lq, H_I, d_I]; w [Lq, H_I];
+    k_idx_bits holds the raw indexer keys of the tokens after the pooled prefix
+    (k_pooled_prefix_bits, [P, d_I], or none). Query row i is at position q_pos0 + i.
+    Returns the pooled keys of the new blocks, and per row: scores, selection,
+    output and lse.
+    """
+    lq, hq, d = q_bits.shape
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    n_sel = budget // r
+    if fetch_kv is None:
+        fetch_kv = _rows_fetcher(k_bits, v_bits)
+        n_keys = k_bits.shape[0]
+    pooled_new = pool_keys(k_idx_bits, r)
+    if k_pooled_prefix_bits is not None and len(k_pooled_prefix_bits):
+        pooled_all = np.concatenate([k_pooled_prefix_bits, pooled_new], axis=0)
+    else:
+        pooled_all = pooled_new
+    kp = bf16_to_f64(pooled_all)
+    rows = np.arange(lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    wq = np.asarray(w, dtype=np.float64)
+    sels = np.zeros((len(rows), n_sel), dtype=np.int64)
+    outs = np.zeros((len(rows), hq, d), dtype=np.float64)
+    lses = np.zeros((len(rows), hq), dtype=np.float64)
+    score_rows = []
+    for c0 in range(0, len(rows), row_chunk):
+        rr = rows[c0 : c0 + row_chunk]
+        pos = q_pos0 + rr
+        s = index_scores(bf16_to_f64(q_idx_bits[rr]), wq[rr], kp, pos, r)
+        for j, (i, t) in enumerate(zip(rr, pos)):
+            own = int(t) // r
+            score_rows.append(s[j, :own].copy())
+            sel = select_blocks(s[j, :own], own, n_sel)
+            toks = kept_tokens(sel, int(t), r, n_keys)
+            k_rows, v_rows = fetch_kv(toks)
+            o, lse = attend(bf16_to_f64(q_bits[i]), k_rows, v_rows, scale)
+            sels[c0 + j], outs[c0 + j], lses[c0 + j] = sel, o, lse
+    return {"pooled": pooled_new, "rows": rows, "scores": score_rows, "sel": sels,
+            "out": outs, "lse": lses}
+
+
+def forward_decode(q_bits, q_idx_bits, w, k_pooled_bits, seq_lens, fetch_kv, *, r: int,
+                   budget: int, scale: Optional[float] = None) -> dict:
+    """QSA decode: one new query token per sequence, at position seq_lens[b] - 1.
+
+    q_bits [B, Hq, d]; q_idx_bits [B, H_I, d_I]; w [B, H_I]; k_pooled_bits
+    [B, nblk, d_I] (the pooled-key cache); ``fetch_kv(b, tokens)`` returns fp64
+    K and V rows [n, Hkv, d] of sequence b. Returns per sequence: scores,
+    selection, output and lse.
+    """
+    bsz, hq, d = q_bits.shape
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    n_sel = budget // r
+    sels = np.zeros((bsz, n_sel), dtype=np.int64)
+    outs = np.zeros((bsz, hq, d), dtype=np.float64)
+    lses = np.zeros((bsz, hq), dtype=np.float64)
+    score_rows = []
+    for b in range(bsz):
+        t = int(seq_lens[b]) - 1
+        own = t // r
+        kp = bf16_to_f64(k_pooled_bits[b, :own])
+        s = index_scores(bf16_to_f64(q_idx_bits[b])[None], np.asarray(w[b], np.float64)[None],
+                         kp, np.array([t]), r)[0] if own else np.zeros(0)
+        score_rows.append(s[:own].copy())
+        sel = select_blocks(s[:own], own, n_sel)
+        toks = kept_tokens(sel, t, r, t + 1)
+        k_rows, v_rows = fetch_kv(b, toks)
+        outs[b], lses[b] = attend(bf16_to_f64(q_bits[b]), k_rows, v_rows, scale)
+        sels[b] = sel
+    return {"scores": score_rows, "sel": sels, "out": outs, "lse": lses}

@@ -1,0 +1,331 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test checks the oracle against a library routine, a brute-force or closed-form
+result, a hand-derived fixture, or an invariant the method's definition fixes, so
+that a dropped term, a wrong sign or index, or a transposed operand fails one of
+them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import qsa_oracle as O
+from synth import bf16_bits, generate, workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bits(x: np.ndarray) -> np.ndarray:
+    """bf16 bits of fp32-exact values via torch's own conversion (library routine)."""
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return bf16_bits(t)
+
+
+# ------------------------------------------------------------------------------------
+# bf16 encoding
+# ------------------------------------------------------------------------------------
+
+
+def test_bf16_round_trip_and_torch_agreement():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1.0, -1.0, 3.0e38, 1e-39, -1e-40]]).astype(np.float32)
+    ref = bf16_bits(torch.from_numpy(x).to(torch.bfloat16))  # fp32 -> bf16, RNE
+    mine = O.f64_to_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(mine, ref)
+    np.testing.assert_array_equal(O.f64_to_bf16(O.bf16_to_f64(ref)), ref)
+
+
+def test_bf16_halfway_cases_round_to_even():
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: even significand (1.0) wins.
+    # 1 + 3*2^-8 is halfway between 1+2^-7 and 1+2^-6: even (1+2^-6) wins.
+    vals = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -40])
+    got = O.bf16_to_f64(O.f64_to_bf16(vals))
+    np.testing.assert_array_equal(got, [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7])
+    # A value that double rounding through fp32 would get wrong: just above halfway by
+    # less than fp32 resolution.
+    v = np.array([1 + 2.0 ** -8 + 2.0 ** -30])
+    assert O.bf16_to_f64(O.f64_to_bf16(v))[0] == 1 + 2.0 ** -7
+
+
+# ------------------------------------------------------------------------------------
+# Pooling
+# ------------------------------------------------------------------------------------
+
+
+def test_pool_matches_torch_mean_and_drops_partial_block():
+    rng = np.random.default_rng(1)
+    k = _bits(rng.standard_normal((4 * 37 + 3, 16)) / 8)
+    pooled = O.pool_keys(k, 4)
+    assert pooled.shape == (37, 16)
+    kt = torch.from_numpy(O.bf16_to_f64(k)).view(-1)[: 37 * 4 * 16].view(37, 4, 16)
+    mean = kt.mean(dim=1)  # fp64 mean; exact in fp32 for these magnitudes
+    assert torch.equal(mean.float().double(), mean)
+    np.testing.assert_array_equal(pooled, bf16_bits(mean.float().to(torch.bfloat16)))
+
+
+def test_pool_of_identical_keys_is_exact():
+    u = _bits(np.array([[0.3, -1.25, 7.0, 1e-3]]))
+    k = np.repeat(u, 4, axis=0)
+    np.testing.assert_array_equal(O.pool_keys(k, 4), u)
+
+
+# ------------------------------------------------------------------------------------
+# Hand-derived selections (tests/golden/hand_selection.json)
+# ------------------------------------------------------------------------------------
+
+
+def _hand_pooled(kind: str) -> np.ndarray:
+    kp = np.zeros((16, 4))
+    for b in range(16):
+        if kind == "one_hot":
+            kp[b, b % 4] = (b + 1) if b % 2 == 0 else -(b + 1)
+        else:
+            kp[b] = [1.0, 0.0, 0.0, 0.0] if b == 2 else [b / 64, 1.0, 1.0, 1.0]
+    return kp
+
+
+def _hand_cases():
+    with open(os.path.join(GOLDEN, "hand_selection.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        for row in case["rows"]:
+            yield case["pooled_keys"], row
+
+
+@pytest.mark.parametrize("kind,row", list(_hand_cases()))
+def test_hand_built_selection(kind, row):
+    kp = _hand_pooled(kind)
+    k_idx = _bits(np.repeat(kp, 4, axis=0))  # every token of a block holds its pooled key
+    pooled = O.pool_keys(k_idx, 4)
+    np.testing.assert_array_equal(O.bf16_to_f64(pooled), kp)
+    t = row["t"]
+    s = O.index_scores(np.array(row["q"], float)[None, None, :], np.array([[row["w"]]]),
+                       O.bf16_to_f64(pooled), np.array([t]), 4)[0]
+    sel = O.select_blocks(s[: t // 4], t // 4, 4)
+    assert sel.tolist() == row["sel"], row["why"]
+
+
+# ------------------------------------------------------------------------------------
+# Full coverage: QSA equals dense causal attention when the budget covers the prefix
+# ------------------------------------------------------------------------------------
+
+
+def _dense_causal_bruteforce(q, k, v, scale):
+    """Dense causal attention written as masked matrices (not the oracle's gather)."""
+    lq, hq, d = q.shape
+    grp = hq // k.shape[1]
+    out = np.zeros_like(q)
+    lse = np.zeros((lq, hq))
+    mask = np.tril(np.ones((lq, lq), bool))
+    for h in range(hq):
+        z = scale * q[:, h, :] @ k[:, h // grp, :].T
+        z = np.where(mask, z, -np.inf)
+        mx = z.max(axis=1, keepdims=True)
+        e = np.exp(z - mx)
+        out[:, h, :] = e @ v[:, h // grp, :] / e.sum(axis=1, keepdims=True)
+        lse[:, h] = (mx + np.log(e.sum(axis=1, keepdims=True)))[:, 0]
+    return out, lse
+
+
+def _small_prefill(L=256, hq=4, hkv=2, d=32, budget=256, seed=5):
+    wl = workload("tiny", lq=L, lk=L, hq=hq, hkv=hkv, d=d, d_i=16, budget=budget, seed=seed,
+                  needle_spacing=64)
+    return wl, generate(wl)
+
+
+def _run_oracle(wl, inp, **kw):
+    return O.forward_prefill(bf16_bits(inp["q"]), bf16_bits(inp["k"]), bf16_bits(inp["v"]),
+                             bf16_bits(inp["q_idx"]), inp["w"].numpy(), bf16_bits(inp["k_idx"]),
+                             r=wl.r, budget=wl.budget, q_pos0=wl.q_pos0,
+                             k_pooled_prefix_bits=(None if inp["k_pooled_prefix"] is None
+                                                   else bf16_bits(inp["k_pooled_prefix"])), **kw)
+
+
+def test_full_budget_equals_dense_causal_attention():
+    wl, inp = _small_prefill(L=256, budget=256)
+    res = _run_oracle(wl, inp)
+    q, k, v = (O.bf16_to_f64(bf16_bits(inp[n])) for n in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(wl.d)
+    ref, ref_lse = _dense_causal_bruteforce(q, k, v, scale)
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["lse"], ref_lse, rtol=0, atol=1e-12)
+    # The textbook routine: torch's scaled_dot_product_attention, fp64 on the CPU.
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    grp = wl.hq // wl.hkv
+    tk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(grp, dim=0)
+    tv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(grp, dim=0)
+    sdpa = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True,
+                                                            scale=scale)
+    np.testing.assert_allclose(res["out"], sdpa.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_rows_before_budget_are_dense():
+    wl, inp = _small_prefill(L=512, budget=128)  # n_sel = 32: rows t < 128 keep everything
+    res = _run_oracle(wl, inp, rows=np.arange(0, 128, 7))
+    q, k, v = (O.bf16_to_f64(bf16_bits(inp[n])) for n in ("q", "k", "v"))
+    ref, _ = _dense_causal_bruteforce(q[:128], k[:128], v[:128], 1.0 / math.sqrt(wl.d))
+    np.testing.assert_allclose(res["out"], ref[res["rows"]], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------
+# Invariants of every selection row, and library reductions
+# ------------------------------------------------------------------------------------
+
+
+def test_selection_invariants_and_bruteforce_ranking():
+    wl = workload("tiny")
+    inp = generate(wl)
+    rows = np.concatenate([np.arange(0, 2048, 37), inp["aligned_rows"][:40], [2047]])
+    res = _run_oracle(wl, inp, rows=rows)
+    n_sel = wl.n_sel
+    for j, i in enumerate(res["rows"]):
+        t = int(i)
+        own = t // 4
+        sel = res["sel"][j]
+        kept = sel[sel >= 0]
+        assert len(kept) == min(n_sel, own + 1)
+        assert kept[-1] == own and np.all(np.diff(kept) > 0) and kept.max() <= own
+        assert np.all(sel[len(kept):] == -1)
+        s = res["scores"][j]
+        # Brute force: plain Python sort by (score desc, id asc).
+        m = min(n_sel - 1, own)
+        best = sorted(range(own), key=lambda b: (-s[b], b))[:m]
+        assert sorted(best) == kept[:-1].tolist()
+        if m < own:
+            unsel = np.setdiff1d(np.arange(own), kept)
+            assert s[kept[:-1]].min() >= s[unsel].max()
+    for i, b in zip(inp["aligned_rows"][:40], inp["aligned_blocks"][:40]):
+        j = int(np.nonzero(res["rows"] == i)[0][0])
+        assert b in res["sel"][j], "needle-aligned row lost its needle"
+
+
+def test_scores_reduce_to_one_gemv_when_relu_is_identity():
+    rng = np.random.default_rng(3)
+    q = np.abs(rng.standard_normal((9, 4, 16)))
+    kp = np.abs(rng.standard_normal((30, 16)))
+    pos = np.full(9, 4 * 30 + 3)
+    s = O.index_scores(q, np.ones((9, 4)), kp, pos, 4)
+    np.testing.assert_allclose(s, np.einsum("nc,bc->nb", q.sum(axis=1), kp), rtol=1e-13)
+
+
+def test_scores_with_relu_against_explicit_loops():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((3, 4, 8))
+    w = rng.random((3, 4))
+    kp = rng.standard_normal((10, 8))
+    pos = np.array([7, 20, 43])
+    s = O.index_scores(q, w, kp, pos, 4)
+    for n in range(3):
+        for b in range(10):
+            if b >= pos[n] // 4:
+                assert np.isnan(s[n, b])
+                continue
+            tot = 0.0
+            for h in range(4):
+                dot = sum(q[n, h, c] * kp[b, c] for c in range(8))
+                tot += w[n, h] * (dot if dot > 0 else 0.0)
+            assert abs(s[n, b] - tot) < 1e-12
+
+
+def test_metamorphic_weight_scale_and_head_permutation():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((4, 4, 16))
+    w = rng.random((4, 4))
+    kp = rng.standard_normal((200, 16))
+    pos = np.array([400, 500, 801, 803])
+    s = O.index_scores(q, w, kp, pos, 4)
+    s3 = O.index_scores(q, 3.5 * w, kp, pos, 4)
+    perm = [2, 0, 3, 1]
+    sp = O.index_scores(q[:, perm], w[:, perm], kp, pos, 4)
+    np.testing.assert_allclose(sp, s, rtol=1e-13)
+    for n in range(4):
+        own = pos[n] // 4
+        a = O.select_blocks(s[n, :own], own, 32)
+        b = O.select_blocks(s3[n, :own], own, 32)
+        np.testing.assert_array_equal(a, b)
+
+
+# ------------------------------------------------------------------------------------
+# Closed forms of the attention stage
+# ------------------------------------------------------------------------------------
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(6)
+    n, hq, hkv, d = 40, 6, 2, 16
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((n, hkv, d))
+    # Constant V per group -> output is that constant.
+    v = np.zeros((n, hkv, d))
+    v[:, 0, :] = 1.5
+    v[:, 1, :] = -2.0
+    o, _ = O.attend(q, k, v, 0.3)
+    np.testing.assert_allclose(o[:3], 1.5, rtol=1e-14)
+    np.testing.assert_allclose(o[3:], -2.0, rtol=1e-14)
+    # q = 0 -> uniform weights: output is the mean of the rows, lse = log(n).
+    v = rng.standard_normal((n, hkv, d))
+    o, lse = O.attend(np.zeros((hq, d)), k, v, 0.3)
+    np.testing.assert_allclose(o[:3], np.broadcast_to(v[:, 0].mean(0), (3, d)), rtol=1e-12)
+    np.testing.assert_allclose(o[3:], np.broadcast_to(v[:, 1].mean(0), (3, d)), rtol=1e-12)
+    np.testing.assert_allclose(lse, math.log(n), rtol=1e-14)
+    # One dominant logit (+40 over the others) -> output is that key's value.
+    k = np.zeros((n, hkv, d))
+    q = np.zeros((hq, d))
+    q[:, 0] = 1.0
+    k[17, :, 0] = 40.0
+    o, lse = O.attend(q, k, v, 1.0)
+    np.testing.assert_allclose(o[:3], np.broadcast_to(v[17, 0], (3, d)), atol=1e-15)
+    np.testing.assert_allclose(lse, 40.0 + math.log1p((n - 1) * math.exp(-40)), rtol=1e-15)
+
+
+def test_own_block_masks_future_keys():
+    # Query at t = 4*b + 1 reads only tokens 4b and 4b+1 of its own block.
+    sel = np.array([0, 3, 5, -1])
+    toks = O.kept_tokens(sel, 21, 4, 64)
+    assert toks.tolist() == [0, 1, 2, 3, 12, 13, 14, 15, 20, 21]
+
+
+# ------------------------------------------------------------------------------------
+# Decode = last prefill row; chunked prefill = rows of the full prefill
+# ------------------------------------------------------------------------------------
+
+
+def test_decode_equals_prefill_last_row():
+    L = 640
+    wl, inp = _small_prefill(L=L, budget=64, seed=8)
+    res = _run_oracle(wl, inp, rows=[L - 1, L - 2])
+    pooled = O.pool_keys(bf16_bits(inp["k_idx"]), 4)
+    kb, vb = bf16_bits(inp["k"]), bf16_bits(inp["v"])
+
+    def fetch(b, toks):
+        return O.bf16_to_f64(kb[toks]), O.bf16_to_f64(vb[toks])
+
+    qb = bf16_bits(inp["q"])
+    qib = bf16_bits(inp["q_idx"])
+    w = inp["w"].numpy()
+    for j, seqlen in enumerate([L, L - 1]):
+        row = seqlen - 1
+        dec = O.forward_decode(qb[row][None], qib[row][None], w[row][None], pooled[None],
+                               [seqlen], fetch, r=4, budget=64)
+        np.testing.assert_array_equal(dec["sel"][0], res["sel"][j])
+        np.testing.assert_allclose(dec["out"][0], res["out"][j], rtol=0, atol=1e-13)
+
+
+def test_chunked_prefill_equals_full_prefill_rows():
+    L, prefix = 768, 512
+    wl, inp = _small_prefill(L=L, budget=64, seed=9)
+    full = _run_oracle(wl, inp, rows=np.arange(prefix, L, 5))
+    kb = bf16_bits(inp["k_idx"])
+    pooled_prefix = O.pool_keys(kb[:prefix], 4)
+    chunk = O.forward_prefill(bf16_bits(inp["q"])[prefix:], bf16_bits(inp["k"]),
+                              bf16_bits(inp["v"]), bf16_bits(inp["q_idx"])[prefix:],
+                              inp["w"].numpy()[prefix:], kb[prefix:], r=4, budget=64,
+                              q_pos0=prefix, k_pooled_prefix_bits=pooled_prefix,
+                              rows=np.arange(0, L - prefix, 5))
+    np.testing.assert_array_equal(chunk["sel"], full["sel"])
+    np.testing.assert_allclose(chunk["out"], full["out"], rtol=0, atol=1e-13)
