@@ -1,0 +1,19 @@
+"""MI355X-native Qwen Sparse Attention (QSA) forward path.
+
+The computation lives in libqsa.so (hand-written HIP kernels for gfx950 behind the C
+ABI of include/qsa.h); this package only builds it and marshals torch tensors to it.
+"""
+from .ops import (  # noqa: F401
+    DecodePlan,
+    PrefillPlan,
+    QSAError,
+    abi_version,
+    qsa_decode_forward,
+    qsa_index_scores,
+    qsa_pool_keys,
+    qsa_prefill_forward,
+    qsa_sparse_attn_decode,
+    qsa_sparse_attn_fwd,
+    qsa_topk_blocks,
+    score_ld,
+)

@@ -1,0 +1,385 @@
+// The C ABI of libqsa (declared in include/qsa.h): argument checking, error
+// reporting, workspace sizing, and the two whole-path drivers. Every check runs
+// on the host before anything is enqueued; nothing here allocates, synchronises
+// or reads device memory.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "qsa.h"
+#include "qsa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qsa_status fail(qsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+qsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return QSA_OK;
+  return fail(QSA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define QSA_REQUIRE(cond, st, ...) \
+  do {                             \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define QSA_TRY(expr)                    \
+  do {                                   \
+    const qsa_status st_ = (expr);       \
+    if (st_ != QSA_OK) return st_;       \
+  } while (0)
+
+qsa_status check_r(int r) {
+  QSA_REQUIRE(r == 4, QSA_ERR_UNSUPPORTED, "micro-block size r=%d: only r=4 is supported", r);
+  return QSA_OK;
+}
+
+qsa_status check_budget(int budget_tokens, int r) {
+  QSA_REQUIRE(budget_tokens > 0 && budget_tokens % r == 0, QSA_ERR_INVALID_ARGUMENT,
+              "budget_tokens=%d must be a positive multiple of r=%d", budget_tokens, r);
+  const int n_sel = budget_tokens / r;
+  QSA_REQUIRE(n_sel >= 4 && n_sel <= 1024, QSA_ERR_UNSUPPORTED,
+              "budget_tokens/r=%d blocks: supported range is 4..1024", n_sel);
+  return QSA_OK;
+}
+
+qsa_status check_indexer_shape(int h_idx, int d_idx) {
+  QSA_REQUIRE(h_idx >= 1 && h_idx <= 4, QSA_ERR_UNSUPPORTED,
+              "indexer heads h_idx=%d: supported 1..4", h_idx);
+  QSA_REQUIRE(d_idx == 64 || d_idx == 128, QSA_ERR_UNSUPPORTED,
+              "indexer dim d_idx=%d: supported 64 or 128", d_idx);
+  return QSA_OK;
+}
+
+qsa_status check_attn_shape(int hq, int hkv, int d) {
+  QSA_REQUIRE(hq > 0 && hkv > 0 && hq % hkv == 0, QSA_ERR_INVALID_ARGUMENT,
+              "hq=%d must be a positive multiple of hkv=%d", hq, hkv);
+  QSA_REQUIRE(hq / hkv <= 16, QSA_ERR_UNSUPPORTED, "heads per KV group %d > 16", hq / hkv);
+  QSA_REQUIRE(d == 128 || d == 256, QSA_ERR_UNSUPPORTED, "head dim d=%d: supported 128 or 256",
+              d);
+  return QSA_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int64_t score_ld(int64_t nblk) { return (nblk + 3) & ~int64_t(3); }
+
+}  // namespace
+
+extern "C" {
+
+int qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+const char* qsa_last_error(void) { return g_err; }
+
+qsa_status qsa_pool_keys(const void* k_idx, int64_t k_idx_row_stride, int64_t n_blocks,
+                         int d_idx, int r, void* k_pooled, int64_t k_pooled_row_stride,
+                         void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_REQUIRE(n_blocks >= 0, QSA_ERR_INVALID_ARGUMENT, "n_blocks=%lld < 0", (long long)n_blocks);
+  QSA_REQUIRE(d_idx > 0 && d_idx % 8 == 0 && d_idx <= 4096, QSA_ERR_UNSUPPORTED,
+              "d_idx=%d must be a multiple of 8 in 8..4096", d_idx);
+  if (n_blocks == 0) return QSA_OK;
+  QSA_REQUIRE(k_idx && k_pooled, QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  QSA_REQUIRE(aligned16(k_idx) && aligned16(k_pooled), QSA_ERR_INVALID_ARGUMENT,
+              "k_idx and k_pooled must be 16-byte aligned");
+  QSA_REQUIRE(k_idx_row_stride >= d_idx && k_idx_row_stride % 8 == 0 &&
+                  k_pooled_row_stride >= d_idx && k_pooled_row_stride % 8 == 0,
+              QSA_ERR_INVALID_ARGUMENT,
+              "row strides (%lld, %lld) must be >= d_idx and multiples of 8 elements",
+              (long long)k_idx_row_stride, (long long)k_pooled_row_stride);
+  return hip_status(
+      qsa::launch_pool_keys(static_cast<const uint16_t*>(k_idx), k_idx_row_stride, n_blocks,
+                            d_idx, r, static_cast<uint16_t*>(k_pooled), k_pooled_row_stride,
+                            static_cast<hipStream_t>(stream)),
+      "qsa_pool_keys launch");
+}
+
+qsa_status qsa_index_scores(int batch, int64_t lq, int h_idx, int d_idx, int r,
+                            const void* q_idx, int64_t q_idx_batch_stride, const float* w,
+                            int64_t w_batch_stride, const void* k_pooled,
+                            int64_t k_pooled_batch_stride, int64_t nblk, int64_t q_pos0,
+                            const int32_t* seq_lens, float* scores, int64_t ld,
+                            int64_t scores_batch_stride, void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_TRY(check_indexer_shape(h_idx, d_idx));
+  QSA_REQUIRE(batch >= 1 && batch <= 65535, QSA_ERR_INVALID_ARGUMENT, "batch=%d", batch);
+  QSA_REQUIRE(lq >= 0 && lq <= ((int64_t)1 << 31) - 64, QSA_ERR_INVALID_ARGUMENT, "lq=%lld",
+              (long long)lq);
+  QSA_REQUIRE(nblk >= 0 && nblk < ((int64_t)1 << 30), QSA_ERR_INVALID_ARGUMENT, "nblk=%lld",
+              (long long)nblk);
+  QSA_REQUIRE(seq_lens || q_pos0 >= 0, QSA_ERR_INVALID_ARGUMENT, "q_pos0=%lld < 0",
+              (long long)q_pos0);
+  QSA_REQUIRE(ld >= nblk && ld % 4 == 0, QSA_ERR_INVALID_ARGUMENT,
+              "ld=%lld must be >= nblk=%lld and a multiple of 4", (long long)ld,
+              (long long)nblk);
+  if (lq == 0 || nblk == 0) return QSA_OK;
+  QSA_REQUIRE(q_idx && w && k_pooled && scores, QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  QSA_REQUIRE(aligned16(q_idx) && aligned16(k_pooled) && aligned16(scores),
+              QSA_ERR_INVALID_ARGUMENT, "q_idx, k_pooled and scores must be 16-byte aligned");
+  if (batch > 1) {
+    QSA_REQUIRE(q_idx_batch_stride % 8 == 0 && k_pooled_batch_stride % 8 == 0 &&
+                    scores_batch_stride % 4 == 0,
+                QSA_ERR_INVALID_ARGUMENT, "batch strides break 16-byte alignment");
+    QSA_REQUIRE(q_idx_batch_stride >= lq * h_idx * d_idx && w_batch_stride >= lq * h_idx &&
+                    k_pooled_batch_stride >= nblk * d_idx && scores_batch_stride >= lq * ld,
+                QSA_ERR_INVALID_ARGUMENT, "batch strides overlap consecutive sequences");
+  }
+  if (!seq_lens) {
+    QSA_REQUIRE((q_pos0 + lq - 1) / r <= nblk + (int64_t)0x7fffffff, QSA_ERR_INVALID_ARGUMENT,
+                "positions overflow");
+  }
+  qsa::ScoreArgs a{static_cast<const uint16_t*>(q_idx), q_idx_batch_stride, w, w_batch_stride,
+                   static_cast<const uint16_t*>(k_pooled), k_pooled_batch_stride, nblk, lq,
+                   h_idx, d_idx, r, q_pos0, seq_lens, scores, ld, scores_batch_stride, batch};
+  return hip_status(qsa::launch_index_scores(a, static_cast<hipStream_t>(stream)),
+                    "qsa_index_scores launch");
+}
+
+size_t qsa_topk_workspace_bytes(int batch, int64_t lq, int64_t nblk, int budget_tokens, int r) {
+  (void)batch; (void)lq; (void)nblk; (void)budget_tokens; (void)r;
+  return 0;
+}
+
+qsa_status qsa_topk_blocks(int batch, int64_t lq, int r, int budget_tokens, const float* scores,
+                           int64_t ld, int64_t scores_batch_stride, int64_t nblk, int64_t q_pos0,
+                           const int32_t* seq_lens, int32_t* sel, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  QSA_TRY(check_r(r));
+  QSA_TRY(check_budget(budget_tokens, r));
+  QSA_REQUIRE(batch >= 1 && batch <= 65535, QSA_ERR_INVALID_ARGUMENT, "batch=%d", batch);
+  QSA_REQUIRE(lq >= 0 && lq <= ((int64_t)1 << 31) - 1, QSA_ERR_INVALID_ARGUMENT, "lq=%lld",
+              (long long)lq);
+  QSA_REQUIRE(nblk >= 0 && nblk < ((int64_t)1 << 30), QSA_ERR_INVALID_ARGUMENT, "nblk=%lld",
+              (long long)nblk);
+  QSA_REQUIRE(seq_lens || q_pos0 >= 0, QSA_ERR_INVALID_ARGUMENT, "q_pos0=%lld < 0",
+              (long long)q_pos0);
+  QSA_REQUIRE(ld >= nblk && ld % 4 == 0, QSA_ERR_INVALID_ARGUMENT,
+              "ld=%lld must be >= nblk and a multiple of 4", (long long)ld);
+  if (lq == 0) return QSA_OK;
+  QSA_REQUIRE(sel && (scores || nblk == 0), QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  QSA_REQUIRE(!scores || aligned16(scores), QSA_ERR_INVALID_ARGUMENT,
+              "scores must be 16-byte aligned");
+  if (batch > 1)
+    QSA_REQUIRE(scores_batch_stride % 4 == 0 && scores_batch_stride >= lq * ld,
+                QSA_ERR_INVALID_ARGUMENT, "scores_batch_stride=%lld",
+                (long long)scores_batch_stride);
+  if (!seq_lens)
+    QSA_REQUIRE((q_pos0 + lq - 1) / r < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT,
+                "positions overflow int32 block ids");
+  qsa::TopkArgs a{scores, ld, scores_batch_stride, lq, nblk, q_pos0, seq_lens, r,
+                  budget_tokens / r, sel, batch};
+  return hip_status(qsa::launch_topk_blocks(a, static_cast<hipStream_t>(stream)),
+                    "qsa_topk_blocks launch");
+}
+
+qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, int r, int n_sel,
+                               const void* q, const void* k, const void* v, const int32_t* sel,
+                               int64_t q_pos0, float softmax_scale, void* out, float* lse,
+                               void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_REQUIRE(n_sel >= 1 && n_sel <= 1024, QSA_ERR_UNSUPPORTED, "n_sel=%d: supported 1..1024",
+              n_sel);
+  QSA_REQUIRE(lq >= 0 && lq < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT, "lq=%lld",
+              (long long)lq);
+  QSA_REQUIRE(q_pos0 >= 0 && q_pos0 + lq <= lk, QSA_ERR_INVALID_ARGUMENT,
+              "query positions [%lld, %lld) must lie inside the %lld keys", (long long)q_pos0,
+              (long long)(q_pos0 + lq), (long long)lk);
+  QSA_REQUIRE(isfinite(softmax_scale), QSA_ERR_INVALID_ARGUMENT, "softmax_scale not finite");
+  if (lq == 0) return QSA_OK;
+  QSA_REQUIRE(q && k && v && sel && out, QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  QSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out),
+              QSA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+  QSA_REQUIRE(lq * hkv / 4 < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT, "grid too large");
+  qsa::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sel = sel;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.lq = lq;
+  a.lk = lk;
+  a.q_pos0 = q_pos0;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.n_sel = n_sel;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return hip_status(qsa::launch_sparse_attn_fwd(a, static_cast<hipStream_t>(stream)),
+                    "qsa_sparse_attn_fwd launch");
+}
+
+size_t qsa_sparse_attn_decode_workspace_bytes(int batch, int hq, int d, int n_sel) {
+  if (batch <= 0 || hq <= 0 || d <= 0 || n_sel <= 0) return 0;
+  const size_t ns = (size_t)qsa::decode_num_splits(n_sel);
+  const size_t slots = (size_t)batch * hq * ns;
+  return align256(slots * d * sizeof(float)) + align256(slots * 2 * sizeof(float));
+}
+
+qsa_status qsa_sparse_attn_decode(int batch, int hq, int hkv, int d, int r, int n_sel,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  int64_t cache_batch_stride, int64_t lmax,
+                                  const int32_t* seq_lens, const int32_t* sel,
+                                  float softmax_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_REQUIRE(n_sel >= 1 && n_sel <= 1024, QSA_ERR_UNSUPPORTED, "n_sel=%d: supported 1..1024",
+              n_sel);
+  QSA_REQUIRE(batch >= 1 && batch <= (1 << 20), QSA_ERR_INVALID_ARGUMENT, "batch=%d", batch);
+  QSA_REQUIRE(lmax >= 1, QSA_ERR_INVALID_ARGUMENT, "lmax=%lld", (long long)lmax);
+  QSA_REQUIRE(isfinite(softmax_scale), QSA_ERR_INVALID_ARGUMENT, "softmax_scale not finite");
+  QSA_REQUIRE(q && k_cache && v_cache && seq_lens && sel && out, QSA_ERR_INVALID_ARGUMENT,
+              "null tensor pointer");
+  QSA_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out),
+              QSA_ERR_INVALID_ARGUMENT, "q, caches and out must be 16-byte aligned");
+  QSA_REQUIRE(batch == 1 || (cache_batch_stride % 8 == 0 &&
+                             cache_batch_stride >= lmax * (int64_t)hkv * d),
+              QSA_ERR_INVALID_ARGUMENT, "cache_batch_stride=%lld", (long long)cache_batch_stride);
+  const size_t need = qsa_sparse_attn_decode_workspace_bytes(batch, hq, d, n_sel);
+  QSA_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), QSA_ERR_WORKSPACE,
+              "decode workspace: need %zu bytes (16-byte aligned), got %zu", need,
+              workspace_bytes);
+  const int ns = qsa::decode_num_splits(n_sel);
+  const size_t slots = (size_t)batch * hq * ns;
+  qsa::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.sel = sel;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.lq = batch;
+  a.lk = lmax;
+  a.seq_lens = seq_lens;
+  a.cache_bs = cache_batch_stride;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.n_sel = n_sel;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align256(slots * d * sizeof(float)));
+  a.n_split = ns;
+  a.steps_per_split = qsa::decode_steps_per_split(n_sel);
+  return hip_status(qsa::launch_sparse_attn_decode(a, static_cast<hipStream_t>(stream)),
+                    "qsa_sparse_attn_decode launch");
+}
+
+// ---- whole prefill path ----
+
+size_t qsa_prefill_workspace_bytes(int64_t lq, int64_t lk, int r, int64_t row_chunk) {
+  if (lq <= 0 || lk <= 0 || r <= 0) return 0;
+  const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
+  return align256((size_t)rc * (size_t)score_ld(lk / r) * sizeof(float));
+}
+
+qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, int hkv, int d,
+                               int h_idx, int d_idx, int r, int budget_tokens, const void* q,
+                               const void* k, const void* v, const void* q_idx, const float* w,
+                               const void* k_idx, int64_t first_raw_token,
+                               const void* k_pooled_prefix, void* k_pooled, float softmax_scale,
+                               int32_t* sel, void* out, float* lse, int64_t row_chunk,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_TRY(check_budget(budget_tokens, r));
+  QSA_TRY(check_indexer_shape(h_idx, d_idx));
+  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_REQUIRE(first_raw_token >= 0 && first_raw_token % r == 0 && first_raw_token <= lk,
+              QSA_ERR_INVALID_ARGUMENT, "first_raw_token=%lld must be a multiple of r in [0, lk]",
+              (long long)first_raw_token);
+  QSA_REQUIRE(first_raw_token == 0 || k_pooled_prefix, QSA_ERR_INVALID_ARGUMENT,
+              "k_pooled_prefix is required when first_raw_token > 0");
+  QSA_REQUIRE(k_pooled && (k_idx || first_raw_token / r == lk / r), QSA_ERR_INVALID_ARGUMENT,
+              "null k_pooled or k_idx");
+  const int64_t nblk = lk / r;
+  const int64_t prefix_blocks = first_raw_token / r;
+  const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
+  const size_t need = qsa_prefill_workspace_bytes(lq, lk, r, row_chunk);
+  QSA_REQUIRE(lq == 0 || (workspace && workspace_bytes >= need && aligned16(workspace)),
+              QSA_ERR_WORKSPACE, "prefill workspace: need %zu bytes (16-byte aligned), got %zu",
+              need, workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (prefix_blocks > 0 && k_pooled_prefix != k_pooled) {
+    QSA_TRY(hip_status(hipMemcpyAsync(k_pooled, k_pooled_prefix,
+                                      (size_t)prefix_blocks * d_idx * sizeof(uint16_t),
+                                      hipMemcpyDeviceToDevice, s),
+                       "copy of the pooled prefix"));
+  }
+  const int64_t new_blocks = nblk - prefix_blocks;
+  if (new_blocks > 0)
+    QSA_TRY(qsa_pool_keys(k_idx, d_idx, new_blocks, d_idx, r,
+                          static_cast<uint16_t*>(k_pooled) + prefix_blocks * d_idx, d_idx,
+                          stream));
+  if (lq == 0) return QSA_OK;
+  const int64_t ld = score_ld(nblk);
+  float* sc = static_cast<float*>(workspace);
+  const int n_sel = budget_tokens / r;
+  for (int64_t c0 = 0; c0 < lq; c0 += rc) {
+    const int64_t n = (lq - c0) < rc ? (lq - c0) : rc;
+    QSA_TRY(qsa_index_scores(1, n, h_idx, d_idx, r,
+                             static_cast<const uint16_t*>(q_idx) + c0 * h_idx * d_idx, 0,
+                             w + c0 * h_idx, 0, k_pooled, 0, nblk, q_pos0 + c0, nullptr, sc, ld,
+                             0, stream));
+    QSA_TRY(qsa_topk_blocks(1, n, r, budget_tokens, sc, ld, 0, nblk, q_pos0 + c0, nullptr,
+                            sel + c0 * n_sel, nullptr, 0, stream));
+  }
+  return qsa_sparse_attn_fwd(lq, lk, hq, hkv, d, r, n_sel, q, k, v, sel, q_pos0, softmax_scale,
+                             out, lse, stream);
+}
+
+// ---- whole decode step ----
+
+size_t qsa_decode_workspace_bytes(int batch, int hq, int d, int64_t lmax, int r,
+                                  int budget_tokens) {
+  if (batch <= 0 || r <= 0 || budget_tokens <= 0) return 0;
+  const size_t sc = align256((size_t)batch * (size_t)score_ld(lmax / r) * sizeof(float));
+  return sc + qsa_sparse_attn_decode_workspace_bytes(batch, hq, d, budget_tokens / r);
+}
+
+qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int d_idx, int r,
+                              int budget_tokens, const void* q, const void* q_idx,
+                              const float* w, const void* k_pooled,
+                              int64_t k_pooled_batch_stride, const void* k_cache,
+                              const void* v_cache, int64_t cache_batch_stride, int64_t lmax,
+                              const int32_t* seq_lens, float softmax_scale, int32_t* sel,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_TRY(check_budget(budget_tokens, r));
+  QSA_REQUIRE(batch >= 1, QSA_ERR_INVALID_ARGUMENT, "batch=%d", batch);
+  const size_t need = qsa_decode_workspace_bytes(batch, hq, d, lmax, r, budget_tokens);
+  QSA_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), QSA_ERR_WORKSPACE,
+              "decode workspace: need %zu bytes (16-byte aligned), got %zu", need,
+              workspace_bytes);
+  const int64_t nblk = lmax / r;
+  const int64_t ld = score_ld(nblk);
+  float* sc = static_cast<float*>(workspace);
+  const size_t sc_bytes = align256((size_t)batch * (size_t)ld * sizeof(float));
+  QSA_TRY(qsa_index_scores(batch, 1, h_idx, d_idx, r, q_idx, (int64_t)h_idx * d_idx, w, h_idx,
+                           k_pooled, k_pooled_batch_stride, nblk, 0, seq_lens, sc, ld, ld,
+                           stream));
+  QSA_TRY(qsa_topk_blocks(batch, 1, r, budget_tokens, sc, ld, ld, nblk, 0, seq_lens, sel,
+                          nullptr, 0, stream));
+  return qsa_sparse_attn_decode(batch, hq, hkv, d, r, budget_tokens / r, q, k_cache, v_cache,
+                                cache_batch_stride, lmax, seq_lens, sel, softmax_scale, out, lse,
+                                static_cast<char*>(workspace) + sc_bytes,
+                                workspace_bytes - sc_bytes, stream);
+}
+
+}  // extern "C"

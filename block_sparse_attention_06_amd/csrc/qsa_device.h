@@ -1,0 +1,70 @@
+// Device-side helpers shared by the QSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Two fp32 values to a packed pair of bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
+// Lane l holds A row (l % 16) and B column (l % 16), k = 8*(l/16) + [0..7];
+// D column (l % 16), rows 4*(l/16) + [0..3].
+__device__ __forceinline__ f32x4 mfma_16x16x32(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x16_bf16: D[16x16] += A[16x16] * B[16x16].
+// Lane l holds A row (l % 16) and B column (l % 16), k = 4*(l/16) + [0..3];
+// D column (l % 16), rows 4*(l/16) + [0..3].
+__device__ __forceinline__ f32x4 mfma_16x16x16(const uint2& a, const uint2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Order-preserving map of a finite fp32 to uint32 (larger float -> larger key),
+// with -0.0 folded onto +0.0 so that the two compare equal.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_xor_max(float x, int mask) {
+  return fmaxf(x, __shfl_xor(x, mask, kWave));
+}
+
+__device__ __forceinline__ float wave_xor_sum(float x, int mask) {
+  return x + __shfl_xor(x, mask, kWave);
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed data that will not be reused soon).
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+}  // namespace qsa

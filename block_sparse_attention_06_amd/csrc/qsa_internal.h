@@ -1,0 +1,83 @@
+// Host-side internals of libqsa: launchers (no argument checking; the C ABI layer
+// validates before calling them) and the shared tuning constants.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+// ---- stage 1 ----
+hipError_t launch_pool_keys(const uint16_t* k_idx, int64_t k_stride, int64_t n_blocks, int d_idx,
+                            int r, uint16_t* k_pooled, int64_t p_stride, hipStream_t stream);
+
+// ---- stage 2 ----
+struct ScoreArgs {
+  const uint16_t* q_idx;
+  int64_t q_bs;
+  const float* w;
+  int64_t w_bs;
+  const uint16_t* kp;
+  int64_t kp_bs;
+  int64_t nblk;
+  int64_t lq;
+  int h_idx;
+  int d_idx;
+  int r;
+  int64_t q_pos0;
+  const int32_t* seq_lens;
+  float* scores;
+  int64_t ld;
+  int64_t s_bs;
+  int batch;
+};
+hipError_t launch_index_scores(const ScoreArgs& a, hipStream_t stream);
+
+// ---- stage 3 ----
+struct TopkArgs {
+  const float* scores;
+  int64_t ld;
+  int64_t s_bs;
+  int64_t lq;
+  int64_t nblk;
+  int64_t q_pos0;
+  const int32_t* seq_lens;
+  int r;
+  int n_sel;
+  int32_t* sel;
+  int batch;
+};
+hipError_t launch_topk_blocks(const TopkArgs& a, hipStream_t stream);
+
+// ---- stage 4 / 4' ----
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* sel;
+  uint16_t* out;
+  float* lse;
+  int64_t lq;       // prefill: query rows; decode: batch
+  int64_t lk;       // prefill: keys; decode: cache capacity per sequence
+  int64_t q_pos0;   // prefill only
+  const int32_t* seq_lens;  // decode only
+  int64_t cache_bs;         // decode only: elements between sequences of the caches
+  int hq;
+  int hkv;
+  int d;
+  int n_sel;
+  float scale_log2;  // softmax scale * log2(e)
+  // decode split-KV partials
+  float* part_o;     // [batch][hq][n_split][d]
+  float* part_ml;    // [batch][hq][n_split][2]
+  int n_split;
+  int steps_per_split;
+};
+hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream);
+
+// Decode split heuristic: number of 4-block steps per split for a given n_sel.
+int decode_steps_per_split(int n_sel);
+int decode_num_splits(int n_sel);
+
+}  // namespace qsa

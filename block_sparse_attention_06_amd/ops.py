@@ -1,0 +1,271 @@
+"""Python binding of libqsa: argument marshalling only.
+
+Each function has the name of the C entry point it calls (include/qsa.h), takes torch
+tensors already on the GPU, allocates outputs and workspaces with torch, and enqueues
+the call on torch's current stream. Every step of the computation runs in the HIP
+library; nothing here computes, and there is no fallback when the library is absent.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+QSA_OK = 0
+
+
+class QSAError(RuntimeError):
+    """A libqsa entry point returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+def _call(name: str, *args) -> None:
+    lib = _lib.load()
+    st = getattr(lib, name)(*args)
+    if st != QSA_OK:
+        raise QSAError(name, st, lib.qsa_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (the QSA path has no CPU implementation)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def score_ld(nblk: int) -> int:
+    return (nblk + 3) // 4 * 4
+
+
+def abi_version() -> int:
+    return _lib.load().qsa_abi_version()
+
+
+# ------------------------------------------------------------------------------------
+# Stages
+# ------------------------------------------------------------------------------------
+
+
+def qsa_pool_keys(k_idx: torch.Tensor, r: int = 4, out: Optional[torch.Tensor] = None):
+    """Mean-pool [n_tok, d_I] bf16 indexer keys into [n_tok // r, d_I] (complete blocks)."""
+    _need(k_idx, "k_idx", torch.bfloat16, contiguous=False)
+    if k_idx.dim() != 2 or k_idx.stride(1) != 1:
+        raise ValueError("k_idx must be [n_tokens, d_idx] with unit column stride")
+    nb, d_i = k_idx.shape[0] // r, k_idx.shape[1]
+    if out is None:
+        out = torch.empty((nb, d_i), dtype=torch.bfloat16, device=k_idx.device)
+    _need(out, "out", torch.bfloat16, k_idx.device, contiguous=False)
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] < nb or out.shape[1] != d_i:
+        raise ValueError("out must be [>= n_tokens // r, d_idx] with unit column stride")
+    _call("qsa_pool_keys", _ptr(k_idx), k_idx.stride(0), nb, d_i, r, _ptr(out), out.stride(0),
+          _stream(k_idx))
+    return out
+
+
+def qsa_index_scores(q_idx: torch.Tensor, w: torch.Tensor, k_pooled: torch.Tensor, *,
+                     q_pos0: int = 0, seq_lens: Optional[torch.Tensor] = None, r: int = 4,
+                     nblk: Optional[int] = None, out: Optional[torch.Tensor] = None):
+    """Block scores. Unbatched: q_idx [Lq,H,dI], w [Lq,H], k_pooled [nblk,dI] -> [Lq, ld].
+    Batched: q_idx [B,Lq,H,dI], w [B,Lq,H], k_pooled [B,nblk,dI] -> [B, Lq, ld]."""
+    batched = q_idx.dim() == 4
+    qb = q_idx if batched else q_idx.unsqueeze(0)
+    wb = w if batched else w.unsqueeze(0)
+    kb = k_pooled if batched else k_pooled.unsqueeze(0)
+    _need(qb, "q_idx", torch.bfloat16)
+    _need(wb, "w", torch.float32, qb.device)
+    _need(kb, "k_pooled", torch.bfloat16, qb.device)
+    bsz, lq, h, di = qb.shape
+    nblk = kb.shape[1] if nblk is None else nblk
+    if nblk > kb.shape[1] or kb.shape[0] != bsz or wb.shape != (bsz, lq, h):
+        raise ValueError("inconsistent shapes")
+    ld = score_ld(nblk)
+    if out is None:
+        out = torch.empty((bsz, lq, ld), dtype=torch.float32, device=qb.device)
+    ob = out if out.dim() == 3 else out.unsqueeze(0)
+    _need(ob, "out", torch.float32, qb.device)
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", torch.int32, qb.device)
+    _call("qsa_index_scores", bsz, lq, h, di, r, _ptr(qb), qb.stride(0), _ptr(wb), wb.stride(0),
+          _ptr(kb), kb.stride(0), nblk, q_pos0, _ptr(seq_lens), _ptr(ob), ob.shape[2],
+          ob.stride(0), _stream(qb))
+    return out if batched or out.dim() == 2 else out[0]
+
+
+def qsa_topk_blocks(scores: torch.Tensor, *, lq: int, nblk: int, budget: int, q_pos0: int = 0,
+                    seq_lens: Optional[torch.Tensor] = None, r: int = 4,
+                    out: Optional[torch.Tensor] = None):
+    """Kept block ids per query row: scores [Lq, ld] or [B, Lq, ld] -> int32 [(B,) Lq, budget/r]."""
+    batched = scores.dim() == 3
+    sb = scores if batched else scores.unsqueeze(0)
+    _need(sb, "scores", torch.float32)
+    bsz = sb.shape[0]
+    n_sel = budget // r
+    if out is None:
+        out = torch.empty((bsz, lq, n_sel), dtype=torch.int32, device=sb.device)
+    _need(out, "out", torch.int32, sb.device)
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", torch.int32, sb.device)
+    ws_bytes = _lib.load().qsa_topk_workspace_bytes(bsz, lq, nblk, budget, r)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=sb.device) if ws_bytes else None
+    _call("qsa_topk_blocks", bsz, lq, r, budget, _ptr(sb), sb.shape[2], sb.stride(0), nblk,
+          q_pos0, _ptr(seq_lens), _ptr(out), _ptr(ws), ws_bytes, _stream(sb))
+    return out if batched else out.view(lq, n_sel)
+
+
+def qsa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor, *,
+                        q_pos0: int = 0, scale: Optional[float] = None, r: int = 4,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        want_lse: bool = True):
+    """Prefill attention over the kept tokens. q [Lq,Hq,d], k/v [Lk,Hkv,d], sel [Lq,n_sel]."""
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, q.device)
+    _need(v, "v", torch.bfloat16, q.device)
+    _need(sel, "sel", torch.int32, q.device)
+    lq, hq, d = q.shape
+    lk, hkv, _ = k.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((lq, hq), dtype=torch.float32, device=q.device)
+    _call("qsa_sparse_attn_fwd", lq, lk, hq, hkv, d, r, sel.shape[1], _ptr(q), _ptr(k), _ptr(v),
+          _ptr(sel), q_pos0, scale, _ptr(out), _ptr(lse), _stream(q))
+    return out, lse
+
+
+def qsa_sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           seq_lens: torch.Tensor, sel: torch.Tensor, *,
+                           scale: Optional[float] = None, r: int = 4):
+    """Decode attention: q [B,Hq,d], caches [B,Lmax,Hkv,d], seq_lens [B], sel [B,n_sel]."""
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, q.device)
+    _need(v_cache, "v_cache", torch.bfloat16, q.device)
+    _need(seq_lens, "seq_lens", torch.int32, q.device)
+    _need(sel, "sel", torch.int32, q.device)
+    bsz, hq, d = q.shape
+    _, lmax, hkv, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    n_sel = sel.shape[-1]
+    out = torch.empty_like(q)
+    lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
+    ws_bytes = _lib.load().qsa_sparse_attn_decode_workspace_bytes(bsz, hq, d, n_sel)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _call("qsa_sparse_attn_decode", bsz, hq, hkv, d, r, n_sel, _ptr(q), _ptr(k_cache),
+          _ptr(v_cache), k_cache.stride(0), lmax, _ptr(seq_lens), _ptr(sel), scale, _ptr(out),
+          _ptr(lse), _ptr(ws), ws_bytes, _stream(q))
+    return out, lse
+
+
+# ------------------------------------------------------------------------------------
+# Whole paths
+# ------------------------------------------------------------------------------------
+
+
+class PrefillPlan:
+    """Preallocated outputs and workspace for repeated prefill calls of one shape."""
+
+    def __init__(self, lq, lk, hq, hkv, d, h_idx, d_idx, budget, *, r=4, row_chunk=4096,
+                 device="cuda"):
+        self.shape = (lq, lk, hq, hkv, d, h_idx, d_idx, budget, r)
+        self.row_chunk = row_chunk
+        dev = torch.device(device)
+        self.sel = torch.empty((lq, budget // r), dtype=torch.int32, device=dev)
+        self.out = torch.empty((lq, hq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((lq, hq), dtype=torch.float32, device=dev)
+        self.k_pooled = torch.empty((lk // r, d_idx), dtype=torch.bfloat16, device=dev)
+        nbytes = _lib.load().qsa_prefill_workspace_bytes(lq, lk, r, row_chunk)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        self.ws_bytes = nbytes
+
+
+def qsa_prefill_forward(q, k, v, q_idx, w, k_idx, *, budget: int, q_pos0: int = 0,
+                        k_pooled_prefix: Optional[torch.Tensor] = None,
+                        scale: Optional[float] = None, r: int = 4, row_chunk: int = 4096,
+                        plan: Optional[PrefillPlan] = None):
+    """Whole prefill: pool the new blocks, score + top-k in row chunks, attention.
+
+    q [Lq,Hq,d], k/v [Lk,Hkv,d], q_idx [Lq,H_I,d_I], w [Lq,H_I]; k_idx holds the raw
+    indexer keys of tokens P*r .. Lk-1 where P = rows of k_pooled_prefix (or 0).
+    Returns (out, lse, sel, k_pooled).
+    """
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("q_idx", q_idx, torch.bfloat16),
+                        ("w", w, torch.float32), ("k_idx", k_idx, torch.bfloat16)):
+        _need(t, name, dt, q.device)
+    lq, hq, d = q.shape
+    lk, hkv, _ = k.shape
+    _, h_idx, d_idx = q_idx.shape
+    prefix_blocks = 0 if k_pooled_prefix is None else k_pooled_prefix.shape[0]
+    if k_pooled_prefix is not None:
+        _need(k_pooled_prefix, "k_pooled_prefix", torch.bfloat16, q.device)
+    if k_idx.shape[0] != lk - prefix_blocks * r:
+        raise ValueError("k_idx must hold the indexer keys of every token after the prefix")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if plan is None:
+        plan = PrefillPlan(lq, lk, hq, hkv, d, h_idx, d_idx, budget, r=r, row_chunk=row_chunk,
+                           device=q.device)
+    _call("qsa_prefill_forward", lq, lk, q_pos0, hq, hkv, d, h_idx, d_idx, r, budget, _ptr(q),
+          _ptr(k), _ptr(v), _ptr(q_idx), _ptr(w), _ptr(k_idx), prefix_blocks * r,
+          _ptr(k_pooled_prefix), _ptr(plan.k_pooled), scale, _ptr(plan.sel), _ptr(plan.out),
+          _ptr(plan.lse), plan.row_chunk, _ptr(plan.ws), plan.ws_bytes, _stream(q))
+    return plan.out, plan.lse, plan.sel, plan.k_pooled
+
+
+class DecodePlan:
+    """Preallocated outputs and workspace for repeated decode steps of one shape."""
+
+    def __init__(self, batch, hq, d, lmax, budget, *, r=4, device="cuda"):
+        dev = torch.device(device)
+        self.sel = torch.empty((batch, budget // r), dtype=torch.int32, device=dev)
+        self.out = torch.empty((batch, hq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+        nbytes = _lib.load().qsa_decode_workspace_bytes(batch, hq, d, lmax, r, budget)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        self.ws_bytes = nbytes
+
+
+def qsa_decode_forward(q, q_idx, w, k_pooled, k_cache, v_cache, seq_lens, *, budget: int,
+                       scale: Optional[float] = None, r: int = 4,
+                       plan: Optional[DecodePlan] = None):
+    """Whole decode step. q [B,Hq,d], q_idx [B,H_I,d_I] (or [B,1,H_I,d_I]), w [B,H_I],
+    k_pooled [B,Lmax/r,d_I], caches [B,Lmax,Hkv,d], seq_lens [B] int32.
+    Returns (out, lse, sel)."""
+    q_idx = q_idx.reshape(q_idx.shape[0], q_idx.shape[-2], q_idx.shape[-1])
+    w = w.reshape(w.shape[0], w.shape[-1])
+    for name, t, dt in (("q", q, torch.bfloat16), ("q_idx", q_idx, torch.bfloat16),
+                        ("w", w, torch.float32), ("k_pooled", k_pooled, torch.bfloat16),
+                        ("k_cache", k_cache, torch.bfloat16), ("v_cache", v_cache, torch.bfloat16),
+                        ("seq_lens", seq_lens, torch.int32)):
+        _need(t, name, dt, q.device)
+    bsz, hq, d = q.shape
+    _, lmax, hkv, _ = k_cache.shape
+    _, h_idx, d_idx = q_idx.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if plan is None:
+        plan = DecodePlan(bsz, hq, d, lmax, budget, r=r, device=q.device)
+    _call("qsa_decode_forward", bsz, hq, hkv, d, h_idx, d_idx, r, budget, _ptr(q), _ptr(q_idx),
+          _ptr(w), _ptr(k_pooled), k_pooled.stride(0), _ptr(k_cache), _ptr(v_cache),
+          k_cache.stride(0), lmax, _ptr(seq_lens), scale, _ptr(plan.sel), _ptr(plan.out),
+          _ptr(plan.lse), _ptr(plan.ws), plan.ws_bytes, _stream(q))
+    return plan.out, plan.lse, plan.sel

@@ -1,0 +1,194 @@
+/*
+ * qsa.h -- C ABI of the Qwen Sparse Attention (QSA) forward path on MI355X (gfx950).
+ *
+ * QSA keeps exact softmax attention but reads only part of the context: a light
+ * indexer scores micro-blocks of r = 4 tokens from mean-pooled keys and keeps the
+ * best blocks up to a token budget; attention then reads only the kept tokens.
+ * Sources, cited by page title and section:
+ *   [DR] "On the Design of Qwen3.8-Next Architecture" (summary page), "four
+ *        architecture components", item 2 "Qwen Sparse Attention (QSA)":
+ *        micro-blocks of r=4, keys mean-pooled, 4 MQA indexer heads, K=2048,
+ *        DeepSeek-DSA-style light indexer + top-k.
+ *   [MR] "Qwen3.8-Flash-Next" (Miles RL recipe), section 1 "Model Introduction":
+ *        each layer projects indexer queries and compressed keys, scores them,
+ *        keeps indexer_budget key tokens per query, attention reads only those;
+ *        selection rows are built outside the attention kernel; 24 heads,
+ *        2 query groups, kv-channels 256.
+ *   [MR5] same page, section 5.3 "Rollout & SGLang": packed THD tensors.
+ *   [RA] release article "Qwen3.8-Flash-Next开源", section "GDN+QSA".
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers; bf16 tensors are passed as void* and
+ *     hold IEEE bfloat16 bit patterns. Strides are in ELEMENTS. Every pointer to a
+ *     bf16 or fp32 tensor must be 16-byte aligned, as must every row stride times
+ *     the element size where a stride is taken.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues
+ *     work on it and returns; nothing is synchronised, no device memory is read on
+ *     the host, and the library allocates nothing: the caller owns every input,
+ *     output and workspace buffer. Calls are thread-safe.
+ *   - Errors detectable on the host (null pointers, shapes, alignment, unsupported
+ *     sizes, short workspace) return a non-zero qsa_status BEFORE any launch, and
+ *     qsa_last_error() then describes it (thread-local text). A failed launch
+ *     returns QSA_ERR_HIP. Faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - Supported sizes: r = 4; attention head dim d in {128, 256}; heads per KV
+ *     group Hq/Hkv in 1..16; indexer heads H_I in 1..4 with dim d_I in {64, 128};
+ *     budget K a multiple of r with 4 <= K/r <= 1024.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+
+typedef enum qsa_status {
+  QSA_OK = 0,
+  QSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad shape, stride or alignment */
+  QSA_ERR_UNSUPPORTED = 2,      /* a size outside the supported set above */
+  QSA_ERR_WORKSPACE = 3,        /* workspace null or smaller than the query says */
+  QSA_ERR_HIP = 4               /* a HIP launch failed; the message names the error */
+} qsa_status;
+
+/* Version of this ABI (QSA_ABI_VERSION of the built library). */
+int qsa_abi_version(void);
+
+/* Text describing the last non-OK status returned on the calling thread ("" if none). */
+const char* qsa_last_error(void);
+
+/*
+ * Stage 1 -- micro-block mean pooling of the indexer keys [DR].
+ * kbar[b][c] = bf16( (k_idx[r*b][c] + ... + k_idx[r*b+r-1][c]) / r ), b < n_blocks,
+ * accumulated in fp32 and rounded once to nearest even. Only complete blocks are
+ * passed: the caller points k_idx at the first token of the first block to pool and
+ * k_pooled at that block's row. No positional encoding is added here; a caller that
+ * wants one applies it to k_pooled afterwards.
+ *   k_idx     bf16 [r*n_blocks rows][d_idx], row i at k_idx + i*k_idx_row_stride
+ *   k_pooled  bf16 [n_blocks][d_idx],        row b at k_pooled + b*k_pooled_row_stride
+ */
+qsa_status qsa_pool_keys(const void* k_idx, int64_t k_idx_row_stride, int64_t n_blocks,
+                         int d_idx, int r, void* k_pooled, int64_t k_pooled_row_stride,
+                         void* stream);
+
+/*
+ * Stage 2 -- light MQA indexer block scores [DR], [RA] (DSA-style reading):
+ *   s[t][b] = sum_{h < h_idx} w[t][h] * max(0, q_idx[t][h] . kbar[b])
+ * for every block b < min(pos(t) / r, nblk), i.e. every complete block strictly
+ * before the query's own block. Entries at b >= pos(t)/r are left unwritten.
+ * Query row i of sequence s sits at position pos = q_pos0 + i when seq_lens is NULL,
+ * else at pos = seq_lens[s] - lq + i (seq_lens is a device array of `batch` int32;
+ * rows with pos < 0 score nothing).
+ *   q_idx    bf16 [batch][lq][h_idx][d_idx], sequence s at q_idx + s*q_idx_batch_stride
+ *   w        fp32 [batch][lq][h_idx],        sequence s at w + s*w_batch_stride
+ *   k_pooled bf16 [batch][nblk][d_idx],      sequence s at k_pooled + s*k_pooled_batch_stride
+ *   scores   fp32 [batch][lq][ld], ld >= nblk and ld % 4 == 0,
+ *            sequence s at scores + s*scores_batch_stride
+ */
+qsa_status qsa_index_scores(int batch, int64_t lq, int h_idx, int d_idx, int r,
+                            const void* q_idx, int64_t q_idx_batch_stride,
+                            const float* w, int64_t w_batch_stride,
+                            const void* k_pooled, int64_t k_pooled_batch_stride, int64_t nblk,
+                            int64_t q_pos0, const int32_t* seq_lens,
+                            float* scores, int64_t ld, int64_t scores_batch_stride,
+                            void* stream);
+
+/*
+ * Stage 3 -- block top-k under the token budget [MR], [DR].
+ * For each query row (positions as in stage 2) with own block o = pos / r and
+ * C = min(o, nblk) candidate blocks 0..C-1: keep the m = min(K/r - 1, C) best
+ * candidates ranked by score (descending, -0.0 == +0.0) then block id (ascending),
+ * plus the own block o. Output row: the kept ids in ascending order (o last),
+ * then -1 up to K/r entries. Exact; no host round trip. Scores must be finite.
+ *   scores  fp32 as written by stage 2
+ *   sel     int32 [batch][lq][K/r], contiguous
+ *   workspace: qsa_topk_workspace_bytes() bytes (0 today; may be NULL).
+ */
+size_t qsa_topk_workspace_bytes(int batch, int64_t lq, int64_t nblk, int budget_tokens, int r);
+qsa_status qsa_topk_blocks(int batch, int64_t lq, int r, int budget_tokens,
+                           const float* scores, int64_t ld, int64_t scores_batch_stride,
+                           int64_t nblk, int64_t q_pos0, const int32_t* seq_lens,
+                           int32_t* sel, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Stage 4 -- exact softmax attention over the kept tokens, prefill [MR], [MR5].
+ * For query row i at t = q_pos0 + i and head h (KV group g = h / (hq/hkv)):
+ *   J = { j : j/r is a kept block of row i, j <= t, j < lk }
+ *   out[i][h] = sum_{j in J} softmax_j(scale * q[i][h] . k[j][g]) v[j][g]
+ *   lse[i][h] = ln sum_{j in J} exp(scale * q[i][h] . k[j][g])
+ * The kernel needs no causal or segment logic beyond masking j > t in the own block.
+ *   q    bf16 [lq][hq][d] (THD), k/v bf16 [lk][hkv][d] (THD), contiguous
+ *   sel  int32 [lq][n_sel] as written by stage 3 (ascending ids, -1 padded)
+ *   out  bf16 [lq][hq][d]; lse fp32 [lq][hq] or NULL
+ */
+qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, int r, int n_sel,
+                               const void* q, const void* k, const void* v,
+                               const int32_t* sel, int64_t q_pos0, float softmax_scale,
+                               void* out, float* lse, void* stream);
+
+/*
+ * Stage 4' -- decode: one new query token per sequence at t = seq_lens[s] - 1, the
+ * same attention as stage 4 over a KV cache, split over the kept blocks into
+ * partial softmax states that a second kernel combines.
+ *   q        bf16 [batch][hq][d]
+ *   k_cache, v_cache bf16 [batch][lmax][hkv][d], sequence s at +s*cache_batch_stride
+ *   seq_lens int32 [batch] on the device, 1 <= seq_lens[s] <= lmax
+ *   sel      int32 [batch][n_sel]
+ *   out      bf16 [batch][hq][d]; lse fp32 [batch][hq] or NULL
+ *   workspace: qsa_sparse_attn_decode_workspace_bytes() bytes
+ */
+size_t qsa_sparse_attn_decode_workspace_bytes(int batch, int hq, int d, int n_sel);
+qsa_status qsa_sparse_attn_decode(int batch, int hq, int hkv, int d, int r, int n_sel,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  int64_t cache_batch_stride, int64_t lmax,
+                                  const int32_t* seq_lens, const int32_t* sel,
+                                  float softmax_scale, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Whole prefill path: pool the new blocks, then for query rows in chunks of
+ * `row_chunk` score + top-k, then attention over all rows. Inputs as in stages 1-4;
+ * k_idx holds the raw indexer keys of tokens first_raw_token .. lk-1 (tokens before
+ * it are covered by k_pooled_prefix, prefix_blocks = first_raw_token / r rows, which
+ * may be NULL when first_raw_token == 0). k_pooled (output, [lk/r][d_idx]) receives
+ * the prefix rows copied and the new rows pooled. sel [lq][K/r] is an output too.
+ * workspace: qsa_prefill_workspace_bytes() bytes (score chunk buffer).
+ */
+size_t qsa_prefill_workspace_bytes(int64_t lq, int64_t lk, int r, int64_t row_chunk);
+qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, int hkv, int d,
+                               int h_idx, int d_idx, int r, int budget_tokens,
+                               const void* q, const void* k, const void* v,
+                               const void* q_idx, const float* w,
+                               const void* k_idx, int64_t first_raw_token,
+                               const void* k_pooled_prefix, void* k_pooled,
+                               float softmax_scale, int32_t* sel, void* out, float* lse,
+                               int64_t row_chunk, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * Whole decode step for `batch` sequences: scores against the pooled-key cache,
+ * top-k, split attention and combine. Inputs as in stages 2-4'; q_idx
+ * [batch][h_idx][d_idx], w [batch][h_idx], k_pooled [batch][lmax/r][d_idx]
+ * (sequence s at + s*k_pooled_batch_stride). sel [batch][K/r] is an output.
+ */
+size_t qsa_decode_workspace_bytes(int batch, int hq, int d, int64_t lmax, int r,
+                                  int budget_tokens);
+qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int d_idx, int r,
+                              int budget_tokens, const void* q, const void* q_idx,
+                              const float* w, const void* k_pooled,
+                              int64_t k_pooled_batch_stride, const void* k_cache,
+                              const void* v_cache, int64_t cache_batch_stride, int64_t lmax,
+                              const int32_t* seq_lens, float softmax_scale, int32_t* sel,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,403 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on an MI355X.
+
+Small cases compare every element; the full-size workloads run in the launch
+configuration of bench.py and compare sampled rows the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_06_amd as Q
+from oracle import qsa_oracle as O
+from parity import bits, check_selection_row, compare_output, LSE_ABS
+from synth import generate, workload
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _randn_bf16(shape, seed, scale=1.0):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=DEV) * scale).to(torch.bfloat16)
+
+
+def _random_selection(rows_t, n_sel, r, seed, nblk_cap=None):
+    """Valid selections (ascending, own last, -1 padded) with random earlier blocks."""
+    rng = np.random.default_rng(seed)
+    sel = np.full((len(rows_t), n_sel), -1, dtype=np.int32)
+    for i, t in enumerate(rows_t):
+        own = int(t) // r
+        cand = own if nblk_cap is None else min(own, nblk_cap)
+        m = min(n_sel - 1, cand)
+        pick = np.sort(rng.choice(cand, size=m, replace=False)) if m else np.zeros(0, int)
+        sel[i, :m] = pick
+        sel[i, m] = own
+    return sel
+
+
+# ------------------------------------------------------------------------------------
+# Stage 1: pooling (bit-exact)
+# ------------------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n_tok,d_i,row_stride", [(2048, 64, 64), (4 * 1000 + 3, 128, 128),
+                                                  (8, 128, 256), (4 * 777, 128, 136)])
+def test_pool_keys_bit_exact(n_tok, d_i, row_stride):
+    _say(f"pool n_tok={n_tok} d_i={d_i} stride={row_stride}")
+    base = _randn_bf16((n_tok, row_stride), seed=n_tok, scale=1 / math.sqrt(d_i))
+    k = base[:, :d_i]
+    out = Q.qsa_pool_keys(k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out), O.pool_keys(bits(k), 4))
+
+
+# ------------------------------------------------------------------------------------
+# Stage 2: scores
+# ------------------------------------------------------------------------------------
+
+
+def _score_bound(q, w, kp):
+    """Magnitude of the summed terms (for the fp32-accumulation tolerance)."""
+    tot = 0
+    for h in range(q.shape[1]):
+        tot = tot + np.abs(w[:, h : h + 1]) * (np.abs(q[:, h, :]) @ np.abs(kp).T)
+    return tot
+
+
+@pytest.mark.parametrize("lq,q_pos0,nblk,h_i,d_i", [(2048, 0, 512, 4, 64), (333, 4 * 97 + 1, 300, 3, 128),
+                                                     (130, 8192, 2100, 4, 128), (64, 5, 40, 1, 64)])
+def test_index_scores(lq, q_pos0, nblk, h_i, d_i):
+    _say(f"scores lq={lq} q_pos0={q_pos0} nblk={nblk} h_i={h_i} d_i={d_i}")
+    q = _randn_bf16((lq, h_i, d_i), 1, 1 / math.sqrt(d_i))
+    kp = _randn_bf16((nblk, d_i), 2, 0.5 / math.sqrt(d_i))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    w = torch.rand((lq, h_i), generator=g, device=DEV)
+    w[::7] *= -1.0  # negative weights too
+    s = Q.qsa_index_scores(q, w, kp, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    qf, kf, wf = O.bf16_to_f64(bits(q)), O.bf16_to_f64(bits(kp)), w.double().cpu().numpy()
+    pos = q_pos0 + np.arange(lq)
+    ref = O.index_scores(qf, wf, kf, pos, 4)
+    bound = _score_bound(qf, wf, kf)
+    got = s.double().cpu().numpy()[:, :nblk]
+    own = np.minimum(pos // 4, nblk)
+    mask = np.arange(nblk)[None, :] < own[:, None]
+    err = np.abs(got - np.nan_to_num(ref))[mask]
+    assert np.all(err <= 2e-5 * bound[mask] + 1e-30), f"max err {err.max()}"
+
+
+def test_index_scores_batched_seq_lens():
+    bsz, lq, h_i, d_i, nblk = 3, 5, 4, 128, 256
+    seq = [1024, 997, 23]
+    _say(f"scores batched seq_lens={seq}")
+    q = _randn_bf16((bsz, lq, h_i, d_i), 4, 1 / math.sqrt(d_i))
+    kp = _randn_bf16((bsz, nblk, d_i), 5, 1 / math.sqrt(d_i))
+    w = torch.rand((bsz, lq, h_i), device=DEV)
+    sl = torch.tensor(seq, dtype=torch.int32, device=DEV)
+    s = Q.qsa_index_scores(q, w, kp, seq_lens=sl)
+    torch.cuda.synchronize()
+    for b in range(bsz):
+        pos = seq[b] - lq + np.arange(lq)
+        qf, kf, wf = O.bf16_to_f64(bits(q[b])), O.bf16_to_f64(bits(kp[b])), w[b].double().cpu().numpy()
+        ref = O.index_scores(qf, wf, kf, pos, 4)
+        bound = _score_bound(qf, wf, kf)
+        got = s[b].double().cpu().numpy()[:, :nblk]
+        for i in range(lq):
+            own = max(0, min(pos[i] // 4, nblk)) if pos[i] >= 0 else 0
+            assert np.all(np.abs(got[i, :own] - ref[i, :own]) <= 2e-5 * bound[i, :own] + 1e-30)
+
+
+# ------------------------------------------------------------------------------------
+# Stage 3: top-k on given scores (same fp32 inputs on both sides: exact equality)
+# ------------------------------------------------------------------------------------
+
+
+def _run_topk(scores_np, q_pos0, nblk, budget, seq_lens=None):
+    lq = scores_np.shape[-2] if scores_np.ndim == 3 else scores_np.shape[0]
+    ld = Q.score_ld(nblk)
+    shp = (scores_np.shape[0], lq, ld) if scores_np.ndim == 3 else (lq, ld)
+    full = np.full(shp, np.nan, dtype=np.float32)  # never-read entries are NaN
+    full[..., : scores_np.shape[-1]] = scores_np
+    st = torch.from_numpy(full).to(DEV)
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    sel = Q.qsa_topk_blocks(st, lq=lq, nblk=nblk, budget=budget, q_pos0=q_pos0, seq_lens=sl)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy()
+
+
+def _check_topk_exact(scores_np, sel, q_pos0, nblk, n_sel, r=4):
+    for i in range(sel.shape[0]):
+        t = q_pos0 + i
+        own = t // r
+        c = min(own, nblk)  # candidates stop at the pooled range; own block still kept
+        m = min(n_sel - 1, c)
+        ranked = O.select_blocks(scores_np[i, :c].astype(np.float64), c, n_sel)
+        ref = np.full(n_sel, -1)
+        ref[:m] = ranked[:m]
+        ref[m] = own
+        np.testing.assert_array_equal(sel[i], ref, err_msg=f"row {i} (t={t})")
+
+
+def _nan_tail(x, q_pos0, r=4):
+    x = x.copy()
+    for i in range(x.shape[0]):
+        x[i, (q_pos0 + i) // r :] = np.nan
+    return x
+
+
+@pytest.mark.parametrize("kind", ["normal", "quantized", "zeros_negzero", "negative", "relu_like"])
+def test_topk_exact(kind):
+    rng = np.random.default_rng(11)
+    lq, q_pos0, budget = 257, 4 * 300 + 2, 256  # n_sel = 64; rows 300..364 blocks
+    nblk = (q_pos0 + lq) // 4 + 1
+    x = rng.standard_normal((lq, nblk)).astype(np.float32)
+    if kind == "quantized":
+        x = np.round(x * 2) / 2
+    elif kind == "zeros_negzero":
+        x = np.where(rng.random(x.shape) < 0.5, np.float32(0.0), np.float32(-0.0))
+        x[:, ::37] = 1.0
+    elif kind == "negative":
+        x = -np.abs(x)
+    elif kind == "relu_like":
+        x = np.maximum(x, 0) * rng.random(x.shape).astype(np.float32)
+    _say(f"topk kind={kind}")
+    sel = _run_topk(_nan_tail(x, q_pos0), q_pos0, nblk, budget)
+    _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
+
+
+def test_topk_short_rows_and_nblk_cap():
+    rng = np.random.default_rng(12)
+    lq, q_pos0, budget, nblk = 300, 0, 128, 50  # rows beyond block 50: candidates capped
+    x = rng.standard_normal((lq, nblk)).astype(np.float32)
+    _say("topk short rows / nblk cap")
+    sel = _run_topk(x, q_pos0, nblk, budget)
+    _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
+
+
+def test_topk_huge_tie_set_takes_lowest_ids():
+    # 20000 candidates, 100 positive, the rest exactly zero: the 411 zeros kept are
+    # the lowest ids (exercises the in-order path beyond the LDS tie capacity).
+    lq, budget = 2, 2048
+    q_pos0 = 4 * 20000
+    nblk = 20001
+    x = np.zeros((lq, nblk), dtype=np.float32)
+    pos = np.random.default_rng(13).choice(20000, 100, replace=False)
+    x[:, pos] = 1.0 + np.arange(100, dtype=np.float32)
+    x[1, 5::2] = -0.0
+    _say("topk huge tie set")
+    sel = _run_topk(_nan_tail(x, q_pos0), q_pos0, nblk, budget)
+    _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
+
+
+def test_topk_decode_rows_batched():
+    rng = np.random.default_rng(14)
+    bsz, nblk, budget = 3, 262144, 2048
+    seq = [1048576, 1048573, 4 * 100000 + 1]
+    x = np.maximum(rng.standard_normal((bsz, 1, nblk)).astype(np.float32), 0)
+    _say("topk decode rows 262K")
+    sel = _run_topk(x, 0, nblk, budget, seq_lens=seq)
+    for b in range(bsz):
+        t = seq[b] - 1
+        own = t // 4
+        ref = O.select_blocks(x[b, 0, :own].astype(np.float64), own, budget // 4)
+        np.testing.assert_array_equal(sel[b, 0], ref)
+
+
+# ------------------------------------------------------------------------------------
+# Stage 4: attention on given selections
+# ------------------------------------------------------------------------------------
+
+
+def _attn_case(lq, lk, q_pos0, hq, hkv, d, budget, seed, unscaled=False, rows=None):
+    sc = 1.0 if unscaled else 1 / math.sqrt(d)
+    q = _randn_bf16((lq, hq, d), seed, sc)
+    k = _randn_bf16((lk, hkv, d), seed + 1, sc)
+    v = _randn_bf16((lk, hkv, d), seed + 2, 1 / math.sqrt(d))
+    pos = q_pos0 + np.arange(lq)
+    n_sel = budget // 4
+    sel_np = _random_selection(pos, n_sel, 4, seed)
+    sel = torch.from_numpy(sel_np).to(DEV)
+    out, lse = Q.qsa_sparse_attn_fwd(q, k, v, sel, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    rows = np.arange(lq) if rows is None else np.asarray(rows)
+    qb, kb, vb = bits(q), bits(k), bits(v)
+    ref = np.zeros((len(rows), hq, d))
+    ref_lse = np.zeros((len(rows), hq))
+    for j, i in enumerate(rows):
+        toks = O.kept_tokens(sel_np[i], int(pos[i]), 4, lk)
+        ref[j], ref_lse[j] = O.attend(O.bf16_to_f64(qb[i]), O.bf16_to_f64(kb[toks]),
+                                      O.bf16_to_f64(vb[toks]), 1 / math.sqrt(d))
+    compare_output(out[torch.from_numpy(rows).to(DEV)], ref, f"attn lq={lq} d={d}")
+    got_lse = lse.double().cpu().numpy()[rows]
+    assert np.max(np.abs(got_lse - ref_lse)) <= LSE_ABS
+
+
+@pytest.mark.parametrize("lq,lk,q_pos0,hq,hkv,d,budget", [
+    (2048, 2048, 0, 4, 1, 128, 256),            # tiny shape
+    (700, 4102, 3402, 24, 2, 256, 2048),        # model shape, ragged Lk, chunk at the end
+    (513, 513, 0, 16, 1, 256, 64),              # 16 heads per group, partial last block
+    (300, 1200, 900, 2, 2, 128, 16),            # 1 head per group, few blocks
+])
+def test_sparse_attn_fwd(lq, lk, q_pos0, hq, hkv, d, budget):
+    _say(f"attn lq={lq} lk={lk} q_pos0={q_pos0} hq={hq} hkv={hkv} d={d} K={budget}")
+    _attn_case(lq, lk, q_pos0, hq, hkv, d, budget, seed=lq)
+
+
+def test_sparse_attn_fwd_softmax_stress():
+    # Unscaled N(0,1) q/k with scale 1/sqrt(d): peaky logits, exercises the rescaling.
+    _say("attn softmax stress")
+    _attn_case(600, 600, 0, 24, 2, 256, 512, seed=77, unscaled=True)
+
+
+def test_sparse_attn_decode():
+    bsz, lmax, hq, hkv, d, budget = 3, 5000, 24, 2, 256, 2048
+    seq = [5000, 4093, 17]
+    _say(f"decode attn seq={seq}")
+    q = _randn_bf16((bsz, hq, d), 31, 1 / math.sqrt(d))
+    kc = _randn_bf16((bsz, lmax, hkv, d), 32, 1 / math.sqrt(d))
+    vc = _randn_bf16((bsz, lmax, hkv, d), 33, 1 / math.sqrt(d))
+    sel_np = np.concatenate([_random_selection([s - 1], budget // 4, 4, 40 + i) for i, s in enumerate(seq)])
+    sl = torch.tensor(seq, dtype=torch.int32, device=DEV)
+    out, lse = Q.qsa_sparse_attn_decode(q, kc, vc, sl, torch.from_numpy(sel_np).to(DEV))
+    torch.cuda.synchronize()
+    for b in range(bsz):
+        t = seq[b] - 1
+        toks = O.kept_tokens(sel_np[b], t, 4, t + 1)
+        ref, ref_lse = O.attend(O.bf16_to_f64(bits(q[b])), O.bf16_to_f64(bits(kc[b][toks])),
+                                O.bf16_to_f64(bits(vc[b][toks])), 1 / math.sqrt(d))
+        compare_output(out[b], ref, f"decode b={b}")
+        assert np.max(np.abs(lse[b].double().cpu().numpy() - ref_lse)) <= LSE_ABS
+
+
+# ------------------------------------------------------------------------------------
+# Whole path against the oracle's whole path
+# ------------------------------------------------------------------------------------
+
+
+class _Rows:
+    """Host copy of selected rows of a large tensor, indexed by absolute row."""
+
+    def __init__(self, shape, rows, data):
+        self.shape = shape
+        self._at = {int(r): j for j, r in enumerate(rows)}
+        self._data = data
+
+    def __getitem__(self, idx):
+        if isinstance(idx, (int, np.integer)):
+            return self._data[self._at[int(idx)]]
+        return self._data[[self._at[int(i)] for i in idx]]
+
+
+def _prefill_parity(name, rows=None, row_chunk=4096, **over):
+    wl = workload(name, **over)
+    _say(f"prefill {wl.name} lq={wl.lq} lk={wl.lk} q_pos0={wl.q_pos0} K={wl.budget}")
+    inp = generate(wl, device=DEV)
+    out, lse, sel, kp = Q.qsa_prefill_forward(
+        inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["w"], inp["k_idx"], budget=wl.budget,
+        q_pos0=wl.q_pos0, k_pooled_prefix=inp["k_pooled_prefix"], row_chunk=row_chunk)
+    torch.cuda.synchronize()
+    if rows is None:
+        rows = np.arange(wl.lq)
+    rows = np.unique(np.concatenate([np.asarray(rows), inp["aligned_rows"][:64], [0, wl.lq - 1]]))
+    rows_t = torch.from_numpy(rows).to(DEV)
+
+    def fetch(toks):
+        tt = torch.from_numpy(toks).to(DEV)
+        return (O.bf16_to_f64(bits(inp["k"][tt])), O.bf16_to_f64(bits(inp["v"][tt])))
+
+    prefix = None if inp["k_pooled_prefix"] is None else bits(inp["k_pooled_prefix"])
+    # Oracle end to end (its own pooling, scores, selection, attention) on the rows.
+    qb = _Rows((wl.lq, wl.hq, wl.d), rows, bits(inp["q"][rows_t]))
+    qib = bits(inp["q_idx"])
+    res = O.forward_prefill(qb, None, None, qib, inp["w"].cpu().numpy(), bits(inp["k_idx"]),
+                            r=wl.r, budget=wl.budget, q_pos0=wl.q_pos0,
+                            k_pooled_prefix_bits=prefix, rows=rows, n_keys=wl.lk,
+                            fetch_kv=fetch)
+    # Pooled keys: bit-exact.
+    np.testing.assert_array_equal(bits(kp[wl.pooled_prefix_blocks:]), res["pooled"])
+    sel_np = sel[rows_t].cpu().numpy()
+    n_exact = 0
+    for j, i in enumerate(rows):
+        t = wl.q_pos0 + int(i)
+        n_exact += check_selection_row(sel_np[j], res["scores"][j], t // 4, wl.n_sel,
+                                       f"{wl.name} row {i}")
+    # Needle-aligned rows keep their needle.
+    for i, b in zip(inp["aligned_rows"][:64], inp["aligned_blocks"][:64]):
+        j = int(np.nonzero(rows == i)[0][0])
+        assert b in sel_np[j], f"row {i} lost needle block {b}"
+    # Output: oracle attention on the GPU's own selection.
+    ref = np.zeros((len(rows), wl.hq, wl.d))
+    for j, i in enumerate(rows):
+        t = wl.q_pos0 + int(i)
+        toks = O.kept_tokens(sel_np[j], t, wl.r, wl.lk)
+        kr, vr = fetch(toks)
+        ref[j], _ = O.attend(O.bf16_to_f64(qb[i]), kr, vr, 1 / math.sqrt(wl.d))
+    max_abs, rel = compare_output(out[rows_t], ref, wl.name)
+    _say(f"  rows={len(rows)} exact_sel={n_exact} max_abs={max_abs:.2e} rel_l2={rel:.2e}")
+    return n_exact, len(rows)
+
+
+def test_prefill_tiny_all_rows():
+    n_exact, n = _prefill_parity("tiny")
+    assert n_exact >= n - 2
+
+
+def test_prefill_tiny_small_chunks_ragged():
+    # Row chunks that do not divide Lq, Lq not a multiple of the 64-row tile.
+    n_exact, n = _prefill_parity("tiny", row_chunk=300, lq=1001, lk=1001)
+    assert n_exact >= n - 2
+
+
+def test_prefill_32k_sampled():
+    rng = np.random.default_rng(21)
+    rows = rng.choice(32768, 48, replace=False)
+    _prefill_parity("prefill32k", rows=rows)
+
+
+def test_prefill_128k_sampled():
+    rng = np.random.default_rng(22)
+    rows = rng.choice(131072, 24, replace=False)
+    _prefill_parity("prefill128k", rows=rows)
+
+
+def test_chunked_prefill_1m_sampled():
+    rng = np.random.default_rng(23)
+    rows = rng.choice(8192, 16, replace=False)
+    _prefill_parity("chunked1m", rows=rows)
+
+
+def test_decode_1m_full():
+    wl = workload("decode1m")
+    _say("decode1m: 8 x 1M")
+    inp = generate(wl, device=DEV)
+    out, lse, sel = Q.qsa_decode_forward(inp["q"], inp["q_idx"], inp["w"], inp["k_pooled"],
+                                         inp["k_cache"], inp["v_cache"], inp["seq_lens"],
+                                         budget=wl.budget)
+    torch.cuda.synchronize()
+
+    def fetch(b, toks):
+        tt = torch.from_numpy(toks).to(DEV)
+        return (O.bf16_to_f64(bits(inp["k_cache"][b][tt])),
+                O.bf16_to_f64(bits(inp["v_cache"][b][tt])))
+
+    kpb = bits(inp["k_pooled"])
+    res = O.forward_decode(bits(inp["q"]), bits(inp["q_idx"])[:, 0], inp["w"].cpu().numpy()[:, 0],
+                           kpb, inp["seq_lens"].cpu().numpy(), fetch, r=4, budget=wl.budget)
+    sel_np = sel.cpu().numpy()
+    for b in range(wl.batch):
+        t = int(inp["seq_lens"][b]) - 1
+        check_selection_row(sel_np[b], res["scores"][b], t // 4, wl.n_sel, f"decode b={b}")
+        toks = O.kept_tokens(sel_np[b], t, 4, t + 1)
+        kr, vr = fetch(b, toks)
+        ref, ref_lse = O.attend(O.bf16_to_f64(bits(inp["q"][b])), kr, vr, 1 / math.sqrt(wl.d))
+        compare_output(out[b], ref, f"decode b={b}")
+        assert np.max(np.abs(lse[b].double().cpu().numpy() - ref_lse)) <= LSE_ABS
