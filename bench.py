@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of the QSA forward path on one MI355X.
+
+One step is one pass of the whole prefill path over the 128K-token workload
+(1 sequence, 24 query heads / 2 KV groups at d=256, indexer 4 heads x 128, r=4,
+budget 2048): pool the indexer keys, score every causal block, keep the top
+blocks, attend over the kept tokens. Inputs are seeded synthetic tensors already
+resident in HBM. The line also reports the 1M-context decode step (8 sequences,
+one new token each) and the oracle's CPU throughput on a bounded sample.
+
+Prints ONE JSON line. Only one GPU is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "QSA fwd tokens/s: 128K prefill & 1M-ctx decode; % MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="prefill128k",
+                   choices=["prefill128k", "prefill32k", "chunked1m", "tiny"])
+    p.add_argument("--row-chunk", type=int, default=4096)
+    p.add_argument("--decode-steps", type=int, default=50)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def kept_tokens(t, n_sel, r=4):
+    """Tokens attended by a query at position t (array) under a full selection."""
+    own = t // r
+    kept_blocks = (own + 1).clip(max=n_sel)
+    return r * (kept_blocks - 1) + (t - r * own) + 1
+
+
+def attention_bytes(wl, t):
+    """Algorithmic bytes of one attention launch: gathered K/V, q, out, sel, lse."""
+    gathered = int(kept_tokens(t, wl.n_sel).sum()) * wl.hkv * 2 * wl.d * 2
+    per_row = wl.hq * wl.d * 2 * 2 + wl.n_sel * 4 + wl.hq * 4
+    return gathered + len(t) * per_row
+
+
+def score_flops(wl, t):
+    """Algorithmic flops of the indexer score GEMM (2 * H_I * d_I per scored block)."""
+    own = (t // wl.r).clip(max=wl.nblk)
+    return int(own.sum()) * 2 * wl.h_i * wl.d_i
+
+
+def bench_prefill(args, torch, Q, wl, inp):
+    dev = inp["q"].device
+    plan = Q.PrefillPlan(wl.lq, wl.lk, wl.hq, wl.hkv, wl.d, wl.h_i, wl.d_i, wl.budget,
+                         row_chunk=args.row_chunk, device=dev)
+    scale = 1.0 / math.sqrt(wl.d)
+
+    def step(ev_a=None, ev_b=None):
+        Q.qsa_prefill_select(inp["q_idx"], inp["w"], inp["k_idx"], lk=wl.lk, budget=wl.budget,
+                             q_pos0=wl.q_pos0, k_pooled_prefix=inp["k_pooled_prefix"], plan=plan)
+        if ev_a is not None:
+            ev_a.record()
+        Q.qsa_sparse_attn_fwd(inp["q"], inp["k"], inp["v"], plan.sel, q_pos0=wl.q_pos0,
+                              scale=scale, out=plan.out, lse=plan.lse)
+        if ev_b is not None:
+            ev_b.record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        step(a, b)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    return wall, attn_ms
+
+
+def bench_decode(args, torch, Q, wl, inp):
+    plan = Q.DecodePlan(wl.batch, wl.hq, wl.d, wl.lk, wl.budget, device=inp["q"].device)
+
+    def step():
+        Q.qsa_decode_forward(inp["q"], inp["q_idx"], inp["w"], inp["k_pooled"], inp["k_cache"],
+                             inp["v_cache"], inp["seq_lens"], budget=wl.budget, plan=plan)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.decode_steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / args.decode_steps
+
+
+def cpu_baseline(wl, inp, budget_s):
+    """The oracle, as it stands, on evenly spread query rows of the same workload."""
+    import numpy as np
+    import torch
+
+    from oracle import qsa_oracle as O
+
+    def bits(t):
+        return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    k_dev, v_dev = inp["k"], inp["v"]
+
+    def fetch(toks):
+        tt = torch.from_numpy(toks).to(k_dev.device)
+        return O.bf16_to_f64(bits(k_dev[tt])), O.bf16_to_f64(bits(v_dev[tt]))
+
+    qib, kib = bits(inp["q_idx"]), bits(inp["k_idx"])
+    w = inp["w"].cpu().numpy()
+    prefix = None if inp["k_pooled_prefix"] is None else bits(inp["k_pooled_prefix"])
+    t0 = time.perf_counter()
+    O.pool_keys(kib, wl.r)
+    t_pool = time.perf_counter() - t0
+    order = np.random.default_rng(0).permutation(wl.lq)
+    done, t_rows = 0, 0.0
+    while t_rows < budget_s and done < len(order):
+        rows = np.sort(order[done:done + 4])
+
+        class _Q:  # the sampled q rows, addressed by absolute row
+            shape = (wl.lq, wl.hq, wl.d)
+            data = {int(r): bits(inp["q"][int(r)]) for r in rows}
+
+            def __getitem__(self, i):
+                return self.data[int(i)]
+
+        t0 = time.perf_counter()
+        O.forward_prefill(_Q(), None, None, qib, w, kib, r=wl.r, budget=wl.budget,
+                          q_pos0=wl.q_pos0, k_pooled_prefix_bits=prefix, rows=rows,
+                          n_keys=wl.lk, fetch_kv=fetch)
+        t_rows += time.perf_counter() - t0 - t_pool  # each call pools again; count it once
+        done += len(rows)
+    total = t_rows + t_pool * done / wl.lq
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    return {"value": done / total, "unit": "tokens/s", "cores": min(cores, blas),
+            "kind": "oracle",
+            "sample": f"{done} random query rows of {wl.name} (whole path per row: scores over "
+                      f"all earlier blocks, top-k, fp64 attention), pooling amortised per row; "
+                      f"{total:.1f} s of CPU time on {cores} cores, BLAS threads {blas}"}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_06_amd as Q
+    from synth import generate, workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = workload(args.workload)
+    inp = generate(wl, device=dev)
+    torch.cuda.synchronize()
+    wall, attn_ms = bench_prefill(args, torch, Q, wl, inp)
+    ms_step = wall / args.steps * 1e3
+    t = wl.q_pos0 + np.arange(wl.lq, dtype=np.int64)
+    a_bytes = attention_bytes(wl, t)
+    achieved = a_bytes / (attn_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": wl.lq * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "seq_len": wl.lk, "query_tokens": wl.lq,
+                   "q_pos0": wl.q_pos0, "heads": f"{wl.hq}q/{wl.hkv}kv", "head_dim": wl.d,
+                   "indexer": f"{wl.h_i}x{wl.d_i}", "r": wl.r, "budget": wl.budget,
+                   "row_chunk": args.row_chunk, "global_batch": 1, "parallelism": "single GPU"},
+        "roofline": {"kernel": "sparse_attn_kernel (kept-token gather + MFMA)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": a_bytes, "avg_launch_ms": attn_ms},
+        "stages_ms": {"select (pool + scores + top-k)": ms_step - attn_ms, "attention": attn_ms},
+        "score_gemm_flops_per_step": score_flops(wl, t),
+    }
+    del inp
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        dwl = workload("decode1m")
+        dinp = generate(dwl, device=dev)
+        torch.cuda.synchronize()
+        s_dec = bench_decode(args, torch, Q, dwl, dinp)
+        own = (dwl.lk - 1) // dwl.r
+        d_bytes = dwl.batch * (own * dwl.d_i * 2 + dwl.budget * dwl.hkv * 2 * dwl.d * 2 +
+                               dwl.hq * dwl.d * 2 * 2)
+        line["decode"] = {"workload": dwl.name, "batch": dwl.batch, "context": dwl.lk,
+                          "value": dwl.batch / s_dec, "unit": "tokens/s", "ms_per_step": s_dec * 1e3,
+                          "steps": args.decode_steps,
+                          "roofline": {"bound": "hbm", "achieved": d_bytes / s_dec / 1e9,
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": d_bytes / s_dec / 1e9 / HBM_PEAK_GBS,
+                                       "algorithmic_bytes_per_step": d_bytes}}
+        del dinp
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        inp = generate(wl, device=dev)
+        line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     qsa_index_scores,
     qsa_pool_keys,
     qsa_prefill_forward,
+    qsa_prefill_select,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_fwd,
     qsa_topk_blocks,

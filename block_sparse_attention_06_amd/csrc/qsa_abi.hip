@@ -289,17 +289,18 @@ size_t qsa_prefill_workspace_bytes(int64_t lq, int64_t lk, int r, int64_t row_ch
   return align256((size_t)rc * (size_t)score_ld(lk / r) * sizeof(float));
 }
 
-qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, int hkv, int d,
-                               int h_idx, int d_idx, int r, int budget_tokens, const void* q,
-                               const void* k, const void* v, const void* q_idx, const float* w,
-                               const void* k_idx, int64_t first_raw_token,
-                               const void* k_pooled_prefix, void* k_pooled, float softmax_scale,
-                               int32_t* sel, void* out, float* lse, int64_t row_chunk,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx, int d_idx,
+                              int r, int budget_tokens, const void* q_idx, const float* w,
+                              const void* k_idx, int64_t first_raw_token,
+                              const void* k_pooled_prefix, void* k_pooled, int32_t* sel,
+                              int64_t row_chunk, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   QSA_TRY(check_r(r));
   QSA_TRY(check_budget(budget_tokens, r));
   QSA_TRY(check_indexer_shape(h_idx, d_idx));
-  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_REQUIRE(lq >= 0 && lk >= 1 && q_pos0 >= 0 && q_pos0 + lq <= lk, QSA_ERR_INVALID_ARGUMENT,
+              "query positions [%lld, %lld) must lie inside the %lld keys", (long long)q_pos0,
+              (long long)(q_pos0 + lq), (long long)lk);
   QSA_REQUIRE(first_raw_token >= 0 && first_raw_token % r == 0 && first_raw_token <= lk,
               QSA_ERR_INVALID_ARGUMENT, "first_raw_token=%lld must be a multiple of r in [0, lk]",
               (long long)first_raw_token);
@@ -307,6 +308,8 @@ qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, i
               "k_pooled_prefix is required when first_raw_token > 0");
   QSA_REQUIRE(k_pooled && (k_idx || first_raw_token / r == lk / r), QSA_ERR_INVALID_ARGUMENT,
               "null k_pooled or k_idx");
+  QSA_REQUIRE(aligned16(k_pooled) && (!k_pooled_prefix || aligned16(k_pooled_prefix)),
+              QSA_ERR_INVALID_ARGUMENT, "pooled-key buffers must be 16-byte aligned");
   const int64_t nblk = lk / r;
   const int64_t prefix_blocks = first_raw_token / r;
   const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
@@ -339,8 +342,22 @@ qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, i
     QSA_TRY(qsa_topk_blocks(1, n, r, budget_tokens, sc, ld, 0, nblk, q_pos0 + c0, nullptr,
                             sel + c0 * n_sel, nullptr, 0, stream));
   }
-  return qsa_sparse_attn_fwd(lq, lk, hq, hkv, d, r, n_sel, q, k, v, sel, q_pos0, softmax_scale,
-                             out, lse, stream);
+  return QSA_OK;
+}
+
+qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, int hkv, int d,
+                               int h_idx, int d_idx, int r, int budget_tokens, const void* q,
+                               const void* k, const void* v, const void* q_idx, const float* w,
+                               const void* k_idx, int64_t first_raw_token,
+                               const void* k_pooled_prefix, void* k_pooled, float softmax_scale,
+                               int32_t* sel, void* out, float* lse, int64_t row_chunk,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_TRY(qsa_prefill_select(lq, lk, q_pos0, h_idx, d_idx, r, budget_tokens, q_idx, w, k_idx,
+                             first_raw_token, k_pooled_prefix, k_pooled, sel, row_chunk,
+                             workspace, workspace_bytes, stream));
+  return qsa_sparse_attn_fwd(lq, lk, hq, hkv, d, r, budget_tokens / r, q, k, v, sel, q_pos0,
+                             softmax_scale, out, lse, stream);
 }
 
 // ---- whole decode step ----

@@ -186,17 +186,47 @@ class PrefillPlan:
     """Preallocated outputs and workspace for repeated prefill calls of one shape."""
 
     def __init__(self, lq, lk, hq, hkv, d, h_idx, d_idx, budget, *, r=4, row_chunk=4096,
-                 device="cuda"):
+                 device="cuda", with_attention=True):
         self.shape = (lq, lk, hq, hkv, d, h_idx, d_idx, budget, r)
         self.row_chunk = row_chunk
         dev = torch.device(device)
         self.sel = torch.empty((lq, budget // r), dtype=torch.int32, device=dev)
-        self.out = torch.empty((lq, hq, d), dtype=torch.bfloat16, device=dev)
-        self.lse = torch.empty((lq, hq), dtype=torch.float32, device=dev)
+        self.out = self.lse = None
+        if with_attention:
+            self.out = torch.empty((lq, hq, d), dtype=torch.bfloat16, device=dev)
+            self.lse = torch.empty((lq, hq), dtype=torch.float32, device=dev)
         self.k_pooled = torch.empty((lk // r, d_idx), dtype=torch.bfloat16, device=dev)
         nbytes = _lib.load().qsa_prefill_workspace_bytes(lq, lk, r, row_chunk)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
         self.ws_bytes = nbytes
+
+
+def _prefill_args(q_idx, w, k_idx, k_pooled_prefix, r, lk):
+    for name, t, dt in (("q_idx", q_idx, torch.bfloat16), ("w", w, torch.float32),
+                        ("k_idx", k_idx, torch.bfloat16)):
+        _need(t, name, dt, q_idx.device)
+    prefix_blocks = 0 if k_pooled_prefix is None else k_pooled_prefix.shape[0]
+    if k_pooled_prefix is not None:
+        _need(k_pooled_prefix, "k_pooled_prefix", torch.bfloat16, q_idx.device)
+    if k_idx.shape[0] != lk - prefix_blocks * r:
+        raise ValueError("k_idx must hold the indexer keys of every token after the prefix")
+    return prefix_blocks
+
+
+def qsa_prefill_select(q_idx, w, k_idx, *, lk: int, budget: int, q_pos0: int = 0,
+                       k_pooled_prefix: Optional[torch.Tensor] = None, r: int = 4,
+                       row_chunk: int = 4096, plan: Optional[PrefillPlan] = None):
+    """Selection half of prefill: pool the new blocks, score + top-k in row chunks.
+    Returns (sel, k_pooled)."""
+    lq, h_idx, d_idx = q_idx.shape
+    prefix_blocks = _prefill_args(q_idx, w, k_idx, k_pooled_prefix, r, lk)
+    if plan is None:
+        plan = PrefillPlan(lq, lk, 1, 1, 128, h_idx, d_idx, budget, r=r, row_chunk=row_chunk,
+                           device=q_idx.device, with_attention=False)
+    _call("qsa_prefill_select", lq, lk, q_pos0, h_idx, d_idx, r, budget, _ptr(q_idx), _ptr(w),
+          _ptr(k_idx), prefix_blocks * r, _ptr(k_pooled_prefix), _ptr(plan.k_pooled),
+          _ptr(plan.sel), plan.row_chunk, _ptr(plan.ws), plan.ws_bytes, _stream(q_idx))
+    return plan.sel, plan.k_pooled
 
 
 def qsa_prefill_forward(q, k, v, q_idx, w, k_idx, *, budget: int, q_pos0: int = 0,
@@ -209,18 +239,12 @@ def qsa_prefill_forward(q, k, v, q_idx, w, k_idx, *, budget: int, q_pos0: int = 
     indexer keys of tokens P*r .. Lk-1 where P = rows of k_pooled_prefix (or 0).
     Returns (out, lse, sel, k_pooled).
     """
-    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
-                        ("v", v, torch.bfloat16), ("q_idx", q_idx, torch.bfloat16),
-                        ("w", w, torch.float32), ("k_idx", k_idx, torch.bfloat16)):
-        _need(t, name, dt, q.device)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, q.device)
     lq, hq, d = q.shape
     lk, hkv, _ = k.shape
     _, h_idx, d_idx = q_idx.shape
-    prefix_blocks = 0 if k_pooled_prefix is None else k_pooled_prefix.shape[0]
-    if k_pooled_prefix is not None:
-        _need(k_pooled_prefix, "k_pooled_prefix", torch.bfloat16, q.device)
-    if k_idx.shape[0] != lk - prefix_blocks * r:
-        raise ValueError("k_idx must hold the indexer keys of every token after the prefix")
+    prefix_blocks = _prefill_args(q_idx, w, k_idx, k_pooled_prefix, r, lk)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     if plan is None:
         plan = PrefillPlan(lq, lk, hq, hkv, d, h_idx, d_idx, budget, r=r, row_chunk=row_chunk,

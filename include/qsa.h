@@ -64,7 +64,8 @@ const char* qsa_last_error(void);
 /*
  * Stage 1 -- micro-block mean pooling of the indexer keys [DR].
  * kbar[b][c] = bf16( (k_idx[r*b][c] + ... + k_idx[r*b+r-1][c]) / r ), b < n_blocks,
- * accumulated in fp32 and rounded once to nearest even. Only complete blocks are
+ * summed in fp64 (exact for bf16 keys), divided by r and rounded once to nearest
+ * even. Only complete blocks are
  * passed: the caller points k_idx at the first token of the first block to pool and
  * k_pooled at that block's row. No positional encoding is added here; a caller that
  * wants one applies it to k_pooled afterwards.
@@ -151,15 +152,26 @@ qsa_status qsa_sparse_attn_decode(int batch, int hq, int hkv, int d, int r, int 
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Whole prefill path: pool the new blocks, then for query rows in chunks of
- * `row_chunk` score + top-k, then attention over all rows. Inputs as in stages 1-4;
- * k_idx holds the raw indexer keys of tokens first_raw_token .. lk-1 (tokens before
- * it are covered by k_pooled_prefix, prefix_blocks = first_raw_token / r rows, which
- * may be NULL when first_raw_token == 0). k_pooled (output, [lk/r][d_idx]) receives
- * the prefix rows copied and the new rows pooled. sel [lq][K/r] is an output too.
- * workspace: qsa_prefill_workspace_bytes() bytes (score chunk buffer).
+ * Selection half of the prefill path: pool the new blocks, then for query rows in
+ * chunks of `row_chunk` compute the block scores and the top-k. Inputs as in stages
+ * 1-3; k_idx holds the raw indexer keys of tokens first_raw_token .. lk-1 (tokens
+ * before it are covered by k_pooled_prefix, first_raw_token / r rows, which may be
+ * NULL when first_raw_token == 0). Outputs: k_pooled [lk/r][d_idx] (prefix rows
+ * copied, new rows pooled) and sel [lq][K/r]. Query row i sits at q_pos0 + i.
+ * workspace: qsa_prefill_workspace_bytes() bytes (the score buffer of one chunk).
  */
 size_t qsa_prefill_workspace_bytes(int64_t lq, int64_t lk, int r, int64_t row_chunk);
+qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx, int d_idx,
+                              int r, int budget_tokens, const void* q_idx, const float* w,
+                              const void* k_idx, int64_t first_raw_token,
+                              const void* k_pooled_prefix, void* k_pooled, int32_t* sel,
+                              int64_t row_chunk, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Whole prefill path: qsa_prefill_select followed by qsa_sparse_attn_fwd on the same
+ * stream. Arguments as in those two calls.
+ */
 qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, int hkv, int d,
                                int h_idx, int d_idx, int r, int budget_tokens,
                                const void* q, const void* k, const void* v,
