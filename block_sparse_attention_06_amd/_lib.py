@@ -29,7 +29,7 @@ SIGNATURES = {
     "qsa_sparse_attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "qsa_sparse_attn_decode": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _L, _L, _P, _P, _F, _P,
                                     _P, _P, _Z, _P]),
-    "qsa_prefill_workspace_bytes": (_Z, [_L, _L, _I, _L]),
+    "qsa_prefill_workspace_bytes": (_Z, [_L, _L, _I, _I, _L]),
     "qsa_prefill_select": (_I, [_L, _L, _L, _I, _I, _I, _I, _P, _P, _P, _L, _P, _P, _P, _L, _P,
                                 _Z, _P]),
     "qsa_prefill_forward": (_I, [_L, _L, _L, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,

@@ -147,23 +147,33 @@ qsa_status qsa_index_scores(int batch, int64_t lq, int h_idx, int d_idx, int r,
                     "qsa_index_scores launch");
 }
 
+qsa::TopkArgs topk_args(int batch, int64_t lq, int r, int budget_tokens, const float* scores,
+                        int64_t ld, int64_t sbs, int64_t nblk, int64_t q_pos0,
+                        const int32_t* seq_lens, int32_t* sel) {
+  return qsa::TopkArgs{scores, ld, sbs, lq, nblk, q_pos0, seq_lens, r, budget_tokens / r, sel,
+                       batch};
+}
+
 size_t qsa_topk_workspace_bytes(int batch, int64_t lq, int64_t nblk, int budget_tokens, int r) {
-  (void)batch; (void)lq; (void)nblk; (void)budget_tokens; (void)r;
-  return 0;
+  if (batch <= 0 || lq <= 0 || nblk <= 0 || r <= 0 || budget_tokens < r) return 0;
+  // Sized for rows whose positions reach the last block (the device may hold seq_lens).
+  qsa::TopkArgs a = topk_args(batch, lq, r, budget_tokens, nullptr, nblk, 0, nblk,
+                              nblk * (int64_t)r, nullptr, nullptr);
+  a.seq_lens = reinterpret_cast<const int32_t*>(1);  // bound by nblk, not by positions
+  return qsa::topk_workspace_bytes(a);
 }
 
 qsa_status qsa_topk_blocks(int batch, int64_t lq, int r, int budget_tokens, const float* scores,
                            int64_t ld, int64_t scores_batch_stride, int64_t nblk, int64_t q_pos0,
                            const int32_t* seq_lens, int32_t* sel, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes;
   QSA_TRY(check_r(r));
   QSA_TRY(check_budget(budget_tokens, r));
   QSA_REQUIRE(batch >= 1 && batch <= 65535, QSA_ERR_INVALID_ARGUMENT, "batch=%d", batch);
   QSA_REQUIRE(lq >= 0 && lq <= ((int64_t)1 << 31) - 1, QSA_ERR_INVALID_ARGUMENT, "lq=%lld",
               (long long)lq);
-  QSA_REQUIRE(nblk >= 0 && nblk < ((int64_t)1 << 30), QSA_ERR_INVALID_ARGUMENT, "nblk=%lld",
-              (long long)nblk);
+  QSA_REQUIRE(nblk >= 0 && nblk < ((int64_t)1 << 22), QSA_ERR_UNSUPPORTED,
+              "nblk=%lld: top-k supports fewer than 2^22 blocks", (long long)nblk);
   QSA_REQUIRE(seq_lens || q_pos0 >= 0, QSA_ERR_INVALID_ARGUMENT, "q_pos0=%lld < 0",
               (long long)q_pos0);
   QSA_REQUIRE(ld >= nblk && ld % 4 == 0, QSA_ERR_INVALID_ARGUMENT,
@@ -179,9 +189,16 @@ qsa_status qsa_topk_blocks(int batch, int64_t lq, int r, int budget_tokens, cons
   if (!seq_lens)
     QSA_REQUIRE((q_pos0 + lq - 1) / r < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT,
                 "positions overflow int32 block ids");
-  qsa::TopkArgs a{scores, ld, scores_batch_stride, lq, nblk, q_pos0, seq_lens, r,
-                  budget_tokens / r, sel, batch};
-  return hip_status(qsa::launch_topk_blocks(a, static_cast<hipStream_t>(stream)),
+  const qsa::TopkArgs a = topk_args(batch, lq, r, budget_tokens, scores, ld,
+                                    scores_batch_stride, nblk, q_pos0, seq_lens, sel);
+  QSA_REQUIRE(qsa::topk_supported(a), QSA_ERR_UNSUPPORTED,
+              "rows of %lld blocks with %d kept blocks exceed the two-level selection",
+              (long long)nblk, budget_tokens / r);
+  const size_t need = qsa::topk_workspace_bytes(a);
+  QSA_REQUIRE(need == 0 || (workspace && workspace_bytes >= need && aligned16(workspace)),
+              QSA_ERR_WORKSPACE, "top-k workspace: need %zu bytes (16-byte aligned), got %zu",
+              need, workspace_bytes);
+  return hip_status(qsa::launch_topk_blocks(a, workspace, static_cast<hipStream_t>(stream)),
                     "qsa_topk_blocks launch");
 }
 
@@ -283,10 +300,12 @@ qsa_status qsa_sparse_attn_decode(int batch, int hq, int hkv, int d, int r, int 
 
 // ---- whole prefill path ----
 
-size_t qsa_prefill_workspace_bytes(int64_t lq, int64_t lk, int r, int64_t row_chunk) {
+size_t qsa_prefill_workspace_bytes(int64_t lq, int64_t lk, int r, int budget_tokens,
+                                   int64_t row_chunk) {
   if (lq <= 0 || lk <= 0 || r <= 0) return 0;
   const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
-  return align256((size_t)rc * (size_t)score_ld(lk / r) * sizeof(float));
+  return align256((size_t)rc * (size_t)score_ld(lk / r) * sizeof(float)) +
+         qsa_topk_workspace_bytes(1, rc, lk / r, budget_tokens, r);
 }
 
 qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx, int d_idx,
@@ -313,7 +332,7 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
   const int64_t nblk = lk / r;
   const int64_t prefix_blocks = first_raw_token / r;
   const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
-  const size_t need = qsa_prefill_workspace_bytes(lq, lk, r, row_chunk);
+  const size_t need = qsa_prefill_workspace_bytes(lq, lk, r, budget_tokens, row_chunk);
   QSA_REQUIRE(lq == 0 || (workspace && workspace_bytes >= need && aligned16(workspace)),
               QSA_ERR_WORKSPACE, "prefill workspace: need %zu bytes (16-byte aligned), got %zu",
               need, workspace_bytes);
@@ -332,6 +351,7 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
   if (lq == 0) return QSA_OK;
   const int64_t ld = score_ld(nblk);
   float* sc = static_cast<float*>(workspace);
+  const size_t sc_bytes = align256((size_t)rc * (size_t)ld * sizeof(float));
   const int n_sel = budget_tokens / r;
   for (int64_t c0 = 0; c0 < lq; c0 += rc) {
     const int64_t n = (lq - c0) < rc ? (lq - c0) : rc;
@@ -340,7 +360,8 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
                              w + c0 * h_idx, 0, k_pooled, 0, nblk, q_pos0 + c0, nullptr, sc, ld,
                              0, stream));
     QSA_TRY(qsa_topk_blocks(1, n, r, budget_tokens, sc, ld, 0, nblk, q_pos0 + c0, nullptr,
-                            sel + c0 * n_sel, nullptr, 0, stream));
+                            sel + c0 * n_sel, static_cast<char*>(workspace) + sc_bytes,
+                            workspace_bytes - sc_bytes, stream));
   }
   return QSA_OK;
 }
@@ -366,7 +387,8 @@ size_t qsa_decode_workspace_bytes(int batch, int hq, int d, int64_t lmax, int r,
                                   int budget_tokens) {
   if (batch <= 0 || r <= 0 || budget_tokens <= 0) return 0;
   const size_t sc = align256((size_t)batch * (size_t)score_ld(lmax / r) * sizeof(float));
-  return sc + qsa_sparse_attn_decode_workspace_bytes(batch, hq, d, budget_tokens / r);
+  const size_t tk = align256(qsa_topk_workspace_bytes(batch, 1, lmax / r, budget_tokens, r));
+  return sc + tk + qsa_sparse_attn_decode_workspace_bytes(batch, hq, d, budget_tokens / r);
 }
 
 qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int d_idx, int r,
@@ -388,15 +410,16 @@ qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int 
   const int64_t ld = score_ld(nblk);
   float* sc = static_cast<float*>(workspace);
   const size_t sc_bytes = align256((size_t)batch * (size_t)ld * sizeof(float));
+  const size_t tk_bytes = align256(qsa_topk_workspace_bytes(batch, 1, nblk, budget_tokens, r));
+  char* tk = static_cast<char*>(workspace) + sc_bytes;
   QSA_TRY(qsa_index_scores(batch, 1, h_idx, d_idx, r, q_idx, (int64_t)h_idx * d_idx, w, h_idx,
                            k_pooled, k_pooled_batch_stride, nblk, 0, seq_lens, sc, ld, ld,
                            stream));
-  QSA_TRY(qsa_topk_blocks(batch, 1, r, budget_tokens, sc, ld, ld, nblk, 0, seq_lens, sel,
-                          nullptr, 0, stream));
+  QSA_TRY(qsa_topk_blocks(batch, 1, r, budget_tokens, sc, ld, ld, nblk, 0, seq_lens, sel, tk,
+                          tk_bytes, stream));
   return qsa_sparse_attn_decode(batch, hq, hkv, d, r, budget_tokens / r, q, k_cache, v_cache,
                                 cache_batch_stride, lmax, seq_lens, sel, softmax_scale, out, lse,
-                                static_cast<char*>(workspace) + sc_bytes,
-                                workspace_bytes - sc_bytes, stream);
+                                tk + tk_bytes, workspace_bytes - sc_bytes - tk_bytes, stream);
 }
 
 }  // extern "C"

@@ -47,7 +47,9 @@ struct TopkArgs {
   int32_t* sel;
   int batch;
 };
-hipError_t launch_topk_blocks(const TopkArgs& a, hipStream_t stream);
+size_t topk_workspace_bytes(const TopkArgs& a);
+bool topk_supported(const TopkArgs& a);
+hipError_t launch_topk_blocks(const TopkArgs& a, void* ws, hipStream_t stream);
 
 // ---- stage 4 / 4' ----
 struct AttnArgs {

@@ -7,16 +7,26 @@
 // blocks, ranked by score (descending) then block id (ascending); emit the kept ids
 // in ascending order, padded with -1.
 //
-// One workgroup per row, exact radix select on order-preserving 32-bit keys:
-//   1. up to three histogram passes over the row (12, 12, 8 key bits), each
-//      restricted to the keys sharing the prefix found so far, until the bucket
-//      that holds the m-th best key has at most kTieCap members;
-//   2. a collection pass: keys above the bucket are kept outright, keys in the
-//      bucket go to an LDS list that is sorted by (key desc, id asc) to take the
-//      rest -- or, if even the full 32-bit key leaves more than kTieCap equal keys,
-//      an in-order scan takes the lowest ids among them;
-//   3. the kept ids are sorted ascending in LDS and written with the own block.
-// No floating-point atomics; the result does not depend on scheduling.
+// One workgroup per row (or per row segment), reading the row about once:
+//   1. a sample of the row (every k-th run of 32 consecutive scores) gives a value
+//      bin above which roughly 2m candidates are expected;
+//   2. one streaming pass appends every candidate at or above that bin (an upper set
+//      of the value order, so if it holds at least m candidates it holds the m best)
+//      to an LDS list;
+//   3. the exact selection below runs on that list -- or, if the list came out
+//      shorter than m or overflowed, on the whole row (same result, more passes).
+// Exact selection of the m best among n candidates:
+//   a. min / max, then a histogram over kLinBins equal-width value bins; the map
+//      x -> floor((x - min) * bins / (max - min)) is monotone and sends equal values
+//      (and -0.0 / +0.0) to one bin, so every candidate in a bin above the bin B that
+//      holds the m-th best ranks before every candidate in B;
+//   b. only if B is large: radix descent on the order-preserving 32-bit key inside B;
+//   c. candidates above the final bucket are kept; the bucket is sorted in LDS by
+//      (key desc, id asc) -- or, when more than kTieCap candidates share one exact
+//      key, a radix select on the id keeps the lowest ids.
+// Rows longer than kSegMax candidates use two launches: each segment keeps its m best
+// (the row's m best are among them), then a merge selects the m best of those.
+// No floating-point atomics; results do not depend on scheduling.
 
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -24,40 +34,89 @@
 namespace qsa {
 
 constexpr int kTkThreads = 256;
-constexpr int kTieCap = 4096;
+constexpr int kWaves = kTkThreads / 64;
+constexpr int kSegMax = 32768;  // candidates per workgroup (bitmap size of the output)
+constexpr int kLinBins = 2048;
+constexpr int kListCap = 2048;  // filtered candidates kept in LDS
+constexpr int kTieCap = 512;
 constexpr int kMaxSel = 1024;
-constexpr int kHistBins = 4096;
+constexpr int kSampleRun = 32;  // consecutive scores per sampled run
+constexpr int kSampleMax = 4096;
 
-struct TopkShared {
-  uint32_t hist[kHistBins];
+enum TopkMode { kRows = 0, kSegments = 1, kMerge = 2 };
+
+struct TkShared {
+  uint32_t hist[kLinBins];
+  float list_val[kListCap];
+  int32_t list_idx[kListCap];
   uint32_t tie_key[kTieCap];
   int32_t tie_idx[kTieCap];
+  uint32_t bitmap[kSegMax / 32];
   int32_t kept[kMaxSel];
-  uint32_t scan[kTkThreads];
+  uint32_t wsum[kWaves];
+  float wred[2 * kWaves];
   int32_t misc[8];
 };
 
-// Block-wide: find digit D with above(D) < need <= above(D) + hist[D], where
-// above(D) counts the keys in digits > D. Results in sm.misc[0..2].
-__device__ void find_digit(TopkShared& sm, int nbins, uint32_t need) {
+// ---- block-level primitives ---------------------------------------------------------
+
+__device__ __forceinline__ uint32_t block_excl_scan(TkShared& sm, uint32_t v, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) sm.wsum[wave] = x;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t s = sm.wsum[w];
+    off += (w < wave) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return off + x - v;
+}
+
+__device__ __forceinline__ void block_minmax(TkShared& sm, float& mn, float& mx) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, d, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+  }
+  if (lane == 0) {
+    sm.wred[wave] = mn;
+    sm.wred[kWaves + wave] = mx;
+  }
+  __syncthreads();
+  mn = sm.wred[0];
+  mx = sm.wred[kWaves];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    mn = fminf(mn, sm.wred[w]);
+    mx = fmaxf(mx, sm.wred[kWaves + w]);
+  }
+  __syncthreads();
+}
+
+// Over hist[0..nbins), find D with above(D) < need <= above(D) + hist[D], above(D) being
+// the count in digits > D (thread 0 owns the highest digits). Results in misc[0..2].
+__device__ __forceinline__ void find_digit(TkShared& sm, int nbins, uint32_t need) {
   const int tid = threadIdx.x;
   const int per = nbins / kTkThreads;
+  const int hi = nbins - tid * per - 1;
   uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += sm.hist[tid * per + i];
-  uint32_t v = local;
-  sm.scan[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kTkThreads; off <<= 1) {
-    const uint32_t add = (tid + off < kTkThreads) ? sm.scan[tid + off] : 0u;
-    __syncthreads();
-    v += add;
-    sm.scan[tid] = v;
-    __syncthreads();
-  }
-  const uint32_t above_me = v - local;  // keys in bins owned by higher threads
-  if (above_me < need && need <= v) {
+  for (int i = 0; i < per; ++i) local += sm.hist[hi - i];
+  uint32_t total;
+  const uint32_t above_me = block_excl_scan(sm, local, total);
+  if (above_me < need && need <= above_me + local) {
     uint32_t acc = above_me;
-    for (int d = (tid + 1) * per - 1; d >= tid * per; --d) {
+    for (int d = hi; d > hi - per; --d) {
       const uint32_t h = sm.hist[d];
       if (acc + h >= need) {
         sm.misc[0] = d;
@@ -71,95 +130,121 @@ __device__ void find_digit(TopkShared& sm, int nbins, uint32_t need) {
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(TopkArgs a) {
-  __shared__ TopkShared sm;
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const int bi = blockIdx.y;
-  const int64_t base = a.seq_lens ? (int64_t)a.seq_lens[bi] - a.lq : a.q_pos0;
-  const int64_t t = base + row;
-  int32_t* out = a.sel + ((int64_t)bi * a.lq + row) * a.n_sel;
-  if (t < 0) {
-    for (int k = tid; k < a.n_sel; k += kTkThreads) out[k] = -1;
-    return;
-  }
-  const int64_t own = t / a.r;
-  const int64_t C = min(own, a.nblk);
-  const int m = (int)min((int64_t)(a.n_sel - 1), C);
-  if (m == C) {  // every earlier block fits in the budget
-    for (int k = tid; k < a.n_sel; k += kTkThreads)
-      out[k] = k < C ? k : (k == C ? (int32_t)own : -1);
-    return;
-  }
-  const float* srow = a.scores + (int64_t)bi * a.s_bs + row * a.ld;
-  const int64_t n4 = (C + 3) / 4;  // float4 reads; ld % 4 == 0 keeps them inside the row
+__device__ __forceinline__ void clear_hist(TkShared& sm, int nbins) {
+  for (int i = threadIdx.x; i < nbins; i += kTkThreads) sm.hist[i] = 0u;
+  __syncthreads();
+}
 
-  // ---- 1. radix descent on the key prefix ----
+// Equal-width value bins over [lo, lo + kLinBins / sc]; monotone, clamped.
+struct LinBins {
+  float lo, sc;
+  __device__ __forceinline__ int operator()(float v) const {
+    return max(0, min(kLinBins - 1, (int)((v - lo) * sc)));
+  }
+};
+
+__device__ __forceinline__ LinBins make_bins(float mn, float mx) {
+  float sc = (float)kLinBins / (mx - mn);
+  if (!(mx > mn) || !(sc < 3.0e38f)) sc = 0.f;  // one value (or no usable range): one bin
+  return LinBins{mn, sc};
+}
+
+// ---- element sources (NaN marks an absent element) ----------------------------------
+
+struct RowSrc {  // values p[i] (NaN: absent), ids ids[i] when given, else lo + i
+  const float* p;
+  const int32_t* ids;
+  int lo;
+  __device__ __forceinline__ float val(int i) const { return p[i]; }
+  __device__ __forceinline__ int id(int i) const { return ids ? ids[i] : lo + i; }
+};
+
+struct PairSrc {  // (value, id) pairs in global or shared memory; id < 0 is absent
+  const float* v;
+  const int32_t* ids;
+  __device__ __forceinline__ float val(int i) const {
+    return ids[i] >= 0 ? v[i] : __builtin_nanf("");
+  }
+  __device__ __forceinline__ int id(int i) const { return ids[i]; }
+};
+
+// ---- exact selection of the m best of n elements of a source ------------------------
+// mark(i) is called exactly once for each selected element (by position i).
+
+template <class Src, class Mark>
+__device__ void select_exact(TkShared& sm, const Src& src, int n, int m, Mark mark) {
+  const int tid = threadIdx.x;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = tid; i < n; i += kTkThreads) {
+    const float v = src.val(i);
+    mn = fminf(mn, v);  // fminf / fmaxf ignore NaN
+    mx = fmaxf(mx, v);
+  }
+  block_minmax(sm, mn, mx);
+  const LinBins bins = make_bins(mn, mx);
+  clear_hist(sm, kLinBins);
+  for (int i = tid; i < n; i += kTkThreads) {
+    const float v = src.val(i);
+    if (v == v) atomicAdd(&sm.hist[bins(v)], 1u);
+  }
+  __syncthreads();
+  find_digit(sm, kLinBins, (uint32_t)m);
+  const int B = sm.misc[0];
+  uint32_t need = (uint32_t)m - (uint32_t)sm.misc[1];
+  uint32_t bucket = (uint32_t)sm.misc[2];
+  __syncthreads();
+
+  // Radix descent on the key inside bin B while the bucket is too large.
   uint32_t prefix = 0;
   int pbits = 0;
-  uint32_t need = (uint32_t)m;
-  uint32_t bucket = 0;
-  for (int level = 0; level < 3; ++level) {
-    const int wbits = level < 2 ? 12 : 8;
-    const int nbins = 1 << wbits;
+  for (int level = 0; level < 3 && bucket > (uint32_t)kTieCap; ++level) {
+    const int wbits = level < 2 ? 11 : 10;
+    const int nb = 1 << wbits;
     const int shift = 32 - pbits - wbits;
-    for (int i = tid; i < nbins; i += kTkThreads) sm.hist[i] = 0;
-    __syncthreads();
-    for (int64_t i4 = tid; i4 < n4; i4 += kTkThreads) {
-      const float4 x = *reinterpret_cast<const float4*>(srow + i4 * 4);
-      const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (i4 * 4 + e < C) {
-          const uint32_t key = order_key(xs[e]);
-          if (pbits == 0 || (key >> (32 - pbits)) == prefix)
-            atomicAdd(&sm.hist[(key >> shift) & (nbins - 1)], 1u);
-        }
+    clear_hist(sm, nb);
+    for (int i = tid; i < n; i += kTkThreads) {
+      const float v = src.val(i);
+      if (v == v && bins(v) == B) {
+        const uint32_t key = order_key(v);
+        if (pbits == 0 || (key >> (32 - pbits)) == prefix)
+          atomicAdd(&sm.hist[(key >> shift) & (nb - 1)], 1u);
       }
     }
     __syncthreads();
-    find_digit(sm, nbins, need);
-    const uint32_t D = (uint32_t)sm.misc[0];
+    find_digit(sm, nb, need);
     need -= (uint32_t)sm.misc[1];
     bucket = (uint32_t)sm.misc[2];
-    prefix = (prefix << wbits) | D;
+    prefix = (prefix << wbits) | (uint32_t)sm.misc[0];
     pbits += wbits;
     __syncthreads();
-    if (bucket <= (uint32_t)kTieCap) break;
   }
+  // rel: 1 above the bucket, 0 in it, -1 below (or absent)
+  auto rel_of = [&](float v) -> int {
+    if (!(v == v)) return -1;
+    const int b = bins(v);
+    if (b != B) return b > B ? 1 : -1;
+    if (pbits == 0) return 0;
+    const uint32_t top = order_key(v) >> (32 - pbits);
+    return top > prefix ? 1 : (top == prefix ? 0 : -1);
+  };
 
-  // ---- 2. collect ----
-  const bool tie_fits = bucket <= (uint32_t)kTieCap;
-  const int n_out = m - (int)need;  // keys strictly above the bucket
-  if (tid == 0) {
-    sm.misc[3] = 0;
-    sm.misc[4] = 0;
-  }
+  const bool fits = bucket <= (uint32_t)kTieCap;
+  if (tid == 0) sm.misc[4] = 0;
   __syncthreads();
-  const int pshift = 32 - pbits;
-  for (int64_t i4 = tid; i4 < n4; i4 += kTkThreads) {
-    const float4 x = *reinterpret_cast<const float4*>(srow + i4 * 4);
-    const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t idx = i4 * 4 + e;
-      if (idx < C) {
-        const uint32_t key = order_key(xs[e]);
-        const uint32_t top = pshift == 32 ? 0u : (key >> pshift);
-        if (top > prefix) {
-          const int p = atomicAdd(&sm.misc[3], 1);
-          sm.kept[p] = (int32_t)idx;
-        } else if (top == prefix && tie_fits) {
-          const int p = atomicAdd(&sm.misc[4], 1);
-          sm.tie_key[p] = key;
-          sm.tie_idx[p] = (int32_t)idx;
-        }
-      }
+  for (int i = tid; i < n; i += kTkThreads) {
+    const float v = src.val(i);
+    const int rel = rel_of(v);
+    if (rel > 0) {
+      mark(i);
+    } else if (rel == 0 && fits) {
+      const int p = atomicAdd(&sm.misc[4], 1);
+      sm.tie_key[p] = order_key(v);
+      sm.tie_idx[p] = src.id(i);
     }
   }
   __syncthreads();
 
-  if (tie_fits) {
+  if (fits) {
     const int n_tie = sm.misc[4];
     int P = 1;
     while (P < n_tie) P <<= 1;
@@ -168,7 +253,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(TopkArgs a) {
       sm.tie_idx[i] = 0x7fffffff;
     }
     __syncthreads();
-    // Bitonic sort into rank order: key descending, then id ascending.
     for (int k = 2; k <= P; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
         for (int i = tid; i < P; i += kTkThreads) {
@@ -177,8 +261,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(TopkArgs a) {
             const uint32_t ka = sm.tie_key[i], kb = sm.tie_key[ixj];
             const int32_t ia = sm.tie_idx[i], ib = sm.tie_idx[ixj];
             const bool a_first = ka > kb || (ka == kb && ia < ib);
-            const bool up = (i & k) == 0;
-            if (up != a_first) {
+            if (((i & k) == 0) != a_first) {
               sm.tie_key[i] = kb;
               sm.tie_key[ixj] = ka;
               sm.tie_idx[i] = ib;
@@ -189,61 +272,346 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(TopkArgs a) {
         __syncthreads();
       }
     }
-    for (int k = tid; k < (int)need; k += kTkThreads) sm.kept[n_out + k] = sm.tie_idx[k];
-  } else {
-    // The full key is known and more than kTieCap candidates share it: take the
-    // `need` lowest ids among them, scanning the row in id order.
-    const int lane = tid & 63, wave = tid >> 6;
-    int taken = 0;
-    for (int64_t b0 = 0; b0 < C && taken < (int)need; b0 += kTkThreads) {
-      const int64_t idx = b0 + tid;
-      const bool flag = idx < C && order_key(srow[idx]) == prefix;
-      const uint64_t bal = __ballot(flag);
-      const int wpre = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) sm.scan[wave] = (uint32_t)__popcll(bal);
-      __syncthreads();
-      int woff = 0, tot = 0;
-      for (int w = 0; w < kTkThreads / 64; ++w) {
-        if (w < wave) woff += (int)sm.scan[w];
-        tot += (int)sm.scan[w];
-      }
-      const int pos = taken + woff + wpre;
-      if (flag && pos < (int)need) sm.kept[n_out + pos] = (int32_t)idx;
-      taken += tot;
-      __syncthreads();
-    }
-  }
-  __syncthreads();
-
-  // ---- 3. ascending ids, own block last, -1 padding ----
-  int P = 1;
-  while (P < m) P <<= 1;
-  for (int i = m + tid; i < P; i += kTkThreads) sm.kept[i] = 0x7fffffff;
-  __syncthreads();
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += kTkThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int32_t x = sm.kept[i], y = sm.kept[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            sm.kept[i] = y;
-            sm.kept[ixj] = x;
-          }
+    if (need > 0) {
+      // The first `need` of the sorted bucket are kept: everything ranking at or
+      // before the need-th entry.
+      const uint32_t lim_key = sm.tie_key[need - 1];
+      const int32_t lim_idx = sm.tie_idx[need - 1];
+      for (int i = tid; i < n; i += kTkThreads) {
+        const float v = src.val(i);
+        if (rel_of(v) == 0) {
+          const uint32_t key = order_key(v);
+          const int32_t d = src.id(i);
+          if (key > lim_key || (key == lim_key && d <= lim_idx)) mark(i);
         }
       }
+    }
+  } else {
+    // pbits == 32: the bucket is one exact key; keep its `need` lowest ids. Radix
+    // select on the 22-bit id, ascending (digits reversed for the generic search).
+    uint32_t iprefix = 0;
+    int ibits = 0;
+    uint32_t ineed = need;
+    for (int level = 0; level < 2; ++level) {
+      const int nb = 1 << 11;
+      const int shift = 22 - ibits - 11;
+      clear_hist(sm, nb);
+      for (int i = tid; i < n; i += kTkThreads) {
+        const uint32_t d = (uint32_t)src.id(i);
+        if (rel_of(src.val(i)) == 0 && (ibits == 0 || (d >> (22 - ibits)) == iprefix))
+          atomicAdd(&sm.hist[nb - 1 - ((d >> shift) & (nb - 1))], 1u);
+      }
+      __syncthreads();
+      find_digit(sm, nb, ineed);
+      ineed -= (uint32_t)sm.misc[1];
+      iprefix = (iprefix << 11) | (uint32_t)(nb - 1 - sm.misc[0]);
+      ibits += 11;
       __syncthreads();
     }
+    for (int i = tid; i < n; i += kTkThreads)
+      if (rel_of(src.val(i)) == 0 && (uint32_t)src.id(i) <= iprefix) mark(i);
   }
-  for (int k = tid; k < a.n_sel; k += kTkThreads)
-    out[k] = k < m ? sm.kept[k] : (k == m ? (int32_t)own : -1);
+  __syncthreads();
 }
 
-hipError_t launch_topk_blocks(const TopkArgs& a, hipStream_t stream) {
+// ---- filtered selection over a row segment ------------------------------------------
+// Selects the m best of row[0..n) (16-byte aligned; NaN entries are absent; ids are
+// ids[i] when given, else lo + i), calling mark(id) once per kept element.
+
+constexpr int kChunkVec = 8;  // float4 loads in flight per thread in the streaming pass
+
+__device__ __forceinline__ float4 load4_masked(const float* row, int i, int n) {
+  const float qn = __builtin_nanf("");
+  if (i + 3 < n) return *reinterpret_cast<const float4*>(row + i);
+  float4 v = make_float4(qn, qn, qn, qn);
+  if (i < n) v.x = row[i];
+  if (i + 1 < n) v.y = row[i + 1];
+  if (i + 2 < n) v.z = row[i + 2];
+  return v;
+}
+
+template <class Mark>
+__device__ void select_row(TkShared& sm, const float* row, const int32_t* ids, int lo, int n,
+                           int m, Mark mark) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // 1. Sample every k-th run of kSampleRun scores (at most kSampleMax samples), held in
+  //    registers: 4 float4 per thread.
+  const int runs = (n + kSampleRun - 1) / kSampleRun;
+  int k = 1;
+  while ((runs + k - 1) / k * kSampleRun > kSampleMax) ++k;
+  const int s_n4 = (runs + k - 1) / k * (kSampleRun / 4);
+  constexpr int kS4 = kSampleMax / 4 / kTkThreads;
+  float smp[kS4][4];
+  float mn = INFINITY, mx = -INFINITY;
+  int s_valid = 0;
+#pragma unroll
+  for (int q = 0; q < kS4; ++q) {
+    const int s4 = tid + kTkThreads * q;
+    const int i = (s4 / (kSampleRun / 4)) * k * kSampleRun + (s4 % (kSampleRun / 4)) * 4;
+    const float qn = __builtin_nanf("");
+    const float4 v = s4 < s_n4 ? load4_masked(row, i, n) : make_float4(qn, qn, qn, qn);
+    smp[q][0] = v.x;
+    smp[q][1] = v.y;
+    smp[q][2] = v.z;
+    smp[q][3] = v.w;
+  }
+#pragma unroll
+  for (int q = 0; q < kS4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mn = fminf(mn, smp[q][e]);
+      mx = fmaxf(mx, smp[q][e]);
+      s_valid += smp[q][e] == smp[q][e];
+    }
+  block_minmax(sm, mn, mx);
+  uint32_t s_total;
+  block_excl_scan(sm, (uint32_t)s_valid, s_total);
+  const LinBins sb = make_bins(mn, mx);
+  // Sample rank aiming at ~2m candidates in the whole segment.
+  const float frac = (float)s_total / (float)n;
+  int rank = (int)ceilf(2.0f * (float)m * frac) + 8;
+  rank = min(rank, (int)s_total);
+  clear_hist(sm, kLinBins);
+#pragma unroll
+  for (int q = 0; q < kS4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (smp[q][e] == smp[q][e]) atomicAdd(&sm.hist[sb(smp[q][e])], 1u);
+  __syncthreads();
+  find_digit(sm, kLinBins, (uint32_t)rank);
+  const int Bs = sm.misc[0];
+  if (tid == 0) sm.misc[5] = 0;  // list length
+  __syncthreads();
+
+  // 2. One pass over the segment: append every element with sample bin >= Bs.
+  constexpr int kChunk = kTkThreads * kChunkVec * 4;
+  for (int c0 = 0; c0 < n; c0 += kChunk) {
+    float4 v[kChunkVec];
+#pragma unroll
+    for (int q = 0; q < kChunkVec; ++q) v[q] = load4_masked(row, c0 + (q * kTkThreads + tid) * 4, n);
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < kChunkVec; ++q) {
+      const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cnt += (xs[e] == xs[e] && sb(xs[e]) >= Bs);
+    }
+    int x = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    int base = 0;
+    if (lane == 63 && x > 0) base = atomicAdd(&sm.misc[5], x);
+    base = __shfl(base, 63, 64);
+    int p = base + x - cnt;
+    if (cnt) {
+#pragma unroll
+      for (int q = 0; q < kChunkVec; ++q) {
+        const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (xs[e] == xs[e] && sb(xs[e]) >= Bs) {
+            if (p < kListCap) {
+              const int i = c0 + (q * kTkThreads + tid) * 4 + e;
+              sm.list_val[p] = xs[e];
+              sm.list_idx[p] = ids ? ids[i] : lo + i;
+            }
+            ++p;
+          }
+      }
+    }
+  }
+  __syncthreads();
+  const int n_list = sm.misc[5];
+  __syncthreads();
+  // 3. Exact selection on the list when it is a valid upper set, else on the segment.
+  if (n_list >= m && n_list <= kListCap) {
+    select_exact(sm, PairSrc{sm.list_val, sm.list_idx}, n_list, m,
+                 [&](int i) { mark(sm.list_idx[i]); });
+  } else {
+    select_exact(sm, RowSrc{row, ids, lo}, n, m, [&](int i) { mark(ids ? ids[i] : lo + i); });
+  }
+}
+
+// ---- kernels ------------------------------------------------------------------------
+
+struct TopkLaunch {
+  TopkArgs a;
+  int seg;          // segment length (kSegments / kMerge)
+  int n_seg;        // segments per row
+  float* cand_val;  // [rows][n_seg][m_pad], NaN where absent
+  int32_t* cand_idx;
+  int m_pad;        // n_sel - 1 rounded up to a multiple of 4
+};
+
+__device__ __forceinline__ void row_geometry(const TopkArgs& a, int64_t row, int bi, int64_t& t,
+                                             int64_t& own, int64_t& C, int& m) {
+  const int64_t base = a.seq_lens ? (int64_t)a.seq_lens[bi] - a.lq : a.q_pos0;
+  t = base + row;
+  own = t >= 0 ? t / a.r : -1;
+  C = t >= 0 ? min(own, a.nblk) : 0;
+  m = (int)min((int64_t)(a.n_sel - 1), C);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
+  __shared__ TkShared sm;
+  const TopkArgs& a = L.a;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int bi = blockIdx.z;
+  const int seg_id = blockIdx.y;
+  int64_t t, own, C;
+  int m;
+  row_geometry(a, row, bi, t, own, C, m);
+  int32_t* out = a.sel + ((int64_t)bi * a.lq + row) * a.n_sel;
+  const int64_t crow = (int64_t)bi * a.lq + row;
+  const float* srow = a.scores + (int64_t)bi * a.s_bs + row * a.ld;
+
+  if (MODE == kSegments) {
+    if (t < 0 || m == C) return;  // the merge launch writes such rows
+    const int lo = seg_id * L.seg;
+    const int n = (int)min(C - lo, (int64_t)L.seg);
+    float* cv = L.cand_val + (crow * L.n_seg + seg_id) * L.m_pad;
+    int32_t* ci = L.cand_idx + (crow * L.n_seg + seg_id) * L.m_pad;
+    const int keep = n > 0 ? min(m, n) : 0;
+    if (keep > 0) {
+      if (tid == 0) sm.misc[7] = 0;
+      __syncthreads();
+      select_row(sm, srow + lo, nullptr, lo, n, keep, [&](int id) {
+        const int p = atomicAdd(&sm.misc[7], 1);
+        cv[p] = srow[id];
+        ci[p] = id;
+      });
+    }
+    for (int k = keep + tid; k < L.m_pad; k += kTkThreads) {
+      cv[k] = __builtin_nanf("");
+      ci[k] = -1;
+    }
+    return;
+  }
+
+  if (t < 0 || m == C) {  // nothing to rank: every earlier block fits
+    for (int k = tid; k < a.n_sel; k += kTkThreads)
+      out[k] = t < 0 ? -1 : (k < C ? k : (k == C ? (int32_t)own : -1));
+    return;
+  }
+
+  if (MODE == kRows) {
+    // C <= kSegMax: kept ids go to a bitmap, written out in ascending order.
+    const int n = (int)C;
+    const int words = (n + 31) / 32;
+    for (int i = tid; i < words; i += kTkThreads) sm.bitmap[i] = 0u;
+    __syncthreads();
+    select_row(sm, srow, nullptr, 0, n, m,
+               [&](int id) { atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31)); });
+    constexpr int wpt = kSegMax / 32 / kTkThreads;  // 4 words per thread
+    uint32_t b[wpt];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int w = 0; w < wpt; ++w) {
+      const int wi = tid * wpt + w;
+      b[w] = wi < words ? sm.bitmap[wi] : 0u;
+      cnt += __popc(b[w]);
+    }
+    uint32_t total;
+    uint32_t off = block_excl_scan(sm, cnt, total);
+#pragma unroll
+    for (int w = 0; w < wpt; ++w) {
+      uint32_t bits = b[w];
+      while (bits) {
+        const int bpos = __ffs(bits) - 1;
+        bits &= bits - 1;
+        out[off++] = (tid * wpt + w) * 32 + bpos;
+      }
+    }
+    for (int k = m + tid; k < a.n_sel; k += kTkThreads) out[k] = k == m ? (int32_t)own : -1;
+  } else {
+    // Merge the segment winners; sort the m kept ids ascending in LDS.
+    const int n = L.n_seg * L.m_pad;
+    if (tid == 0) sm.misc[7] = 0;
+    __syncthreads();
+    select_row(sm, L.cand_val + crow * n, L.cand_idx + crow * n, 0, n, m, [&](int id) {
+      const int p = atomicAdd(&sm.misc[7], 1);
+      sm.kept[p] = id;
+    });
+    int P = 1;
+    while (P < m) P <<= 1;
+    for (int i = m + tid; i < P; i += kTkThreads) sm.kept[i] = 0x7fffffff;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P; i += kTkThreads) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const int32_t u = sm.kept[i], v = sm.kept[ixj];
+            if ((u > v) == ((i & k) == 0)) {
+              sm.kept[i] = v;
+              sm.kept[ixj] = u;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int k = tid; k < a.n_sel; k += kTkThreads)
+      out[k] = k < m ? sm.kept[k] : (k == m ? (int32_t)own : -1);
+  }
+}
+
+// ---- host side ----------------------------------------------------------------------
+
+static int64_t max_candidates(const TopkArgs& a) {
+  // Upper bound of C over the launch's rows (positions may come from the device).
+  if (a.seq_lens) return a.nblk;
+  const int64_t t_last = a.q_pos0 + a.lq - 1;
+  return t_last < 0 ? 0 : min(t_last / a.r, a.nblk);
+}
+
+static void split_plan(const TopkArgs& a, int& seg, int& n_seg) {
+  const int64_t cmax = max_candidates(a);
+  seg = kSegMax;
+  // Few long rows (decode): shorter segments so that enough workgroups run.
+  while (seg > 4096 && a.batch * a.lq * ((cmax + seg - 1) / seg) < 512) seg /= 2;
+  n_seg = (int)((cmax + seg - 1) / seg);
+}
+
+static int m_pad_of(int n_sel) { return (n_sel - 1 + 3) & ~3; }
+
+size_t topk_workspace_bytes(const TopkArgs& a) {
+  if (max_candidates(a) <= kSegMax) return 0;
+  int seg, n_seg;
+  split_plan(a, seg, n_seg);
+  const size_t per = (size_t)a.batch * a.lq * n_seg * m_pad_of(a.n_sel);
+  return ((per * 4 + 255) & ~size_t(255)) * 2;
+}
+
+bool topk_supported(const TopkArgs& a) {
+  int seg, n_seg;
+  split_plan(a, seg, n_seg);
+  return max_candidates(a) <= kSegMax || (int64_t)n_seg * m_pad_of(a.n_sel) < ((int64_t)1 << 30);
+}
+
+hipError_t launch_topk_blocks(const TopkArgs& a, void* ws, hipStream_t stream) {
   if (a.lq <= 0 || a.batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)a.lq, (unsigned)a.batch), dim3(kTkThreads),
-                     0, stream, a);
+  TopkLaunch L{a, 0, 0, nullptr, nullptr, m_pad_of(a.n_sel)};
+  if (max_candidates(a) <= kSegMax) {
+    hipLaunchKernelGGL(topk_kernel<kRows>, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
+                       dim3(kTkThreads), 0, stream, L);
+    return hipGetLastError();
+  }
+  split_plan(a, L.seg, L.n_seg);
+  const size_t per = (size_t)a.batch * a.lq * L.n_seg * L.m_pad;
+  L.cand_val = static_cast<float*>(ws);
+  L.cand_idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ((per * 4 + 255) & ~size_t(255)));
+  hipLaunchKernelGGL(topk_kernel<kSegments>,
+                     dim3((unsigned)a.lq, (unsigned)L.n_seg, (unsigned)a.batch), dim3(kTkThreads),
+                     0, stream, L);
+  hipLaunchKernelGGL(topk_kernel<kMerge>, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
+                     dim3(kTkThreads), 0, stream, L);
   return hipGetLastError();
 }
 

@@ -196,7 +196,7 @@ class PrefillPlan:
             self.out = torch.empty((lq, hq, d), dtype=torch.bfloat16, device=dev)
             self.lse = torch.empty((lq, hq), dtype=torch.float32, device=dev)
         self.k_pooled = torch.empty((lk // r, d_idx), dtype=torch.bfloat16, device=dev)
-        nbytes = _lib.load().qsa_prefill_workspace_bytes(lq, lk, r, row_chunk)
+        nbytes = _lib.load().qsa_prefill_workspace_bytes(lq, lk, r, budget, row_chunk)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
         self.ws_bytes = nbytes
 

@@ -107,7 +107,8 @@ qsa_status qsa_index_scores(int batch, int64_t lq, int h_idx, int d_idx, int r,
  * then -1 up to K/r entries. Exact; no host round trip. Scores must be finite.
  *   scores  fp32 as written by stage 2
  *   sel     int32 [batch][lq][K/r], contiguous
- *   workspace: qsa_topk_workspace_bytes() bytes (0 today; may be NULL).
+ *   workspace: qsa_topk_workspace_bytes() bytes, 16-byte aligned (0 when every row
+ *   has at most 32768 candidates: then it may be NULL). Requires nblk < 2^22.
  */
 size_t qsa_topk_workspace_bytes(int batch, int64_t lq, int64_t nblk, int budget_tokens, int r);
 qsa_status qsa_topk_blocks(int batch, int64_t lq, int r, int budget_tokens,
@@ -158,9 +159,10 @@ qsa_status qsa_sparse_attn_decode(int batch, int hq, int hkv, int d, int r, int 
  * before it are covered by k_pooled_prefix, first_raw_token / r rows, which may be
  * NULL when first_raw_token == 0). Outputs: k_pooled [lk/r][d_idx] (prefix rows
  * copied, new rows pooled) and sel [lq][K/r]. Query row i sits at q_pos0 + i.
- * workspace: qsa_prefill_workspace_bytes() bytes (the score buffer of one chunk).
+ * workspace: qsa_prefill_workspace_bytes() bytes (one chunk's scores + top-k space).
  */
-size_t qsa_prefill_workspace_bytes(int64_t lq, int64_t lk, int r, int64_t row_chunk);
+size_t qsa_prefill_workspace_bytes(int64_t lq, int64_t lk, int r, int budget_tokens,
+                                   int64_t row_chunk);
 qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx, int d_idx,
                               int r, int budget_tokens, const void* q_idx, const float* w,
                               const void* k_idx, int64_t first_raw_token,

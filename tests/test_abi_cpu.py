@@ -92,8 +92,11 @@ def test_workspace_queries_and_short_workspace(lib):
                                       FAKE, FAKE, ctypes.c_float(0.06), FAKE, None, FAKE, n - 1,
                                       None) == 3
     assert "workspace" in _err(lib)
-    p = lib.qsa_prefill_workspace_bytes(131072, 131072, 4, 4096)
+    p = lib.qsa_prefill_workspace_bytes(131072, 131072, 4, 2048, 4096)
     assert p >= 4096 * 32768 * 4
     d = lib.qsa_decode_workspace_bytes(8, 24, 256, 1 << 20, 4, 2048)
     assert d >= 8 * 262144 * 4 + n
     assert lib.qsa_topk_workspace_bytes(1, 10, 10, 2048, 4) == 0
+    assert lib.qsa_topk_workspace_bytes(1, 10, 32768, 2048, 4) == 0
+    # rows longer than one workgroup's 32768 candidates use a two-level selection
+    assert lib.qsa_topk_workspace_bytes(8, 1, 262144, 2048, 4) >= 8 * 32 * 511 * 8

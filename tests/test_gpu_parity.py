@@ -198,6 +198,26 @@ def test_topk_huge_tie_set_takes_lowest_ids():
     _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
 
 
+@pytest.mark.parametrize("sampled_high", [True, False])
+def test_topk_adversarial_sample(sampled_high):
+    # The kernel estimates its threshold from every 8th run of 32 scores (rows of
+    # 32768 candidates). Large values only in the sampled runs make the estimate too
+    # high (fewer than m candidates pass); only outside them, too low (the candidate
+    # list overflows). Both must fall back to the exact selection over the whole row.
+    rng = np.random.default_rng(15 + sampled_high)
+    lq, budget = 3, 2048
+    q_pos0 = 4 * 32768
+    nblk = 32768 + 4
+    x = rng.random((lq, nblk)).astype(np.float32)
+    runs = np.arange(nblk) // 32
+    sampled = runs % 8 == 0
+    hi = sampled if sampled_high else ~sampled
+    x[:, hi] += 10.0
+    _say(f"topk adversarial sampled_high={sampled_high}")
+    sel = _run_topk(_nan_tail(x, q_pos0), q_pos0, nblk, budget)
+    _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
+
+
 def test_topk_decode_rows_batched():
     rng = np.random.default_rng(14)
     bsz, nblk, budget = 3, 262144, 2048
