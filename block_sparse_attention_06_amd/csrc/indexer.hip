@@ -71,10 +71,13 @@ hipError_t launch_pool_keys(const uint16_t* k_idx, int64_t k_stride, int64_t n_b
 // zero rows), so with v_mfma_f32_16x16x32_bf16 the 4 heads of one token land in one
 // lane's 4 accumulators and the weighted ReLU sum over heads is register-local.
 // Workgroup: 4 waves x 16 tokens = 64 query rows; it walks its range of blocks in
-// tiles of 64 pooled keys staged through LDS (shared by the 4 waves), each wave
-// keeping its queries in registers for the whole walk. Causal skipping: the
-// workgroup stops at the last block any of its rows needs, and each score is
-// written only for blocks before its row's own block.
+// tiles of 64 pooled keys, double-buffered in LDS (one barrier per tile), each wave
+// keeping its queries in registers. Columns are permuted so that within a tile, MFMA
+// column c of sub-tile j is block 4c + j: each lane then owns 4 consecutive blocks
+// of a token and writes them as one 16-byte store (a full 256-byte line per token per
+// tile). Causal skipping: the workgroup stops at the last block any of its rows
+// needs; stores wholly past a row's own block are skipped (the rest of a 16-byte
+// store past the own block carries unspecified values, never read).
 // ------------------------------------------------------------------------------------
 
 constexpr int kScoreRows = 64;   // query rows per workgroup
@@ -85,7 +88,8 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
   constexpr int NC = DI / 32;      // 32-dim MFMA k-chunks
   constexpr int ROW = DI + 8;      // LDS row in bf16 elements, padded by 16 B
   constexpr int VPR = DI / 8;      // 16-byte vectors per pooled key
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kScoreTileN * ROW];
+  constexpr int LPT = kScoreTileN * VPR / 256;  // 16-byte loads per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kScoreTileN * ROW];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -100,11 +104,34 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
   const int64_t n_begin = (int64_t)blockIdx.y * n_per_wg;
   const int64_t n_end = min(n_begin + n_per_wg, nb_need);
   if (n_begin >= n_end) return;
+  const int n_tiles = (int)((n_end - n_begin + kScoreTileN - 1) / kScoreTileN);
 
   const uint16_t* qb = a.q_idx + (int64_t)bi * a.q_bs;
   const float* wb = a.w + (int64_t)bi * a.w_bs;
   const uint16_t* kpb = a.kp + (int64_t)bi * a.kp_bs;
   float* sb = a.scores + (int64_t)bi * a.s_bs;
+
+  // Tile loader: thread -> LPT 16-byte vectors of the 64 x DI tile.
+  uint4 stage[LPT];
+  auto load_tile = [&](int64_t n0) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int v = threadIdx.x + 256 * u;
+      const int row = v / VPR, cv = v - row * VPR;
+      const int64_t blk = n0 + row;
+      stage[u] = blk < a.nblk ? ld16(kpb + blk * DI + cv * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int v = threadIdx.x + 256 * u;
+      const int row = v / VPR, cv = v - row * VPR;
+      *reinterpret_cast<uint4*>(&tile[buf][row * ROW + cv * 8]) = stage[u];
+    }
+  };
+
+  load_tile(n_begin);
 
   // A operands: this wave's 16 tokens as 4 M-tiles of (4 tokens x 4 heads).
   uint4 A[4][NC];
@@ -120,46 +147,52 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
   // Epilogue data for the accumulator rows this lane holds: token (mt*4 + quad).
   float W[4][4];
   int64_t lim[4];
-  int64_t tok_of[4];
+  float* orow[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int64_t tok = i0 + wave * 16 + mt * 4 + quad;
     const int64_t t = base + tok;
     const bool valid = tok < a.lq && t >= 0;
-    tok_of[mt] = tok;
     lim[mt] = valid ? min(t / a.r, a.nblk) : 0;
+    orow[mt] = sb + (valid ? tok : 0) * a.ld;
 #pragma unroll
     for (int h = 0; h < 4; ++h) W[mt][h] = (valid && h < a.h_idx) ? wb[tok * a.h_idx + h] : 0.f;
   }
 
-  for (int64_t n0 = n_begin; n0 < n_end; n0 += kScoreTileN) {
-    __syncthreads();
-    for (int v = threadIdx.x; v < kScoreTileN * VPR; v += 256) {
-      const int row = v / VPR, cv = v - row * VPR;
-      const int64_t blk = n0 + row;
-      const uint4 x = blk < a.nblk ? ld16(kpb + blk * DI + cv * 8) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&tile[row * ROW + cv * 8]) = x;
-    }
-    __syncthreads();
+  store_tile(0);
+  __syncthreads();
+  for (int it = 0; it < n_tiles; ++it) {
+    const int64_t n0 = n_begin + (int64_t)it * kScoreTileN;
+    const bool more = it + 1 < n_tiles;
+    if (more) load_tile(n0 + kScoreTileN);
+    const uint16_t* tb = tile[it & 1];
+    f32x4 acc[4][4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int j = 0; j < 4; ++j) {
       uint4 B[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        B[c] = *reinterpret_cast<const uint4*>(&tile[(nt * 16 + c16) * ROW + c * 32 + quad * 8]);
-      const int64_t blk = n0 + nt * 16 + c16;
+        B[c] = *reinterpret_cast<const uint4*>(&tb[(4 * c16 + j) * ROW + c * 32 + quad * 8]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc = mfma_16x16x32(A[mt][c], B[c], acc);
-        if (blk < lim[mt]) {
-          const float s = W[mt][0] * fmaxf(acc[0], 0.f) + W[mt][1] * fmaxf(acc[1], 0.f) +
-                          W[mt][2] * fmaxf(acc[2], 0.f) + W[mt][3] * fmaxf(acc[3], 0.f);
-          sb[tok_of[mt] * a.ld + blk] = s;
-        }
+        for (int c = 0; c < NC; ++c) acc[mt][j] = mfma_16x16x32(A[mt][c], B[c], acc[mt][j]);
       }
     }
+    const int64_t blk0 = n0 + 4 * c16;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      float s[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        s[j] = W[mt][0] * fmaxf(acc[mt][j][0], 0.f) + W[mt][1] * fmaxf(acc[mt][j][1], 0.f) +
+               W[mt][2] * fmaxf(acc[mt][j][2], 0.f) + W[mt][3] * fmaxf(acc[mt][j][3], 0.f);
+      if (blk0 < lim[mt])
+        *reinterpret_cast<float4*>(orow[mt] + blk0) = make_float4(s[0], s[1], s[2], s[3]);
+    }
+    if (more) store_tile((it + 1) & 1);
+    __syncthreads();
   }
 }
 

@@ -80,7 +80,8 @@ qsa_status qsa_pool_keys(const void* k_idx, int64_t k_idx_row_stride, int64_t n_
  * Stage 2 -- light MQA indexer block scores [DR], [RA] (DSA-style reading):
  *   s[t][b] = sum_{h < h_idx} w[t][h] * max(0, q_idx[t][h] . kbar[b])
  * for every block b < min(pos(t) / r, nblk), i.e. every complete block strictly
- * before the query's own block. Entries at b >= pos(t)/r are left unwritten.
+ * before the query's own block. Entries at b >= pos(t)/r hold unspecified values
+ * (up to the next multiple of 4; never read by stage 3).
  * Query row i of sequence s sits at position pos = q_pos0 + i when seq_lens is NULL,
  * else at pos = seq_lens[s] - lq + i (seq_lens is a device array of `batch` int32;
  * rows with pos < 0 score nothing).
