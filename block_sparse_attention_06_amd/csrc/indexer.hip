@@ -196,10 +196,165 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
   }
 }
 
+// ------------------------------------------------------------------------------------
+// Stage 2 for a few query rows per sequence (decode): a streaming scan of the pooled
+// keys. One wave per (sequence, row, range of blocks), no LDS and no barriers: the
+// wave keeps its token's 4 heads as the A operand (rows 0-3 of the MFMA tile, the rest
+// zero) and loads pooled keys straight into B operands, two 64-block tiles in flight
+// (the next tile is loaded before the current one is multiplied). Same column
+// permutation and 16-byte stores as the GEMM above.
+// ------------------------------------------------------------------------------------
+
+template <int DI, bool CAND>
+__global__ __launch_bounds__(256) void index_scores_scan_kernel(ScoreArgs a, int n_ranges,
+                                                                int blocks_per_wave) {
+  // With CAND, a wave's range is one top-k segment (kTopkWaveSeg blocks, 16 tiles of
+  // 64): each tile's rank keys are parked in LDS (one per lane), and at the end the
+  // wave extracts the segment's kTopkWaveKeep best for the top-k merge.
+  __shared__ uint64_t rk_lds[CAND ? 4 : 1][CAND ? 16 * 64 : 1];
+  constexpr int NC = DI / 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15;
+  const int quad = lane >> 4;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t per_seq = a.lq * n_ranges;
+  const int bi = (int)(item / per_seq);
+  if (bi >= a.batch) return;
+  const int64_t rem = item - (int64_t)bi * per_seq;
+  const int64_t row = rem / n_ranges;
+  const int rg = (int)(rem - row * n_ranges);
+  const int64_t base = a.seq_lens ? (int64_t)a.seq_lens[bi] - a.lq : a.q_pos0;
+  const int64_t t = base + row;
+  if (t < 0) return;
+  const int64_t lim = min(t / a.r, a.nblk);
+  const int64_t n0 = (int64_t)rg * blocks_per_wave;
+  const int64_t n1 = min(n0 + blocks_per_wave, lim);
+  const int64_t cslot = ((int64_t)bi * a.lq + row) * a.cand.n_seg + rg;
+  if (n0 >= n1) {
+    if (CAND && lane < kTopkWaveKeep) {  // an empty segment: padding only
+      a.cand.cand_val[cslot * kTopkWaveKeep + lane] = __builtin_nanf("");
+      a.cand.cand_idx[cslot * kTopkWaveKeep + lane] = -1;
+      if (lane == 0) a.cand.bnd_idx[cslot] = -1;
+    }
+    return;
+  }
+
+  const uint16_t* kpb = a.kp + (int64_t)bi * a.kp_bs;
+  float* orow = a.scores + (int64_t)bi * a.s_bs + row * a.ld;
+  // A: row c16 is head c16 of this token (zero beyond the indexer heads).
+  uint4 A[NC];
+  {
+    const bool ok = c16 < min(a.h_idx, 4);
+    const uint16_t* p = a.q_idx + (int64_t)bi * a.q_bs + (row * a.h_idx + (ok ? c16 : 0)) * DI +
+                        quad * 8;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) A[c] = ok ? ld16(p + c * 32) : make_uint4(0, 0, 0, 0);
+  }
+  float W[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+    W[h] = h < a.h_idx ? a.w[(int64_t)bi * a.w_bs + row * a.h_idx + h] : 0.f;
+
+  uint4 B0[4][NC], B1[4][NC];
+  auto load = [&](uint4 (&B)[4][NC], int64_t nb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t blk = min(nb + 4 * c16 + j, n1 - 1);  // clamped; extra columns unused
+      const uint16_t* p = kpb + blk * DI + quad * 8;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) B[j][c] = ld16(p + c * 32);
+    }
+  };
+  auto compute = [&](const uint4 (&B)[4][NC], int64_t nb) {
+    float s[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc = mfma_16x16x32(A[c], B[j][c], acc);
+      s[j] = W[0] * fmaxf(acc[0], 0.f) + W[1] * fmaxf(acc[1], 0.f) + W[2] * fmaxf(acc[2], 0.f) +
+             W[3] * fmaxf(acc[3], 0.f);
+    }
+    const int64_t blk0 = nb + 4 * c16;
+    if (quad == 0 && blk0 < n1)
+      *reinterpret_cast<float4*>(orow + blk0) = make_float4(s[0], s[1], s[2], s[3]);
+    if constexpr (CAND) {
+      // Lane L takes block nb + L: element L % 4 of quad-0 lane L / 4.
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = __shfl(s[j], lane >> 2, 64);
+      const int j = lane & 3;
+      const float mine = j == 0 ? v[0] : (j == 1 ? v[1] : (j == 2 ? v[2] : v[3]));
+      const int64_t blk = nb + lane;
+      const int it = (int)((nb - n0) >> 6);
+      rk_lds[wave][it * 64 + lane] = blk < n1 ? rank_key(mine, (int32_t)blk) : 0ull;
+    }
+  };
+  const int n_tiles = (int)((n1 - n0 + 63) / 64);
+  load(B0, n0);
+  for (int it = 0; it < n_tiles; it += 2) {
+    const int64_t nb = n0 + (int64_t)it * 64;
+    if (it + 1 < n_tiles) load(B1, nb + 64);
+    compute(B0, nb);
+    if (it + 2 < n_tiles) load(B0, nb + 128);
+    if (it + 1 < n_tiles) compute(B1, nb + 64);
+  }
+  if constexpr (CAND) {
+    uint64_t rk[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rk[i] = i < n_tiles ? rk_lds[wave][i * 64 + lane] : 0ull;
+    const int n_valid = (int)(n1 - n0);
+    const int keep = min(n_valid, kTopkWaveKeep);
+    float* cv = a.cand.cand_val + cslot * kTopkWaveKeep;
+    int32_t* ci = a.cand.cand_idx + cslot * kTopkWaveKeep;
+    const uint64_t last = wave_extract_top(rk, keep, [&](int k, uint64_t w) {
+      cv[k] = key_to_float((uint32_t)(w >> 32));
+      ci[k] = rank_key_id(w);
+    });
+    if (lane == 0) {
+      for (int k = keep; k < kTopkWaveKeep; ++k) {
+        cv[k] = __builtin_nanf("");
+        ci[k] = -1;
+      }
+      const bool truncated = n_valid > keep;
+      a.cand.bnd_val[cslot] = truncated ? key_to_float((uint32_t)(last >> 32)) : 0.f;
+      a.cand.bnd_idx[cslot] = truncated ? rank_key_id(last) : -1;
+    }
+  }
+}
+
 hipError_t launch_index_scores(const ScoreArgs& a, hipStream_t stream) {
   if (a.lq <= 0 || a.batch <= 0 || a.nblk <= 0) return hipSuccess;
+  if (a.lq <= 4 || a.cand.cand_val) {
+    // About 2048 waves (two per SIMD): one round over the GPU, 64-block tiles. With
+    // candidates, a wave covers exactly one top-k segment.
+    const int64_t rows = (int64_t)a.batch * a.lq;
+    int64_t bpw = (rows * a.nblk + 2047) / 2048;
+    bpw = (bpw + 63) / 64 * 64;
+    if (bpw < 64) bpw = 64;
+    if (a.cand.cand_val) bpw = kTopkWaveSeg;
+    const int n_ranges = (int)((a.nblk + bpw - 1) / bpw);
+    const int64_t waves = rows * n_ranges;
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (a.cand.cand_val) {
+      if (a.d_idx == 128)
+        hipLaunchKernelGGL((index_scores_scan_kernel<128, true>), grid, dim3(256), 0, stream, a,
+                           n_ranges, (int)bpw);
+      else
+        hipLaunchKernelGGL((index_scores_scan_kernel<64, true>), grid, dim3(256), 0, stream, a,
+                           n_ranges, (int)bpw);
+    } else if (a.d_idx == 128) {
+      hipLaunchKernelGGL((index_scores_scan_kernel<128, false>), grid, dim3(256), 0, stream, a,
+                         n_ranges, (int)bpw);
+    } else {
+      hipLaunchKernelGGL((index_scores_scan_kernel<64, false>), grid, dim3(256), 0, stream, a,
+                         n_ranges, (int)bpw);
+    }
+    return hipGetLastError();
+  }
   // Blocks per workgroup along the key axis: enough workgroups to fill 256 CUs
-  // even when few query rows are scored (decode), long walks otherwise.
+  // even when few query rows are scored, long walks otherwise.
   const int64_t row_tiles = (a.lq + kScoreRows - 1) / kScoreRows;
   int64_t n_per_wg = 2048;
   while (n_per_wg > kScoreTileN && row_tiles * a.batch * ((a.nblk + n_per_wg - 1) / n_per_wg) < 2048)

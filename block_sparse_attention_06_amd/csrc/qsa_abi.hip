@@ -401,7 +401,19 @@ qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int 
                               void* stream) {
   QSA_TRY(check_r(r));
   QSA_TRY(check_budget(budget_tokens, r));
-  QSA_REQUIRE(batch >= 1, QSA_ERR_INVALID_ARGUMENT, "batch=%d", batch);
+  QSA_TRY(check_indexer_shape(h_idx, d_idx));
+  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_REQUIRE(batch >= 1 && batch <= 65535, QSA_ERR_INVALID_ARGUMENT, "batch=%d", batch);
+  QSA_REQUIRE(lmax >= r && lmax / r < ((int64_t)1 << 22), QSA_ERR_UNSUPPORTED,
+              "lmax=%lld: 4 <= lmax and lmax / r < 2^22", (long long)lmax);
+  QSA_REQUIRE(q_idx && w && k_pooled && seq_lens && sel, QSA_ERR_INVALID_ARGUMENT,
+              "null tensor pointer");
+  QSA_REQUIRE(aligned16(q_idx) && aligned16(k_pooled), QSA_ERR_INVALID_ARGUMENT,
+              "q_idx and k_pooled must be 16-byte aligned");
+  QSA_REQUIRE(batch == 1 || (k_pooled_batch_stride % 8 == 0 &&
+                             k_pooled_batch_stride >= (lmax / r) * (int64_t)d_idx),
+              QSA_ERR_INVALID_ARGUMENT, "k_pooled_batch_stride=%lld",
+              (long long)k_pooled_batch_stride);
   const size_t need = qsa_decode_workspace_bytes(batch, hq, d, lmax, r, budget_tokens);
   QSA_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), QSA_ERR_WORKSPACE,
               "decode workspace: need %zu bytes (16-byte aligned), got %zu", need,
@@ -412,11 +424,23 @@ qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int 
   const size_t sc_bytes = align256((size_t)batch * (size_t)ld * sizeof(float));
   const size_t tk_bytes = align256(qsa_topk_workspace_bytes(batch, 1, nblk, budget_tokens, r));
   char* tk = static_cast<char*>(workspace) + sc_bytes;
-  QSA_TRY(qsa_index_scores(batch, 1, h_idx, d_idx, r, q_idx, (int64_t)h_idx * d_idx, w, h_idx,
-                           k_pooled, k_pooled_batch_stride, nblk, 0, seq_lens, sc, ld, ld,
-                           stream));
-  QSA_TRY(qsa_topk_blocks(batch, 1, r, budget_tokens, sc, ld, ld, nblk, 0, seq_lens, sel, tk,
-                          tk_bytes, stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  qsa::ScoreArgs sa{static_cast<const uint16_t*>(q_idx), (int64_t)h_idx * d_idx, w, h_idx,
+                    static_cast<const uint16_t*>(k_pooled), k_pooled_batch_stride, nblk, 1,
+                    h_idx, d_idx, r, 0, seq_lens, sc, ld, ld, batch, {}};
+  const qsa::TopkArgs ta = topk_args(batch, 1, r, budget_tokens, sc, ld, ld, nblk, 0, seq_lens,
+                                     sel);
+  QSA_REQUIRE(qsa::topk_supported(ta), QSA_ERR_UNSUPPORTED, "rows of %lld blocks",
+              (long long)nblk);
+  if (tk_bytes > 0) {
+    // Long rows: the scan also emits per-segment candidates, then one merge launch.
+    sa.cand = qsa::topk_candidates(ta, tk);
+    QSA_TRY(hip_status(qsa::launch_index_scores(sa, s), "decode score scan launch"));
+    QSA_TRY(hip_status(qsa::launch_topk_merge(ta, tk, s), "decode top-k merge launch"));
+  } else {
+    QSA_TRY(hip_status(qsa::launch_index_scores(sa, s), "decode score scan launch"));
+    QSA_TRY(hip_status(qsa::launch_topk_blocks(ta, tk, s), "decode top-k launch"));
+  }
   return qsa_sparse_attn_decode(batch, hq, hkv, d, r, budget_tokens / r, q, k_cache, v_cache,
                                 cache_batch_stride, lmax, seq_lens, sel, softmax_scale, out, lse,
                                 tk + tk_bytes, workspace_bytes - sc_bytes - tk_bytes, stream);

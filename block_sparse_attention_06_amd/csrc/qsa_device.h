@@ -47,6 +47,55 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key (-0.0 comes back as +0.0).
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Rank composite of a (score, id) pair: larger means ranked earlier (score
+// descending, then id ascending). 0 is below every finite score's composite.
+__device__ __forceinline__ uint64_t rank_key(float v, int32_t id) {
+  return ((uint64_t)order_key(v) << 32) | (uint64_t)(0xffffffffu - (uint32_t)id);
+}
+
+__device__ __forceinline__ int32_t rank_key_id(uint64_t rk) {
+  return (int32_t)(0xffffffffu - (uint32_t)rk);
+}
+
+// Wave-wide: extract the `keep` largest of the 64 x 16 rank keys held by the lanes
+// (0 = empty slot), largest first; calls emit(k, rank_key) on the lane that held the
+// k-th one. Returns the last extracted key (wave-uniform), 0 if keep == 0.
+template <class Emit>
+__device__ __forceinline__ uint64_t wave_extract_top(uint64_t (&rk)[16], int keep, Emit emit) {
+  uint64_t last = 0;
+  for (int k = 0; k < keep; ++k) {
+    uint64_t best = 0;
+    int slot = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (rk[i] > best) {
+        best = rk[i];
+        slot = i;
+      }
+    uint64_t wbest = best;
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)wbest, d, 64);
+      const uint32_t hi = __shfl_xor((uint32_t)(wbest >> 32), d, 64);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      wbest = o > wbest ? o : wbest;
+    }
+    if (best == wbest && wbest != 0) {  // ids are unique: one lane holds the winner
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i == slot) rk[i] = 0ull;
+      emit(k, wbest);
+    }
+    last = wbest;
+  }
+  return last;
+}
+
 __device__ __forceinline__ float wave_xor_max(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, kWave));
 }

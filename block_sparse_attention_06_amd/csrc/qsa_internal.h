@@ -11,6 +11,18 @@ namespace qsa {
 hipError_t launch_pool_keys(const uint16_t* k_idx, int64_t k_stride, int64_t n_blocks, int d_idx,
                             int r, uint16_t* k_pooled, int64_t p_stride, hipStream_t stream);
 
+// Two-level top-k: per segment of kTopkWaveSeg candidates, the kTopkWaveKeep best as
+// (score, id) pairs (id -1: empty) and the worst kept one when the segment had more.
+constexpr int kTopkWaveSeg = 1024;
+constexpr int kTopkWaveKeep = 16;
+struct TopkCandidates {
+  float* cand_val;   // [rows][n_seg][kTopkWaveKeep]
+  int32_t* cand_idx;
+  float* bnd_val;    // [rows][n_seg]
+  int32_t* bnd_idx;  // -1: the segment kept all its candidates
+  int n_seg;
+};
+
 // ---- stage 2 ----
 struct ScoreArgs {
   const uint16_t* q_idx;
@@ -30,6 +42,7 @@ struct ScoreArgs {
   int64_t ld;
   int64_t s_bs;
   int batch;
+  TopkCandidates cand;  // optional (few rows per sequence): also emit segment candidates
 };
 hipError_t launch_index_scores(const ScoreArgs& a, hipStream_t stream);
 
@@ -50,6 +63,10 @@ struct TopkArgs {
 size_t topk_workspace_bytes(const TopkArgs& a);
 bool topk_supported(const TopkArgs& a);
 hipError_t launch_topk_blocks(const TopkArgs& a, void* ws, hipStream_t stream);
+// Candidate layout inside a top-k workspace (when topk_workspace_bytes(a) > 0), and
+// the merge launch alone (for a caller that wrote the candidates itself).
+TopkCandidates topk_candidates(const TopkArgs& a, void* ws);
+hipError_t launch_topk_merge(const TopkArgs& a, void* ws, hipStream_t stream);
 
 // ---- stage 4 / 4' ----
 struct AttnArgs {

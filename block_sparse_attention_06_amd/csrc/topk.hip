@@ -24,9 +24,15 @@
 //   c. candidates above the final bucket are kept; the bucket is sorted in LDS by
 //      (key desc, id asc) -- or, when more than kTieCap candidates share one exact
 //      key, a radix select on the id keeps the lowest ids.
-// Rows longer than kSegMax candidates use two launches: each segment keeps its m best
-// (the row's m best are among them), then a merge selects the m best of those.
+// Rows longer than kSegMax candidates use two launches: one wave per segment of
+// kWaveSeg scores keeps its kWaveKeep best (repeated wave-wide maximum, no barriers)
+// and reports the worst of them; the merge selects the m best of all kept candidates,
+// which is the row's answer when every truncated segment's reported worst ranks at
+// or after the m-th selected (nothing left behind could rank higher); otherwise the
+// merge repeats the exact selection over the whole row.
 // No floating-point atomics; results do not depend on scheduling.
+
+#include <type_traits>
 
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -43,24 +49,33 @@ constexpr int kMaxSel = 1024;
 constexpr int kSampleRun = 32;  // consecutive scores per sampled run
 constexpr int kSampleMax = 4096;
 
-enum TopkMode { kRows = 0, kSegments = 1, kMerge = 2 };
+constexpr int kWaveSeg = kTopkWaveSeg;    // scores per wave in the first pass
+constexpr int kWaveKeep = kTopkWaveKeep;  // candidates kept per wave segment
 
-struct TkShared {
+enum TopkMode { kRows = 0, kMerge = 2 };
+
+template <int LIST, int BWORDS>
+struct TkSharedT {
+  static constexpr int kList = LIST;         // filtered candidates kept in LDS
+  static constexpr int kBitmapWords = BWORDS;  // output bitmap (ids < 32 * BWORDS)
   uint32_t hist[kLinBins];
-  float list_val[kListCap];
-  int32_t list_idx[kListCap];
+  float list_val[LIST];
+  int32_t list_idx[LIST];
   uint32_t tie_key[kTieCap];
   int32_t tie_idx[kTieCap];
-  uint32_t bitmap[kSegMax / 32];
+  uint32_t bitmap[BWORDS];
   int32_t kept[kMaxSel];
   uint32_t wsum[kWaves];
   float wred[2 * kWaves];
   int32_t misc[8];
 };
+using TkRowsShared = TkSharedT<kListCap, kSegMax / 32>;       // ~37 KB
+using TkMergeShared = TkSharedT<2 * kListCap, 262144 / 32>;   // ~82 KB
 
 // ---- block-level primitives ---------------------------------------------------------
 
-__device__ __forceinline__ uint32_t block_excl_scan(TkShared& sm, uint32_t v, uint32_t& total) {
+template <class SM>
+__device__ __forceinline__ uint32_t block_excl_scan(SM& sm, uint32_t v, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -82,7 +97,8 @@ __device__ __forceinline__ uint32_t block_excl_scan(TkShared& sm, uint32_t v, ui
   return off + x - v;
 }
 
-__device__ __forceinline__ void block_minmax(TkShared& sm, float& mn, float& mx) {
+template <class SM>
+__device__ __forceinline__ void block_minmax(SM& sm, float& mn, float& mx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int d = 32; d > 0; d >>= 1) {
@@ -106,7 +122,8 @@ __device__ __forceinline__ void block_minmax(TkShared& sm, float& mn, float& mx)
 
 // Over hist[0..nbins), find D with above(D) < need <= above(D) + hist[D], above(D) being
 // the count in digits > D (thread 0 owns the highest digits). Results in misc[0..2].
-__device__ __forceinline__ void find_digit(TkShared& sm, int nbins, uint32_t need) {
+template <class SM>
+__device__ __forceinline__ void find_digit(SM& sm, int nbins, uint32_t need) {
   const int tid = threadIdx.x;
   const int per = nbins / kTkThreads;
   const int hi = nbins - tid * per - 1;
@@ -130,7 +147,8 @@ __device__ __forceinline__ void find_digit(TkShared& sm, int nbins, uint32_t nee
   __syncthreads();
 }
 
-__device__ __forceinline__ void clear_hist(TkShared& sm, int nbins) {
+template <class SM>
+__device__ __forceinline__ void clear_hist(SM& sm, int nbins) {
   for (int i = threadIdx.x; i < nbins; i += kTkThreads) sm.hist[i] = 0u;
   __syncthreads();
 }
@@ -147,6 +165,32 @@ __device__ __forceinline__ LinBins make_bins(float mn, float mx) {
   float sc = (float)kLinBins / (mx - mn);
   if (!(mx > mn) || !(sc < 3.0e38f)) sc = 0.f;  // one value (or no usable range): one bin
   return LinBins{mn, sc};
+}
+
+// Block-wide minimum of a 64-bit value (the worst-ranked of the threads' values).
+template <class SM>
+__device__ __forceinline__ uint64_t block_min_u64(SM& sm, uint64_t v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o < v ? o : v;
+  }
+  if (lane == 0) {
+    sm.wsum[wave] = (uint32_t)v;
+    sm.wred[wave] = __uint_as_float((uint32_t)(v >> 32));
+  }
+  __syncthreads();
+  uint64_t r = ~0ull;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint64_t o = ((uint64_t)__float_as_uint(sm.wred[w]) << 32) | sm.wsum[w];
+    r = o < r ? o : r;
+  }
+  __syncthreads();
+  return r;
 }
 
 // ---- element sources (NaN marks an absent element) ----------------------------------
@@ -169,24 +213,49 @@ struct PairSrc {  // (value, id) pairs in global or shared memory; id < 0 is abs
 };
 
 // ---- exact selection of the m best of n elements of a source ------------------------
-// mark(i) is called exactly once for each selected element (by position i).
+// mark(i) is called exactly once for each selected element (by position i). With
+// REGS (n <= kTkThreads * kRegSlots) each thread first loads its elements into
+// registers with independent loads, and every pass runs on registers; otherwise each
+// pass streams the source again.
 
-template <class Src, class Mark>
-__device__ void select_exact(TkShared& sm, const Src& src, int n, int m, Mark mark) {
+constexpr int kRegSlots = 16;  // largest register-held share per thread
+
+template <int SLOTS, class SM, class Src, class Mark>
+__device__ void select_exact_impl(SM& sm, const Src& src, int n, int m, Mark mark) {
+  constexpr bool REGS = SLOTS > 0;
+  constexpr int kRegSlots = REGS ? SLOTS : 1;
   const int tid = threadIdx.x;
+  float xr[kRegSlots];
+  int32_t ir[kRegSlots];
+  if constexpr (REGS) {
+#pragma unroll
+    for (int j = 0; j < kRegSlots; ++j) {
+      const int i = tid + kTkThreads * j;
+      xr[j] = i < n ? src.val(i) : __builtin_nanf("");
+      ir[j] = i < n ? src.id(i) : -1;
+    }
+  }
+  // each(f): f(position, value, id) over this thread's elements (NaN value: absent)
+  auto each = [&](auto&& f) {
+    if constexpr (REGS) {
+#pragma unroll
+      for (int j = 0; j < kRegSlots; ++j) f(tid + kTkThreads * j, xr[j], ir[j]);
+    } else {
+      for (int i = tid; i < n; i += kTkThreads) f(i, src.val(i), src.id(i));
+    }
+  };
+
   float mn = INFINITY, mx = -INFINITY;
-  for (int i = tid; i < n; i += kTkThreads) {
-    const float v = src.val(i);
+  each([&](int, float v, int) {
     mn = fminf(mn, v);  // fminf / fmaxf ignore NaN
     mx = fmaxf(mx, v);
-  }
+  });
   block_minmax(sm, mn, mx);
   const LinBins bins = make_bins(mn, mx);
   clear_hist(sm, kLinBins);
-  for (int i = tid; i < n; i += kTkThreads) {
-    const float v = src.val(i);
+  each([&](int, float v, int) {
     if (v == v) atomicAdd(&sm.hist[bins(v)], 1u);
-  }
+  });
   __syncthreads();
   find_digit(sm, kLinBins, (uint32_t)m);
   const int B = sm.misc[0];
@@ -202,14 +271,13 @@ __device__ void select_exact(TkShared& sm, const Src& src, int n, int m, Mark ma
     const int nb = 1 << wbits;
     const int shift = 32 - pbits - wbits;
     clear_hist(sm, nb);
-    for (int i = tid; i < n; i += kTkThreads) {
-      const float v = src.val(i);
+    each([&](int, float v, int) {
       if (v == v && bins(v) == B) {
         const uint32_t key = order_key(v);
         if (pbits == 0 || (key >> (32 - pbits)) == prefix)
           atomicAdd(&sm.hist[(key >> shift) & (nb - 1)], 1u);
       }
-    }
+    });
     __syncthreads();
     find_digit(sm, nb, need);
     need -= (uint32_t)sm.misc[1];
@@ -231,17 +299,16 @@ __device__ void select_exact(TkShared& sm, const Src& src, int n, int m, Mark ma
   const bool fits = bucket <= (uint32_t)kTieCap;
   if (tid == 0) sm.misc[4] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += kTkThreads) {
-    const float v = src.val(i);
+  each([&](int i, float v, int id) {
     const int rel = rel_of(v);
     if (rel > 0) {
       mark(i);
     } else if (rel == 0 && fits) {
       const int p = atomicAdd(&sm.misc[4], 1);
       sm.tie_key[p] = order_key(v);
-      sm.tie_idx[p] = src.id(i);
+      sm.tie_idx[p] = id;
     }
-  }
+  });
   __syncthreads();
 
   if (fits) {
@@ -277,14 +344,12 @@ __device__ void select_exact(TkShared& sm, const Src& src, int n, int m, Mark ma
       // before the need-th entry.
       const uint32_t lim_key = sm.tie_key[need - 1];
       const int32_t lim_idx = sm.tie_idx[need - 1];
-      for (int i = tid; i < n; i += kTkThreads) {
-        const float v = src.val(i);
+      each([&](int i, float v, int id) {
         if (rel_of(v) == 0) {
           const uint32_t key = order_key(v);
-          const int32_t d = src.id(i);
-          if (key > lim_key || (key == lim_key && d <= lim_idx)) mark(i);
+          if (key > lim_key || (key == lim_key && id <= lim_idx)) mark(i);
         }
-      }
+      });
     }
   } else {
     // pbits == 32: the bucket is one exact key; keep its `need` lowest ids. Radix
@@ -296,11 +361,11 @@ __device__ void select_exact(TkShared& sm, const Src& src, int n, int m, Mark ma
       const int nb = 1 << 11;
       const int shift = 22 - ibits - 11;
       clear_hist(sm, nb);
-      for (int i = tid; i < n; i += kTkThreads) {
-        const uint32_t d = (uint32_t)src.id(i);
-        if (rel_of(src.val(i)) == 0 && (ibits == 0 || (d >> (22 - ibits)) == iprefix))
+      each([&](int, float v, int id) {
+        const uint32_t d = (uint32_t)id;
+        if (rel_of(v) == 0 && (ibits == 0 || (d >> (22 - ibits)) == iprefix))
           atomicAdd(&sm.hist[nb - 1 - ((d >> shift) & (nb - 1))], 1u);
-      }
+      });
       __syncthreads();
       find_digit(sm, nb, ineed);
       ineed -= (uint32_t)sm.misc[1];
@@ -308,15 +373,25 @@ __device__ void select_exact(TkShared& sm, const Src& src, int n, int m, Mark ma
       ibits += 11;
       __syncthreads();
     }
-    for (int i = tid; i < n; i += kTkThreads)
-      if (rel_of(src.val(i)) == 0 && (uint32_t)src.id(i) <= iprefix) mark(i);
+    each([&](int i, float v, int id) {
+      if (rel_of(v) == 0 && (uint32_t)id <= iprefix) mark(i);
+    });
   }
   __syncthreads();
 }
 
+// SLOTS: register-held elements per thread for n <= kTkThreads * SLOTS (0: stream).
+template <int SLOTS, class SM, class Src, class Mark>
+__device__ __forceinline__ void select_exact(SM& sm, const Src& src, int n, int m, Mark mark) {
+  if (SLOTS > 0 && n <= kTkThreads * SLOTS)
+    select_exact_impl<SLOTS>(sm, src, n, m, mark);
+  else
+    select_exact_impl<0>(sm, src, n, m, mark);
+}
+
 // ---- filtered selection over a row segment ------------------------------------------
 // Selects the m best of row[0..n) (16-byte aligned; NaN entries are absent; ids are
-// ids[i] when given, else lo + i), calling mark(id) once per kept element.
+// ids[i] when given, else lo + i), calling mark(id, value) once per kept element.
 
 constexpr int kChunkVec = 8;  // float4 loads in flight per thread in the streaming pass
 
@@ -330,8 +405,8 @@ __device__ __forceinline__ float4 load4_masked(const float* row, int i, int n) {
   return v;
 }
 
-template <class Mark>
-__device__ void select_row(TkShared& sm, const float* row, const int32_t* ids, int lo, int n,
+template <class SM, class Mark>
+__device__ void select_row(SM& sm, const float* row, const int32_t* ids, int lo, int n,
                            int m, Mark mark) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -414,7 +489,7 @@ __device__ void select_row(TkShared& sm, const float* row, const int32_t* ids, i
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (xs[e] == xs[e] && sb(xs[e]) >= Bs) {
-            if (p < kListCap) {
+            if (p < SM::kList) {
               const int i = c0 + (q * kTkThreads + tid) * 4 + e;
               sm.list_val[p] = xs[e];
               sm.list_idx[p] = ids ? ids[i] : lo + i;
@@ -428,11 +503,12 @@ __device__ void select_row(TkShared& sm, const float* row, const int32_t* ids, i
   const int n_list = sm.misc[5];
   __syncthreads();
   // 3. Exact selection on the list when it is a valid upper set, else on the segment.
-  if (n_list >= m && n_list <= kListCap) {
-    select_exact(sm, PairSrc{sm.list_val, sm.list_idx}, n_list, m,
-                 [&](int i) { mark(sm.list_idx[i]); });
+  if (n_list >= m && n_list <= SM::kList) {
+    select_exact<SM::kList / kTkThreads>(sm, PairSrc{sm.list_val, sm.list_idx}, n_list, m,
+                                         [&](int i) { mark(sm.list_idx[i], sm.list_val[i]); });
   } else {
-    select_exact(sm, RowSrc{row, ids, lo}, n, m, [&](int i) { mark(ids ? ids[i] : lo + i); });
+    select_exact<0>(sm, RowSrc{row, ids, lo}, n, m,
+                    [&](int i) { mark(ids ? ids[i] : lo + i, row[i]); });
   }
 }
 
@@ -442,9 +518,11 @@ struct TopkLaunch {
   TopkArgs a;
   int seg;          // segment length (kSegments / kMerge)
   int n_seg;        // segments per row
-  float* cand_val;  // [rows][n_seg][m_pad], NaN where absent
+  float* cand_val;  // [rows][n_seg][kseg], NaN where absent
   int32_t* cand_idx;
-  int m_pad;        // n_sel - 1 rounded up to a multiple of 4
+  float* bnd_val;   // [rows][n_seg]: worst kept of a truncated segment (id -1: complete)
+  int32_t* bnd_idx;
+  int kseg;         // candidates kept per segment (multiple of 4)
 };
 
 __device__ __forceinline__ void row_geometry(const TopkArgs& a, int64_t row, int bi, int64_t& t,
@@ -456,14 +534,41 @@ __device__ __forceinline__ void row_geometry(const TopkArgs& a, int64_t row, int
   m = (int)min((int64_t)(a.n_sel - 1), C);
 }
 
+// Writes the ids marked in sm.bitmap (ids < 32 * words) to out[0..) in ascending order.
+template <class SM>
+__device__ __forceinline__ void write_bitmap_ids(SM& sm, int words, int32_t* out) {
+  const int tid = threadIdx.x;
+  constexpr int wpt = SM::kBitmapWords / kTkThreads;
+  uint32_t b[wpt];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int w = 0; w < wpt; ++w) {
+    const int wi = tid * wpt + w;
+    b[w] = wi < words ? sm.bitmap[wi] : 0u;
+    cnt += __popc(b[w]);
+  }
+  uint32_t total;
+  uint32_t off = block_excl_scan(sm, cnt, total);
+#pragma unroll
+  for (int w = 0; w < wpt; ++w) {
+    const int wi = tid * wpt + w;
+    uint32_t bits = b[w];
+    while (bits) {
+      const int bpos = __ffs(bits) - 1;
+      bits &= bits - 1;
+      out[off++] = wi * 32 + bpos;
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
-  __shared__ TkShared sm;
+  using SM = typename std::conditional<MODE == kRows, TkRowsShared, TkMergeShared>::type;
+  __shared__ SM sm;
   const TopkArgs& a = L.a;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int bi = blockIdx.z;
-  const int seg_id = blockIdx.y;
   int64_t t, own, C;
   int m;
   row_geometry(a, row, bi, t, own, C, m);
@@ -471,94 +576,138 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
   const int64_t crow = (int64_t)bi * a.lq + row;
   const float* srow = a.scores + (int64_t)bi * a.s_bs + row * a.ld;
 
-  if (MODE == kSegments) {
-    if (t < 0 || m == C) return;  // the merge launch writes such rows
-    const int lo = seg_id * L.seg;
-    const int n = (int)min(C - lo, (int64_t)L.seg);
-    float* cv = L.cand_val + (crow * L.n_seg + seg_id) * L.m_pad;
-    int32_t* ci = L.cand_idx + (crow * L.n_seg + seg_id) * L.m_pad;
-    const int keep = n > 0 ? min(m, n) : 0;
-    if (keep > 0) {
-      if (tid == 0) sm.misc[7] = 0;
-      __syncthreads();
-      select_row(sm, srow + lo, nullptr, lo, n, keep, [&](int id) {
-        const int p = atomicAdd(&sm.misc[7], 1);
-        cv[p] = srow[id];
-        ci[p] = id;
-      });
-    }
-    for (int k = keep + tid; k < L.m_pad; k += kTkThreads) {
-      cv[k] = __builtin_nanf("");
-      ci[k] = -1;
-    }
-    return;
-  }
-
   if (t < 0 || m == C) {  // nothing to rank: every earlier block fits
     for (int k = tid; k < a.n_sel; k += kTkThreads)
       out[k] = t < 0 ? -1 : (k < C ? k : (k == C ? (int32_t)own : -1));
     return;
   }
 
-  if (MODE == kRows) {
+  if constexpr (MODE == kRows) {
     // C <= kSegMax: kept ids go to a bitmap, written out in ascending order.
     const int n = (int)C;
     const int words = (n + 31) / 32;
     for (int i = tid; i < words; i += kTkThreads) sm.bitmap[i] = 0u;
     __syncthreads();
     select_row(sm, srow, nullptr, 0, n, m,
-               [&](int id) { atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31)); });
-    constexpr int wpt = kSegMax / 32 / kTkThreads;  // 4 words per thread
-    uint32_t b[wpt];
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int w = 0; w < wpt; ++w) {
-      const int wi = tid * wpt + w;
-      b[w] = wi < words ? sm.bitmap[wi] : 0u;
-      cnt += __popc(b[w]);
-    }
-    uint32_t total;
-    uint32_t off = block_excl_scan(sm, cnt, total);
-#pragma unroll
-    for (int w = 0; w < wpt; ++w) {
-      uint32_t bits = b[w];
-      while (bits) {
-        const int bpos = __ffs(bits) - 1;
-        bits &= bits - 1;
-        out[off++] = (tid * wpt + w) * 32 + bpos;
-      }
-    }
+               [&](int id, float) { atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31)); });
+    write_bitmap_ids(sm, words, out);
     for (int k = m + tid; k < a.n_sel; k += kTkThreads) out[k] = k == m ? (int32_t)own : -1;
   } else {
-    // Merge the segment winners; sort the m kept ids ascending in LDS.
-    const int n = L.n_seg * L.m_pad;
+    // Merge the segment winners, check that no truncated segment could hide a better
+    // candidate (else redo the selection on the whole row), write the ids ascending.
+    const int n = L.n_seg * kWaveKeep;
+    const float* cv = L.cand_val + crow * n;
+    const int32_t* ci = L.cand_idx + crow * n;
+    const bool use_bitmap = C <= (int64_t)SM::kBitmapWords * 32;
+    const int words = use_bitmap ? (int)((C + 31) / 32) : 0;
+    for (int i = tid; i < words; i += kTkThreads) sm.bitmap[i] = 0u;
     if (tid == 0) sm.misc[7] = 0;
     __syncthreads();
-    select_row(sm, L.cand_val + crow * n, L.cand_idx + crow * n, 0, n, m, [&](int id) {
-      const int p = atomicAdd(&sm.misc[7], 1);
-      sm.kept[p] = id;
-    });
-    int P = 1;
-    while (P < m) P <<= 1;
-    for (int i = m + tid; i < P; i += kTkThreads) sm.kept[i] = 0x7fffffff;
-    __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < P; i += kTkThreads) {
-          const int ixj = i ^ j;
-          if (ixj > i) {
-            const int32_t u = sm.kept[i], v = sm.kept[ixj];
-            if ((u > v) == ((i & k) == 0)) {
-              sm.kept[i] = v;
-              sm.kept[ixj] = u;
+    uint64_t worst = ~0ull;
+    auto keep_id = [&](int id, float v) {
+      if (use_bitmap) {
+        atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31));
+      } else {
+        const int p = atomicAdd(&sm.misc[7], 1);
+        sm.kept[p] = id;
+      }
+      const uint64_t rk = rank_key(v, id);
+      worst = rk < worst ? rk : worst;
+    };
+    if (n <= kTkThreads * kRegSlots) {
+      // Few candidates: each thread holds its share in registers.
+      select_exact<kRegSlots>(sm, PairSrc{cv, ci}, n, m, [&](int i) { keep_id(ci[i], cv[i]); });
+    } else {
+      select_row(sm, cv, ci, 0, n, m, keep_id);
+    }
+    worst = block_min_u64(sm, worst);
+    bool bad = false;
+    for (int sg = tid; sg < L.n_seg; sg += kTkThreads) {
+      const int32_t bid = L.bnd_idx[crow * L.n_seg + sg];
+      if (bid >= 0 && rank_key(L.bnd_val[crow * L.n_seg + sg], bid) > worst) bad = true;
+    }
+    if (__syncthreads_or(bad)) {
+      for (int i = tid; i < words; i += kTkThreads) sm.bitmap[i] = 0u;
+      if (tid == 0) sm.misc[7] = 0;
+      __syncthreads();
+      select_row(sm, srow, nullptr, 0, (int)C, m, keep_id);
+    }
+    if (use_bitmap) {
+      write_bitmap_ids(sm, words, out);
+    } else {
+      int P = 1;
+      while (P < m) P <<= 1;
+      for (int i = m + tid; i < P; i += kTkThreads) sm.kept[i] = 0x7fffffff;
+      __syncthreads();
+      for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+          for (int i = tid; i < P; i += kTkThreads) {
+            const int ixj = i ^ j;
+            if (ixj > i) {
+              const int32_t u = sm.kept[i], v = sm.kept[ixj];
+              if ((u > v) == ((i & k) == 0)) {
+                sm.kept[i] = v;
+                sm.kept[ixj] = u;
+              }
             }
           }
+          __syncthreads();
         }
-        __syncthreads();
       }
+      for (int k = tid; k < m; k += kTkThreads) out[k] = sm.kept[k];
     }
-    for (int k = tid; k < a.n_sel; k += kTkThreads)
-      out[k] = k < m ? sm.kept[k] : (k == m ? (int32_t)own : -1);
+    for (int k = m + tid; k < a.n_sel; k += kTkThreads) out[k] = k == m ? (int32_t)own : -1;
+  }
+}
+
+// First pass over long rows: wave w of the launch takes segment (row, seg) of
+// kWaveSeg scores, each lane holding 16 of them, and extracts its kWaveKeep best by
+// repeated wave-wide maxima of (score, id) rank keys.
+__global__ __launch_bounds__(256) void topk_wave_segments_kernel(TopkLaunch L) {
+  const TopkArgs& a = L.a;
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)a.batch * a.lq;
+  const int64_t crow = item / L.n_seg;
+  if (crow >= rows) return;
+  const int seg_id = (int)(item - crow * L.n_seg);
+  const int bi = (int)(crow / a.lq);
+  const int64_t row = crow - (int64_t)bi * a.lq;
+  int64_t t, own, C;
+  int m;
+  row_geometry(a, row, bi, t, own, C, m);
+  float* cv = L.cand_val + (crow * L.n_seg + seg_id) * kWaveKeep;
+  int32_t* ci = L.cand_idx + (crow * L.n_seg + seg_id) * kWaveKeep;
+  if (t < 0 || m == C) return;  // the merge writes such rows without reading candidates
+  const int lo = seg_id * kWaveSeg;
+  const int n = (int)max((int64_t)0, min(C - lo, (int64_t)kWaveSeg));
+  const float* src = a.scores + (int64_t)bi * a.s_bs + row * a.ld + lo;
+  // lane holds positions 4*(lane + 64*q) + e, q < 4
+  uint64_t rk[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int p = 4 * (lane + 64 * q);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p < n) v = *reinterpret_cast<const float4*>(src + p);  // inside the row: ld % 4 == 0
+    const float xs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rk[4 * q + e] = p + e < n ? rank_key(xs[e], lo + p + e) : 0ull;
+  }
+  const int keep = min(n, kWaveKeep);
+  const uint64_t last = wave_extract_top(rk, keep, [&](int k, uint64_t w) {
+    const int32_t id = rank_key_id(w);
+    cv[k] = src[id - lo];
+    ci[k] = id;
+  });
+  if (lane == 0) {
+    for (int k = keep; k < kWaveKeep; ++k) {
+      cv[k] = __builtin_nanf("");
+      ci[k] = -1;
+    }
+    const bool truncated = n > keep;
+    L.bnd_val[crow * L.n_seg + seg_id] =
+        truncated ? a.scores[(int64_t)bi * a.s_bs + row * a.ld + rank_key_id(last)] : 0.f;
+    L.bnd_idx[crow * L.n_seg + seg_id] = truncated ? rank_key_id(last) : -1;
   }
 }
 
@@ -571,45 +720,64 @@ static int64_t max_candidates(const TopkArgs& a) {
   return t_last < 0 ? 0 : min(t_last / a.r, a.nblk);
 }
 
-static void split_plan(const TopkArgs& a, int& seg, int& n_seg) {
-  const int64_t cmax = max_candidates(a);
-  seg = kSegMax;
-  // Few long rows (decode): shorter segments so that enough workgroups run.
-  while (seg > 4096 && a.batch * a.lq * ((cmax + seg - 1) / seg) < 512) seg /= 2;
-  n_seg = (int)((cmax + seg - 1) / seg);
+static int n_wave_segs(const TopkArgs& a) {
+  return (int)((max_candidates(a) + kWaveSeg - 1) / kWaveSeg);
 }
 
-static int m_pad_of(int n_sel) { return (n_sel - 1 + 3) & ~3; }
+static size_t align_up(size_t n) { return (n + 255) & ~size_t(255); }
 
 size_t topk_workspace_bytes(const TopkArgs& a) {
   if (max_candidates(a) <= kSegMax) return 0;
-  int seg, n_seg;
-  split_plan(a, seg, n_seg);
-  const size_t per = (size_t)a.batch * a.lq * n_seg * m_pad_of(a.n_sel);
-  return ((per * 4 + 255) & ~size_t(255)) * 2;
+  const size_t rows = (size_t)a.batch * a.lq;
+  const size_t segs = rows * n_wave_segs(a);
+  return 2 * align_up(segs * kWaveKeep * 4) + 2 * align_up(segs * 4);
 }
 
 bool topk_supported(const TopkArgs& a) {
-  int seg, n_seg;
-  split_plan(a, seg, n_seg);
-  return max_candidates(a) <= kSegMax || (int64_t)n_seg * m_pad_of(a.n_sel) < ((int64_t)1 << 30);
+  return max_candidates(a) <= kSegMax ||
+         (int64_t)n_wave_segs(a) * kWaveKeep < ((int64_t)1 << 30);
+}
+
+TopkCandidates topk_candidates(const TopkArgs& a, void* ws) {
+  const int n_seg = n_wave_segs(a);
+  const size_t segs = (size_t)a.batch * a.lq * n_seg;
+  char* p = static_cast<char*>(ws);
+  TopkCandidates c;
+  c.n_seg = n_seg;
+  c.cand_val = reinterpret_cast<float*>(p);
+  p += align_up(segs * kWaveKeep * 4);
+  c.cand_idx = reinterpret_cast<int32_t*>(p);
+  p += align_up(segs * kWaveKeep * 4);
+  c.bnd_val = reinterpret_cast<float*>(p);
+  p += align_up(segs * 4);
+  c.bnd_idx = reinterpret_cast<int32_t*>(p);
+  return c;
+}
+
+static TopkLaunch merge_launch(const TopkArgs& a, void* ws) {
+  const TopkCandidates c = topk_candidates(a, ws);
+  return TopkLaunch{a, kWaveSeg, c.n_seg, c.cand_val, c.cand_idx, c.bnd_val, c.bnd_idx, kWaveKeep};
+}
+
+hipError_t launch_topk_merge(const TopkArgs& a, void* ws, hipStream_t stream) {
+  if (a.lq <= 0 || a.batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel<kMerge>, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
+                     dim3(kTkThreads), 0, stream, merge_launch(a, ws));
+  return hipGetLastError();
 }
 
 hipError_t launch_topk_blocks(const TopkArgs& a, void* ws, hipStream_t stream) {
   if (a.lq <= 0 || a.batch <= 0) return hipSuccess;
-  TopkLaunch L{a, 0, 0, nullptr, nullptr, m_pad_of(a.n_sel)};
   if (max_candidates(a) <= kSegMax) {
+    TopkLaunch L{a, 0, 0, nullptr, nullptr, nullptr, nullptr, 0};
     hipLaunchKernelGGL(topk_kernel<kRows>, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
                        dim3(kTkThreads), 0, stream, L);
     return hipGetLastError();
   }
-  split_plan(a, L.seg, L.n_seg);
-  const size_t per = (size_t)a.batch * a.lq * L.n_seg * L.m_pad;
-  L.cand_val = static_cast<float*>(ws);
-  L.cand_idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ((per * 4 + 255) & ~size_t(255)));
-  hipLaunchKernelGGL(topk_kernel<kSegments>,
-                     dim3((unsigned)a.lq, (unsigned)L.n_seg, (unsigned)a.batch), dim3(kTkThreads),
-                     0, stream, L);
+  const TopkLaunch L = merge_launch(a, ws);
+  const size_t segs = (size_t)a.batch * a.lq * L.n_seg;
+  hipLaunchKernelGGL(topk_wave_segments_kernel, dim3((unsigned)((segs + 3) / 4)), dim3(256), 0,
+                     stream, L);
   hipLaunchKernelGGL(topk_kernel<kMerge>, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
                      dim3(kTkThreads), 0, stream, L);
   return hipGetLastError();

@@ -98,5 +98,6 @@ def test_workspace_queries_and_short_workspace(lib):
     assert d >= 8 * 262144 * 4 + n
     assert lib.qsa_topk_workspace_bytes(1, 10, 10, 2048, 4) == 0
     assert lib.qsa_topk_workspace_bytes(1, 10, 32768, 2048, 4) == 0
-    # rows longer than one workgroup's 32768 candidates use a two-level selection
-    assert lib.qsa_topk_workspace_bytes(8, 1, 262144, 2048, 4) >= 8 * 32 * 511 * 8
+    # rows longer than one workgroup's 32768 candidates use a two-level selection:
+    # 8 rows x 64 segments x 64 kept (value, id) pairs plus one boundary per segment
+    assert lib.qsa_topk_workspace_bytes(8, 1, 262144, 2048, 4) >= 8 * 64 * (64 + 1) * 8

@@ -218,6 +218,26 @@ def test_topk_adversarial_sample(sampled_high):
     _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
 
 
+def test_topk_long_rows_concentrated_best():
+    # Rows longer than one workgroup's 32768 candidates are split into segments that
+    # each keep only a few candidates. Here every one of the best blocks sits in one
+    # segment (and, in the second row, the scores rise with the block id), so the
+    # merge must notice the truncation and redo the selection over the whole row.
+    rng = np.random.default_rng(16)
+    bsz, nblk, budget = 2, 262144, 2048
+    seq = [1048576, 1048576 - 4 * 1000]
+    x = rng.random((bsz, 1, nblk)).astype(np.float32)
+    x[0, 0, 100000:100600] += 5.0
+    x[1, 0, :] = np.arange(nblk, dtype=np.float32) / nblk
+    _say("topk long rows, concentrated best")
+    sel = _run_topk(x, 0, nblk, budget, seq_lens=seq)
+    for b in range(bsz):
+        t = seq[b] - 1
+        own = t // 4
+        ref = O.select_blocks(x[b, 0, :own].astype(np.float64), own, budget // 4)
+        np.testing.assert_array_equal(sel[b, 0], ref)
+
+
 def test_topk_decode_rows_batched():
     rng = np.random.default_rng(14)
     bsz, nblk, budget = 3, 262144, 2048
@@ -393,6 +413,45 @@ def test_chunked_prefill_1m_sampled():
     rng = np.random.default_rng(23)
     rows = rng.choice(8192, 16, replace=False)
     _prefill_parity("chunked1m", rows=rows)
+
+
+def test_decode_forward_mixed_lengths_and_fallback():
+    # 3 sequences in a 160K-token cache (rows longer than one top-k workgroup):
+    # full, ragged (not a multiple of r) and short (everything fits in the budget).
+    # Sequence 0's pooled keys grow along one direction that its indexer queries
+    # share, so its best blocks are the last ones: the segment candidates of the
+    # fused scan are truncated there and the merge must fall back to the whole row.
+    wl = workload("decode1m", batch=3, lk=163840)
+    seq = [163840, 163840 - 4001, 1500]
+    _say(f"decode forward mixed lengths {seq}")
+    inp = generate(wl, device=DEV, seq_lens=seq)
+    nblk = wl.lk // 4
+    u = torch.nn.functional.normalize(torch.randn(wl.d_i, device=DEV), dim=0)
+    ramp = torch.linspace(0.1, 1.0, nblk, device=DEV)
+    inp["k_pooled"][0] = (ramp[:, None] * u[None, :]).to(torch.bfloat16)
+    inp["q_idx"][0, 0] = u.to(torch.bfloat16)[None, :].expand(wl.h_i, -1)
+    out, lse, sel = Q.qsa_decode_forward(inp["q"], inp["q_idx"], inp["w"], inp["k_pooled"],
+                                         inp["k_cache"], inp["v_cache"], inp["seq_lens"],
+                                         budget=wl.budget)
+    torch.cuda.synchronize()
+
+    def fetch(b, toks):
+        tt = torch.from_numpy(toks).to(DEV)
+        return (O.bf16_to_f64(bits(inp["k_cache"][b][tt])),
+                O.bf16_to_f64(bits(inp["v_cache"][b][tt])))
+
+    res = O.forward_decode(bits(inp["q"]), bits(inp["q_idx"])[:, 0], inp["w"].cpu().numpy()[:, 0],
+                           bits(inp["k_pooled"]), np.array(seq), fetch, r=4, budget=wl.budget)
+    sel_np = sel.cpu().numpy()
+    for b in range(3):
+        t = seq[b] - 1
+        check_selection_row(sel_np[b], res["scores"][b], t // 4, wl.n_sel, f"decode b={b}")
+        toks = O.kept_tokens(sel_np[b], t, 4, t + 1)
+        kr, vr = fetch(b, toks)
+        ref, _ = O.attend(O.bf16_to_f64(bits(inp["q"][b])), kr, vr, 1 / math.sqrt(wl.d))
+        compare_output(out[b], ref, f"decode b={b}")
+    # the best blocks of sequence 0 are among its last ones (ties go to lower ids)
+    assert sel_np[0][0] > (seq[0] - 1) // 4 - 4 * wl.n_sel
 
 
 def test_decode_1m_full():
