@@ -51,6 +51,61 @@ def copy_calibration(torch, mib):
     print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 3}), flush=True)
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+COUNTERS = os.path.join(ROOT, "profiles", "sparse_attn_prefill128k_counters.md")
+ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_06_amd", "csrc", f)
+                for f in ("attention.hip", "qsa_device.h")]
+
+
+def attention_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or None when
+    the summary is missing or was taken on a different attention kernel source."""
+    import re
+    try:
+        with open(COUNTERS) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch=(\d+) kernel_source=([0-9a-f]+)", text)
+    if not m or m.group(2) != attention_source_hash():
+        return None
+    return int(m.group(1))
+
+
+def gather_ceiling(torch, Q, dev, mib, sequential, n_waves=65536, steps=32):
+    """GB/s of the library's gather probe: 4 KiB blocks, the attention step's pattern."""
+    buf = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    nblk = (mib << 20) // 4096
+    n_ids = n_waves * steps * 4
+    if sequential:
+        ids = (torch.arange(n_ids, device=dev, dtype=torch.int64) % nblk).to(torch.int32)
+    else:
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        ids = torch.randint(0, nblk, (n_ids,), generator=g, device=dev, dtype=torch.int32)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    Q.qsa_probe_gather(buf, ids, steps, sink)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(3)]
+    for a, b in evs:
+        a.record()
+        Q.qsa_probe_gather(buf, ids, steps, sink)
+        b.record()
+    torch.cuda.synchronize()
+    ms = min(a.elapsed_time(b) for a, b in evs)
+    del buf, ids
+    return n_waves * steps * 16384 / (ms * 1e-3) / 1e9
+
+
 def kept_tokens(t, n_sel, r=4):
     """Tokens attended by a query at position t (array) under a full selection."""
     own = t // r
@@ -221,11 +276,18 @@ def main():
                    "row_chunk": args.row_chunk, "global_batch": 1, "parallelism": "single GPU"},
         "roofline": {"kernel": "sparse_attn_kernel (kept-token gather + MFMA)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(),
                      "algorithmic_bytes_per_launch": a_bytes, "avg_launch_ms": attn_ms},
         "stages_ms": {"select (pool + scores + top-k)": ms_step - attn_ms, "attention": attn_ms},
         "score_gemm_flops_per_step": score_flops(wl, t),
     }
+    kv_mib = (2 * wl.lk * wl.hkv * wl.d * 2) >> 20
+    ceil_rand = gather_ceiling(torch, Q, dev, kv_mib, sequential=False)
+    ceil_seq = gather_ceiling(torch, Q, dev, 2048, sequential=True)
+    line["gather_ceiling"] = {
+        "random_4KiB_blocks_GBs": ceil_rand, "random_buffer_MiB": kv_mib,
+        "sequential_stream_GBs": ceil_seq, "sequential_buffer_MiB": 2048,
+        "attention_frac_of_random_ceiling": achieved / ceil_rand}
     del inp
     torch.cuda.empty_cache()
     if not args.no_decode:

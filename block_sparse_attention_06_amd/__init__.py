@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     qsa_pool_keys,
     qsa_prefill_forward,
     qsa_prefill_select,
+    qsa_probe_gather,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_fwd,
     qsa_topk_blocks,

@@ -293,3 +293,22 @@ def qsa_decode_forward(q, q_idx, w, k_pooled, k_cache, v_cache, seq_lens, *, bud
           k_cache.stride(0), lmax, _ptr(seq_lens), scale, _ptr(plan.sel), _ptr(plan.out),
           _ptr(plan.lse), _ptr(plan.ws), plan.ws_bytes, _stream(q))
     return plan.out, plan.lse, plan.sel
+
+
+def qsa_probe_gather(buf: torch.Tensor, block_ids: torch.Tensor, steps: int, sink: torch.Tensor):
+    """Measurement aid: read random (or given) 4 KiB blocks of `buf` (see include/qsa.h).
+
+    block_ids int32 [n_waves * steps * 4] on the GPU; checked on the host to lie inside buf.
+    """
+    _need(buf, "buf", buf.dtype, contiguous=True)
+    _need(block_ids, "block_ids", torch.int32, buf.device)
+    _need(sink, "sink", torch.int32, buf.device)
+    n_blocks = buf.numel() * buf.element_size() // 4096
+    if block_ids.numel() % (4 * steps) or sink.numel() < 1024:
+        raise ValueError("block_ids must hold n_waves * steps * 4 ids; sink >= 1024 entries")
+    lo, hi = int(block_ids.min()), int(block_ids.max())
+    if lo < 0 or hi >= n_blocks:
+        raise ValueError(f"block ids [{lo}, {hi}] outside the {n_blocks} blocks of buf")
+    n_waves = block_ids.numel() // (4 * steps)
+    _call("qsa_probe_gather", _ptr(buf), buf.numel() * buf.element_size(), _ptr(block_ids),
+          n_waves, steps, _ptr(sink), _stream(buf))
