@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) void index_scores_scan_kernel(ScoreArgs a, int
              W[3] * fmaxf(acc[3], 0.f);
     }
     const int64_t blk0 = nb + 4 * c16;
-    if (quad == 0 && blk0 < n1)
+    if (!CAND && quad == 0 && blk0 < n1)
       *reinterpret_cast<float4*>(orow + blk0) = make_float4(s[0], s[1], s[2], s[3]);
     if constexpr (CAND) {
       // Lane L takes block nb + L: element L % 4 of quad-0 lane L / 4.
@@ -292,23 +292,49 @@ __global__ __launch_bounds__(256) void index_scores_scan_kernel(ScoreArgs a, int
     }
   };
   const int n_tiles = (int)((n1 - n0 + 63) / 64);
+  // Each tile's loads are issued before the previous tile's MFMAs: the prefetches are
+  // unconditional (addresses past the range clamp to its last block) and a scheduling
+  // barrier keeps the compiler from sinking them below the MFMAs, which would leave a
+  // wave only one tile in flight while it waits.
   load(B0, n0);
   for (int it = 0; it < n_tiles; it += 2) {
     const int64_t nb = n0 + (int64_t)it * 64;
-    if (it + 1 < n_tiles) load(B1, nb + 64);
+    load(B1, nb + 64);
+    __builtin_amdgcn_sched_barrier(0);
     compute(B0, nb);
-    if (it + 2 < n_tiles) load(B0, nb + 128);
+    load(B0, nb + 128);
+    __builtin_amdgcn_sched_barrier(0);
     if (it + 1 < n_tiles) compute(B1, nb + 64);
   }
   if constexpr (CAND) {
+    const int n_valid = (int)(n1 - n0);
+    // The segment's scores leave in one burst of coalesced float4 stores after its
+    // loads (stores interleaved with the key stream cost HBM read/write turnarounds);
+    // the rank keys in LDS carry each score, a -0 coming back as +0.
+    const uint64_t* seg = rk_lds[wave];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int p = q * 256 + 4 * lane;
+      if (p < n_valid) {
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = key_to_float((uint32_t)(seg[p + e] >> 32));
+        if (p + 4 <= n_valid) {
+          *reinterpret_cast<float4*>(orow + n0 + p) = make_float4(f[0], f[1], f[2], f[3]);
+        } else {
+          for (int e = 0; e < n_valid - p; ++e) orow[n0 + p + e] = f[e];
+        }
+      }
+    }
     uint64_t rk[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) rk[i] = i < n_tiles ? rk_lds[wave][i * 64 + lane] : 0ull;
-    const int n_valid = (int)(n1 - n0);
+    for (int i = 0; i < 16; ++i) rk[i] = i < n_tiles ? seg[i * 64 + lane] : 0ull;
     const int keep = min(n_valid, kTopkWaveKeep);
     float* cv = a.cand.cand_val + cslot * kTopkWaveKeep;
     int32_t* ci = a.cand.cand_idx + cslot * kTopkWaveKeep;
-    const uint64_t last = wave_extract_top(rk, keep, [&](int k, uint64_t w) {
+    // The extraction packs its survivors into the first 64 slots of this wave's keys,
+    // which are all in registers by now.
+    const uint64_t last = wave_extract_top(rk, keep, rk_lds[wave], [&](int k, uint64_t w) {
       cv[k] = key_to_float((uint32_t)(w >> 32));
       ci[k] = rank_key_id(w);
     });

@@ -62,11 +62,24 @@ __device__ __forceinline__ int32_t rank_key_id(uint64_t rk) {
   return (int32_t)(0xffffffffu - (uint32_t)rk);
 }
 
-// Wave-wide: extract the `keep` largest of the 64 x 16 rank keys held by the lanes
-// (0 = empty slot), largest first; calls emit(k, rank_key) on the lane that held the
-// k-th one. Returns the last extracted key (wave-uniform), 0 if keep == 0.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Position of this lane among the set lanes of `mask` below it.
+__device__ __forceinline__ int lane_prefix(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Wave-wide, by repeated maxima: extract the `keep` largest of the 64 x 16 rank keys
+// held by the lanes (0 = empty slot), largest first; calls emit(k, rank_key) on the
+// lane that held the k-th one. Returns the last extracted key (wave-uniform), 0 if
+// keep == 0. Costs one wave-wide reduction per key.
 template <class Emit>
-__device__ __forceinline__ uint64_t wave_extract_top(uint64_t (&rk)[16], int keep, Emit emit) {
+__device__ __forceinline__ uint64_t wave_extract_top_iter(uint64_t (&rk)[16], int keep, Emit emit) {
   uint64_t last = 0;
   for (int k = 0; k < keep; ++k) {
     uint64_t best = 0;
@@ -94,6 +107,50 @@ __device__ __forceinline__ uint64_t wave_extract_top(uint64_t (&rk)[16], int kee
     last = wbest;
   }
   return last;
+}
+
+// Same contract as wave_extract_top_iter for keep <= 16, in three wave-wide passes
+// instead of one reduction per key:
+//  1. the keep-th largest of the 64 lane maxima, thr, is a lower bound of the keep-th
+//     largest key (the keep lane maxima >= thr are distinct keys);
+//  2. the keys >= thr (at least keep of them) are packed into `scratch`, 64 wave-private
+//     LDS slots (more than 64 of them, possible only when the largest keys crowd into
+//     few lanes, falls back to the repeated maxima);
+//  3. each packed key's rank is the number of packed keys above it.
+// The nonzero keys must be distinct (rank keys carry the id).
+template <class Emit>
+__device__ __forceinline__ uint64_t wave_extract_top(uint64_t (&rk)[16], int keep,
+                                                     uint64_t* scratch, Emit emit) {
+  if (keep <= 0) return 0;
+  const int lane = threadIdx.x & 63;
+  uint64_t mx = rk[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = rk[i] > mx ? rk[i] : mx;
+  int above = 0;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) above += readlane_u64(mx, j) > mx ? 1 : 0;
+  const uint64_t hit = __ballot(mx != 0 && above == keep - 1);
+  // Fewer than keep nonempty lanes: every nonzero key is a candidate.
+  const uint64_t thr = hit ? readlane_u64(mx, __builtin_ctzll(hit)) : 1ull;
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool in = rk[i] >= thr;
+    const uint64_t m = __ballot(in);
+    const int pos = total + lane_prefix(m);
+    if (in && pos < 64) scratch[pos] = rk[i];
+    total += __popcll(m);
+  }
+  if (total > 64) return wave_extract_top_iter(rk, keep, emit);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t v = lane < total ? scratch[lane] : 0ull;
+  int r = 0;
+  for (int j = 0; j < total; ++j) r += readlane_u64(v, j) > v ? 1 : 0;
+  if (lane < total && r < keep) emit(r, v);
+  const uint64_t at = __ballot(lane < total && r == keep - 1);
+  return readlane_u64(v, __builtin_ctzll(at));
 }
 
 __device__ __forceinline__ float wave_xor_max(float x, int mask) {

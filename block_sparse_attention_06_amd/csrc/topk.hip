@@ -25,7 +25,7 @@
 //      (key desc, id asc) -- or, when more than kTieCap candidates share one exact
 //      key, a radix select on the id keeps the lowest ids.
 // Rows longer than kSegMax candidates use two launches: one wave per segment of
-// kWaveSeg scores keeps its kWaveKeep best (repeated wave-wide maximum, no barriers)
+// kWaveSeg scores keeps its kWaveKeep best (wave-wide passes, no barriers)
 // and reports the worst of them; the merge selects the m best of all kept candidates,
 // which is the row's answer when every truncated segment's reported worst ranks at
 // or after the m-th selected (nothing left behind could rank higher); otherwise the
@@ -661,9 +661,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
 }
 
 // First pass over long rows: wave w of the launch takes segment (row, seg) of
-// kWaveSeg scores, each lane holding 16 of them, and extracts its kWaveKeep best by
-// repeated wave-wide maxima of (score, id) rank keys.
+// kWaveSeg scores, each lane holding 16 of them, and extracts its kWaveKeep best
+// (score, id) rank keys.
 __global__ __launch_bounds__(256) void topk_wave_segments_kernel(TopkLaunch L) {
+  __shared__ uint64_t scratch[4][64];
   const TopkArgs& a = L.a;
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -694,7 +695,7 @@ __global__ __launch_bounds__(256) void topk_wave_segments_kernel(TopkLaunch L) {
     for (int e = 0; e < 4; ++e) rk[4 * q + e] = p + e < n ? rank_key(xs[e], lo + p + e) : 0ull;
   }
   const int keep = min(n, kWaveKeep);
-  const uint64_t last = wave_extract_top(rk, keep, [&](int k, uint64_t w) {
+  const uint64_t last = wave_extract_top(rk, keep, scratch[threadIdx.x >> 6], [&](int k, uint64_t w) {
     const int32_t id = rank_key_id(w);
     cv[k] = src[id - lo];
     ci[k] = id;
