@@ -561,6 +561,118 @@ __device__ __forceinline__ void write_bitmap_ids(SM& sm, int words, int32_t* out
   }
 }
 
+// Ascending sort of 16 ids in registers (bitonic network).
+__device__ __forceinline__ void sort16_asc(int32_t (&x)[16]) {
+#pragma unroll
+  for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          const int32_t a = x[i], b = x[l];
+          const bool up = (i & k) == 0;
+          x[i] = up ? min(a, b) : max(a, b);
+          x[l] = up ? max(a, b) : min(a, b);
+        }
+      }
+}
+
+// Merge of the segment winners when every segment fits one thread (n_seg <= threads,
+// kWaveKeep == 16): thread s holds segment s's candidates as rank keys. The m-th best
+// key T comes from one value histogram plus a rank count inside T's bin (at most 64
+// entries, else 1 is returned and the general merge runs). With fewer than m
+// candidates, or a truncated segment whose reported worst ranks above T (it may hide
+// a better candidate), 2 is returned: the whole row must be selected. Otherwise each thread writes its kept ids, sorted, at its
+// offset; segments cover ascending id ranges, so the output is ascending. Returns 0.
+template <class SM>
+__device__ int merge_segments_fast(SM& sm, const TopkLaunch& L, int64_t crow, int m,
+                                   int32_t* out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const bool have = tid < L.n_seg;
+  const int64_t slot = crow * L.n_seg + (have ? tid : 0);
+  float v[16];
+  int32_t id[16];
+  const float4* cv4 = reinterpret_cast<const float4*>(L.cand_val + slot * kWaveKeep);
+  const int4* ci4 = reinterpret_cast<const int4*>(L.cand_idx + slot * kWaveKeep);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float qn = __builtin_nanf("");
+    const float4 a = have ? cv4[q] : make_float4(qn, qn, qn, qn);
+    const int4 b = have ? ci4[q] : make_int4(-1, -1, -1, -1);
+    v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
+    id[4 * q] = b.x; id[4 * q + 1] = b.y; id[4 * q + 2] = b.z; id[4 * q + 3] = b.w;
+  }
+  const int32_t bid = have ? L.bnd_idx[slot] : -1;
+  const uint64_t bkey = bid >= 0 ? rank_key(L.bnd_val[slot], bid) : 0ull;
+  float mn = INFINITY, mx = -INFINITY;
+  uint32_t n_valid = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (id[j] < 0) v[j] = __builtin_nanf("");  // absent
+    mn = fminf(mn, v[j]);
+    mx = fmaxf(mx, v[j]);
+    n_valid += v[j] == v[j] ? 1u : 0u;
+  }
+  // Fewer candidates than places (short rows of a long launch): the whole row decides.
+  uint32_t total_valid;
+  block_excl_scan(sm, n_valid, total_valid);
+  if (total_valid < (uint32_t)m) return 2;
+  block_minmax(sm, mn, mx);
+  const LinBins bins = make_bins(mn, mx);
+  clear_hist(sm, kLinBins);
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (v[j] == v[j]) atomicAdd(&sm.hist[bins(v[j])], 1u);
+  __syncthreads();
+  find_digit(sm, kLinBins, (uint32_t)m);
+  const int B = sm.misc[0];
+  const int need = m - sm.misc[1];
+  const int bucket = sm.misc[2];
+  if (tid == 0) sm.misc[4] = 0;
+  __syncthreads();
+  if (bucket > 64) return 1;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (v[j] == v[j] && bins(v[j]) == B) {
+      const int p = atomicAdd(&sm.misc[4], 1);
+      sm.tie_key[p] = order_key(v[j]);
+      sm.tie_idx[p] = id[j];
+    }
+  __syncthreads();
+  if (tid < 64) {
+    const int nb = sm.misc[4];
+    const uint64_t k = lane < nb ? rank_key(key_to_float(sm.tie_key[lane]), sm.tie_idx[lane]) : 0ull;
+    int r = 0;
+    for (int j = 0; j < nb; ++j) r += readlane_u64(k, j) > k ? 1 : 0;
+    if (lane < nb && r == need - 1) {
+      sm.misc[5] = (int32_t)(uint32_t)(k >> 32);
+      sm.misc[6] = (int32_t)(uint32_t)k;
+    }
+  }
+  __syncthreads();
+  const uint64_t T = ((uint64_t)(uint32_t)sm.misc[5] << 32) | (uint32_t)sm.misc[6];
+  if (__syncthreads_or(bkey > T)) return 2;
+  int32_t kept[16];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const bool k = v[j] == v[j] && rank_key(v[j], id[j]) >= T;
+    kept[j] = k ? id[j] : 0x7fffffff;
+    cnt += k ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t off = block_excl_scan(sm, cnt, total);
+  if (cnt) {
+    sort16_asc(kept);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((uint32_t)j < cnt) out[off + j] = kept[j];
+  }
+  return 0;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
   using SM = typename std::conditional<MODE == kRows, TkRowsShared, TkMergeShared>::type;
@@ -595,6 +707,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
   } else {
     // Merge the segment winners, check that no truncated segment could hide a better
     // candidate (else redo the selection on the whole row), write the ids ascending.
+    int fast = 1;
+    if (L.n_seg <= kTkThreads) {
+      fast = merge_segments_fast(sm, L, crow, m, out);
+      if (fast == 0) {
+        for (int k = m + tid; k < a.n_sel; k += kTkThreads) out[k] = k == m ? (int32_t)own : -1;
+        return;
+      }
+    }
     const int n = L.n_seg * kWaveKeep;
     const float* cv = L.cand_val + crow * n;
     const int32_t* ci = L.cand_idx + crow * n;
@@ -614,17 +734,25 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
       const uint64_t rk = rank_key(v, id);
       worst = rk < worst ? rk : worst;
     };
-    if (n <= kTkThreads * kRegSlots) {
-      // Few candidates: each thread holds its share in registers.
-      select_exact<kRegSlots>(sm, PairSrc{cv, ci}, n, m, [&](int i) { keep_id(ci[i], cv[i]); });
-    } else {
-      select_row(sm, cv, ci, 0, n, m, keep_id);
+    bool bad = fast == 2;  // the fast merge found the candidates insufficient
+    if (!bad) {
+      uint32_t my_valid = 0, total_valid;
+      for (int i = tid; i < n; i += kTkThreads) my_valid += ci[i] >= 0 && cv[i] == cv[i];
+      block_excl_scan(sm, my_valid, total_valid);
+      bad = total_valid < (uint32_t)m;  // fewer candidates than places: whole row
     }
-    worst = block_min_u64(sm, worst);
-    bool bad = false;
-    for (int sg = tid; sg < L.n_seg; sg += kTkThreads) {
-      const int32_t bid = L.bnd_idx[crow * L.n_seg + sg];
-      if (bid >= 0 && rank_key(L.bnd_val[crow * L.n_seg + sg], bid) > worst) bad = true;
+    if (!bad) {
+      if (n <= kTkThreads * kRegSlots) {
+        // Few candidates: each thread holds its share in registers.
+        select_exact<kRegSlots>(sm, PairSrc{cv, ci}, n, m, [&](int i) { keep_id(ci[i], cv[i]); });
+      } else {
+        select_row(sm, cv, ci, 0, n, m, keep_id);
+      }
+      worst = block_min_u64(sm, worst);
+      for (int sg = tid; sg < L.n_seg; sg += kTkThreads) {
+        const int32_t bid = L.bnd_idx[crow * L.n_seg + sg];
+        if (bid >= 0 && rank_key(L.bnd_val[crow * L.n_seg + sg], bid) > worst) bad = true;
+      }
     }
     if (__syncthreads_or(bad)) {
       for (int i = tid; i < words; i += kTkThreads) sm.bitmap[i] = 0u;

@@ -252,6 +252,26 @@ def test_topk_decode_rows_batched():
         np.testing.assert_array_equal(sel[b, 0], ref)
 
 
+@pytest.mark.parametrize("budget", [2048, 4096])
+def test_topk_merge_short_and_tied_rows(budget):
+    # Rows of a long launch (262144 pooled blocks: the two-pass top-k runs) that the
+    # segment winners cannot settle: fewer candidates than places (a short sequence,
+    # and with budget 4096 also a row just past one workgroup's 32768 candidates),
+    # and a row of equal scores (one value bin holds every candidate; the lowest ids
+    # win). The last row is ordinary.
+    rng = np.random.default_rng(17)
+    nblk = 262144
+    seq = [5000, 4 * 33000 + 3, 1048576, 1048576 - 77]
+    x = rng.random((len(seq), 1, nblk)).astype(np.float32)
+    x[2, 0, :] = 0.5
+    _say(f"topk merge short and tied rows, budget {budget}")
+    sel = _run_topk(x, 0, nblk, budget, seq_lens=seq)
+    for b in range(len(seq)):
+        own = (seq[b] - 1) // 4
+        ref = O.select_blocks(x[b, 0, :own].astype(np.float64), own, budget // 4)
+        np.testing.assert_array_equal(sel[b, 0], ref, err_msg=f"row {b} (seq {seq[b]})")
+
+
 # ------------------------------------------------------------------------------------
 # Stage 4: attention on given selections
 # ------------------------------------------------------------------------------------
@@ -416,13 +436,15 @@ def test_chunked_prefill_1m_sampled():
 
 
 def test_decode_forward_mixed_lengths_and_fallback():
-    # 3 sequences in a 160K-token cache (rows longer than one top-k workgroup):
-    # full, ragged (not a multiple of r) and short (everything fits in the budget).
-    # Sequence 0's pooled keys grow along one direction that its indexer queries
-    # share, so its best blocks are the last ones: the segment candidates of the
-    # fused scan are truncated there and the merge must fall back to the whole row.
-    wl = workload("decode1m", batch=3, lk=163840)
-    seq = [163840, 163840 - 4001, 1500]
+    # 4 sequences in a 160K-token cache (rows longer than one top-k workgroup):
+    # full, ragged (not a multiple of r), short (everything fits in the budget) and
+    # one whose two segments hold fewer candidates than places (the merge must select
+    # over the whole row). Sequence 0's pooled keys grow along one direction that its
+    # indexer queries share, so its best blocks are the last ones: the segment
+    # candidates of the fused scan are truncated there and the merge must fall back
+    # to the whole row.
+    wl = workload("decode1m", batch=4, lk=163840)
+    seq = [163840, 163840 - 4001, 1500, 5000]
     _say(f"decode forward mixed lengths {seq}")
     inp = generate(wl, device=DEV, seq_lens=seq)
     nblk = wl.lk // 4
@@ -443,7 +465,7 @@ def test_decode_forward_mixed_lengths_and_fallback():
     res = O.forward_decode(bits(inp["q"]), bits(inp["q_idx"])[:, 0], inp["w"].cpu().numpy()[:, 0],
                            bits(inp["k_pooled"]), np.array(seq), fetch, r=4, budget=wl.budget)
     sel_np = sel.cpu().numpy()
-    for b in range(3):
+    for b in range(len(seq)):
         t = seq[b] - 1
         check_selection_row(sel_np[b], res["scores"][b], t // 4, wl.n_sel, f"decode b={b}")
         toks = O.kept_tokens(sel_np[b], t, 4, t + 1)
