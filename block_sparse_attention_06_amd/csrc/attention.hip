@@ -222,26 +222,55 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
 }
 
 // Combine the decode partials of one (sequence, head): rescale each split's
-// (m, l, o) to the common max and normalise.
+// (m, l, o) to the common max and normalise. Thread s first holds split s's (m, l)
+// (n_split <= D), so every partial is requested at once rather than one after the
+// other; then thread `dim` sums its column over the splits, eight loads in flight.
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
+  constexpr int NW = D / 64;
+  __shared__ float wgt[D];
+  __shared__ float red[2][NW];
   const int64_t bh = blockIdx.x;
-  const int dim = threadIdx.x;
-  const float* ml = a.part_ml + bh * a.n_split * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, acc = 0.f;
-  if (M > -INFINITY) {
-    for (int s = 0; s < a.n_split; ++s) {
-      const float ms = ml[2 * s];
-      const float wgt = ms > -INFINITY ? exp2f(ms - M) : 0.f;
-      L += wgt * ml[2 * s + 1];
-      acc += wgt * a.part_o[(bh * a.n_split + s) * D + dim];
-    }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ns = a.n_split;
+  const float* ml = a.part_ml + bh * ns * 2;
+  float ms = -INFINITY, ls = 0.f;
+  if (tid < ns) {
+    ms = ml[2 * tid];
+    ls = ml[2 * tid + 1];
   }
+  float M = ms;
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red[0][w]);
+  const float ws = ms > -INFINITY ? exp2f(ms - M) : 0.f;
+  wgt[tid] = ws;
+  float L = ws * ls;
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) L += __shfl_xor(L, d, 64);
+  if (lane == 0) red[1][wave] = L;
+  __syncthreads();
+  L = red[1][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) L += red[1][w];
+  const float* po = a.part_o + bh * ns * D + tid;
+  float acc = 0.f;
+  int s = 0;
+  for (; s + 8 <= ns; s += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = po[(int64_t)(s + u) * D];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += wgt[s + u] * x[u];
+  }
+  for (; s < ns; ++s) acc += wgt[s] * po[(int64_t)s * D];
   const float o = L > 0.f ? acc / L : 0.f;
-  a.out[bh * D + dim] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xffffu);
-  if (a.lse && dim == 0) a.lse[bh] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
+  a.out[bh * D + tid] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xffffu);
+  if (a.lse && tid == 0) a.lse[bh] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
 }
 
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream) {
@@ -257,7 +286,7 @@ hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream) {
 
 int decode_steps_per_split(int n_sel) {
   const int steps = (n_sel + 3) / 4;
-  const int target_splits = 32;
+  const int target_splits = 64;
   return steps <= target_splits ? 1 : (steps + target_splits - 1) / target_splits;
 }
 
@@ -269,6 +298,7 @@ int decode_num_splits(int n_sel) {
 
 hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream) {
   if (a.lq <= 0) return hipSuccess;
+  if (a.n_split < 1 || a.n_split > a.d) return hipErrorInvalidValue;  // combine: a split per thread
   const int64_t items = a.lq * a.hkv * a.n_split;
   const dim3 grid((unsigned)((items + 3) / 4));
   const dim3 cgrid((unsigned)(a.lq * a.hq));
