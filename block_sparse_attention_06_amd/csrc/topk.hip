@@ -580,20 +580,27 @@ __device__ __forceinline__ void sort16_asc(int32_t (&x)[16]) {
 }
 
 // Merge of the segment winners when every segment fits one thread (n_seg <= threads,
-// kWaveKeep == 16): thread s holds segment s's candidates as rank keys. The m-th best
-// key T comes from one value histogram plus a rank count inside T's bin (at most 64
-// entries, else 1 is returned and the general merge runs). With fewer than m
-// candidates, or a truncated segment whose reported worst ranks above T (it may hide
-// a better candidate), 2 is returned: the whole row must be selected. Otherwise each thread writes its kept ids, sorted, at its
-// offset; segments cover ascending id ranges, so the output is ascending. Returns 0.
-template <class SM>
-__device__ int merge_segments_fast(SM& sm, const TopkLaunch& L, int64_t crow, int m,
-                                   int32_t* out) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const bool have = tid < L.n_seg;
-  const int64_t slot = crow * L.n_seg + (have ? tid : 0);
+// kWaveKeep == 16): thread s holds segment s's candidates. merge_fetch issues their
+// loads at kernel entry (they do not depend on the row's length) and clears the value
+// histogram meanwhile; merge_segments_fast then finds the m-th best key T from one
+// value histogram plus a rank count inside T's bin (at most 64 entries, else it
+// returns 1 and the general merge runs). With fewer than m candidates, or a truncated
+// segment whose reported worst ranks above T (it may hide a better candidate), it
+// returns 2: the whole row must be selected. Otherwise each thread writes its kept
+// ids, sorted, at its offset (segments cover ascending id ranges, so the output is
+// ascending) and it returns 0.
+struct MergeRegs {
   float v[16];
   int32_t id[16];
+  uint64_t bkey;
+};
+
+template <class SM>
+__device__ __forceinline__ void merge_fetch(SM& sm, const TopkLaunch& L, int64_t crow,
+                                            MergeRegs& r) {
+  const int tid = threadIdx.x;
+  const bool have = tid < L.n_seg;
+  const int64_t slot = crow * L.n_seg + (have ? tid : 0);
   const float4* cv4 = reinterpret_cast<const float4*>(L.cand_val + slot * kWaveKeep);
   const int4* ci4 = reinterpret_cast<const int4*>(L.cand_idx + slot * kWaveKeep);
 #pragma unroll
@@ -601,27 +608,53 @@ __device__ int merge_segments_fast(SM& sm, const TopkLaunch& L, int64_t crow, in
     const float qn = __builtin_nanf("");
     const float4 a = have ? cv4[q] : make_float4(qn, qn, qn, qn);
     const int4 b = have ? ci4[q] : make_int4(-1, -1, -1, -1);
-    v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
-    id[4 * q] = b.x; id[4 * q + 1] = b.y; id[4 * q + 2] = b.z; id[4 * q + 3] = b.w;
+    r.v[4 * q] = a.x; r.v[4 * q + 1] = a.y; r.v[4 * q + 2] = a.z; r.v[4 * q + 3] = a.w;
+    r.id[4 * q] = b.x; r.id[4 * q + 1] = b.y; r.id[4 * q + 2] = b.z; r.id[4 * q + 3] = b.w;
   }
   const int32_t bid = have ? L.bnd_idx[slot] : -1;
-  const uint64_t bkey = bid >= 0 ? rank_key(L.bnd_val[slot], bid) : 0ull;
+  const float bval = have ? L.bnd_val[slot] : 0.f;
+  r.bkey = bid >= 0 ? rank_key(bval, bid) : 0ull;
+  for (int i = tid; i < kLinBins; i += kTkThreads) sm.hist[i] = 0u;
+  if (tid == 0) sm.misc[4] = 0;
+}
+
+template <class SM>
+__device__ __forceinline__ int merge_segments_fast(SM& sm, MergeRegs& r, int m, int32_t* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* v = r.v;
+  const int32_t* id = r.id;
+  // One reduction for the value range and the number of candidates.
   float mn = INFINITY, mx = -INFINITY;
   uint32_t n_valid = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (id[j] < 0) v[j] = __builtin_nanf("");  // absent
-    mn = fminf(mn, v[j]);
+    mn = fminf(mn, v[j]);  // fminf / fmaxf ignore NaN
     mx = fmaxf(mx, v[j]);
     n_valid += v[j] == v[j] ? 1u : 0u;
   }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, d, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+    n_valid += __shfl_xor(n_valid, d, 64);
+  }
+  if (lane == 0) {
+    sm.wred[wave] = mn;
+    sm.wred[kWaves + wave] = mx;
+    sm.wsum[wave] = n_valid;
+  }
+  __syncthreads();  // also orders merge_fetch's histogram clear before the counts
+  n_valid = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    mn = fminf(mn, sm.wred[w]);
+    mx = fmaxf(mx, sm.wred[kWaves + w]);
+    n_valid += sm.wsum[w];
+  }
   // Fewer candidates than places (short rows of a long launch): the whole row decides.
-  uint32_t total_valid;
-  block_excl_scan(sm, n_valid, total_valid);
-  if (total_valid < (uint32_t)m) return 2;
-  block_minmax(sm, mn, mx);
+  if (n_valid < (uint32_t)m) return 2;
   const LinBins bins = make_bins(mn, mx);
-  clear_hist(sm, kLinBins);
 #pragma unroll
   for (int j = 0; j < 16; ++j)
     if (v[j] == v[j]) atomicAdd(&sm.hist[bins(v[j])], 1u);
@@ -630,8 +663,6 @@ __device__ int merge_segments_fast(SM& sm, const TopkLaunch& L, int64_t crow, in
   const int B = sm.misc[0];
   const int need = m - sm.misc[1];
   const int bucket = sm.misc[2];
-  if (tid == 0) sm.misc[4] = 0;
-  __syncthreads();
   if (bucket > 64) return 1;
 #pragma unroll
   for (int j = 0; j < 16; ++j)
@@ -641,19 +672,19 @@ __device__ int merge_segments_fast(SM& sm, const TopkLaunch& L, int64_t crow, in
       sm.tie_idx[p] = id[j];
     }
   __syncthreads();
-  if (tid < 64) {
+  if (wave == 0) {
     const int nb = sm.misc[4];
-    const uint64_t k = lane < nb ? rank_key(key_to_float(sm.tie_key[lane]), sm.tie_idx[lane]) : 0ull;
-    int r = 0;
-    for (int j = 0; j < nb; ++j) r += readlane_u64(k, j) > k ? 1 : 0;
-    if (lane < nb && r == need - 1) {
+    const uint64_t k =
+        lane < nb ? rank_key(key_to_float(sm.tie_key[lane]), sm.tie_idx[lane]) : 0ull;
+    int rk = 0;
+    for (int j = 0; j < nb; ++j) rk += readlane_u64(k, j) > k ? 1 : 0;
+    if (lane < nb && rk == need - 1) {
       sm.misc[5] = (int32_t)(uint32_t)(k >> 32);
       sm.misc[6] = (int32_t)(uint32_t)k;
     }
   }
   __syncthreads();
   const uint64_t T = ((uint64_t)(uint32_t)sm.misc[5] << 32) | (uint32_t)sm.misc[6];
-  if (__syncthreads_or(bkey > T)) return 2;
   int32_t kept[16];
   uint32_t cnt = 0;
 #pragma unroll
@@ -662,8 +693,12 @@ __device__ int merge_segments_fast(SM& sm, const TopkLaunch& L, int64_t crow, in
     kept[j] = k ? id[j] : 0x7fffffff;
     cnt += k ? 1u : 0u;
   }
+  // The offsets scan also carries the truncation check: a flagged thread adds 1 << 16
+  // (counts stay below 4096), so the total shows whether any segment failed it.
+  constexpr uint32_t kBad = 1u << 16;
   uint32_t total;
-  const uint32_t off = block_excl_scan(sm, cnt, total);
+  const uint32_t off = block_excl_scan(sm, cnt + (r.bkey > T ? kBad : 0u), total);
+  if (total >= kBad) return 2;
   if (cnt) {
     sort16_asc(kept);
 #pragma unroll
@@ -681,11 +716,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int bi = blockIdx.z;
+  const int64_t crow = (int64_t)bi * a.lq + row;
+  MergeRegs mr;
+  const bool fast_merge = MODE == kMerge && L.n_seg <= kTkThreads;
+  if (fast_merge) merge_fetch(sm, L, crow, mr);
   int64_t t, own, C;
   int m;
   row_geometry(a, row, bi, t, own, C, m);
   int32_t* out = a.sel + ((int64_t)bi * a.lq + row) * a.n_sel;
-  const int64_t crow = (int64_t)bi * a.lq + row;
   const float* srow = a.scores + (int64_t)bi * a.s_bs + row * a.ld;
 
   if (t < 0 || m == C) {  // nothing to rank: every earlier block fits
@@ -708,8 +746,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
     // Merge the segment winners, check that no truncated segment could hide a better
     // candidate (else redo the selection on the whole row), write the ids ascending.
     int fast = 1;
-    if (L.n_seg <= kTkThreads) {
-      fast = merge_segments_fast(sm, L, crow, m, out);
+    if (fast_merge) {
+      fast = merge_segments_fast(sm, mr, m, out);
       if (fast == 0) {
         for (int k = m + tid; k < a.n_sel; k += kTkThreads) out[k] = k == m ? (int32_t)own : -1;
         return;
