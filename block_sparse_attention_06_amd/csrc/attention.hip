@@ -24,8 +24,8 @@
 //     each lane again owns 8 contiguous dims per head: 16-byte output stores.
 // Softmax: fp32, base-2 with the scale folded in, running max per head shared by
 // the 4 lanes that hold the head's keys, per-lane partial sums reduced at the end.
-// Decode splits each sequence's kept blocks over waves and writes (m, l, o)
-// partials that a second kernel combines.
+// Decode splits each sequence's kept blocks over waves, merges the four waves of a
+// workgroup in LDS and writes (m, l, o) partials that a second kernel combines.
 
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -40,9 +40,113 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-template <int D, bool DECODE>
+// One step = 4 kept blocks (16 keys) of one (query, KV group): the operands of a
+// step, gathered straight from global memory.
+template <int D>
+struct AttnStep {
+  static constexpr int NC = D / 32;   // k-chunks of Q.K^T
+  static constexpr int NH = D / 128;  // 128-dim halves
+  uint4 Kc[NC];
+  uint4 Vr[4][NH];
+};
+
+__device__ __forceinline__ int pick4(int b0, int b1, int b2, int b3, int i) {
+  return i == 0 ? b0 : (i == 1 ? b1 : (i == 2 ? b2 : b3));
+}
+
+// Issues the loads of one step. Block ids < 0 (padding) and keys after position t
+// read an in-bounds row that the softmax masks.
+template <int D>
+__device__ __forceinline__ void attn_load_step(AttnStep<D>& st, const int (&b4)[4],
+                                               const uint16_t* kb, const uint16_t* vb,
+                                               int64_t kstride, int g, int64_t t, int c16,
+                                               int quad) {
+  // K rows: key (c16) = token (c16 & 3) of block slot (c16 >> 2).
+  const int bk = pick4(b4[0], b4[1], b4[2], b4[3], c16 >> 2);
+  int64_t tk = (int64_t)bk * 4 + (c16 & 3);
+  tk = bk < 0 ? 0 : min(tk, t);
+  const uint16_t* kp = kb + tk * kstride + g * D + quad * 8;
+#pragma unroll
+  for (int c = 0; c < AttnStep<D>::NC; ++c) st.Kc[c] = ld16(kp + c * 32);
+  // V rows: this lane's 4 keys are the 4 tokens of block slot `quad`.
+  const int bv = pick4(b4[0], b4[1], b4[2], b4[3], quad);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    int64_t tv = (int64_t)bv * 4 + kk;
+    tv = bv < 0 ? 0 : min(tv, t);
+    const uint16_t* vp = vb + tv * kstride + g * D + c16 * 8;
+#pragma unroll
+    for (int hf = 0; hf < AttnStep<D>::NH; ++hf) st.Vr[kk][hf] = ld16(vp + hf * 128);
+  }
+}
+
+// S^T = K.Q^T, online softmax update of (m_run, l_run), O = O*alpha + P.V.
+template <int D>
+__device__ __forceinline__ void attn_compute_step(const AttnStep<D>& st, const int (&b4)[4],
+                                                  const uint4 (&Qc)[D / 32], f32x4 (&O)[D / 16],
+                                                  float& m_run, float& l_run, float sl2,
+                                                  int64_t t, int quad) {
+  constexpr int NC = D / 32, NH = D / 128, NT = D / 16;
+  f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) S = mfma_16x16x32(st.Kc[c], Qc[c], S);
+
+  // Row 4*quad+i of S^T is token bv*4 + i.
+  const int bv = pick4(b4[0], b4[1], b4[2], b4[3], quad);
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = bv >= 0 && (int64_t)bv * 4 + i <= t;
+    x[i] = ok ? S[i] * sl2 : -INFINITY;
+  }
+  float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  mt = wave_xor_max(mt, 16);
+  mt = wave_xor_max(mt, 32);
+  const float m_new = fmaxf(m_run, mt);
+  const float alpha = exp2f(m_run - m_new);
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = exp2f(x[i] - m_new);
+  l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  m_run = m_new;
+
+  float ai[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * quad + i, kWave);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) O[n][i] *= ai[i];
+  }
+
+  const uint2 P = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+#pragma unroll
+  for (int hf = 0; hf < NH; ++hf) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int wi = e >> 1, hi = e & 1;
+      const uint32_t lo =
+          half_of(word_of(st.Vr[0][hf], wi), hi) | (half_of(word_of(st.Vr[1][hf], wi), hi) << 16);
+      const uint32_t up =
+          half_of(word_of(st.Vr[2][hf], wi), hi) | (half_of(word_of(st.Vr[3][hf], wi), hi) << 16);
+      O[hf * 8 + e] = mfma_16x16x16(P, make_uint2(lo, up), O[hf * 8 + e]);
+    }
+  }
+}
+
+// Q^T as the B operand: column = head c16 of the group, k = dims 32c + 8*quad + [0..7].
+template <int D>
+__device__ __forceinline__ void attn_load_q(uint4 (&Qc)[D / 32], const uint16_t* qrow, int g,
+                                            int G, int c16, int quad) {
+  const bool hv = c16 < G;
+  const uint16_t* qp = qrow + (int64_t)(g * G + (hv ? c16 : 0)) * D + quad * 8;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) Qc[c] = hv ? ld16(qp + c * 32) : make_uint4(0, 0, 0, 0);
+}
+
+// Prefill: one wave per (query row, KV group) walks the row's kept blocks.
+template <int D>
 __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
-  constexpr int NC = D / 32;   // k-chunks of Q.K^T
   constexpr int NH = D / 128;  // 128-dim halves
   constexpr int NT = D / 16;   // output dim tiles
   const int lane = threadIdx.x & 63;
@@ -52,45 +156,16 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
   const int G = a.hq / a.hkv;
 
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  int64_t row, t;
-  int g, split = 0, s_begin, s_end;
-  const uint16_t *kb, *vb;
+  const int64_t row = item / a.hkv;
+  const int g = (int)(item - row * a.hkv);
+  if (row >= a.lq) return;
+  const int64_t t = a.q_pos0 + row;
   const int n_steps = (a.n_sel + 3) / 4;
-  if (!DECODE) {
-    row = item / a.hkv;
-    g = (int)(item - row * a.hkv);
-    if (row >= a.lq) return;
-    t = a.q_pos0 + row;
-    kb = a.k;
-    vb = a.v;
-    s_begin = 0;
-    s_end = n_steps;
-  } else {
-    const int64_t per_seq = (int64_t)a.hkv * a.n_split;
-    row = item / per_seq;
-    if (row >= a.lq) return;
-    const int rem = (int)(item - row * per_seq);
-    g = rem / a.n_split;
-    split = rem - g * a.n_split;
-    t = (int64_t)a.seq_lens[row] - 1;
-    kb = a.k + row * a.cache_bs;
-    vb = a.v + row * a.cache_bs;
-    s_begin = split * a.steps_per_split;
-    s_end = min(s_begin + a.steps_per_split, n_steps);
-    if (t < 0) s_end = s_begin;
-  }
   const int32_t* srow = a.sel + row * a.n_sel;
-  const uint16_t* qrow = a.q + row * (int64_t)a.hq * D;
   const int64_t kstride = (int64_t)a.hkv * D;  // elements between consecutive tokens
 
-  // Q^T as the B operand: column = head c16 of this group, k = dims 32c + 8*quad + [0..7].
-  uint4 Qc[NC];
-  {
-    const bool hv = c16 < G;
-    const uint16_t* qp = qrow + (int64_t)(g * G + (hv ? c16 : 0)) * D + quad * 8;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) Qc[c] = hv ? ld16(qp + c * 32) : make_uint4(0, 0, 0, 0);
-  }
+  uint4 Qc[D / 32];
+  attn_load_q<D>(Qc, a.q + row * (int64_t)a.hq * D, g, G, c16, quad);
 
   f32x4 O[NT];
 #pragma unroll
@@ -98,77 +173,14 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
   float m_run = -INFINITY;  // running max (log2 domain) of head c16
   float l_run = 0.f;        // this lane's partial sum for head c16
 
-  const float sl2 = a.scale_log2;
-  for (int s = s_begin; s < s_end; ++s) {
+  for (int s = 0; s < n_steps; ++s) {
     int b4[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) b4[j] = (4 * s + j < a.n_sel) ? srow[4 * s + j] : -1;
     if (b4[0] < 0) break;  // -1 padding reached
-
-    // K rows: key (c16) = token (c16 & 3) of block slot (c16 >> 2).
-    const int slot_k = c16 >> 2;
-    const int bk = slot_k == 0 ? b4[0] : (slot_k == 1 ? b4[1] : (slot_k == 2 ? b4[2] : b4[3]));
-    int64_t tk = (int64_t)bk * 4 + (c16 & 3);
-    tk = bk < 0 ? 0 : min(tk, t);  // masked keys read an in-bounds row
-    const uint16_t* kp = kb + tk * kstride + g * D + quad * 8;
-    uint4 Kc[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) Kc[c] = ld16(kp + c * 32);
-
-    // V rows: this lane's 4 keys are the 4 tokens of block slot `quad`.
-    const int bv = quad == 0 ? b4[0] : (quad == 1 ? b4[1] : (quad == 2 ? b4[2] : b4[3]));
-    uint4 Vr[4][NH];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      int64_t tv = (int64_t)bv * 4 + kk;
-      tv = bv < 0 ? 0 : min(tv, t);
-      const uint16_t* vp = vb + tv * kstride + g * D + c16 * 8;
-#pragma unroll
-      for (int hf = 0; hf < NH; ++hf) Vr[kk][hf] = ld16(vp + hf * 128);
-    }
-
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NC; ++c) S = mfma_16x16x32(Kc[c], Qc[c], S);
-
-    // Row 4*quad+i of S^T is token bv*4 + i.
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = bv >= 0 && (int64_t)bv * 4 + i <= t;
-      x[i] = ok ? S[i] * sl2 : -INFINITY;
-    }
-    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = wave_xor_max(mt, 16);
-    mt = wave_xor_max(mt, 32);
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = exp2f(x[i] - m_new);
-    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m_run = m_new;
-
-    float ai[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * quad + i, kWave);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) O[n][i] *= ai[i];
-    }
-
-    const uint2 P = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-#pragma unroll
-    for (int hf = 0; hf < NH; ++hf) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wi = e >> 1, hi = e & 1;
-        const uint32_t lo = half_of(word_of(Vr[0][hf], wi), hi) | (half_of(word_of(Vr[1][hf], wi), hi) << 16);
-        const uint32_t up = half_of(word_of(Vr[2][hf], wi), hi) | (half_of(word_of(Vr[3][hf], wi), hi) << 16);
-        O[hf * 8 + e] = mfma_16x16x16(P, make_uint2(lo, up), O[hf * 8 + e]);
-      }
-    }
+    AttnStep<D> st;
+    attn_load_step<D>(st, b4, a.k, a.v, kstride, g, t, c16, quad);
+    attn_compute_step<D>(st, b4, Qc, O, m_run, l_run, a.scale_log2, t, quad);
   }
 
   float l_tot = wave_xor_sum(l_run, 16);
@@ -176,63 +188,152 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
   float lh[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lh[i] = __shfl(l_tot, 4 * quad + i, kWave);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * quad + i;
+    if (hl < G) {
+      const float inv = lh[i] > 0.f ? 1.f / lh[i] : 0.f;
+      uint16_t* op = a.out + (row * a.hq + g * G + hl) * (int64_t)D + c16 * 8;
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) {
+        uint4 v;
+        v.x = pack_bf16x2(O[hf * 8 + 0][i] * inv, O[hf * 8 + 1][i] * inv);
+        v.y = pack_bf16x2(O[hf * 8 + 2][i] * inv, O[hf * 8 + 3][i] * inv);
+        v.z = pack_bf16x2(O[hf * 8 + 4][i] * inv, O[hf * 8 + 5][i] * inv);
+        v.w = pack_bf16x2(O[hf * 8 + 6][i] * inv, O[hf * 8 + 7][i] * inv);
+        *reinterpret_cast<uint4*>(op + hf * 128) = v;
+      }
+    }
+  }
+  if (a.lse && quad == 0 && c16 < G)
+    a.lse[row * a.hq + g * G + c16] = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+}
 
-  if (!DECODE) {
+// Decode: a workgroup per (sequence, KV group, range of 4*SPS steps); each wave takes
+// SPS consecutive steps. The wave reads all its block ids first (they are uniform:
+// scalar loads) and keeps two steps' loads in flight. The four waves then merge
+// their (m, l, O) in LDS, so one partial per workgroup and head goes to memory for
+// the combine kernel.
+template <int D, int SPS>
+__global__ __launch_bounds__(256) void sparse_attn_decode_kernel(AttnArgs a) {
+  constexpr int NH = D / 128;
+  constexpr int NT = D / 16;
+  constexpr int kMaxG = 16;
+  __shared__ float red_o[4][kMaxG][D];
+  __shared__ float red_ml[4][kMaxG][2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15;
+  const int quad = lane >> 4;
+  const int G = a.hq / a.hkv;
+
+  const int64_t wg = blockIdx.x;  // (row, g, wg_split)
+  const int64_t per_seq = (int64_t)a.hkv * a.n_split;
+  const int64_t row = wg / per_seq;
+  if (row >= a.lq) return;
+  const int rem = (int)(wg - row * per_seq);
+  const int g = rem / a.n_split;
+  const int wg_split = rem - g * a.n_split;
+  const int64_t t = (int64_t)a.seq_lens[row] - 1;
+  const uint16_t* kb = a.k + row * a.cache_bs;
+  const uint16_t* vb = a.v + row * a.cache_bs;
+  const int32_t* srow = a.sel + row * a.n_sel;
+  const int64_t kstride = (int64_t)a.hkv * D;
+  const int s_begin = (wg_split * 4 + wave) * SPS;
+
+  int ids[SPS][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hl = 4 * quad + i;
-      if (hl < G) {
-        const float inv = lh[i] > 0.f ? 1.f / lh[i] : 0.f;
-        uint16_t* op = a.out + (row * a.hq + g * G + hl) * (int64_t)D + c16 * 8;
+  for (int si = 0; si < SPS; ++si)
 #pragma unroll
-        for (int hf = 0; hf < NH; ++hf) {
-          uint4 v;
-          v.x = pack_bf16x2(O[hf * 8 + 0][i] * inv, O[hf * 8 + 1][i] * inv);
-          v.y = pack_bf16x2(O[hf * 8 + 2][i] * inv, O[hf * 8 + 3][i] * inv);
-          v.z = pack_bf16x2(O[hf * 8 + 4][i] * inv, O[hf * 8 + 5][i] * inv);
-          v.w = pack_bf16x2(O[hf * 8 + 6][i] * inv, O[hf * 8 + 7][i] * inv);
-          *reinterpret_cast<uint4*>(op + hf * 128) = v;
-        }
+    for (int j = 0; j < 4; ++j) {
+      const int k = 4 * (s_begin + si) + j;
+      ids[si][j] = (t >= 0 && k < a.n_sel) ? srow[k] : -1;
+    }
+
+  uint4 Qc[D / 32];
+  attn_load_q<D>(Qc, a.q + row * (int64_t)a.hq * D, g, G, c16, quad);
+  f32x4 O[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Loads are issued for every step (padding reads an in-bounds row); a step whose
+  // first block is padding is skipped (the padding is at the end of the row).
+  AttnStep<D> A, B;
+  attn_load_step<D>(A, ids[0], kb, vb, kstride, g, t, c16, quad);
+#pragma unroll
+  for (int si = 0; si < SPS; si += 2) {
+    if (si + 1 < SPS) attn_load_step<D>(B, ids[si + 1], kb, vb, kstride, g, t, c16, quad);
+    if (ids[si][0] >= 0)
+      attn_compute_step<D>(A, ids[si], Qc, O, m_run, l_run, a.scale_log2, t, quad);
+    if (si + 2 < SPS) attn_load_step<D>(A, ids[si + 2], kb, vb, kstride, g, t, c16, quad);
+    if (si + 1 < SPS && ids[si + 1][0] >= 0)
+      attn_compute_step<D>(B, ids[si + 1], Qc, O, m_run, l_run, a.scale_log2, t, quad);
+  }
+
+  float l_tot = wave_xor_sum(l_run, 16);
+  l_tot = wave_xor_sum(l_tot, 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * quad + i;
+    if (hl < G) {
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) {
+        float* dst = &red_o[wave][hl][hf * 128 + c16 * 8];
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(O[hf * 8 + 0][i], O[hf * 8 + 1][i], O[hf * 8 + 2][i], O[hf * 8 + 3][i]);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(O[hf * 8 + 4][i], O[hf * 8 + 5][i], O[hf * 8 + 6][i], O[hf * 8 + 7][i]);
       }
     }
-    if (a.lse && quad == 0 && c16 < G)
-      a.lse[row * a.hq + g * G + c16] = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
-  } else {
+  }
+  if (quad == 0 && c16 < G) {
+    red_ml[wave][c16][0] = m_run;
+    red_ml[wave][c16][1] = l_tot;
+  }
+  __syncthreads();
+  // Merge the four waves' partials: rescale to the common max (a wave without keys
+  // has m = -inf and contributes nothing).
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, dim = idx - h * D;
+    float M = red_ml[0][h][0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hl = 4 * quad + i;
-      if (hl < G) {
-        const int64_t slot = (row * a.hq + g * G + hl) * (int64_t)a.n_split + split;
-        float* op = a.part_o + slot * D + c16 * 8;
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, red_ml[w][h][0]);
+    float o = 0.f, L = 0.f;
 #pragma unroll
-        for (int hf = 0; hf < NH; ++hf) {
-          *reinterpret_cast<float4*>(op + hf * 128) =
-              make_float4(O[hf * 8 + 0][i], O[hf * 8 + 1][i], O[hf * 8 + 2][i], O[hf * 8 + 3][i]);
-          *reinterpret_cast<float4*>(op + hf * 128 + 4) =
-              make_float4(O[hf * 8 + 4][i], O[hf * 8 + 5][i], O[hf * 8 + 6][i], O[hf * 8 + 7][i]);
-        }
-      }
+    for (int w = 0; w < 4; ++w) {
+      const float mw = red_ml[w][h][0];
+      const float f = mw > -INFINITY ? exp2f(mw - M) : 0.f;
+      o += f * red_o[w][h][dim];
+      L += f * red_ml[w][h][1];
     }
-    if (quad == 0 && c16 < G) {
-      const int64_t slot = (row * a.hq + g * G + c16) * (int64_t)a.n_split + split;
-      a.part_ml[slot * 2 + 0] = m_run;
-      a.part_ml[slot * 2 + 1] = l_tot;
+    const int64_t slot = (row * a.hq + g * G + h) * (int64_t)a.n_split + wg_split;
+    a.part_o[slot * D + dim] = o;
+    if (dim == 0) {
+      a.part_ml[slot * 2 + 0] = M;
+      a.part_ml[slot * 2 + 1] = L;
     }
   }
 }
 
 // Combine the decode partials of one (sequence, head): rescale each split's
-// (m, l, o) to the common max and normalise. Thread s first holds split s's (m, l)
-// (n_split <= D), so every partial is requested at once rather than one after the
-// other; then thread `dim` sums its column over the splits, eight loads in flight.
+// (m, l, o) to the common max and normalise. The loads of the first 16 partial
+// outputs of column `dim` are issued together with the (m, l) loads (thread s holds
+// split s's; n_split <= D), so the common case takes one round trip to memory.
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   constexpr int NW = D / 64;
+  constexpr int kEarly = 16;
   __shared__ float wgt[D];
   __shared__ float red[2][NW];
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ns = a.n_split;
+  const float* po = a.part_o + bh * ns * D + tid;
+  float x[kEarly];
+#pragma unroll
+  for (int u = 0; u < kEarly; ++u) x[u] = u < ns ? po[(int64_t)u * D] : 0.f;
   const float* ml = a.part_ml + bh * ns * 2;
   float ms = -INFINITY, ls = 0.f;
   if (tid < ns) {
@@ -257,17 +358,11 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   L = red[1][0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) L += red[1][w];
-  const float* po = a.part_o + bh * ns * D + tid;
   float acc = 0.f;
-  int s = 0;
-  for (; s + 8 <= ns; s += 8) {
-    float x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = po[(int64_t)(s + u) * D];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc += wgt[s + u] * x[u];
-  }
-  for (; s < ns; ++s) acc += wgt[s] * po[(int64_t)s * D];
+  for (int u = 0; u < kEarly; ++u)
+    if (u < ns) acc += wgt[u] * x[u];
+  for (int s = kEarly; s < ns; ++s) acc += wgt[s] * po[(int64_t)s * D];
   const float o = L > 0.f ? acc / L : 0.f;
   a.out[bh * D + tid] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xffffu);
   if (a.lse && tid == 0) a.lse[bh] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
@@ -278,37 +373,51 @@ hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = a.lq * a.hkv;
   const dim3 grid((unsigned)((items + 3) / 4));
   if (a.d == 256)
-    hipLaunchKernelGGL((sparse_attn_kernel<256, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(sparse_attn_kernel<256>, grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((sparse_attn_kernel<128, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(sparse_attn_kernel<128>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
+// Decode splits: a wave takes SPS steps of 4 blocks (SPS = 1, 2 or 4, so that about
+// 64 waves share a (sequence, KV group)), a workgroup 4 waves; n_split counts the
+// workgroups (= partials) per (sequence, head).
 int decode_steps_per_split(int n_sel) {
   const int steps = (n_sel + 3) / 4;
-  const int target_splits = 64;
-  return steps <= target_splits ? 1 : (steps + target_splits - 1) / target_splits;
+  return steps <= 64 ? 1 : (steps <= 128 ? 2 : 4);
 }
 
 int decode_num_splits(int n_sel) {
   const int steps = (n_sel + 3) / 4;
   const int sps = decode_steps_per_split(n_sel);
-  return (steps + sps - 1) / sps;
+  const int waves = (steps + sps - 1) / sps;
+  return (waves + 3) / 4;
 }
 
 hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream) {
   if (a.lq <= 0) return hipSuccess;
-  if (a.n_split < 1 || a.n_split > a.d) return hipErrorInvalidValue;  // combine: a split per thread
-  const int64_t items = a.lq * a.hkv * a.n_split;
-  const dim3 grid((unsigned)((items + 3) / 4));
+  // combine: a partial per thread; merge in LDS: at most 16 heads per group
+  if (a.n_split < 1 || a.n_split > a.d || a.hq / a.hkv > 16) return hipErrorInvalidValue;
+  const int sps = a.steps_per_split;
+  if ((int64_t)a.n_split * 4 * sps * 4 < a.n_sel) return hipErrorInvalidValue;  // ranges cover n_sel
+  const dim3 grid((unsigned)(a.lq * a.hkv * a.n_split));
   const dim3 cgrid((unsigned)(a.lq * a.hq));
+#define QSA_DECODE_LAUNCH(DD, S) \
+  hipLaunchKernelGGL((sparse_attn_decode_kernel<DD, S>), grid, dim3(256), 0, stream, a)
   if (a.d == 256) {
-    hipLaunchKernelGGL((sparse_attn_kernel<256, true>), grid, dim3(256), 0, stream, a);
+    if (sps == 1) QSA_DECODE_LAUNCH(256, 1);
+    else if (sps == 2) QSA_DECODE_LAUNCH(256, 2);
+    else if (sps == 4) QSA_DECODE_LAUNCH(256, 4);
+    else return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_combine_kernel<256>), cgrid, dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((sparse_attn_kernel<128, true>), grid, dim3(256), 0, stream, a);
+    if (sps == 1) QSA_DECODE_LAUNCH(128, 1);
+    else if (sps == 2) QSA_DECODE_LAUNCH(128, 2);
+    else if (sps == 4) QSA_DECODE_LAUNCH(128, 4);
+    else return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_combine_kernel<128>), cgrid, dim3(128), 0, stream, a);
   }
+#undef QSA_DECODE_LAUNCH
   return hipGetLastError();
 }
 

@@ -99,7 +99,8 @@ hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_probe_gather(const void* buf, const int32_t* ids, int steps, int64_t n_waves,
                                uint32_t* sink, hipStream_t stream);
 
-// Decode split heuristic: number of 4-block steps per split for a given n_sel.
+// Decode split heuristic for a given n_sel: 4-block steps per wave (1, 2 or 4) and
+// workgroups of 4 waves (= partials) per (sequence, head).
 int decode_steps_per_split(int n_sel);
 int decode_num_splits(int n_sel);
 
