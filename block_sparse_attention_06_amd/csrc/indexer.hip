@@ -208,10 +208,11 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
 template <int DI, bool CAND>
 __global__ __launch_bounds__(256) void index_scores_scan_kernel(ScoreArgs a, int n_ranges,
                                                                 int blocks_per_wave) {
-  // With CAND, a wave's range is one top-k segment (kTopkWaveSeg blocks, 16 tiles of
-  // 64): each tile's rank keys are parked in LDS (one per lane), and at the end the
-  // wave extracts the segment's kTopkWaveKeep best for the top-k merge.
-  __shared__ uint64_t rk_lds[CAND ? 4 : 1][CAND ? 16 * 64 : 1];
+  // With CAND, a wave's range is one top-k segment (kTopkWaveSeg blocks, tiles of 64):
+  // each tile's rank keys are parked in LDS (one per lane), and at the end the wave
+  // extracts the segment's kTopkWaveKeep best for the top-k merge.
+  constexpr int kSegTiles = kTopkWaveSeg / 64;
+  __shared__ uint64_t rk_lds[CAND ? 4 : 1][CAND ? kTopkWaveSeg : 1];
   constexpr int NC = DI / 32;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256) void index_scores_scan_kernel(ScoreArgs a, int
       const int64_t blk = min(nb + 4 * c16 + j, n1 - 1);  // clamped; extra columns unused
       const uint16_t* p = kpb + blk * DI + quad * 8;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) B[j][c] = ld16(p + c * 32);
+      for (int c = 0; c < NC; ++c) B[j][c] = ld16_stream(p + c * 32);  // read once per pass
     }
   };
   auto compute = [&](const uint4 (&B)[4][NC], int64_t nb) {
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(256) void index_scores_scan_kernel(ScoreArgs a, int
     // the rank keys in LDS carry each score, a -0 coming back as +0.
     const uint64_t* seg = rk_lds[wave];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kTopkWaveSeg / 256; ++q) {
       const int p = q * 256 + 4 * lane;
       if (p < n_valid) {
         float f[4];
@@ -326,15 +327,15 @@ __global__ __launch_bounds__(256) void index_scores_scan_kernel(ScoreArgs a, int
         }
       }
     }
-    uint64_t rk[16];
+    uint64_t rk[kSegTiles];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) rk[i] = i < n_tiles ? seg[i * 64 + lane] : 0ull;
+    for (int i = 0; i < kSegTiles; ++i) rk[i] = i < n_tiles ? seg[i * 64 + lane] : 0ull;
     const int keep = min(n_valid, kTopkWaveKeep);
     float* cv = a.cand.cand_val + cslot * kTopkWaveKeep;
     int32_t* ci = a.cand.cand_idx + cslot * kTopkWaveKeep;
     // The extraction packs its survivors into the first 64 slots of this wave's keys,
     // which are all in registers by now.
-    const uint64_t last = wave_extract_top(rk, keep, rk_lds[wave], [&](int k, uint64_t w) {
+    const uint64_t last = wave_extract_top<kSegTiles>(rk, keep, rk_lds[wave], [&](int k, uint64_t w) {
       cv[k] = key_to_float((uint32_t)(w >> 32));
       ci[k] = rank_key_id(w);
     });

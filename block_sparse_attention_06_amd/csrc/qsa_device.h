@@ -74,18 +74,19 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Wave-wide, by repeated maxima: extract the `keep` largest of the 64 x 16 rank keys
-// held by the lanes (0 = empty slot), largest first; calls emit(k, rank_key) on the
-// lane that held the k-th one. Returns the last extracted key (wave-uniform), 0 if
+// Wave-wide, by repeated maxima: extract the `keep` largest of the 64 x SLOTS rank
+// keys held by the lanes (0 = empty slot), largest first; calls emit(k, rank_key) on
+// the lane that held the k-th one. Returns the last extracted key (wave-uniform), 0 if
 // keep == 0. Costs one wave-wide reduction per key.
-template <class Emit>
-__device__ __forceinline__ uint64_t wave_extract_top_iter(uint64_t (&rk)[16], int keep, Emit emit) {
+template <int SLOTS, class Emit>
+__device__ __forceinline__ uint64_t wave_extract_top_iter(uint64_t (&rk)[SLOTS], int keep,
+                                                          Emit emit) {
   uint64_t last = 0;
   for (int k = 0; k < keep; ++k) {
     uint64_t best = 0;
     int slot = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < SLOTS; ++i)
       if (rk[i] > best) {
         best = rk[i];
         slot = i;
@@ -100,7 +101,7 @@ __device__ __forceinline__ uint64_t wave_extract_top_iter(uint64_t (&rk)[16], in
     }
     if (best == wbest && wbest != 0) {  // ids are unique: one lane holds the winner
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < SLOTS; ++i)
         if (i == slot) rk[i] = 0ull;
       emit(k, wbest);
     }
@@ -118,14 +119,14 @@ __device__ __forceinline__ uint64_t wave_extract_top_iter(uint64_t (&rk)[16], in
 //     few lanes, falls back to the repeated maxima);
 //  3. each packed key's rank is the number of packed keys above it.
 // The nonzero keys must be distinct (rank keys carry the id).
-template <class Emit>
-__device__ __forceinline__ uint64_t wave_extract_top(uint64_t (&rk)[16], int keep,
+template <int SLOTS, class Emit>
+__device__ __forceinline__ uint64_t wave_extract_top(uint64_t (&rk)[SLOTS], int keep,
                                                      uint64_t* scratch, Emit emit) {
   if (keep <= 0) return 0;
   const int lane = threadIdx.x & 63;
   uint64_t mx = rk[0];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = rk[i] > mx ? rk[i] : mx;
+  for (int i = 1; i < SLOTS; ++i) mx = rk[i] > mx ? rk[i] : mx;
   int above = 0;
 #pragma unroll
   for (int j = 0; j < 64; ++j) above += readlane_u64(mx, j) > mx ? 1 : 0;
@@ -134,14 +135,14 @@ __device__ __forceinline__ uint64_t wave_extract_top(uint64_t (&rk)[16], int kee
   const uint64_t thr = hit ? readlane_u64(mx, __builtin_ctzll(hit)) : 1ull;
   int total = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < SLOTS; ++i) {
     const bool in = rk[i] >= thr;
     const uint64_t m = __ballot(in);
     const int pos = total + lane_prefix(m);
     if (in && pos < 64) scratch[pos] = rk[i];
     total += __popcll(m);
   }
-  if (total > 64) return wave_extract_top_iter(rk, keep, emit);
+  if (total > 64) return wave_extract_top_iter<SLOTS>(rk, keep, emit);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

@@ -13,8 +13,12 @@ hipError_t launch_pool_keys(const uint16_t* k_idx, int64_t k_stride, int64_t n_b
 
 // Two-level top-k: per segment of kTopkWaveSeg candidates, the kTopkWaveKeep best as
 // (score, id) pairs (id -1: empty) and the worst kept one when the segment had more.
+// kTopkWaveSeg is a multiple of 256 up to 1024 (a wave's lanes hold kTopkWaveSeg / 64
+// each); kTopkWaveKeep is a multiple of 4 up to 16.
 constexpr int kTopkWaveSeg = 1024;
 constexpr int kTopkWaveKeep = 16;
+static_assert(kTopkWaveSeg % 256 == 0 && kTopkWaveSeg <= 1024, "segment size");
+static_assert(kTopkWaveKeep % 4 == 0 && kTopkWaveKeep <= 16, "kept per segment");
 struct TopkCandidates {
   float* cand_val;   // [rows][n_seg][kTopkWaveKeep]
   int32_t* cand_idx;

@@ -561,14 +561,15 @@ __device__ __forceinline__ void write_bitmap_ids(SM& sm, int words, int32_t* out
   }
 }
 
-// Ascending sort of 16 ids in registers (bitonic network).
-__device__ __forceinline__ void sort16_asc(int32_t (&x)[16]) {
+// Ascending sort of N ids in registers (bitonic network, N a power of 2).
+template <int N>
+__device__ __forceinline__ void sort_ids_asc(int32_t (&x)[N]) {
 #pragma unroll
-  for (int k = 2; k <= 16; k <<= 1)
+  for (int k = 2; k <= N; k <<= 1)
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < N; ++i) {
         const int l = i ^ j;
         if (l > i) {
           const int32_t a = x[i], b = x[l];
@@ -579,47 +580,59 @@ __device__ __forceinline__ void sort16_asc(int32_t (&x)[16]) {
       }
 }
 
-// Merge of the segment winners when every segment fits one thread (n_seg <= threads,
-// kWaveKeep == 16): thread s holds segment s's candidates. merge_fetch issues their
-// loads at kernel entry (they do not depend on the row's length) and clears the value
-// histogram meanwhile; merge_segments_fast then finds the m-th best key T from one
-// value histogram plus a rank count inside T's bin (at most 64 entries, else it
-// returns 1 and the general merge runs). With fewer than m candidates, or a truncated
-// segment whose reported worst ranks above T (it may hide a better candidate), it
-// returns 2: the whole row must be selected. Otherwise each thread writes its kept
-// ids, sorted, at its offset (segments cover ascending id ranges, so the output is
-// ascending) and it returns 0.
+// Merge of the segment winners when every segment fits a thread's share: thread t
+// holds segments t + kTkThreads*j (j < kMergeSPT) with their kWaveKeep candidates
+// each. merge_fetch issues their loads at kernel entry (they do not depend on the
+// row's length) and clears the value histogram meanwhile; merge_segments_fast then
+// finds the m-th best key T from one value histogram plus a rank count inside T's bin
+// (at most 64 entries, else it returns 1 and the general merge runs). With fewer than
+// m candidates, or a truncated segment whose reported worst ranks above T (it may
+// hide a better candidate), it returns 2: the whole row must be selected. Otherwise
+// each segment's kept ids are written, sorted, at the segment's offset (segments
+// cover ascending id ranges, so the output is ascending) and it returns 0.
+// segments per thread: enough for rows of 2^18 blocks (1M tokens at r = 4)
+constexpr int kMergeSPT = (262144 / kWaveSeg + kTkThreads - 1) / kTkThreads;
+constexpr int kMergeCand = kMergeSPT * kWaveKeep;  // candidates per thread
+static_assert(kWaveKeep % 4 == 0 && (kWaveKeep & (kWaveKeep - 1)) == 0, "kept per segment");
+
 struct MergeRegs {
-  float v[16];
-  int32_t id[16];
-  uint64_t bkey;
+  float v[kMergeCand];
+  int32_t id[kMergeCand];
+  uint64_t bkey[kMergeSPT];
 };
 
 template <class SM>
 __device__ __forceinline__ void merge_fetch(SM& sm, const TopkLaunch& L, int64_t crow,
                                             MergeRegs& r) {
   const int tid = threadIdx.x;
-  const bool have = tid < L.n_seg;
-  const int64_t slot = crow * L.n_seg + (have ? tid : 0);
-  const float4* cv4 = reinterpret_cast<const float4*>(L.cand_val + slot * kWaveKeep);
-  const int4* ci4 = reinterpret_cast<const int4*>(L.cand_idx + slot * kWaveKeep);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float qn = __builtin_nanf("");
-    const float4 a = have ? cv4[q] : make_float4(qn, qn, qn, qn);
-    const int4 b = have ? ci4[q] : make_int4(-1, -1, -1, -1);
-    r.v[4 * q] = a.x; r.v[4 * q + 1] = a.y; r.v[4 * q + 2] = a.z; r.v[4 * q + 3] = a.w;
-    r.id[4 * q] = b.x; r.id[4 * q + 1] = b.y; r.id[4 * q + 2] = b.z; r.id[4 * q + 3] = b.w;
+  for (int j = 0; j < kMergeSPT; ++j) {
+    const int seg = tid + kTkThreads * j;
+    const bool have = seg < L.n_seg;
+    const int64_t slot = crow * L.n_seg + (have ? seg : 0);
+    const float4* cv4 = reinterpret_cast<const float4*>(L.cand_val + slot * kWaveKeep);
+    const int4* ci4 = reinterpret_cast<const int4*>(L.cand_idx + slot * kWaveKeep);
+#pragma unroll
+    for (int q = 0; q < kWaveKeep / 4; ++q) {
+      const float qn = __builtin_nanf("");
+      const float4 a = have ? cv4[q] : make_float4(qn, qn, qn, qn);
+      const int4 b = have ? ci4[q] : make_int4(-1, -1, -1, -1);
+      float* v = r.v + j * kWaveKeep + 4 * q;
+      int32_t* id = r.id + j * kWaveKeep + 4 * q;
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      id[0] = b.x; id[1] = b.y; id[2] = b.z; id[3] = b.w;
+    }
+    const int32_t bid = have ? L.bnd_idx[slot] : -1;
+    const float bval = have ? L.bnd_val[slot] : 0.f;
+    r.bkey[j] = bid >= 0 ? rank_key(bval, bid) : 0ull;
   }
-  const int32_t bid = have ? L.bnd_idx[slot] : -1;
-  const float bval = have ? L.bnd_val[slot] : 0.f;
-  r.bkey = bid >= 0 ? rank_key(bval, bid) : 0ull;
   for (int i = tid; i < kLinBins; i += kTkThreads) sm.hist[i] = 0u;
   if (tid == 0) sm.misc[4] = 0;
 }
 
 template <class SM>
 __device__ __forceinline__ int merge_segments_fast(SM& sm, MergeRegs& r, int m, int32_t* out) {
+  constexpr int KC = kMergeCand;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float* v = r.v;
   const int32_t* id = r.id;
@@ -627,7 +640,7 @@ __device__ __forceinline__ int merge_segments_fast(SM& sm, MergeRegs& r, int m, 
   float mn = INFINITY, mx = -INFINITY;
   uint32_t n_valid = 0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < KC; ++j) {
     if (id[j] < 0) v[j] = __builtin_nanf("");  // absent
     mn = fminf(mn, v[j]);  // fminf / fmaxf ignore NaN
     mx = fmaxf(mx, v[j]);
@@ -656,7 +669,7 @@ __device__ __forceinline__ int merge_segments_fast(SM& sm, MergeRegs& r, int m, 
   if (n_valid < (uint32_t)m) return 2;
   const LinBins bins = make_bins(mn, mx);
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+  for (int j = 0; j < KC; ++j)
     if (v[j] == v[j]) atomicAdd(&sm.hist[bins(v[j])], 1u);
   __syncthreads();
   find_digit(sm, kLinBins, (uint32_t)m);
@@ -665,7 +678,7 @@ __device__ __forceinline__ int merge_segments_fast(SM& sm, MergeRegs& r, int m, 
   const int bucket = sm.misc[2];
   if (bucket > 64) return 1;
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+  for (int j = 0; j < KC; ++j)
     if (v[j] == v[j] && bins(v[j]) == B) {
       const int p = atomicAdd(&sm.misc[4], 1);
       sm.tie_key[p] = order_key(v[j]);
@@ -685,25 +698,46 @@ __device__ __forceinline__ int merge_segments_fast(SM& sm, MergeRegs& r, int m, 
   }
   __syncthreads();
   const uint64_t T = ((uint64_t)(uint32_t)sm.misc[5] << 32) | (uint32_t)sm.misc[6];
-  int32_t kept[16];
-  uint32_t cnt = 0;
+  bool bad = false;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const bool k = v[j] == v[j] && rank_key(v[j], id[j]) >= T;
-    kept[j] = k ? id[j] : 0x7fffffff;
-    cnt += k ? 1u : 0u;
+  for (int j = 0; j < kMergeSPT; ++j) bad |= r.bkey[j] > T;
+  // Per-segment counts packed in 16-bit fields (a field's total stays below
+  // kTkThreads * kWaveKeep <= 4096), one scan for all of this thread's segments. With
+  // one field the scan also carries the truncation check: a flagged thread adds
+  // 1 << 16, so the total shows whether any segment failed it.
+  static_assert(kMergeSPT <= 2, "two 16-bit count fields");
+  if (kMergeSPT > 1 && __syncthreads_or(bad)) return 2;
+  uint32_t cnt[kMergeSPT], packed = (kMergeSPT == 1 && bad) ? (1u << 16) : 0u;
+#pragma unroll
+  for (int j = 0; j < kMergeSPT; ++j) {
+    cnt[j] = 0;
+#pragma unroll
+    for (int e = 0; e < kWaveKeep; ++e) {
+      const int c = j * kWaveKeep + e;
+      cnt[j] += (v[c] == v[c] && rank_key(v[c], id[c]) >= T) ? 1u : 0u;
+    }
+    packed |= cnt[j] << (16 * j);
   }
-  // The offsets scan also carries the truncation check: a flagged thread adds 1 << 16
-  // (counts stay below 4096), so the total shows whether any segment failed it.
-  constexpr uint32_t kBad = 1u << 16;
   uint32_t total;
-  const uint32_t off = block_excl_scan(sm, cnt + (r.bkey > T ? kBad : 0u), total);
-  if (total >= kBad) return 2;
-  if (cnt) {
-    sort16_asc(kept);
+  const uint32_t off = block_excl_scan(sm, packed, total);
+  if (kMergeSPT == 1 && total >= (1u << 16)) return 2;
+  uint32_t base = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if ((uint32_t)j < cnt) out[off + j] = kept[j];
+  for (int j = 0; j < kMergeSPT; ++j) {
+    const uint32_t o = base + ((off >> (16 * j)) & 0xffffu);
+    base += (total >> (16 * j)) & 0xffffu;
+    if (cnt[j]) {
+      int32_t kept[kWaveKeep];
+#pragma unroll
+      for (int e = 0; e < kWaveKeep; ++e) {
+        const int c = j * kWaveKeep + e;
+        kept[e] = (v[c] == v[c] && rank_key(v[c], id[c]) >= T) ? id[c] : 0x7fffffff;
+      }
+      sort_ids_asc<kWaveKeep>(kept);
+#pragma unroll
+      for (int e = 0; e < kWaveKeep; ++e)
+        if ((uint32_t)e < cnt[j]) out[o + e] = kept[e];
+    }
   }
   return 0;
 }
@@ -718,7 +752,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
   const int bi = blockIdx.z;
   const int64_t crow = (int64_t)bi * a.lq + row;
   MergeRegs mr;
-  const bool fast_merge = MODE == kMerge && L.n_seg <= kTkThreads;
+  const bool fast_merge = MODE == kMerge && L.n_seg <= kTkThreads * kMergeSPT;
   if (fast_merge) merge_fetch(sm, L, crow, mr);
   int64_t t, own, C;
   int m;
@@ -827,7 +861,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
 }
 
 // First pass over long rows: wave w of the launch takes segment (row, seg) of
-// kWaveSeg scores, each lane holding 16 of them, and extracts its kWaveKeep best
+// kWaveSeg scores, each lane holding kWaveSeg / 64 of them, and extracts its kWaveKeep best
 // (score, id) rank keys.
 __global__ __launch_bounds__(256) void topk_wave_segments_kernel(TopkLaunch L) {
   __shared__ uint64_t scratch[4][64];
@@ -849,10 +883,11 @@ __global__ __launch_bounds__(256) void topk_wave_segments_kernel(TopkLaunch L) {
   const int lo = seg_id * kWaveSeg;
   const int n = (int)max((int64_t)0, min(C - lo, (int64_t)kWaveSeg));
   const float* src = a.scores + (int64_t)bi * a.s_bs + row * a.ld + lo;
-  // lane holds positions 4*(lane + 64*q) + e, q < 4
-  uint64_t rk[16];
+  // lane holds positions 4*(lane + 64*q) + e, q < kWaveSeg / 256
+  constexpr int kQ = kWaveSeg / 256;
+  uint64_t rk[4 * kQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kQ; ++q) {
     const int p = 4 * (lane + 64 * q);
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p < n) v = *reinterpret_cast<const float4*>(src + p);  // inside the row: ld % 4 == 0
@@ -861,7 +896,8 @@ __global__ __launch_bounds__(256) void topk_wave_segments_kernel(TopkLaunch L) {
     for (int e = 0; e < 4; ++e) rk[4 * q + e] = p + e < n ? rank_key(xs[e], lo + p + e) : 0ull;
   }
   const int keep = min(n, kWaveKeep);
-  const uint64_t last = wave_extract_top(rk, keep, scratch[threadIdx.x >> 6], [&](int k, uint64_t w) {
+  const uint64_t last = wave_extract_top<4 * kQ>(rk, keep, scratch[threadIdx.x >> 6],
+                                                 [&](int k, uint64_t w) {
     const int32_t id = rank_key_id(w);
     cv[k] = src[id - lo];
     ci[k] = id;

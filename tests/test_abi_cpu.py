@@ -86,8 +86,10 @@ def test_topk_and_attention_validation(lib):
 
 
 def test_workspace_queries_and_short_workspace(lib):
+    # 512 kept blocks = 128 steps of 4: 64 waves of 2 steps, merged 4 per workgroup,
+    # so 16 (o[256], m, l) fp32 partials per (sequence, head)
     n = lib.qsa_sparse_attn_decode_workspace_bytes(8, 24, 256, 512)
-    assert n >= 8 * 24 * 32 * 258 * 4
+    assert n >= 8 * 24 * 16 * 258 * 4
     assert lib.qsa_sparse_attn_decode(8, 24, 2, 256, 4, 512, FAKE, FAKE, FAKE, 1 << 29, 1 << 20,
                                       FAKE, FAKE, ctypes.c_float(0.06), FAKE, None, FAKE, n - 1,
                                       None) == 3
@@ -99,5 +101,5 @@ def test_workspace_queries_and_short_workspace(lib):
     assert lib.qsa_topk_workspace_bytes(1, 10, 10, 2048, 4) == 0
     assert lib.qsa_topk_workspace_bytes(1, 10, 32768, 2048, 4) == 0
     # rows longer than one workgroup's 32768 candidates use a two-level selection:
-    # 8 rows x 64 segments x 64 kept (value, id) pairs plus one boundary per segment
-    assert lib.qsa_topk_workspace_bytes(8, 1, 262144, 2048, 4) >= 8 * 64 * (64 + 1) * 8
+    # 8 rows x 256 segments x 16 kept (value, id) pairs plus one boundary per segment
+    assert lib.qsa_topk_workspace_bytes(8, 1, 262144, 2048, 4) >= 8 * 256 * (16 + 1) * 8
