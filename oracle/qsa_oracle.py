@@ -1,4 +1,5 @@
-"""CPU oracle of the Qwen Sparse Attention (QSA) forward path.
+"""CPU oracle of the Qwen Sparse Attention (QSA) forward path and of the sparse
+attention's backward over a fixed selection.
 
 TEST INFRASTRUCTURE ONLY. This is the plain, slow, obviously correct fp64 numpy
 statement of what the path computes, used to check the HIP library. Only the test
@@ -174,6 +175,66 @@ def attend(q_t: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float
         o[h] = (p @ v_rows[:, g, :]) / den
         lse[h] = mx + np.log(den)
     return o, lse
+
+
+def attend_backward(q_t: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
+                    do_t: np.ndarray, scale: float):
+    """Gradients of attend(q_t, k_rows, v_rows) given do_t [Hq, d], the gradient of
+    the loss with respect to the output o [Hq, d].
+
+    The selection is a constant of the backward pass ([MR] ships a forward and a
+    backward sparse-attention kernel over selection rows built outside the kernel):
+    no gradient reaches the indexer through the top-k. Per head h (KV group g), with
+    z = scale * K_g q_h, p = softmax(z), o_h = p V_g:
+      dv_g += p (outer) do_h,    dp = V_g do_h,
+      dz = p * (dp - p . dp)     (softmax Jacobian),
+      dq_h = scale * dz K_g,     dk_g += scale * dz (outer) q_h.
+    Returns (dq [Hq, d], dk [n, Hkv, d], dv [n, Hkv, d]).
+    """
+    hq, d = q_t.shape
+    n, hkv, _ = k_rows.shape
+    grp = hq // hkv
+    dq = np.zeros((hq, d), dtype=np.float64)
+    dk = np.zeros((n, hkv, d), dtype=np.float64)
+    dv = np.zeros((n, hkv, d), dtype=np.float64)
+    for h in range(hq):
+        g = h // grp
+        z = scale * (k_rows[:, g, :] @ q_t[h])
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        dv[:, g, :] += np.outer(p, do_t[h])
+        dp = v_rows[:, g, :] @ do_t[h]
+        dz = p * (dp - p @ dp)
+        dq[h] = scale * (dz @ k_rows[:, g, :])
+        dk[:, g, :] += scale * np.outer(dz, q_t[h])
+    return dq, dk, dv
+
+
+def backward_prefill(q_bits, k_bits, v_bits, sel, dout, *, r: int, q_pos0: int = 0,
+                     scale: Optional[float] = None) -> dict:
+    """Backward of the sparse attention over given selections, for every query row.
+
+    q_bits [Lq, Hq, d], k_bits/v_bits [Lk, Hkv, d] (bf16 bit patterns); sel [Lq, n_sel]
+    block ids (-1 padded); dout [Lq, Hq, d] fp64 (the output gradient). Row i is at
+    position q_pos0 + i and reads kept_tokens(sel[i]). The key and value gradients
+    sum the contributions of every row that read the token.
+    Returns dq [Lq, Hq, d], dk and dv [Lk, Hkv, d], fp64.
+    """
+    lq, hq, d = q_bits.shape
+    lk, hkv, _ = k_bits.shape
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    k = bf16_to_f64(k_bits)
+    v = bf16_to_f64(v_bits)
+    dq = np.zeros((lq, hq, d), dtype=np.float64)
+    dk = np.zeros((lk, hkv, d), dtype=np.float64)
+    dv = np.zeros((lk, hkv, d), dtype=np.float64)
+    for i in range(lq):
+        toks = kept_tokens(sel[i], q_pos0 + i, r, lk)
+        dq[i], dkr, dvr = attend_backward(bf16_to_f64(q_bits[i]), k[toks], v[toks],
+                                          np.asarray(dout[i], dtype=np.float64), scale)
+        np.add.at(dk, toks, dkr)
+        np.add.at(dv, toks, dvr)
+    return {"dq": dq, "dk": dk, "dv": dv}
 
 
 # --------------------------------------------------------------------------------------

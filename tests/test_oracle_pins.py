@@ -329,3 +329,113 @@ def test_chunked_prefill_equals_full_prefill_rows():
                               rows=np.arange(0, L - prefix, 5))
     np.testing.assert_array_equal(chunk["sel"], full["sel"])
     np.testing.assert_allclose(chunk["out"], full["out"], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------
+# Backward of the sparse attention over a fixed selection
+# ------------------------------------------------------------------------------------
+
+
+def _bwd_case(seed, lq=12, lk=24, hq=4, hkv=2, d=8, r=4, n_sel=3, q_pos0=12, qscale=1.0):
+    rng = np.random.default_rng(seed)
+    q = _bits(rng.standard_normal((lq, hq, d)) * qscale)
+    k = _bits(rng.standard_normal((lk, hkv, d)))
+    v = _bits(rng.standard_normal((lk, hkv, d)))
+    sel = np.full((lq, n_sel), -1, dtype=np.int64)
+    for i in range(lq):
+        own = (q_pos0 + i) // r
+        others = rng.choice(own, min(n_sel - 1, own), replace=False) if own else []
+        row = np.sort(np.concatenate([np.asarray(others, dtype=np.int64), [own]]))
+        sel[i, : len(row)] = row
+    dout = rng.standard_normal((lq, hq, d))
+    return q, k, v, sel, dout
+
+
+def _loss(q, k, v, sel, dout, r, q_pos0, scale):
+    """sum(dout * o) as a function of fp64 q, k, v (the oracle's forward)."""
+    tot = 0.0
+    for i in range(q.shape[0]):
+        toks = O.kept_tokens(sel[i], q_pos0 + i, r, k.shape[0])
+        o, _ = O.attend(q[i], k[toks], v[toks], scale)
+        tot += float((dout[i] * o).sum())
+    return tot
+
+
+def test_backward_matches_central_differences():
+    # The analytic gradients against numerical derivatives of the oracle's own forward
+    # (a dropped softmax-Jacobian term, a wrong sign or a transposed operand fails).
+    q, k, v, sel, dout = _bwd_case(30)
+    r, q_pos0, scale = 4, 12, 0.7
+    g = O.backward_prefill(q, k, v, sel, dout, r=r, q_pos0=q_pos0, scale=scale)
+    qf, kf, vf = O.bf16_to_f64(q), O.bf16_to_f64(k), O.bf16_to_f64(v)
+    eps = 1e-6
+    rng = np.random.default_rng(31)
+    for name, arr, grad in (("q", qf, g["dq"]), ("k", kf, g["dk"]), ("v", vf, g["dv"])):
+        for _ in range(25):
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            args = {"q": qf, "k": kf, "v": vf}
+            args[name] = plus
+            lp = _loss(args["q"], args["k"], args["v"], sel, dout, r, q_pos0, scale)
+            args[name] = minus
+            lm = _loss(args["q"], args["k"], args["v"], sel, dout, r, q_pos0, scale)
+            num = (lp - lm) / (2 * eps)
+            assert abs(num - grad[idx]) <= 1e-7 * max(1.0, abs(num)), (name, idx, num, grad[idx])
+
+
+def test_backward_matches_torch_autograd_dense_masked():
+    # Library routine: torch autograd (CPU, fp64) through a dense softmax attention whose
+    # mask allows exactly each row's kept tokens.
+    q, k, v, sel, dout = _bwd_case(32, lq=10, lk=20, hq=6, hkv=2, d=16, n_sel=3, q_pos0=8)
+    r, q_pos0, scale = 4, 8, 0.25
+    g = O.backward_prefill(q, k, v, sel, dout, r=r, q_pos0=q_pos0, scale=scale)
+    lq, hq, d = q.shape
+    lk, hkv, _ = k.shape
+    mask = torch.zeros((lq, lk), dtype=torch.bool)
+    for i in range(lq):
+        mask[i, torch.from_numpy(O.kept_tokens(sel[i], q_pos0 + i, r, lk))] = True
+    qt = torch.from_numpy(O.bf16_to_f64(q)).requires_grad_()
+    kt = torch.from_numpy(O.bf16_to_f64(k)).requires_grad_()
+    vt = torch.from_numpy(O.bf16_to_f64(v)).requires_grad_()
+    grp = hq // hkv
+    kk = kt.repeat_interleave(grp, dim=1)  # [lk, hq, d], head h reads group h // grp
+    vv = vt.repeat_interleave(grp, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt.transpose(0, 1), kk.transpose(0, 1), vv.transpose(0, 1),
+        attn_mask=mask[None], scale=scale).transpose(0, 1)
+    (o * torch.from_numpy(dout)).sum().backward()
+    np.testing.assert_allclose(g["dq"], qt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dk"], kt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dv"], vt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_closed_forms_and_invariants():
+    r, q_pos0, scale = 4, 12, 0.5
+    q, k, v, sel, dout = _bwd_case(33)
+    lk = k.shape[0]
+    # (1) Softmax rows sum to one, so the logits' gradient sums to zero per (row, head):
+    #     the key gradients of a KV group sum to zero over all keys.
+    g = O.backward_prefill(q, k, v, sel, dout, r=r, q_pos0=q_pos0, scale=scale)
+    np.testing.assert_allclose(g["dk"].sum(axis=0), 0.0, atol=1e-12)
+    # (2) dv sums dout over the reading rows with weight p: summed over keys it is the
+    #     sum of every row's dout per group (p sums to one).
+    grp = q.shape[1] // k.shape[1]
+    want = dout.reshape(dout.shape[0], k.shape[1], grp, -1).sum(axis=(0, 2))
+    np.testing.assert_allclose(g["dv"].sum(axis=0), want, atol=1e-10)
+    # (3) V constant per group: o does not depend on q or k, so dq = dk = 0.
+    vc = np.repeat(v[:1], lk, axis=0)
+    g = O.backward_prefill(q, k, vc, sel, dout, r=r, q_pos0=q_pos0, scale=scale)
+    np.testing.assert_allclose(g["dq"], 0.0, atol=1e-12)
+    np.testing.assert_allclose(g["dk"], 0.0, atol=1e-12)
+    # (4) q = 0: uniform weights over each row's kept tokens, so dv[j] is the sum of
+    #     dout / |J_i| over the rows i that read j.
+    qz = np.zeros_like(q)
+    g = O.backward_prefill(qz, k, v, sel, dout, r=r, q_pos0=q_pos0, scale=scale)
+    want = np.zeros_like(g["dv"])
+    for i in range(q.shape[0]):
+        toks = O.kept_tokens(sel[i], q_pos0 + i, r, lk)
+        for h in range(q.shape[1]):
+            want[toks, h // grp] += dout[i, h] / len(toks)
+    np.testing.assert_allclose(g["dv"], want, atol=1e-12)
