@@ -1,4 +1,4 @@
-"""MI355X-native Qwen Sparse Attention (QSA) forward path.
+"""MI355X-native Qwen Sparse Attention (QSA) forward path and sparse-attention backward.
 
 The computation lives in libqsa.so (hand-written HIP kernels for gfx950 behind the C
 ABI of include/qsa.h); this package only builds it and marshals torch tensors to it.
@@ -14,6 +14,7 @@ from .ops import (  # noqa: F401
     qsa_prefill_forward,
     qsa_prefill_select,
     qsa_probe_gather,
+    qsa_sparse_attn_bwd,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_fwd,
     qsa_topk_blocks,

@@ -240,6 +240,70 @@ qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, i
                     "qsa_sparse_attn_fwd launch");
 }
 
+size_t qsa_sparse_attn_bwd_workspace_bytes(int64_t lq, int64_t lk, int hq, int r, int n_sel) {
+  if (lq <= 0 || lk <= 0 || hq <= 0 || r <= 0 || n_sel <= 0) return 0;
+  return qsa::bwd_layout(lq, lk, hq, n_sel, r).total;
+}
+
+qsa_status qsa_sparse_attn_bwd(int64_t lq, int64_t lk, int hq, int hkv, int d, int r, int n_sel,
+                               const void* q, const void* k, const void* v, const int32_t* sel,
+                               int64_t q_pos0, float softmax_scale, const void* out,
+                               const float* lse, const void* dout, float* dq, float* dk,
+                               float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_REQUIRE(n_sel >= 1 && n_sel <= 1024, QSA_ERR_UNSUPPORTED, "n_sel=%d: supported 1..1024",
+              n_sel);
+  QSA_REQUIRE(lq >= 0 && lq * (int64_t)n_sel < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT,
+              "lq=%lld: lq * n_sel must stay below 2^31", (long long)lq);
+  QSA_REQUIRE(lk >= 1 && lk < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT, "lk=%lld",
+              (long long)lk);
+  QSA_REQUIRE(q_pos0 >= 0 && q_pos0 + lq <= lk, QSA_ERR_INVALID_ARGUMENT,
+              "query positions [%lld, %lld) must lie inside the %lld keys", (long long)q_pos0,
+              (long long)(q_pos0 + lq), (long long)lk);
+  QSA_REQUIRE(isfinite(softmax_scale), QSA_ERR_INVALID_ARGUMENT, "softmax_scale not finite");
+  QSA_REQUIRE(k && v && dk && dv, QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  QSA_REQUIRE(aligned16(k) && aligned16(v) && aligned16(dk) && aligned16(dv),
+              QSA_ERR_INVALID_ARGUMENT, "k, v, dk and dv must be 16-byte aligned");
+  QSA_REQUIRE(lq == 0 || (q && sel && out && lse && dout && dq), QSA_ERR_INVALID_ARGUMENT,
+              "null tensor pointer");
+  QSA_REQUIRE(lq == 0 || (aligned16(q) && aligned16(out) && aligned16(dout) && aligned16(dq)),
+              QSA_ERR_INVALID_ARGUMENT, "q, out, dout and dq must be 16-byte aligned");
+  const size_t need = qsa_sparse_attn_bwd_workspace_bytes(lq, lk, hq, r, n_sel);
+  QSA_REQUIRE(lq == 0 || (workspace && workspace_bytes >= need && aligned16(workspace)),
+              QSA_ERR_WORKSPACE, "backward workspace: need %zu bytes (16-byte aligned), got %zu",
+              need, workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (lq == 0) {  // no query reads any key: zero gradients (a fill kernel, not a memset)
+    QSA_TRY(hip_status(qsa::launch_fill_zero(dk, lk * hkv * d, s), "dk clear"));
+    return hip_status(qsa::launch_fill_zero(dv, lk * hkv * d, s), "dv clear");
+  }
+  qsa::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sel = sel;
+  a.out = static_cast<const uint16_t*>(out);
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.lq = lq;
+  a.lk = lk;
+  a.q_pos0 = q_pos0;
+  a.n_kb = (lk + r - 1) / r;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.n_sel = n_sel;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return hip_status(qsa::launch_sparse_attn_bwd(a, static_cast<char*>(workspace), workspace_bytes,
+                                                s),
+                    "qsa_sparse_attn_bwd launch (or sort scratch larger than reserved)");
+}
+
 size_t qsa_sparse_attn_decode_workspace_bytes(int batch, int hq, int d, int n_sel) {
   if (batch <= 0 || hq <= 0 || d <= 0 || n_sel <= 0) return 0;
   const size_t ns = (size_t)qsa::decode_num_splits(n_sel);

@@ -99,6 +99,40 @@ struct AttnArgs {
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream);
 
+// ---- stage 4 backward ----
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* sel;
+  const uint16_t* out;   // forward output (bf16), for D = dO . O
+  const float* lse;      // forward lse (natural log)
+  const uint16_t* dout;  // output gradient (bf16)
+  float* dq;             // [lq][hq][d]
+  float* dk;             // [lk][hkv][d]
+  float* dv;
+  float* dbuf;                // workspace: D [lq][hq]
+  const int32_t* pair_rows;   // workspace: rows of the (block, row) pairs sorted by block
+  int32_t* start;             // workspace: [n_kb + 1] first pair of each key block
+  int64_t lq;
+  int64_t lk;
+  int64_t q_pos0;
+  int64_t n_kb;  // key blocks (the last may be partial): ceil(lk / 4)
+  int hq;
+  int hkv;
+  int d;
+  int n_sel;
+  float scale;
+  float scale_log2;
+};
+// Byte offsets of the backward's workspace parts.
+struct BwdLayout {
+  size_t dbuf, keys0, keys1, rows0, rows1, start, temp, temp_bytes, total;
+};
+BwdLayout bwd_layout(int64_t lq, int64_t lk, int hq, int n_sel, int r);
+hipError_t launch_sparse_attn_bwd(BwdArgs a, char* ws, size_t ws_bytes, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+
 // ---- measurement aid ----
 hipError_t launch_probe_gather(const void* buf, const int32_t* ids, int steps, int64_t n_waves,
                                uint32_t* sink, hipStream_t stream);

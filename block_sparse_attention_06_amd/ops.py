@@ -154,6 +154,35 @@ def qsa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: 
     return out, lse
 
 
+def qsa_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor,
+                        out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, *,
+                        q_pos0: int = 0, scale: Optional[float] = None, r: int = 4,
+                        workspace: Optional[torch.Tensor] = None):
+    """Gradients of qsa_sparse_attn_fwd with respect to q, k, v over the same selection.
+
+    out/lse are the forward's outputs, dout [Lq,Hq,d] bf16 the output gradient.
+    Returns fp32 (dq [Lq,Hq,d], dk [Lk,Hkv,d], dv [Lk,Hkv,d])."""
+    _need(q, "q", torch.bfloat16)
+    for name, t, dt in (("k", k, torch.bfloat16), ("v", v, torch.bfloat16), ("sel", sel, torch.int32),
+                        ("out", out, torch.bfloat16), ("lse", lse, torch.float32),
+                        ("dout", dout, torch.bfloat16)):
+        _need(t, name, dt, q.device)
+    lq, hq, d = q.shape
+    lk, hkv, _ = k.shape
+    n_sel = sel.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq = torch.empty((lq, hq, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((lk, hkv, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty((lk, hkv, d), dtype=torch.float32, device=q.device)
+    nbytes = _lib.load().qsa_sparse_attn_bwd_workspace_bytes(lq, lk, hq, r, n_sel)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _call("qsa_sparse_attn_bwd", lq, lk, hq, hkv, d, r, n_sel, _ptr(q), _ptr(k), _ptr(v),
+          _ptr(sel), q_pos0, scale, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+          _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q))
+    return dq, dk, dv
+
+
 def qsa_sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            seq_lens: torch.Tensor, sel: torch.Tensor, *,
                            scale: Optional[float] = None, r: int = 4):

@@ -135,6 +135,35 @@ qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, i
                                void* out, float* lse, void* stream);
 
 /*
+ * Stage 4 backward -- gradients of the stage-4 attention with respect to q, k and v
+ * over the same selection rows, which are constants here ([MR]: the recipe trains
+ * through a forward and a backward sparse-attention kernel fed with selection rows
+ * built outside the kernel; no gradient reaches the indexer through the top-k).
+ * With P the softmax weights of row i over its kept tokens J_i:
+ *   dv[j][g] = sum_{i: j in J_i} sum_{h in g} P[i][h][j] dout[i][h]
+ *   dS[i][h][j] = P[i][h][j] (dout[i][h] . v[j][g] - dout[i][h] . out[i][h])
+ *   dq[i][h] = scale sum_{j in J_i} dS[i][h][j] k[j][g]
+ *   dk[j][g] = scale sum_{i: j in J_i} sum_{h in g} dS[i][h][j] q[i][h]
+ * P is recomputed from lse; the row term dout . out uses the forward's bf16 output.
+ * Every sum runs in a fixed order: results do not depend on scheduling.
+ *   q, k, v, sel, q_pos0, softmax_scale: as for qsa_sparse_attn_fwd
+ *   out  bf16 [lq][hq][d], lse fp32 [lq][hq]: the forward's outputs (both required)
+ *   dout bf16 [lq][hq][d]: gradient of the loss with respect to out
+ *   dq   fp32 [lq][hq][d]; dk, dv fp32 [lk][hkv][d], fully written (keys that no row
+ *        reads get 0)
+ *   workspace: qsa_sparse_attn_bwd_workspace_bytes() bytes, 16-byte aligned (an
+ *   upper bound when no GPU is visible to the query; the call checks that the sort's
+ *   scratch on its device fits and returns QSA_ERR_HIP if not). lq * n_sel < 2^31.
+ */
+size_t qsa_sparse_attn_bwd_workspace_bytes(int64_t lq, int64_t lk, int hq, int r, int n_sel);
+qsa_status qsa_sparse_attn_bwd(int64_t lq, int64_t lk, int hq, int hkv, int d, int r, int n_sel,
+                               const void* q, const void* k, const void* v,
+                               const int32_t* sel, int64_t q_pos0, float softmax_scale,
+                               const void* out, const float* lse, const void* dout,
+                               float* dq, float* dk, float* dv, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * Stage 4' -- decode: one new query token per sequence at t = seq_lens[s] - 1, the
  * same attention as stage 4 over a KV cache, split over the kept blocks into
  * partial softmax states that a second kernel combines.

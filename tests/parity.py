@@ -8,6 +8,11 @@
   equality.
 * Attention output (bf16): max-abs <= 2e-2 and relative L2 <= 5e-3 over the whole
   compared output, with the oracle run on the GPU's own (validated) selection.
+* Attention gradients (fp32 outputs of the backward): relative L2 <= 1e-2 and max-abs
+  <= 2e-2 * max |reference| per gradient. The GPU rounds each product's weight
+  operand (P for dv, dS for dq and dk) to bf16 (relative 2^-9) and takes the row term
+  D from the forward's bf16 output; two such roundings per gradient give twice the
+  forward's 5e-3 rel-L2 budget.
 """
 from __future__ import annotations
 
@@ -20,6 +25,8 @@ REL_GAP = 1e-3
 OUT_MAX_ABS = 2e-2
 OUT_REL_L2 = 5e-3
 LSE_ABS = 2e-3
+GRAD_REL_L2 = 1e-2
+GRAD_MAX_REL = 2e-2
 
 
 def check_selection_row(sel_gpu: np.ndarray, scores_ref: np.ndarray, own: int, n_sel: int,
@@ -64,3 +71,13 @@ def compare_output(out_gpu: torch.Tensor, out_ref: np.ndarray, where: str = ""):
 
 def bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def compare_grad(got_gpu: torch.Tensor, ref: np.ndarray, where: str = ""):
+    got = got_gpu.double().cpu().numpy()
+    scale = max(float(np.abs(ref).max()), 1e-300)
+    max_rel = float(np.abs(got - ref).max()) / scale if ref.size else 0.0
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    assert rel <= GRAD_REL_L2, f"{where}: rel-L2 {rel:.3e} > {GRAD_REL_L2}"
+    assert max_rel <= GRAD_MAX_REL, f"{where}: max-abs / max|ref| {max_rel:.3e} > {GRAD_MAX_REL}"
+    return max_rel, rel

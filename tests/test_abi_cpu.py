@@ -103,3 +103,29 @@ def test_workspace_queries_and_short_workspace(lib):
     # rows longer than one workgroup's 32768 candidates use a two-level selection:
     # 8 rows x 256 segments x 16 kept (value, id) pairs plus one boundary per segment
     assert lib.qsa_topk_workspace_bytes(8, 1, 262144, 2048, 4) >= 8 * 256 * (16 + 1) * 8
+
+
+def test_backward_validation_and_workspace(lib):
+    f = ctypes.c_float(0.0625)
+
+    def bwd(lq=10, lk=100, hq=24, hkv=2, d=256, r=4, n_sel=512, q=FAKE, k=FAKE, v=FAKE,
+            sel=FAKE, pos0=0, scale=f, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+            ws=FAKE, ws_bytes=1 << 40):
+        return lib.qsa_sparse_attn_bwd(lq, lk, hq, hkv, d, r, n_sel, q, k, v, sel, pos0, scale,
+                                       out, lse, dout, dq, dk, dv, ws, ws_bytes, None)
+
+    assert bwd(hkv=5) == 1                        # 24 % 5
+    assert bwd(d=192) == 2
+    assert bwd(r=3) == 2
+    assert bwd(n_sel=2048) == 2
+    assert bwd(pos0=95) == 1                      # rows past Lk
+    assert bwd(scale=ctypes.c_float(float("inf"))) == 1
+    assert bwd(lse=None) == 1 and "null" in _err(lib)
+    assert bwd(dout=None) == 1
+    assert bwd(dk=MISALIGNED) == 1 and "aligned" in _err(lib)
+    assert bwd(lq=1 << 22, lk=1 << 23, n_sel=1024) == 1  # lq * n_sel >= 2^31
+    n = lib.qsa_sparse_attn_bwd_workspace_bytes(10, 100, 24, 4, 512)
+    # D [lq][hq] fp32, four int32 arrays of lq * n_sel (block, row) pairs, 26 block starts
+    assert n >= 10 * 24 * 4 + 4 * 10 * 512 * 4 + 26 * 4
+    assert bwd(ws_bytes=n - 1) == 3 and "workspace" in _err(lib)
+    assert bwd(ws=MISALIGNED) == 3
