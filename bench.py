@@ -34,6 +34,8 @@ def parse_args():
     p.add_argument("--row-chunk", type=int, default=4096)
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip the sparse-attention backward measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -153,7 +155,54 @@ def bench_prefill(args, torch, Q, wl, inp):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     attn_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-    return wall, attn_ms
+    return wall, attn_ms, plan
+
+
+def backward_bytes(wl, t):
+    """Algorithmic bytes of one backward call over full selections at positions t.
+
+    Query side: the kept K and V rows (as the forward), q, dout and out per row, sel,
+    lse, dq and D. Key side: per (kept block, row) pair and KV group the row's q and
+    dout for the group's heads plus lse and D, the pair itself (block and row, 8 B,
+    written and read once), each key block's K and V, and dk, dv."""
+    import numpy as np
+    grp = wl.hq // wl.hkv
+    gathered = int(kept_tokens(t, wl.n_sel).sum()) * wl.hkv * 2 * wl.d * 2
+    per_row = wl.hq * wl.d * 2 * 3 + wl.n_sel * 4 + wl.hq * 4 * 2 + wl.hq * wl.d * 4
+    pairs = int(np.minimum(t // wl.r + 1, wl.n_sel).sum())
+    per_pair = wl.hkv * (2 * grp * wl.d * 2 + 2 * grp * 4) + 16
+    keys = wl.lk * wl.hkv * wl.d * (2 * 2 + 2 * 4)
+    return gathered + len(t) * per_row + pairs * per_pair + keys
+
+
+def bench_backward(torch, Q, wl, inp, plan, reps=2):
+    """Whole backward call (inverse selection, dq, dk/dv) on the forward's outputs."""
+    g = torch.Generator(device=inp["q"].device)
+    g.manual_seed(11)
+    dout = torch.randn(inp["q"].shape, generator=g, device=inp["q"].device).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(wl.d)
+    nbytes = Q.ops._lib.load().qsa_sparse_attn_bwd_workspace_bytes(wl.lq, wl.lk, wl.hq, wl.r,
+                                                                   wl.n_sel)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=inp["q"].device)
+
+    def run():
+        return Q.qsa_sparse_attn_bwd(inp["q"], inp["k"], inp["v"], plan.sel, plan.out, plan.lse,
+                                     dout, q_pos0=wl.q_pos0, scale=scale, workspace=ws)
+
+    grads = run()
+    del grads
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        grads = run()
+        b.record()
+        del grads
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+    del ws, dout
+    return ms
 
 
 def bench_decode(args, torch, Q, wl, inp):
@@ -252,7 +301,7 @@ def main():
     wl = workload(args.workload)
     inp = generate(wl, device=dev)
     torch.cuda.synchronize()
-    wall, attn_ms = bench_prefill(args, torch, Q, wl, inp)
+    wall, attn_ms, plan = bench_prefill(args, torch, Q, wl, inp)
     ms_step = wall / args.steps * 1e3
     t = wl.q_pos0 + np.arange(wl.lq, dtype=np.int64)
     a_bytes = attention_bytes(wl, t)
@@ -288,7 +337,17 @@ def main():
         "random_4KiB_blocks_GBs": ceil_rand, "random_buffer_MiB": kv_mib,
         "sequential_stream_GBs": ceil_seq, "sequential_buffer_MiB": 2048,
         "attention_frac_of_random_ceiling": achieved / ceil_rand}
-    del inp
+    if not args.no_backward:
+        b_ms = bench_backward(torch, Q, wl, inp, plan)
+        b_bytes = backward_bytes(wl, t)
+        b_gbs = b_bytes / (b_ms * 1e-3) / 1e9
+        line["backward"] = {
+            "workload": wl.name, "what": "dq, dk, dv of the sparse attention (fp32) from out, "
+            "lse and a random bf16 dout; inverse selection included",
+            "ms": b_ms, "tokens_per_s": wl.lq / (b_ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": b_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": b_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": b_bytes}}
+    del inp, plan
     torch.cuda.empty_cache()
     if not args.no_decode:
         dwl = workload("decode1m")

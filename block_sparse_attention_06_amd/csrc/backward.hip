@@ -253,19 +253,51 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_dkdv_kernel(BwdArgs a) {
   const float sl2 = a.scale_log2;
   const int32_t p0 = a.start[kb], p1 = a.start[kb + 1];
   const bool hv = c16 < G;  // A rows: head c16
-  for (int32_t p = p0; p < p1; ++p) {
-    const int64_t row = a.pair_rows[p];
-    const int64_t t = a.q_pos0 + row;
+
+  // Software pipeline over the rows: a row's q and dO of head c16 (A operands, k =
+  // dims 32c + 8*quad + [0..7]) with its lse and D of heads 4*quad + i are loaded one
+  // row ahead, into the registers the previous row's S and dP MFMAs have just read.
+  // They cover every line of the row's q and dO for the group, so the second layout
+  // (4 heads per lane, 8 dims each: the B operands of dV and dK), loaded after the
+  // MFMAs of S and dP, comes from cache.
+  uint4 Qa[NC], dOa[NC];
+  float L2[4], Dh[4];
+  int64_t row = 0;
+  auto load_first = [&](int32_t p) {
+    row = a.pair_rows[p];
     const int64_t hbase = (row * a.hq + g * G) * (int64_t)D;
-    // q and dO rows, head c16 (A operands, k = dims 32c + 8*quad + [0..7]).
-    uint4 Qa[NC], dOa[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int64_t off = hbase + (int64_t)(hv ? c16 : 0) * D + quad * 8 + c * 32;
       Qa[c] = hv ? ld16(a.q + off) : make_uint4(0, 0, 0, 0);
       dOa[c] = hv ? ld16(a.dout + off) : make_uint4(0, 0, 0, 0);
     }
-    // q and dO with 4 heads per lane (heads 4*quad + kk), 8 dims each (B operands).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * quad + i;
+      L2[i] = h < G ? a.lse[row * a.hq + g * G + h] * kLog2e : 0.f;
+      Dh[i] = h < G ? a.dbuf[row * a.hq + g * G + h] : 0.f;
+    }
+  };
+  if (p0 < p1) load_first(p0);
+  for (int32_t p = p0; p < p1; ++p) {
+    f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      S = mfma_16x16x32(Qa[c], Kb[c], S);
+      dP = mfma_16x16x32(dOa[c], Vb[c], dP);
+    }
+    const int64_t t = a.q_pos0 + row;
+    const int64_t hbase = (row * a.hq + g * G) * (int64_t)D;
+    float l2[4], dh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      l2[i] = L2[i];
+      dh[i] = Dh[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // The next row (past the list: the last row again, in bounds).
+    load_first(min(p + 1, p1 - 1));
     uint4 Qr[NH][4], dOr[NH][4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -278,28 +310,15 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_dkdv_kernel(BwdArgs a) {
         dOr[hf][kk] = ok ? ld16(a.dout + off + hf * 128) : make_uint4(0, 0, 0, 0);
       }
     }
-    float L2[4], Dh[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * quad + i;
-      L2[i] = h < G ? a.lse[row * a.hq + g * G + h] * kLog2e : 0.f;
-      Dh[i] = h < G ? a.dbuf[row * a.hq + g * G + h] : 0.f;
-    }
-
-    f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      S = mfma_16x16x32(Qa[c], Kb[c], S);
-      dP = mfma_16x16x32(dOa[c], Vb[c], dP);
-    }
+    __builtin_amdgcn_sched_barrier(0);
     // Row 4*quad+i is head 4*quad+i; column c16 is token kb*4 + c16.
     float pv[4], ds[4];
     const bool key_ok = c16 < 4 && kb * 4 + c16 <= t && kb * 4 + c16 < a.lk;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = key_ok && 4 * quad + i < G;
-      pv[i] = ok ? exp2f(S[i] * sl2 - L2[i]) : 0.f;
-      ds[i] = pv[i] * (dP[i] - Dh[i]);
+      pv[i] = ok ? exp2f(S[i] * sl2 - l2[i]) : 0.f;
+      ds[i] = pv[i] * (dP[i] - dh[i]);
     }
     const uint2 Ap = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
     const uint2 As = make_uint2(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]));
