@@ -1,5 +1,5 @@
-"""CPU oracle of the Qwen Sparse Attention (QSA) forward path and of the sparse
-attention's backward over a fixed selection.
+"""CPU oracle of the Qwen Sparse Attention (QSA) forward path, of the sparse
+attention's backward over a fixed selection, and of the indexer's KL warm-up loss.
 
 TEST INFRASTRUCTURE ONLY. This is the plain, slow, obviously correct fp64 numpy
 statement of what the path computes, used to check the HIP library. Only the test
@@ -235,6 +235,87 @@ def backward_prefill(q_bits, k_bits, v_bits, sel, dout, *, r: int, q_pos0: int =
         np.add.at(dk, toks, dkr)
         np.add.at(dv, toks, dvr)
     return {"dq": dq, "dk": dk, "dv": dv}
+
+
+# --------------------------------------------------------------------------------------
+# Indexer warm-up: KL distillation of the full attention onto the block scores  [DR]
+# --------------------------------------------------------------------------------------
+# [DR] trains the indexer in two stages, the first a warm-up that distils the full
+# attention distribution, max-pooled to the block level, into the indexer by a KL
+# loss. Readings: the heads' probabilities are summed (one indexer serves all heads),
+# the target lives on the blocks the indexer scores (complete blocks before the own
+# block, which is always kept) and is L1-normalised there; the indexer's distribution
+# is the softmax of its scores over the same blocks; the loss is KL(target || indexer)
+# summed over query rows; the target carries no gradient.
+
+
+def kl_block_target(q_t: np.ndarray, k_rows: np.ndarray, t: int, r: int, scale: float):
+    """Distillation target of the query at position t over blocks 0 .. t // r - 1.
+
+    q_t [Hq, d]; k_rows [t + 1, Hkv, d] holds keys 0..t (fp64). The full causal
+    attention probabilities of every head are summed, max-pooled over each block's r
+    tokens and normalised to sum to one. Empty when no block is scored.
+    """
+    own = t // r
+    if own == 0:
+        return np.zeros(0)
+    hq = q_t.shape[0]
+    grp = hq // k_rows.shape[1]
+    a = np.zeros(t + 1, dtype=np.float64)
+    for h in range(hq):
+        z = scale * (k_rows[:, h // grp, :] @ q_t[h])
+        e = np.exp(z - z.max())
+        a += e / e.sum()
+    pooled = a[: own * r].reshape(own, r).max(axis=1)
+    return pooled / pooled.sum()
+
+
+def indexer_kl(scores_row: np.ndarray, target: np.ndarray):
+    """KL(target || softmax(scores)) over one row's scored blocks, and its gradient with
+    respect to the scores, softmax(scores) - target. Returns (loss, ds)."""
+    if len(scores_row) == 0:
+        return 0.0, np.zeros(0)
+    m = scores_row.max()
+    lse = m + np.log(np.exp(scores_row - m).sum())
+    logq = scores_row - lse
+    nz = target > 0  # 0 * log 0 = 0
+    loss = float(np.sum(target[nz] * (np.log(target[nz]) - logq[nz])))
+    return loss, np.exp(logq) - target
+
+
+def index_scores_backward(q_idx: np.ndarray, w: np.ndarray, k_pooled: np.ndarray,
+                          ds: np.ndarray, positions: np.ndarray, r: int):
+    """Gradients of the block scores (index_scores) with respect to q_idx [n, H_I, d_I],
+    w [n, H_I] and k_pooled [nblk, d_I], given ds [n, nblk] = dL/ds (entries of blocks a
+    row does not score are ignored). With z = q_idx[i,h] . k_pooled[b]:
+      dw[i,h] = sum_b ds[i,b] max(0, z),  dz = ds[i,b] w[i,h] [z > 0],
+      dq_idx[i,h] = sum_b dz k_pooled[b],  dk_pooled[b] = sum_{i,h} dz q_idx[i,h].
+    The ReLU's derivative at 0 is taken as 0. Returns (dq_idx, dw, dk_pooled).
+    """
+    n, n_heads, _ = q_idx.shape
+    own = np.asarray(positions) // r
+    cols = np.arange(k_pooled.shape[0])
+    g = np.where(cols[None, :] < own[:, None], np.nan_to_num(ds), 0.0)
+    dq = np.zeros_like(q_idx, dtype=np.float64)
+    dw = np.zeros((n, n_heads), dtype=np.float64)
+    dkp = np.zeros_like(k_pooled, dtype=np.float64)
+    for h in range(n_heads):
+        z = q_idx[:, h, :] @ k_pooled.T
+        dw[:, h] = (g * np.maximum(z, 0.0)).sum(axis=1)
+        dz = g * w[:, h : h + 1] * (z > 0)
+        dq[:, h, :] = dz @ k_pooled
+        dkp += dz.T @ q_idx[:, h, :]
+    return dq, dw, dkp
+
+
+def pool_keys_backward(dk_pooled: np.ndarray, r: int, n_tokens: int) -> np.ndarray:
+    """Gradient of the mean pooling: each token of a complete block gets its block's
+    gradient / r (the bf16 rounding of the pooled key is passed straight through);
+    tokens of a trailing partial block get 0."""
+    out = np.zeros((n_tokens, dk_pooled.shape[1]), dtype=np.float64)
+    nb = min(dk_pooled.shape[0], n_tokens // r)
+    out[: nb * r] = np.repeat(dk_pooled[:nb] / r, r, axis=0)
+    return out
 
 
 # --------------------------------------------------------------------------------------

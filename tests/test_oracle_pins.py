@@ -439,3 +439,100 @@ def test_backward_closed_forms_and_invariants():
         for h in range(q.shape[1]):
             want[toks, h // grp] += dout[i, h] / len(toks)
     np.testing.assert_allclose(g["dv"], want, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------
+# Indexer warm-up: KL distillation target, loss and the indexer's gradients
+# ------------------------------------------------------------------------------------
+
+
+def test_kl_target_against_torch_softmax_and_max_pool():
+    # Library routines: torch softmax over the causal logits, summed over heads, then
+    # torch's max_pool1d over r-token windows, normalised.
+    rng = np.random.default_rng(50)
+    hq, hkv, d, r = 6, 2, 16, 4
+    k = O.bf16_to_f64(_bits(rng.standard_normal((40, hkv, d))))
+    for t in (3, 4, 17, 39):
+        q = O.bf16_to_f64(_bits(rng.standard_normal((hq, d))))
+        got = O.kl_block_target(q, k[: t + 1], t, r, 0.3)
+        kk = torch.from_numpy(k[: t + 1]).repeat_interleave(hq // hkv, dim=1)  # [t+1, hq, d]
+        z = 0.3 * torch.einsum("hd,jhd->hj", torch.from_numpy(q), kk)
+        a = torch.softmax(z, dim=1).sum(0)
+        own = t // r
+        if own == 0:
+            assert got.size == 0
+            continue
+        pooled = torch.nn.functional.max_pool1d(a[None, None, : own * r], r, r)[0, 0]
+        np.testing.assert_allclose(got, (pooled / pooled.sum()).numpy(), rtol=1e-12, atol=0)
+
+
+def test_kl_target_closed_forms():
+    rng = np.random.default_rng(51)
+    hq, hkv, d, r, t = 4, 1, 8, 4, 23
+    k = rng.standard_normal((t + 1, hkv, d))
+    # q = 0: uniform attention, so every complete block pools the same value.
+    np.testing.assert_allclose(O.kl_block_target(np.zeros((hq, d)), k, t, r, 1.0),
+                               np.full(t // r, 1.0 / (t // r)), rtol=1e-14)
+    # One key dominating every head: the target sits on its block.
+    q = np.zeros((hq, d))
+    q[:, 0] = 1.0
+    k2 = k.copy()
+    k2[:, :, 0] = 0.0
+    k2[9, :, 0] = 80.0
+    p = O.kl_block_target(q, k2, t, r, 1.0)
+    assert p.argmax() == 9 // r and p[9 // r] > 0.99
+
+
+def test_indexer_kl_against_torch_kl_div_and_autograd():
+    rng = np.random.default_rng(52)
+    s = rng.standard_normal(37) * 3
+    p = rng.random(37)
+    p[[3, 10]] = 0.0
+    p /= p.sum()
+    loss, ds = O.indexer_kl(s, p)
+    st = torch.from_numpy(s).requires_grad_()
+    ref = torch.nn.functional.kl_div(torch.log_softmax(st, 0), torch.from_numpy(p),
+                                     reduction="sum")
+    ref.backward()
+    ref_v = float(ref.detach())
+    assert abs(loss - ref_v) <= 1e-12 * max(1.0, abs(ref_v))
+    np.testing.assert_allclose(ds, st.grad.numpy(), rtol=1e-12, atol=1e-15)
+    # KL is zero exactly when the target is the indexer's own distribution.
+    q = np.exp(s - s.max())
+    q /= q.sum()
+    assert abs(O.indexer_kl(s, q)[0]) < 1e-13
+
+
+def test_index_scores_backward_central_differences():
+    # d/dx of sum(ds * s(x)) numerically, for q_idx, w and the pooled keys (inputs drawn
+    # so that no q.k sits within the step of the ReLU's kink).
+    rng = np.random.default_rng(53)
+    n, hh, di, nblk, r = 5, 3, 6, 7, 4
+    pos = np.array([4, 9, 17, 28, 31])
+    q = rng.standard_normal((n, hh, di))
+    w = rng.random((n, hh))
+    kp = rng.standard_normal((nblk, di))
+    ds = rng.standard_normal((n, nblk))
+    dq, dw, dkp = O.index_scores_backward(q, w, kp, ds, pos, r)
+
+    def f(q_, w_, kp_):
+        sc = O.index_scores(q_, w_, kp_, pos, r)
+        return float(np.nansum(sc * ds))
+
+    eps = 1e-6
+    for name, arr, grad in (("q", q, dq), ("w", w, dw), ("kp", kp, dkp)):
+        for idx in np.ndindex(arr.shape):
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            args = {"q": q, "w": w, "kp": kp}
+            args[name] = plus
+            fp = f(args["q"], args["w"], args["kp"])
+            args[name] = minus
+            fm = f(args["q"], args["w"], args["kp"])
+            num = (fp - fm) / (2 * eps)
+            assert abs(num - grad[idx]) <= 1e-7 * max(1.0, abs(num)), (name, idx, num, grad[idx])
+    # The pooling's gradient spreads each block's gradient over its r tokens / r.
+    g = O.pool_keys_backward(dkp, r, nblk * r + 2)
+    np.testing.assert_allclose(g[: nblk * r].reshape(nblk, r, di).sum(1), dkp, rtol=1e-14)
+    assert np.all(g[nblk * r:] == 0)
