@@ -1,4 +1,5 @@
-"""MI355X-native Qwen Sparse Attention (QSA) forward path and sparse-attention backward.
+"""MI355X-native Qwen Sparse Attention (QSA): forward path, sparse-attention backward and
+the indexer's KL warm-up.
 
 The computation lives in libqsa.so (hand-written HIP kernels for gfx950 behind the C
 ABI of include/qsa.h); this package only builds it and marshals torch tensors to it.
@@ -10,6 +11,9 @@ from .ops import (  # noqa: F401
     abi_version,
     qsa_decode_forward,
     qsa_index_scores,
+    qsa_index_scores_bwd,
+    qsa_indexer_kl_loss,
+    qsa_indexer_kl_target,
     qsa_pool_keys,
     qsa_prefill_forward,
     qsa_prefill_select,

@@ -29,6 +29,10 @@ SIGNATURES = {
     "qsa_sparse_attn_bwd_workspace_bytes": (_Z, [_L, _L, _I, _I, _I]),
     "qsa_sparse_attn_bwd": (_I, [_L, _L, _I, _I, _I, _I, _I, _P, _P, _P, _P, _L, _F, _P, _P, _P,
                                  _P, _P, _P, _P, _Z, _P]),
+    "qsa_indexer_kl_target": (_I, [_L, _L, _I, _I, _I, _I, _P, _P, _L, _F, _P, _P, _L, _P]),
+    "qsa_indexer_kl_loss": (_I, [_L, _L, _I, _L, _P, _P, _L, _P, _P, _P]),
+    "qsa_index_scores_bwd": (_I, [_L, _I, _I, _I, _P, _P, _P, _L, _L, _P, _L, _P, _P, _P, _P,
+                                  _L, _P]),
     "qsa_sparse_attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "qsa_sparse_attn_decode": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _L, _L, _P, _P, _F, _P,
                                     _P, _P, _Z, _P]),

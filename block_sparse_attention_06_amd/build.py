@@ -13,8 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libqsa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "backward.hip", "probe.hip",
-           "qsa_abi.hip"]
+SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "backward.hip", "warmup.hip",
+           "probe.hip", "qsa_abi.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code (the hipcc host pass warns
 # that it does not know the feature; that warning is harmless).

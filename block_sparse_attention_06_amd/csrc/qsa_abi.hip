@@ -304,6 +304,77 @@ qsa_status qsa_sparse_attn_bwd(int64_t lq, int64_t lk, int hq, int hkv, int d, i
                     "qsa_sparse_attn_bwd launch (or sort scratch larger than reserved)");
 }
 
+// ---- indexer warm-up ----
+
+qsa_status qsa_indexer_kl_target(int64_t lq, int64_t lk, int hq, int hkv, int d, int r,
+                                 const void* q, const void* k, int64_t q_pos0,
+                                 float softmax_scale, float* lse, float* target, int64_t ld,
+                                 void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_REQUIRE(lq >= 0 && lq < ((int64_t)1 << 31) && lk >= 1, QSA_ERR_INVALID_ARGUMENT,
+              "lq=%lld lk=%lld", (long long)lq, (long long)lk);
+  QSA_REQUIRE(q_pos0 >= 0 && q_pos0 + lq <= lk, QSA_ERR_INVALID_ARGUMENT,
+              "query positions [%lld, %lld) must lie inside the %lld keys", (long long)q_pos0,
+              (long long)(q_pos0 + lq), (long long)lk);
+  QSA_REQUIRE(isfinite(softmax_scale), QSA_ERR_INVALID_ARGUMENT, "softmax_scale not finite");
+  const int64_t nblk = lk / r;
+  QSA_REQUIRE(ld >= nblk && ld % 4 == 0, QSA_ERR_INVALID_ARGUMENT,
+              "ld=%lld: needs ld >= lk / r = %lld and ld %% 4 == 0", (long long)ld,
+              (long long)nblk);
+  if (lq == 0) return QSA_OK;
+  QSA_REQUIRE(q && k && lse && target, QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  QSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(target), QSA_ERR_INVALID_ARGUMENT,
+              "q, k and target must be 16-byte aligned");
+  qsa::KlArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse, target,
+                lq, lk, q_pos0, nblk, ld, hq, hkv, d, r,
+                softmax_scale * 1.4426950408889634f};
+  return hip_status(qsa::launch_kl_target(a, static_cast<hipStream_t>(stream)),
+                    "qsa_indexer_kl_target launch");
+}
+
+qsa_status qsa_indexer_kl_loss(int64_t lq, int64_t nblk, int r, int64_t q_pos0,
+                               const float* scores, const float* target, int64_t ld,
+                               float* loss, float* dscores, void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_REQUIRE(lq >= 0 && lq < ((int64_t)1 << 31) && nblk >= 0 && q_pos0 >= 0,
+              QSA_ERR_INVALID_ARGUMENT, "lq=%lld nblk=%lld q_pos0=%lld", (long long)lq,
+              (long long)nblk, (long long)q_pos0);
+  QSA_REQUIRE(ld >= nblk && ld % 4 == 0, QSA_ERR_INVALID_ARGUMENT, "ld=%lld", (long long)ld);
+  if (lq == 0) return QSA_OK;
+  QSA_REQUIRE(scores && target && loss && dscores, QSA_ERR_INVALID_ARGUMENT,
+              "null tensor pointer");
+  qsa::KlLossArgs a{scores, target, loss, dscores, lq, q_pos0, nblk, ld, r};
+  return hip_status(qsa::launch_kl_loss(a, static_cast<hipStream_t>(stream)),
+                    "qsa_indexer_kl_loss launch");
+}
+
+qsa_status qsa_index_scores_bwd(int64_t lq, int h_idx, int d_idx, int r, const void* q_idx,
+                                const float* w, const void* k_pooled, int64_t nblk,
+                                int64_t q_pos0, const float* dscores, int64_t ld,
+                                float* dq_idx, float* dw, float* dk_pooled, float* dk_idx,
+                                int64_t n_tokens, void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_TRY(check_indexer_shape(h_idx, d_idx));
+  QSA_REQUIRE(lq >= 0 && lq < ((int64_t)1 << 31) && nblk >= 0 && nblk < ((int64_t)1 << 31) &&
+                  q_pos0 >= 0,
+              QSA_ERR_INVALID_ARGUMENT, "lq=%lld nblk=%lld q_pos0=%lld", (long long)lq,
+              (long long)nblk, (long long)q_pos0);
+  QSA_REQUIRE(ld >= nblk && ld % 4 == 0, QSA_ERR_INVALID_ARGUMENT, "ld=%lld", (long long)ld);
+  QSA_REQUIRE(!dk_idx || (n_tokens >= 0 && n_tokens < ((int64_t)1 << 40)),
+              QSA_ERR_INVALID_ARGUMENT, "n_tokens=%lld", (long long)n_tokens);
+  QSA_REQUIRE(q_idx && w && dscores && dq_idx && dw && (nblk == 0 || (k_pooled && dk_pooled)),
+              QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  QSA_REQUIRE(aligned16(q_idx) && aligned16(dscores) && aligned16(dq_idx) &&
+                  (nblk == 0 || (aligned16(k_pooled) && aligned16(dk_pooled))),
+              QSA_ERR_INVALID_ARGUMENT, "q_idx, k_pooled, dscores and outputs must be 16-byte aligned");
+  qsa::IdxBwdArgs a{static_cast<const uint16_t*>(q_idx), w,
+                    static_cast<const uint16_t*>(k_pooled), dscores, dq_idx, dw, dk_pooled,
+                    dk_idx, lq, q_pos0, nblk, ld, dk_idx ? n_tokens : 0, h_idx, d_idx, r};
+  return hip_status(qsa::launch_index_scores_bwd(a, static_cast<hipStream_t>(stream)),
+                    "qsa_index_scores_bwd launch");
+}
+
 size_t qsa_sparse_attn_decode_workspace_bytes(int batch, int hq, int d, int n_sel) {
   if (batch <= 0 || hq <= 0 || d <= 0 || n_sel <= 0) return 0;
   const size_t ns = (size_t)qsa::decode_num_splits(n_sel);

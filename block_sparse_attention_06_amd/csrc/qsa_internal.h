@@ -133,6 +133,56 @@ BwdLayout bwd_layout(int64_t lq, int64_t lk, int hq, int n_sel, int r);
 hipError_t launch_sparse_attn_bwd(BwdArgs a, char* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 
+// ---- indexer warm-up (KL distillation) ----
+struct KlArgs {
+  const uint16_t* q;  // [lq][hq][d]
+  const uint16_t* k;  // [lk][hkv][d]
+  float* lse;         // [lq][hq], dense causal
+  float* target;      // [lq][ld], unnormalised pooled probabilities of the scored blocks
+  int64_t lq;
+  int64_t lk;
+  int64_t q_pos0;
+  int64_t nblk;
+  int64_t ld;
+  int hq;
+  int hkv;
+  int d;
+  int r;
+  float scale_log2;
+};
+struct KlLossArgs {
+  const float* scores;  // [lq][ld]
+  const float* target;  // [lq][ld]
+  float* loss;          // [lq]
+  float* dscores;       // [lq][ld]
+  int64_t lq;
+  int64_t q_pos0;
+  int64_t nblk;
+  int64_t ld;
+  int r;
+};
+struct IdxBwdArgs {
+  const uint16_t* q_idx;  // [lq][h_idx][d_idx]
+  const float* w;         // [lq][h_idx]
+  const uint16_t* kp;     // [nblk][d_idx]
+  const float* dscores;   // [lq][ld]
+  float* dq_idx;          // [lq][h_idx][d_idx]
+  float* dw;              // [lq][h_idx]
+  float* dk_pooled;       // [nblk][d_idx]
+  float* dk_idx;          // [n_tokens][d_idx] or null
+  int64_t lq;
+  int64_t q_pos0;
+  int64_t nblk;
+  int64_t ld;
+  int64_t n_tokens;
+  int h_idx;
+  int d_idx;
+  int r;
+};
+hipError_t launch_kl_target(const KlArgs& a, hipStream_t stream);
+hipError_t launch_kl_loss(const KlLossArgs& a, hipStream_t stream);
+hipError_t launch_index_scores_bwd(const IdxBwdArgs& a, hipStream_t stream);
+
 // ---- measurement aid ----
 hipError_t launch_probe_gather(const void* buf, const int32_t* ids, int steps, int64_t n_waves,
                                uint32_t* sink, hipStream_t stream);

@@ -183,6 +183,61 @@ def qsa_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: 
     return dq, dk, dv
 
 
+def qsa_indexer_kl_target(q: torch.Tensor, k: torch.Tensor, *, q_pos0: int = 0,
+                          scale: Optional[float] = None, r: int = 4):
+    """Dense attention statistics for the indexer warm-up: (lse [Lq,Hq], target [Lq, ld])
+    with target the unnormalised block max of the head-summed probabilities."""
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, q.device)
+    lq, hq, d = q.shape
+    lk, hkv, _ = k.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    ld = score_ld(lk // r)
+    lse = torch.empty((lq, hq), dtype=torch.float32, device=q.device)
+    target = torch.empty((lq, ld), dtype=torch.float32, device=q.device)
+    _call("qsa_indexer_kl_target", lq, lk, hq, hkv, d, r, _ptr(q), _ptr(k), q_pos0, scale,
+          _ptr(lse), _ptr(target), ld, _stream(q))
+    return lse, target
+
+
+def qsa_indexer_kl_loss(scores: torch.Tensor, target: torch.Tensor, *, nblk: int,
+                        q_pos0: int = 0, r: int = 4):
+    """KL(target || softmax(scores)) per row over its scored blocks, and dL/dscores."""
+    _need(scores, "scores", torch.float32)
+    _need(target, "target", torch.float32, scores.device)
+    lq, ld = scores.shape
+    if target.shape != scores.shape:
+        raise ValueError("scores and target must have the same shape")
+    loss = torch.empty(lq, dtype=torch.float32, device=scores.device)
+    dscores = torch.empty_like(scores)
+    _call("qsa_indexer_kl_loss", lq, nblk, r, q_pos0, _ptr(scores), _ptr(target), ld,
+          _ptr(loss), _ptr(dscores), _stream(scores))
+    return loss, dscores
+
+
+def qsa_index_scores_bwd(q_idx: torch.Tensor, w: torch.Tensor, k_pooled: torch.Tensor,
+                         dscores: torch.Tensor, *, q_pos0: int = 0, r: int = 4,
+                         nblk: Optional[int] = None, n_tokens: Optional[int] = None):
+    """Gradients of the block scores: (dq_idx, dw, dk_pooled[, dk_idx]) in fp32.
+    q_idx [Lq,H,dI], w [Lq,H], k_pooled [nblk,dI], dscores [Lq, ld]. With n_tokens, also
+    the raw indexer keys' gradient [n_tokens, dI] through the mean pooling."""
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(w, "w", torch.float32, q_idx.device)
+    _need(k_pooled, "k_pooled", torch.bfloat16, q_idx.device)
+    _need(dscores, "dscores", torch.float32, q_idx.device)
+    lq, h, di = q_idx.shape
+    nblk = k_pooled.shape[0] if nblk is None else nblk
+    dq = torch.empty((lq, h, di), dtype=torch.float32, device=q_idx.device)
+    dw = torch.empty((lq, h), dtype=torch.float32, device=q_idx.device)
+    dkp = torch.empty((max(nblk, 1), di), dtype=torch.float32, device=q_idx.device)
+    dki = None if n_tokens is None else torch.empty((n_tokens, di), dtype=torch.float32,
+                                                    device=q_idx.device)
+    _call("qsa_index_scores_bwd", lq, h, di, r, _ptr(q_idx), _ptr(w), _ptr(k_pooled), nblk,
+          q_pos0, _ptr(dscores), dscores.shape[1], _ptr(dq), _ptr(dw), _ptr(dkp), _ptr(dki),
+          0 if n_tokens is None else n_tokens, _stream(q_idx))
+    return (dq, dw, dkp[:nblk]) if dki is None else (dq, dw, dkp[:nblk], dki)
+
+
 def qsa_sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            seq_lens: torch.Tensor, sel: torch.Tensor, *,
                            scale: Optional[float] = None, r: int = 4):

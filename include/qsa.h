@@ -164,6 +164,48 @@ qsa_status qsa_sparse_attn_bwd(int64_t lq, int64_t lk, int hq, int hkv, int d, i
                                size_t workspace_bytes, void* stream);
 
 /*
+ * Indexer warm-up -- KL distillation of the full attention onto the block scores
+ * ([DR]: before sparse training the indexer is warmed up by distilling the full
+ * attention distribution, max-pooled to blocks, into it with a KL loss). Readings:
+ * the heads' probabilities are summed; the target lives on the blocks the indexer
+ * scores for row i (b < B_i = min(t_i / r, lk / r), t_i = q_pos0 + i) and is
+ * normalised there; the indexer's distribution is softmax(s[i][b]) over the same
+ * blocks; the loss of row i is KL(target || indexer); the target is a constant.
+ *
+ * qsa_indexer_kl_target: dense causal attention statistics of the main heads.
+ *   lse[i][h] = ln sum_{j <= t_i} exp(scale q[i][h] . k[j][g]), fp32 [lq][hq];
+ *   target[i][b] = max_{j in block b} sum_h exp(scale q[i][h] . k[j][g] - lse[i][h])
+ *   for b < B_i (unnormalised), fp32 [lq][ld] (ld >= lk / r, ld % 4 == 0; entries
+ *   b >= B_i are not written). q, k as for qsa_sparse_attn_fwd.
+ * qsa_indexer_kl_loss: from the indexer scores s [lq][ld] (stage 2) and target,
+ *   loss[i] = KL(p_i || softmax(s_i)) with p_i = target_i / sum_b target_i[b] (0 when
+ *   B_i = 0), fp32 [lq]; dscores[i][b] = softmax(s_i)[b] - p_i[b] for b < B_i,
+ *   fp32 [lq][ld] (the rest not written). Sums in fp64. nblk = lk / r.
+ * qsa_index_scores_bwd: gradients of the stage-2 scores with respect to the
+ *   indexer's inputs given dscores (entries b >= B_i are ignored). With
+ *   z = q_idx[i][h] . k_pooled[b]: dw[i][h] = sum_b dscores[i][b] max(0, z);
+ *   dz = dscores[i][b] w[i][h] [z > 0] (bf16 in the MFMA products);
+ *   dq_idx[i][h] = sum_b dz k_pooled[b]; dk_pooled[b] = sum_{i,h} dz q_idx[i][h]; all
+ *   fp32, q_idx/w/k_pooled laid out as for qsa_index_scores (unbatched). dk_idx, if
+ *   not NULL, receives the raw indexer keys' gradient through the mean pooling,
+ *   fp32 [n_tokens][d_idx]: dk_pooled[j / r] / r for tokens of complete blocks, 0
+ *   for the rest (the pooled key's bf16 rounding is passed straight through). The
+ *   ReLU's derivative at 0 is 0. Every sum has a fixed order (no atomics).
+ */
+qsa_status qsa_indexer_kl_target(int64_t lq, int64_t lk, int hq, int hkv, int d, int r,
+                                 const void* q, const void* k, int64_t q_pos0,
+                                 float softmax_scale, float* lse, float* target, int64_t ld,
+                                 void* stream);
+qsa_status qsa_indexer_kl_loss(int64_t lq, int64_t nblk, int r, int64_t q_pos0,
+                               const float* scores, const float* target, int64_t ld,
+                               float* loss, float* dscores, void* stream);
+qsa_status qsa_index_scores_bwd(int64_t lq, int h_idx, int d_idx, int r, const void* q_idx,
+                                const float* w, const void* k_pooled, int64_t nblk,
+                                int64_t q_pos0, const float* dscores, int64_t ld,
+                                float* dq_idx, float* dw, float* dk_pooled, float* dk_idx,
+                                int64_t n_tokens, void* stream);
+
+/*
  * Stage 4' -- decode: one new query token per sequence at t = seq_lens[s] - 1, the
  * same attention as stage 4 over a KV cache, split over the kept blocks into
  * partial softmax states that a second kernel combines.

@@ -129,3 +129,33 @@ def test_backward_validation_and_workspace(lib):
     assert n >= 10 * 24 * 4 + 4 * 10 * 512 * 4 + 26 * 4
     assert bwd(ws_bytes=n - 1) == 3 and "workspace" in _err(lib)
     assert bwd(ws=MISALIGNED) == 3
+
+
+def test_warmup_validation(lib):
+    f = ctypes.c_float(0.0625)
+    # target: heads per group, head dim, positions, ld
+    assert lib.qsa_indexer_kl_target(10, 100, 24, 5, 256, 4, FAKE, FAKE, 0, f, FAKE, FAKE, 28,
+                                     None) == 1
+    assert lib.qsa_indexer_kl_target(10, 100, 24, 2, 192, 4, FAKE, FAKE, 0, f, FAKE, FAKE, 28,
+                                     None) == 2
+    assert lib.qsa_indexer_kl_target(10, 100, 24, 2, 256, 4, FAKE, FAKE, 95, f, FAKE, FAKE, 28,
+                                     None) == 1
+    assert lib.qsa_indexer_kl_target(10, 100, 24, 2, 256, 4, FAKE, FAKE, 0, f, FAKE, FAKE, 24,
+                                     None) == 1 and "ld" in _err(lib)  # ld < lk / r
+    assert lib.qsa_indexer_kl_target(10, 100, 24, 2, 256, 4, FAKE, FAKE, 0, f, None, FAKE, 28,
+                                     None) == 1
+    assert lib.qsa_indexer_kl_target(0, 100, 24, 2, 256, 4, None, None, 0, f, None, None, 28,
+                                     None) == 0  # nothing to do
+    # loss: ld, null pointers
+    assert lib.qsa_indexer_kl_loss(10, 25, 4, 0, FAKE, FAKE, 26, FAKE, FAKE, None) == 1
+    assert lib.qsa_indexer_kl_loss(10, 25, 4, 0, FAKE, None, 28, FAKE, FAKE, None) == 1
+    assert lib.qsa_indexer_kl_loss(10, 25, 3, 0, FAKE, FAKE, 28, FAKE, FAKE, None) == 2
+    # indexer backward: heads, dims, alignment
+    assert lib.qsa_index_scores_bwd(10, 5, 128, 4, FAKE, FAKE, FAKE, 25, 0, FAKE, 28, FAKE,
+                                    FAKE, FAKE, None, 0, None) == 2
+    assert lib.qsa_index_scores_bwd(10, 4, 96, 4, FAKE, FAKE, FAKE, 25, 0, FAKE, 28, FAKE,
+                                    FAKE, FAKE, None, 0, None) == 2
+    assert lib.qsa_index_scores_bwd(10, 4, 128, 4, FAKE, FAKE, FAKE, 25, 0, MISALIGNED, 28,
+                                    FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert lib.qsa_index_scores_bwd(10, 4, 128, 4, FAKE, FAKE, FAKE, 25, 0, FAKE, 22, FAKE,
+                                    FAKE, FAKE, None, 0, None) == 1  # ld < nblk
