@@ -36,6 +36,8 @@ def parse_args():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-backward", action="store_true",
                    help="skip the sparse-attention backward measurement")
+    p.add_argument("--no-warmup", action="store_true",
+                   help="skip the indexer KL warm-up measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -222,6 +224,51 @@ def bench_decode(args, torch, Q, wl, inp):
     return (time.perf_counter() - t0) / args.decode_steps
 
 
+def bench_warmup(torch, Q, name="prefill32k", reps=2):
+    """The indexer's KL warm-up on one workload: dense target (lse pass + pooled pass),
+    indexer scores, KL loss with its score gradient, and the indexer's backward."""
+    import numpy as np
+    from synth import generate, workload
+    wl = workload(name)
+    inp = generate(wl, device="cuda")
+    kp = Q.qsa_pool_keys(inp["k_idx"])
+    scale = 1.0 / math.sqrt(wl.d)
+    nblk = wl.lk // wl.r
+    ev = {k: [] for k in ("target", "scores", "loss", "indexer_bwd")}
+    for rep in range(reps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        e[0].record()
+        lse, target = Q.qsa_indexer_kl_target(inp["q"], inp["k"], q_pos0=wl.q_pos0, scale=scale)
+        e[1].record()
+        scores = Q.qsa_index_scores(inp["q_idx"], inp["w"], kp, q_pos0=wl.q_pos0)
+        e[2].record()
+        loss, ds = Q.qsa_indexer_kl_loss(scores, target, nblk=nblk, q_pos0=wl.q_pos0)
+        e[3].record()
+        grads = Q.qsa_index_scores_bwd(inp["q_idx"], inp["w"], kp, ds, q_pos0=wl.q_pos0,
+                                       n_tokens=wl.lk)
+        e[4].record()
+        torch.cuda.synchronize()
+        if rep:
+            for i, k in enumerate(ev):
+                ev[k].append(e[i].elapsed_time(e[i + 1]))
+        del lse, target, scores, loss, ds, grads
+    ms = {k: sum(v) / len(v) for k, v in ev.items()}
+    t = wl.q_pos0 + np.arange(wl.lq, dtype=np.int64)
+    # dense passes: S = q.k over all causal keys, once for the lse and once for the
+    # target (2 flop per multiply-add, every head)
+    dense_flops = 2 * int((t + 1).sum()) * wl.hq * wl.d * 2
+    tflops = dense_flops / (ms["target"] * 1e-3) / 1e12
+    own = np.minimum(t // wl.r, nblk)
+    idx_flops = 3 * int(own.sum()) * 2 * wl.h_i * wl.d_i  # z twice recomputed + dq + dkbar
+    del inp, kp
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "ms": ms, "total_ms": sum(ms.values()),
+            "target_roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0,
+                                "unit": "TFLOP/s", "frac": tflops / 2500.0,
+                                "flops_per_call": dense_flops},
+            "indexer_bwd_tflops": idx_flops / (ms["indexer_bwd"] * 1e-3) / 1e12}
+
+
 def cpu_baseline(wl, inp, budget_s):
     """The oracle, as it stands, on evenly spread query rows of the same workload."""
     import numpy as np
@@ -349,6 +396,8 @@ def main():
                          "frac": b_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": b_bytes}}
     del inp, plan
     torch.cuda.empty_cache()
+    if not args.no_warmup:
+        line["indexer_warmup"] = bench_warmup(torch, Q)
     if not args.no_decode:
         dwl = workload("decode1m")
         dinp = generate(dwl, device=dev)
