@@ -70,16 +70,22 @@ def attention_source_hash():
     return h.hexdigest()[:16]
 
 
+def progress(msg):
+    """One line on stderr per finished phase (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def counted_traffic():
-    """HBM bytes per attention launch from the committed counter summary, or None when
-    the summary is missing or was taken on a different attention kernel source."""
+    """HBM bytes of one attention call over all rows (all its launches) from the
+    committed counter summary, or None when the summary is missing or was taken on a
+    different attention kernel source."""
     import re
     try:
         with open(COUNTERS) as f:
             text = f.read()
     except OSError:
         return None
-    m = re.search(r"traffic_bytes_per_launch=(\d+) kernel_source=([0-9a-f]+)", text)
+    m = re.search(r"traffic_bytes_per_call=(\d+) kernel_source=([0-9a-f]+)", text)
     if not m or m.group(2) != attention_source_hash():
         return None
     return int(m.group(1))
@@ -348,11 +354,17 @@ def main():
     wl = workload(args.workload)
     inp = generate(wl, device=dev)
     torch.cuda.synchronize()
+    progress(f"inputs of {wl.name} resident")
     wall, attn_ms, plan = bench_prefill(args, torch, Q, wl, inp)
+    progress(f"prefill: {wall / args.steps * 1e3:.2f} ms per step, attention {attn_ms:.2f} ms")
     ms_step = wall / args.steps * 1e3
     t = wl.q_pos0 + np.arange(wl.lq, dtype=np.int64)
     a_bytes = attention_bytes(wl, t)
     achieved = a_bytes / (attn_ms * 1e-3) / 1e9
+    rows_pl = Q.qsa_sparse_attn_fwd_rows_per_launch(wl.hkv, wl.d)
+    rows_pl = rows_pl if rows_pl > 0 else wl.lq
+    n_launch = -(-wl.lq // rows_pl)
+    traffic = counted_traffic()
     line = {
         "metric": METRIC,
         "value": wl.lq * args.steps / wall,
@@ -372,14 +384,22 @@ def main():
                    "row_chunk": args.row_chunk, "global_batch": 1, "parallelism": "single GPU"},
         "roofline": {"kernel": "sparse_attn_kernel (kept-token gather + MFMA)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(),
-                     "algorithmic_bytes_per_launch": a_bytes, "avg_launch_ms": attn_ms},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "hbm_frac_from_traffic": (traffic / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+                                               if traffic else None),
+                     "per": f"one qsa_sparse_attn_fwd call over all {wl.lq} rows = "
+                            f"{n_launch} launches of {rows_pl} rows",
+                     "launches_per_call": n_launch,
+                     "algorithmic_bytes_per_call": a_bytes, "avg_call_ms": attn_ms,
+                     "algorithmic_bytes_per_launch": a_bytes / n_launch,
+                     "avg_launch_ms": attn_ms / n_launch},
         "stages_ms": {"select (pool + scores + top-k)": ms_step - attn_ms, "attention": attn_ms},
         "score_gemm_flops_per_step": score_flops(wl, t),
     }
     kv_mib = (2 * wl.lk * wl.hkv * wl.d * 2) >> 20
     ceil_rand = gather_ceiling(torch, Q, dev, kv_mib, sequential=False)
     ceil_seq = gather_ceiling(torch, Q, dev, 2048, sequential=True)
+    progress(f"gather ceiling: {ceil_rand:.0f} GB/s random, {ceil_seq:.0f} GB/s sequential")
     line["gather_ceiling"] = {
         "random_4KiB_blocks_GBs": ceil_rand, "random_buffer_MiB": kv_mib,
         "sequential_stream_GBs": ceil_seq, "sequential_buffer_MiB": 2048,
@@ -388,6 +408,7 @@ def main():
         b_ms = bench_backward(torch, Q, wl, inp, plan)
         b_bytes = backward_bytes(wl, t)
         b_gbs = b_bytes / (b_ms * 1e-3) / 1e9
+        progress(f"backward: {b_ms:.1f} ms")
         line["backward"] = {
             "workload": wl.name, "what": "dq, dk, dv of the sparse attention (fp32) from out, "
             "lse and a random bf16 dout; inverse selection included",
@@ -398,11 +419,13 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_warmup:
         line["indexer_warmup"] = bench_warmup(torch, Q)
+        progress("indexer warm-up done")
     if not args.no_decode:
         dwl = workload("decode1m")
         dinp = generate(dwl, device=dev)
         torch.cuda.synchronize()
         s_dec = bench_decode(args, torch, Q, dwl, dinp)
+        progress(f"decode: {s_dec * 1e6:.1f} us per step")
         own = (dwl.lk - 1) // dwl.r
         d_bytes = dwl.batch * (own * dwl.d_i * 2 + dwl.budget * dwl.hkv * 2 * dwl.d * 2 +
                                dwl.hq * dwl.d * 2 * 2)
@@ -418,6 +441,7 @@ def main():
     if not args.no_cpu_baseline:
         inp = generate(wl, device=dev)
         line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        progress("cpu baseline done")
     print(json.dumps(line), flush=True)
 
 

@@ -21,6 +21,7 @@ from .ops import (  # noqa: F401
     qsa_sparse_attn_bwd,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_fwd,
+    qsa_sparse_attn_fwd_rows_per_launch,
     qsa_topk_blocks,
     score_ld,
 )

@@ -9,9 +9,11 @@
 //
 // Work decomposition: one wave per (query token, KV group). The wave keeps the
 // group's <= 16 query heads in registers and walks the row's kept blocks 4 at a
-// time (16 keys); the kept blocks of neighbouring queries are unrelated, so each
-// wave gathers its own K/V straight from global memory into MFMA operands -- no
-// LDS round trip and no cross-wave synchronisation.
+// time (16 keys); the kept blocks of neighbouring queries differ, so each wave
+// gathers its own K/V straight from global memory into MFMA operands -- no LDS round
+// trip and no cross-wave synchronisation. Blocks that many rows keep are shared
+// through L2 instead: the launcher starts the rows one resident generation at a
+// time, so that rows in flight walk their ascending block lists in step.
 //
 //   S^T[16 keys x 16 heads] = K[16 x d] . Q^T        8 x v_mfma_f32_16x16x32_bf16
 //     lane l: key row (l%16) -> 16 B of that key; output: head (l%16), keys 4*(l/16)+i
@@ -26,6 +28,10 @@
 // the 4 lanes that hold the head's keys, per-lane partial sums reduced at the end.
 // Decode splits each sequence's kept blocks over waves, merges the four waves of a
 // workgroup in LDS and writes (m, l, o) partials that a second kernel combines.
+
+#include <mutex>
+#include <tuple>
+#include <vector>
 
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -368,14 +374,73 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   if (a.lse && tid == 0) a.lse[bh] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
 }
 
+namespace {
+
+// Workgroups of `kernel` (block_threads threads, no dynamic LDS) that the current
+// device holds at once: compute units x workgroups per unit, cached per kernel and
+// device; 0 when the runtime cannot say.
+int resident_workgroups(const void* kernel, int block_threads) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static std::mutex mu;
+  static std::vector<std::tuple<const void*, int, int>> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : cache)
+    if (std::get<0>(e) == kernel && std::get<1>(e) == dev) return std::get<2>(e);
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) !=
+          hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  cache.emplace_back(kernel, dev, cus * per_cu);
+  return cus * per_cu;
+}
+
+const void* sparse_attn_fn(int d) {
+  return d == 256 ? reinterpret_cast<const void*>(&sparse_attn_kernel<256>)
+                  : reinterpret_cast<const void*>(&sparse_attn_kernel<128>);
+}
+
+}  // namespace
+
+// One resident generation of 256-thread workgroups, each taking 4 (row, KV group)
+// waves; -1 when the occupancy is unknown.
+int64_t sparse_attn_fwd_rows_per_launch(int hkv, int d) {
+  const int64_t gen = resident_workgroups(sparse_attn_fn(d), 256);
+  if (gen <= 0) return -1;
+  const int64_t rows = (gen * 4 + hkv - 1) / hkv;
+  return rows > 0 ? rows : 1;
+}
+
+// The rows are launched one generation at a time: as many workgroups as the device
+// holds at once. Rows that start together walk their ascending kept-block lists at
+// the same pace, so a block that several of them kept is read by all of them within
+// a short time and comes from L2 after the first read. In one grid over all rows the
+// resident workgroups drift apart as they finish at different times, and such
+// blocks come from beyond L2 again. At 128K tokens (24/2 heads, d=256, K=2048) on
+// MI355X: one grid 66.8 ms, L2 hit rate 10 %; generations of 512 workgroups
+// 44.1 ms, L2 hit rate 53 %, half the bytes fetched. Each row's sums run in the
+// same order either way, so the outputs are identical.
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream) {
   if (a.lq <= 0) return hipSuccess;
-  const int64_t items = a.lq * a.hkv;
-  const dim3 grid((unsigned)((items + 3) / 4));
-  if (a.d == 256)
-    hipLaunchKernelGGL(sparse_attn_kernel<256>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(sparse_attn_kernel<128>, grid, dim3(256), 0, stream, a);
+  int64_t rows = sparse_attn_fwd_rows_per_launch(a.hkv, a.d);
+  if (rows <= 0) rows = a.lq;
+  for (int64_t c0 = 0; c0 < a.lq; c0 += rows) {
+    AttnArgs c = a;
+    c.lq = a.lq - c0 < rows ? a.lq - c0 : rows;
+    c.q_pos0 = a.q_pos0 + c0;
+    c.q = a.q + c0 * a.hq * a.d;
+    c.out = a.out + c0 * a.hq * a.d;
+    c.sel = a.sel + c0 * a.n_sel;
+    c.lse = a.lse ? a.lse + c0 * a.hq : nullptr;
+    const dim3 grid((unsigned)((c.lq * c.hkv + 3) / 4));
+    if (a.d == 256)
+      hipLaunchKernelGGL(sparse_attn_kernel<256>, grid, dim3(256), 0, stream, c);
+    else
+      hipLaunchKernelGGL(sparse_attn_kernel<128>, grid, dim3(256), 0, stream, c);
+  }
   return hipGetLastError();
 }
 

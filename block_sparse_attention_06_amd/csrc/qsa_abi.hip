@@ -202,10 +202,13 @@ qsa_status qsa_topk_blocks(int batch, int64_t lq, int r, int budget_tokens, cons
                     "qsa_topk_blocks launch");
 }
 
-qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, int r, int n_sel,
-                               const void* q, const void* k, const void* v, const int32_t* sel,
-                               int64_t q_pos0, float softmax_scale, void* out, float* lse,
-                               void* stream) {
+namespace {
+
+// Argument checks of the sparse attention forward, shared by every entry point that
+// launches it, so that a call fails before it has launched anything.
+qsa_status check_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, int r, int n_sel,
+                          const void* q, const void* k, const void* v, const int32_t* sel,
+                          int64_t q_pos0, float softmax_scale, const void* out) {
   QSA_TRY(check_r(r));
   QSA_TRY(check_attn_shape(hq, hkv, d));
   QSA_REQUIRE(n_sel >= 1 && n_sel <= 1024, QSA_ERR_UNSUPPORTED, "n_sel=%d: supported 1..1024",
@@ -221,6 +224,18 @@ qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, i
   QSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out),
               QSA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
   QSA_REQUIRE(lq * hkv / 4 < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT, "grid too large");
+  return QSA_OK;
+}
+
+}  // namespace
+
+qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, int r, int n_sel,
+                               const void* q, const void* k, const void* v, const int32_t* sel,
+                               int64_t q_pos0, float softmax_scale, void* out, float* lse,
+                               void* stream) {
+  QSA_TRY(check_attn_fwd(lq, lk, hq, hkv, d, r, n_sel, q, k, v, sel, q_pos0, softmax_scale,
+                         out));
+  if (lq == 0) return QSA_OK;
   qsa::AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -238,6 +253,11 @@ qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, i
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   return hip_status(qsa::launch_sparse_attn_fwd(a, static_cast<hipStream_t>(stream)),
                     "qsa_sparse_attn_fwd launch");
+}
+
+int64_t qsa_sparse_attn_fwd_rows_per_launch(int hkv, int d) {
+  if (hkv < 1 || (d != 128 && d != 256)) return 0;
+  return qsa::sparse_attn_fwd_rows_per_launch(hkv, d);
 }
 
 size_t qsa_sparse_attn_bwd_workspace_bytes(int64_t lq, int64_t lk, int hq, int r, int n_sel) {
@@ -508,7 +528,9 @@ qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, i
                                const void* k_pooled_prefix, void* k_pooled, float softmax_scale,
                                int32_t* sel, void* out, float* lse, int64_t row_chunk,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_TRY(check_budget(budget_tokens, r));
+  QSA_TRY(check_attn_fwd(lq, lk, hq, hkv, d, r, budget_tokens / r, q, k, v, sel, q_pos0,
+                         softmax_scale, out));
   QSA_TRY(qsa_prefill_select(lq, lk, q_pos0, h_idx, d_idx, r, budget_tokens, q_idx, w, k_idx,
                              first_raw_token, k_pooled_prefix, k_pooled, sel, row_chunk,
                              workspace, workspace_bytes, stream));

@@ -97,6 +97,8 @@ struct AttnArgs {
   int steps_per_split;
 };
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream);
+// Rows per launch of launch_sparse_attn_fwd on the current device; -1 if unknown.
+int64_t sparse_attn_fwd_rows_per_launch(int hkv, int d);
 hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream);
 
 // ---- stage 4 backward ----

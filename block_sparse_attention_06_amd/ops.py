@@ -154,6 +154,14 @@ def qsa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: 
     return out, lse
 
 
+def qsa_sparse_attn_fwd_rows_per_launch(hkv: int, d: int, device=None) -> int:
+    """Rows per GPU launch of qsa_sparse_attn_fwd on `device` (the current device by
+    default); -1 when the runtime cannot report the occupancy, 0 for unsupported
+    arguments."""
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        return int(_lib.load().qsa_sparse_attn_fwd_rows_per_launch(hkv, d))
+
+
 def qsa_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor,
                         out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, *,
                         q_pos0: int = 0, scale: Optional[float] = None, r: int = 4,

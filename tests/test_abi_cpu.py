@@ -85,6 +85,13 @@ def test_topk_and_attention_validation(lib):
                                    ctypes.c_float(float("nan")), FAKE, None, None) == 1
 
 
+def test_attention_rows_per_launch_query(lib):
+    assert lib.qsa_sparse_attn_fwd_rows_per_launch(2, 192) == 0   # d unsupported
+    assert lib.qsa_sparse_attn_fwd_rows_per_launch(0, 256) == 0
+    n = lib.qsa_sparse_attn_fwd_rows_per_launch(2, 256)
+    assert n == -1 or n >= 2                                       # -1: no device to ask
+
+
 def test_workspace_queries_and_short_workspace(lib):
     # 512 kept blocks = 128 steps of 4: 64 waves of 2 steps, merged 4 per workgroup,
     # so 16 (o[256], m, l) fp32 partials per (sequence, head)

@@ -359,7 +359,8 @@ class _Rows:
 
 def _prefill_parity(name, rows=None, row_chunk=4096, **over):
     wl = workload(name, **over)
-    _say(f"prefill {wl.name} lq={wl.lq} lk={wl.lk} q_pos0={wl.q_pos0} K={wl.budget}")
+    _say(f"prefill {wl.name} lq={wl.lq} lk={wl.lk} q_pos0={wl.q_pos0} K={wl.budget} "
+         f"row_chunk={row_chunk}")
     inp = generate(wl, device=DEV)
     out, lse, sel, kp = Q.qsa_prefill_forward(
         inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["w"], inp["k_idx"], budget=wl.budget,
@@ -415,6 +416,37 @@ def test_prefill_tiny_small_chunks_ragged():
     # Row chunks that do not divide Lq, Lq not a multiple of the 64-row tile.
     n_exact, n = _prefill_parity("tiny", row_chunk=300, lq=1001, lk=1001)
     assert n_exact >= n - 2
+
+
+def test_prefill_generation_boundaries_against_oracle():
+    # The attention runs in launches of one resident generation of workgroups. Rows on
+    # both sides of those boundaries, a query window that starts past a pooled prefix,
+    # ragged selection chunks.
+    n = Q.qsa_sparse_attn_fwd_rows_per_launch(2, 256)
+    _say(f"rows per attention launch: {n}")
+    assert 2 <= n < 6000
+    rows = sorted({0, 1, n - 1, n, n + 1, 2 * n - 1, 2 * n, 6001, 9999, 11999})
+    _prefill_parity("prefill32k", rows=rows, row_chunk=2500, lq=12000, lk=40000, q_pos0=28000,
+                    pooled_prefix_blocks=5000)
+
+
+def test_attention_independent_of_row_split():
+    # Each row's result depends on that row only: the attention over all rows equals,
+    # bit for bit, the attention over arbitrary row slices (different launch splits).
+    wl = workload("prefill32k", lq=6000, lk=40000, q_pos0=34000, pooled_prefix_blocks=5000)
+    _say(f"attention row split lq={wl.lq} lk={wl.lk} q_pos0={wl.q_pos0}")
+    inp = generate(wl, device=DEV)
+    out, lse, sel, _ = Q.qsa_prefill_forward(
+        inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["w"], inp["k_idx"], budget=wl.budget,
+        q_pos0=wl.q_pos0, k_pooled_prefix=inp["k_pooled_prefix"], row_chunk=2500)
+    o2 = torch.zeros_like(out)
+    l2 = torch.zeros_like(lse)
+    scale = 1.0 / math.sqrt(wl.d)
+    for c0, c1 in ((0, 777), (777, 2000), (2000, 2001), (2001, 5999), (5999, 6000)):
+        Q.qsa_sparse_attn_fwd(inp["q"][c0:c1], inp["k"], inp["v"], sel[c0:c1],
+                              q_pos0=wl.q_pos0 + c0, scale=scale, out=o2[c0:c1], lse=l2[c0:c1])
+    torch.cuda.synchronize()
+    assert torch.equal(o2, out) and torch.equal(l2, lse)
 
 
 def test_prefill_32k_sampled():
