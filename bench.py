@@ -38,6 +38,8 @@ def parse_args():
                    help="skip the sparse-attention backward measurement")
     p.add_argument("--no-warmup", action="store_true",
                    help="skip the indexer KL warm-up measurement")
+    p.add_argument("--no-varlen", action="store_true",
+                   help="skip the packed variable-length prefill batch")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -275,6 +277,54 @@ def bench_warmup(torch, Q, name="prefill32k", reps=2):
             "indexer_bwd_tflops": idx_flops / (ms["indexer_bwd"] * 1e-3) / 1e12}
 
 
+def bench_varlen(torch, Q, n_seqs=16, total=131072, floor=2048, reps=3):
+    """A packed (THD) prefill batch: n_seqs sequences of a seeded length mix summing to
+    `total` tokens (each a whole prompt: its queries are all its tokens), model shapes
+    of prefill128k; the whole varlen prefill per call, and its attention alone."""
+    import numpy as np
+    from synth import generate_varlen, serving_lengths, workload
+    wl = workload("prefill128k")
+    lens = serving_lengths(n_seqs, total, floor, seed=7)
+    inp = generate_varlen(wl, [(n, n) for n in lens], device="cuda")
+    max_len = max(lens)
+    plan = Q.VarlenPlan(n_seqs, total, max_len, max_len, wl.hq, wl.d, wl.d_i, wl.budget,
+                        device="cuda")
+    scale = 1.0 / math.sqrt(wl.d)
+
+    def run():
+        return Q.qsa_prefill_varlen_forward(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["w"],
+                                            inp["k_idx"], inp["cu_q"], inp["cu_k"],
+                                            budget=wl.budget, max_lq=max_len, max_lk=max_len,
+                                            scale=scale, plan=plan)
+
+    def attn():
+        return Q.qsa_sparse_attn_varlen_fwd(inp["q"], inp["k"], inp["v"], plan.sel, inp["cu_q"],
+                                            inp["cu_k"], scale=scale, out=plan.out, lse=plan.lse)
+
+    ms = {}
+    for name, f in (("forward", run), ("attention", attn)):
+        f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        ms[name] = a.elapsed_time(b) / reps
+    t = np.concatenate([np.arange(n, dtype=np.int64) for n in lens])
+    a_bytes = attention_bytes(wl, t)
+    del inp, plan
+    torch.cuda.empty_cache()
+    return {"workload": f"{n_seqs} packed prompts of prefill128k shapes, {total} tokens",
+            "lengths": lens, "row_chunk": 16384 // n_seqs, "ms": ms["forward"],
+            "tokens_per_s": total / (ms["forward"] * 1e-3), "attention_ms": ms["attention"],
+            "attention_roofline": {"bound": "hbm", "achieved": a_bytes / ms["attention"] / 1e6,
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": a_bytes / ms["attention"] / 1e6 / HBM_PEAK_GBS,
+                                   "algorithmic_bytes_per_call": a_bytes}}
+
+
 def cpu_baseline(wl, inp, budget_s):
     """The oracle, as it stands, on evenly spread query rows of the same workload."""
     import numpy as np
@@ -420,6 +470,9 @@ def main():
     if not args.no_warmup:
         line["indexer_warmup"] = bench_warmup(torch, Q)
         progress("indexer warm-up done")
+    if not args.no_varlen:
+        line["varlen"] = bench_varlen(torch, Q)
+        progress(f"varlen: {line['varlen']['ms']:.2f} ms per packed batch")
     if not args.no_decode:
         dwl = workload("decode1m")
         dinp = generate(dwl, device=dev)

@@ -7,6 +7,7 @@ ABI of include/qsa.h); this package only builds it and marshals torch tensors to
 from .ops import (  # noqa: F401
     DecodePlan,
     PrefillPlan,
+    VarlenPlan,
     QSAError,
     abi_version,
     qsa_decode_forward,
@@ -17,11 +18,13 @@ from .ops import (  # noqa: F401
     qsa_pool_keys,
     qsa_prefill_forward,
     qsa_prefill_select,
+    qsa_prefill_varlen_forward,
     qsa_probe_gather,
     qsa_sparse_attn_bwd,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_fwd,
     qsa_sparse_attn_fwd_rows_per_launch,
+    qsa_sparse_attn_varlen_fwd,
     qsa_topk_blocks,
     score_ld,
 )

@@ -162,13 +162,29 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
   const int G = a.hq / a.hkv;
 
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t row = item / a.hkv;
-  const int g = (int)(item - row * a.hkv);
-  if (row >= a.lq) return;
-  const int64_t t = a.q_pos0 + row;
+  const int64_t lrow = item / a.hkv;
+  const int g = (int)(item - lrow * a.hkv);
+  if (lrow >= a.lq) return;
+  const int64_t row = a.row_begin + lrow;      // row of q, sel, out and lse
+  const int64_t kstride = (int64_t)a.hkv * D;  // elements between consecutive tokens
+  const uint16_t* kb = a.k;
+  const uint16_t* vb = a.v;
+  int64_t t = a.q_pos0 + row;
+  if (a.cu_q) {
+    // Packed sequences: the row's sequence is the last one starting at or before it.
+    int lo = 0, hi = a.batch_vl;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cu_q[mid] <= row) lo = mid; else hi = mid;
+    }
+    const int64_t q0 = a.cu_q[lo], q1 = a.cu_q[lo + 1];
+    const int64_t k0 = a.cu_k[lo], k1 = a.cu_k[lo + 1];
+    t = (k1 - k0) - (q1 - q0) + (row - q0);
+    kb += k0 * kstride;
+    vb += k0 * kstride;
+  }
   const int n_steps = (a.n_sel + 3) / 4;
   const int32_t* srow = a.sel + row * a.n_sel;
-  const int64_t kstride = (int64_t)a.hkv * D;  // elements between consecutive tokens
 
   uint4 Qc[D / 32];
   attn_load_q<D>(Qc, a.q + row * (int64_t)a.hq * D, g, G, c16, quad);
@@ -185,7 +201,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
     for (int j = 0; j < 4; ++j) b4[j] = (4 * s + j < a.n_sel) ? srow[4 * s + j] : -1;
     if (b4[0] < 0) break;  // -1 padding reached
     AttnStep<D> st;
-    attn_load_step<D>(st, b4, a.k, a.v, kstride, g, t, c16, quad);
+    attn_load_step<D>(st, b4, kb, vb, kstride, g, t, c16, quad);
     attn_compute_step<D>(st, b4, Qc, O, m_run, l_run, a.scale_log2, t, quad);
   }
 
@@ -430,11 +446,7 @@ hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream) {
   for (int64_t c0 = 0; c0 < a.lq; c0 += rows) {
     AttnArgs c = a;
     c.lq = a.lq - c0 < rows ? a.lq - c0 : rows;
-    c.q_pos0 = a.q_pos0 + c0;
-    c.q = a.q + c0 * a.hq * a.d;
-    c.out = a.out + c0 * a.hq * a.d;
-    c.sel = a.sel + c0 * a.n_sel;
-    c.lse = a.lse ? a.lse + c0 * a.hq : nullptr;
+    c.row_begin = a.row_begin + c0;
     const dim3 grid((unsigned)((c.lq * c.hkv + 3) / 4));
     if (a.d == 256)
       hipLaunchKernelGGL(sparse_attn_kernel<256>, grid, dim3(256), 0, stream, c);

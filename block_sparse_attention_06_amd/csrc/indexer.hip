@@ -27,14 +27,9 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
   return __float_as_uint((float)y) >> 16;  // y is exact in bf16, hence in fp32
 }
 
-__global__ __launch_bounds__(256) void pool_keys_kernel(const uint16_t* __restrict__ k,
-                                                        int64_t ks, int64_t nb, int d, int r,
-                                                        uint16_t* __restrict__ p, int64_t ps) {
-  const int vec = d >> 3;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t b = gid / vec;
-  if (b >= nb) return;
-  const int c = (int)(gid - b * vec) * 8;
+// 8 columns c..c+7 of pooled block b: the mean of keys b*r .. b*r+r-1 (row stride ks).
+__device__ __forceinline__ void pool_block8(const uint16_t* __restrict__ k, int64_t ks, int64_t b,
+                                            int c, int r, uint16_t* __restrict__ dst) {
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
@@ -51,7 +46,35 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const uint16_t* __restri
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     o[e] = f64_to_bf16_bits(acc[2 * e] / r) | (f64_to_bf16_bits(acc[2 * e + 1] / r) << 16);
-  *reinterpret_cast<uint4*>(p + b * ps + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__global__ __launch_bounds__(256) void pool_keys_kernel(const uint16_t* __restrict__ k,
+                                                        int64_t ks, int64_t nb, int d, int r,
+                                                        uint16_t* __restrict__ p, int64_t ps) {
+  const int vec = d >> 3;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = gid / vec;
+  if (b >= nb) return;
+  const int c = (int)(gid - b * vec) * 8;
+  pool_block8(k, ks, b, c, r, p + b * ps + c);
+}
+
+// Packed sequences: sequence blockIdx.y pools its complete blocks (at most max_nb) from
+// its own key tokens into its slot of the padded output p[batch][max_nb][d].
+__global__ __launch_bounds__(256) void pool_keys_varlen_kernel(const uint16_t* __restrict__ k,
+                                                               const int32_t* __restrict__ cu_k,
+                                                               int64_t max_nb, int d, int r,
+                                                               uint16_t* __restrict__ p) {
+  const int vec = d >> 3;
+  const int bi = blockIdx.y;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = gid / vec;
+  const int64_t k0 = cu_k[bi];
+  const int64_t nb = min(((int64_t)cu_k[bi + 1] - k0) / r, max_nb);
+  if (b >= nb) return;
+  const int c = (int)(gid - b * vec) * 8;
+  pool_block8(k + k0 * d, d, b, c, r, p + ((int64_t)bi * max_nb + b) * d + c);
 }
 
 hipError_t launch_pool_keys(const uint16_t* k_idx, int64_t k_stride, int64_t n_blocks, int d_idx,
@@ -61,6 +84,16 @@ hipError_t launch_pool_keys(const uint16_t* k_idx, int64_t k_stride, int64_t n_b
   const int64_t grid = (threads + 255) / 256;
   hipLaunchKernelGGL(pool_keys_kernel, dim3((unsigned)grid), dim3(256), 0, stream, k_idx,
                      k_stride, n_blocks, d_idx, r, k_pooled, p_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_keys_varlen(const uint16_t* k_idx, const int32_t* cu_k, int batch,
+                                   int64_t max_nb, int d_idx, int r, uint16_t* k_pooled,
+                                   hipStream_t stream) {
+  if (max_nb <= 0 || batch <= 0) return hipSuccess;
+  const int64_t grid = (max_nb * (d_idx / 8) + 255) / 256;
+  hipLaunchKernelGGL(pool_keys_varlen_kernel, dim3((unsigned)grid, (unsigned)batch), dim3(256), 0,
+                     stream, k_idx, cu_k, max_nb, d_idx, r, k_pooled);
   return hipGetLastError();
 }
 
@@ -96,9 +129,20 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
   const int c16 = lane & 15;
   const int quad = lane >> 4;
   const int bi = blockIdx.z;
-  const int64_t base = a.seq_lens ? (int64_t)a.seq_lens[bi] - a.lq : a.q_pos0;
+  int64_t base = a.seq_lens ? (int64_t)a.seq_lens[bi] - a.lq : a.q_pos0;
+  int64_t lq = a.lq;
+  const uint16_t* qb = a.q_idx + (int64_t)bi * a.q_bs;
+  const float* wb = a.w + (int64_t)bi * a.w_bs;
+  if (a.vl.cu_q) {  // packed sequences: this sequence's rows of the launch
+    const SeqRows sr = varlen_rows(a.vl, bi, a.lq);
+    lq = sr.n;
+    base = sr.pos;
+    qb = a.q_idx + sr.first * a.h_idx * DI;
+    wb = a.w + sr.first * a.h_idx;
+  }
   const int64_t i0 = (int64_t)blockIdx.x * kScoreRows;
-  const int64_t t_last = base + min(i0 + kScoreRows - 1, a.lq - 1);
+  if (i0 >= lq) return;
+  const int64_t t_last = base + min(i0 + kScoreRows - 1, lq - 1);
   if (t_last < 0) return;
   const int64_t nb_need = min(t_last / a.r, a.nblk);
   const int64_t n_begin = (int64_t)blockIdx.y * n_per_wg;
@@ -106,8 +150,6 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
   if (n_begin >= n_end) return;
   const int n_tiles = (int)((n_end - n_begin + kScoreTileN - 1) / kScoreTileN);
 
-  const uint16_t* qb = a.q_idx + (int64_t)bi * a.q_bs;
-  const float* wb = a.w + (int64_t)bi * a.w_bs;
   const uint16_t* kpb = a.kp + (int64_t)bi * a.kp_bs;
   float* sb = a.scores + (int64_t)bi * a.s_bs;
 
@@ -139,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
   for (int mt = 0; mt < 4; ++mt) {
     const int64_t tok = i0 + wave * 16 + mt * 4 + (c16 >> 2);
     const int h = c16 & 3;
-    const bool ok = tok < a.lq && h < a.h_idx;
+    const bool ok = tok < lq && h < a.h_idx;
     const uint16_t* p = qb + (tok * a.h_idx + h) * DI + quad * 8;
 #pragma unroll
     for (int c = 0; c < NC; ++c) A[mt][c] = ok ? ld16(p + c * 32) : make_uint4(0, 0, 0, 0);
@@ -152,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
   for (int mt = 0; mt < 4; ++mt) {
     const int64_t tok = i0 + wave * 16 + mt * 4 + quad;
     const int64_t t = base + tok;
-    const bool valid = tok < a.lq && t >= 0;
+    const bool valid = tok < lq && t >= 0;
     lim[mt] = valid ? min(t / a.r, a.nblk) : 0;
     orow[mt] = sb + (valid ? tok : 0) * a.ld;
 #pragma unroll
@@ -353,7 +395,7 @@ __global__ __launch_bounds__(256) void index_scores_scan_kernel(ScoreArgs a, int
 
 hipError_t launch_index_scores(const ScoreArgs& a, hipStream_t stream) {
   if (a.lq <= 0 || a.batch <= 0 || a.nblk <= 0) return hipSuccess;
-  if (a.lq <= 4 || a.cand.cand_val) {
+  if ((a.lq <= 4 || a.cand.cand_val) && !a.vl.cu_q) {
     // About 2048 waves (two per SIMD): one round over the GPU, 64-block tiles. With
     // candidates, a wave covers exactly one top-k segment.
     const int64_t rows = (int64_t)a.batch * a.lq;

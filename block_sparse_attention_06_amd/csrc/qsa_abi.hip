@@ -538,6 +538,163 @@ qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, i
                              softmax_scale, out, lse, stream);
 }
 
+// ---- packed variable-length sequences ----
+
+namespace {
+
+qsa::TopkArgs varlen_topk_args(int batch, int64_t rows, int r, int budget_tokens,
+                               const float* scores, int64_t ld, int64_t sbs, int64_t max_nblk,
+                               int32_t* sel, qsa::Varlen vl) {
+  qsa::TopkArgs a = topk_args(batch, rows, r, budget_tokens, scores, ld, sbs, max_nblk, 0,
+                              nullptr, sel);
+  a.vl = vl;
+  return a;
+}
+
+int64_t varlen_row_chunk(int64_t max_lq, int64_t row_chunk) {
+  return row_chunk > 0 ? (row_chunk < max_lq ? row_chunk : max_lq) : max_lq;
+}
+
+qsa_status check_varlen(int batch, const int32_t* cu_q, const int32_t* cu_k, int64_t max_lq,
+                        int64_t max_lk, int r) {
+  QSA_TRY(check_r(r));
+  QSA_REQUIRE(batch >= 1 && batch <= 65535, QSA_ERR_INVALID_ARGUMENT, "batch=%d", batch);
+  QSA_REQUIRE(cu_q && cu_k, QSA_ERR_INVALID_ARGUMENT, "null cu_seqlens");
+  QSA_REQUIRE(max_lq >= 0 && max_lk >= 0 && max_lq <= max_lk && max_lk < ((int64_t)1 << 31),
+              QSA_ERR_INVALID_ARGUMENT, "max_lq=%lld, max_lk=%lld", (long long)max_lq,
+              (long long)max_lk);
+  QSA_REQUIRE(max_lk / r < ((int64_t)1 << 22), QSA_ERR_UNSUPPORTED,
+              "max_lk=%lld: top-k supports fewer than 2^22 blocks", (long long)max_lk);
+  return QSA_OK;
+}
+
+}  // namespace
+
+size_t qsa_prefill_varlen_workspace_bytes(int batch, int64_t max_lq, int64_t max_lk, int r,
+                                          int budget_tokens, int64_t row_chunk) {
+  if (batch <= 0 || max_lq <= 0 || max_lk <= 0 || r <= 0 || budget_tokens < r) return 0;
+  const int64_t rc = varlen_row_chunk(max_lq, row_chunk);
+  const int64_t nblk = max_lk / r;
+  const int64_t ld = score_ld(nblk);
+  // Sized for rows whose positions reach the last block (lengths live on the device).
+  const qsa::Varlen any{reinterpret_cast<const int32_t*>(1), nullptr, 0};
+  const qsa::TopkArgs ta =
+      varlen_topk_args(batch, rc, r, budget_tokens, nullptr, ld, rc * ld, nblk, nullptr, any);
+  return align256((size_t)batch * rc * ld * sizeof(float)) + qsa::topk_workspace_bytes(ta);
+}
+
+qsa_status qsa_prefill_varlen_select(int batch, const int32_t* cu_seqlens_q,
+                                     const int32_t* cu_seqlens_k, int64_t max_lq,
+                                     int64_t max_lk, int h_idx, int d_idx, int r,
+                                     int budget_tokens, const void* q_idx, const float* w,
+                                     const void* k_idx, void* k_pooled, int32_t* sel,
+                                     int64_t row_chunk, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  QSA_TRY(check_varlen(batch, cu_seqlens_q, cu_seqlens_k, max_lq, max_lk, r));
+  QSA_TRY(check_budget(budget_tokens, r));
+  QSA_TRY(check_indexer_shape(h_idx, d_idx));
+  const int64_t nblk = max_lk / r;
+  QSA_REQUIRE(k_pooled && (k_idx || nblk == 0), QSA_ERR_INVALID_ARGUMENT,
+              "null k_pooled or k_idx");
+  QSA_REQUIRE(aligned16(k_pooled) && (!k_idx || aligned16(k_idx)), QSA_ERR_INVALID_ARGUMENT,
+              "k_idx and k_pooled must be 16-byte aligned");
+  if (max_lq > 0) {
+    QSA_REQUIRE(q_idx && w && sel, QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    QSA_REQUIRE(aligned16(q_idx), QSA_ERR_INVALID_ARGUMENT, "q_idx must be 16-byte aligned");
+    const size_t need =
+        qsa_prefill_varlen_workspace_bytes(batch, max_lq, max_lk, r, budget_tokens, row_chunk);
+    QSA_REQUIRE(need == 0 || (workspace && workspace_bytes >= need && aligned16(workspace)),
+                QSA_ERR_WORKSPACE,
+                "varlen prefill workspace: need %zu bytes (16-byte aligned), got %zu", need,
+                workspace_bytes);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(hip_status(qsa::launch_pool_keys_varlen(static_cast<const uint16_t*>(k_idx),
+                                                  cu_seqlens_k, batch, nblk, d_idx, r,
+                                                  static_cast<uint16_t*>(k_pooled), s),
+                     "varlen pooling launch"));
+  if (max_lq == 0) return QSA_OK;
+  const int64_t rc = varlen_row_chunk(max_lq, row_chunk);
+  const int64_t ld = score_ld(nblk);
+  float* sc = static_cast<float*>(workspace);
+  char* tk = static_cast<char*>(workspace) + align256((size_t)batch * rc * ld * sizeof(float));
+  for (int64_t c0 = 0; c0 < max_lq; c0 += rc) {
+    const int64_t n = (max_lq - c0) < rc ? (max_lq - c0) : rc;
+    const qsa::Varlen vl{cu_seqlens_q, cu_seqlens_k, c0};
+    qsa::ScoreArgs sa{static_cast<const uint16_t*>(q_idx), 0, w, 0,
+                      static_cast<const uint16_t*>(k_pooled), nblk * d_idx, nblk, n, h_idx,
+                      d_idx, r, 0, nullptr, sc, ld, rc * ld, batch, {}, vl};
+    QSA_TRY(hip_status(qsa::launch_index_scores(sa, s), "varlen score launch"));
+    const qsa::TopkArgs ta =
+        varlen_topk_args(batch, n, r, budget_tokens, sc, ld, rc * ld, nblk, sel, vl);
+    QSA_TRY(hip_status(qsa::launch_topk_blocks(ta, tk, s), "varlen top-k launch"));
+  }
+  return QSA_OK;
+}
+
+qsa_status qsa_sparse_attn_varlen_fwd(int batch, const int32_t* cu_seqlens_q,
+                                      const int32_t* cu_seqlens_k, int64_t total_q, int hq,
+                                      int hkv, int d, int r, int n_sel, const void* q,
+                                      const void* k, const void* v, const int32_t* sel,
+                                      float softmax_scale, void* out, float* lse, void* stream) {
+  QSA_TRY(check_r(r));
+  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_REQUIRE(batch >= 1 && batch <= 65535, QSA_ERR_INVALID_ARGUMENT, "batch=%d", batch);
+  QSA_REQUIRE(cu_seqlens_q && cu_seqlens_k, QSA_ERR_INVALID_ARGUMENT, "null cu_seqlens");
+  QSA_REQUIRE(n_sel >= 1 && n_sel <= 1024, QSA_ERR_UNSUPPORTED, "n_sel=%d: supported 1..1024",
+              n_sel);
+  QSA_REQUIRE(total_q >= 0 && total_q < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT,
+              "total_q=%lld", (long long)total_q);
+  QSA_REQUIRE(isfinite(softmax_scale), QSA_ERR_INVALID_ARGUMENT, "softmax_scale not finite");
+  if (total_q == 0) return QSA_OK;
+  QSA_REQUIRE(q && k && v && sel && out, QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  QSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out),
+              QSA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+  qsa::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sel = sel;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.lq = total_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.n_sel = n_sel;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.batch_vl = batch;
+  return hip_status(qsa::launch_sparse_attn_fwd(a, static_cast<hipStream_t>(stream)),
+                    "qsa_sparse_attn_varlen_fwd launch");
+}
+
+qsa_status qsa_prefill_varlen_forward(int batch, const int32_t* cu_seqlens_q,
+                                      const int32_t* cu_seqlens_k, int64_t total_q,
+                                      int64_t max_lq, int64_t max_lk, int hq, int hkv, int d,
+                                      int h_idx, int d_idx, int r, int budget_tokens,
+                                      const void* q, const void* k, const void* v,
+                                      const void* q_idx, const float* w, const void* k_idx,
+                                      void* k_pooled, float softmax_scale, int32_t* sel,
+                                      void* out, float* lse, int64_t row_chunk,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  QSA_TRY(check_budget(budget_tokens, r));
+  QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_REQUIRE(total_q >= 0 && total_q < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT,
+              "total_q=%lld", (long long)total_q);
+  QSA_REQUIRE(isfinite(softmax_scale), QSA_ERR_INVALID_ARGUMENT, "softmax_scale not finite");
+  QSA_REQUIRE(total_q == 0 || (q && k && v && out && aligned16(q) && aligned16(k) &&
+                               aligned16(v) && aligned16(out)),
+              QSA_ERR_INVALID_ARGUMENT, "q, k, v and out must be non-null and 16-byte aligned");
+  QSA_TRY(qsa_prefill_varlen_select(batch, cu_seqlens_q, cu_seqlens_k, max_lq, max_lk, h_idx,
+                                    d_idx, r, budget_tokens, q_idx, w, k_idx, k_pooled, sel,
+                                    row_chunk, workspace, workspace_bytes, stream));
+  return qsa_sparse_attn_varlen_fwd(batch, cu_seqlens_q, cu_seqlens_k, total_q, hq, hkv, d, r,
+                                    budget_tokens / r, q, k, v, sel, softmax_scale, out, lse,
+                                    stream);
+}
+
 // ---- whole decode step ----
 
 size_t qsa_decode_workspace_bytes(int batch, int hq, int d, int64_t lmax, int r,

@@ -7,9 +7,36 @@
 
 namespace qsa {
 
+// Packed variable-length sequences (THD): sequence b owns the query rows
+// cu_q[b] .. cu_q[b+1]-1 and the key tokens cu_k[b] .. cu_k[b+1]-1 of the packed
+// tensors, its queries being its last cu_q[b+1]-cu_q[b] tokens. A score or top-k
+// launch takes the local query rows row0 .. row0+lq-1 of every sequence.
+struct Varlen {
+  const int32_t* cu_q;  // device [batch + 1]; null: not packed
+  const int32_t* cu_k;  // device [batch + 1]
+  int64_t row0;
+};
+
+// The rows of sequence bi in a launch of lq local rows: how many exist, the packed
+// index of the launch's first row, and that row's position among the sequence's keys.
+struct SeqRows {
+  int64_t n, first, pos;
+};
+__device__ __forceinline__ SeqRows varlen_rows(const Varlen& v, int bi, int64_t lq) {
+  const int64_t q0 = v.cu_q[bi], q1 = v.cu_q[bi + 1];
+  const int64_t lk = (int64_t)v.cu_k[bi + 1] - v.cu_k[bi];
+  const int64_t left = q1 - q0 - v.row0;
+  return SeqRows{left < 0 ? 0 : (left < lq ? left : lq), q0 + v.row0, lk - (q1 - q0) + v.row0};
+}
+
 // ---- stage 1 ----
 hipError_t launch_pool_keys(const uint16_t* k_idx, int64_t k_stride, int64_t n_blocks, int d_idx,
                             int r, uint16_t* k_pooled, int64_t p_stride, hipStream_t stream);
+// Packed sequences (keys cu_k[b] .. cu_k[b+1]-1 of k_idx [.][d_idx]) into the padded
+// k_pooled [batch][max_nb][d_idx]; blocks past a sequence's complete blocks are untouched.
+hipError_t launch_pool_keys_varlen(const uint16_t* k_idx, const int32_t* cu_k, int batch,
+                                   int64_t max_nb, int d_idx, int r, uint16_t* k_pooled,
+                                   hipStream_t stream);
 
 // Two-level top-k: per segment of kTopkWaveSeg candidates, the kTopkWaveKeep best as
 // (score, id) pairs (id -1: empty) and the worst kept one when the segment had more.
@@ -47,6 +74,7 @@ struct ScoreArgs {
   int64_t s_bs;
   int batch;
   TopkCandidates cand;  // optional (few rows per sequence): also emit segment candidates
+  Varlen vl;            // packed sequences: q_idx / w rows packed, kp and scores per sequence
 };
 hipError_t launch_index_scores(const ScoreArgs& a, hipStream_t stream);
 
@@ -63,6 +91,7 @@ struct TopkArgs {
   int n_sel;
   int32_t* sel;
   int batch;
+  Varlen vl;  // packed sequences: sel rows packed, scores per sequence (chunk-local rows)
 };
 size_t topk_workspace_bytes(const TopkArgs& a);
 bool topk_supported(const TopkArgs& a);
@@ -95,6 +124,13 @@ struct AttnArgs {
   float* part_ml;    // [batch][hq][n_split][2]
   int n_split;
   int steps_per_split;
+  // prefill: the launch takes rows row_begin .. row_begin + lq - 1; with cu_q / cu_k
+  // (device [batch + 1]) the rows and keys are packed sequences, each row's position
+  // counted within its own sequence
+  int64_t row_begin;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int batch_vl;
 };
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream);
 // Rows per launch of launch_sparse_attn_fwd on the current device; -1 if unknown.

@@ -525,13 +525,23 @@ struct TopkLaunch {
   int kseg;         // candidates kept per segment (multiple of 4)
 };
 
-__device__ __forceinline__ void row_geometry(const TopkArgs& a, int64_t row, int bi, int64_t& t,
-                                             int64_t& own, int64_t& C, int& m) {
-  const int64_t base = a.seq_lens ? (int64_t)a.seq_lens[bi] - a.lq : a.q_pos0;
+// Position t, own block, candidate count C and kept count m of launch row `row` of
+// sequence bi; returns the row's output (null when packed sequence bi has no such row).
+__device__ __forceinline__ int32_t* row_geometry(const TopkArgs& a, int64_t row, int bi,
+                                                 int64_t& t, int64_t& own, int64_t& C, int& m) {
+  int64_t base = a.seq_lens ? (int64_t)a.seq_lens[bi] - a.lq : a.q_pos0;
+  int32_t* out = a.sel + ((int64_t)bi * a.lq + row) * a.n_sel;
+  if (a.vl.cu_q) {
+    const SeqRows sr = varlen_rows(a.vl, bi, a.lq);
+    if (row >= sr.n) return nullptr;
+    base = sr.pos;
+    out = a.sel + (sr.first + row) * a.n_sel;
+  }
   t = base + row;
   own = t >= 0 ? t / a.r : -1;
   C = t >= 0 ? min(own, a.nblk) : 0;
   m = (int)min((int64_t)(a.n_sel - 1), C);
+  return out;
 }
 
 // Writes the ids marked in sm.bitmap (ids < 32 * words) to out[0..) in ascending order.
@@ -756,8 +766,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
   if (fast_merge) merge_fetch(sm, L, crow, mr);
   int64_t t, own, C;
   int m;
-  row_geometry(a, row, bi, t, own, C, m);
-  int32_t* out = a.sel + ((int64_t)bi * a.lq + row) * a.n_sel;
+  int32_t* out = row_geometry(a, row, bi, t, own, C, m);
+  if (!out) return;  // packed sequence shorter than this launch's rows
   const float* srow = a.scores + (int64_t)bi * a.s_bs + row * a.ld;
 
   if (t < 0 || m == C) {  // nothing to rank: every earlier block fits
@@ -876,7 +886,7 @@ __global__ __launch_bounds__(256) void topk_wave_segments_kernel(TopkLaunch L) {
   const int64_t row = crow - (int64_t)bi * a.lq;
   int64_t t, own, C;
   int m;
-  row_geometry(a, row, bi, t, own, C, m);
+  if (!row_geometry(a, row, bi, t, own, C, m)) return;
   float* cv = L.cand_val + (crow * L.n_seg + seg_id) * kWaveKeep;
   int32_t* ci = L.cand_idx + (crow * L.n_seg + seg_id) * kWaveKeep;
   if (t < 0 || m == C) return;  // the merge writes such rows without reading candidates
@@ -918,7 +928,7 @@ __global__ __launch_bounds__(256) void topk_wave_segments_kernel(TopkLaunch L) {
 
 static int64_t max_candidates(const TopkArgs& a) {
   // Upper bound of C over the launch's rows (positions may come from the device).
-  if (a.seq_lens) return a.nblk;
+  if (a.seq_lens || a.vl.cu_q) return a.nblk;
   const int64_t t_last = a.q_pos0 + a.lq - 1;
   return t_last < 0 ? 0 : min(t_last / a.r, a.nblk);
 }

@@ -348,6 +348,90 @@ def qsa_prefill_forward(q, k, v, q_idx, w, k_idx, *, budget: int, q_pos0: int = 
     return plan.out, plan.lse, plan.sel, plan.k_pooled
 
 
+def _bounds(cu_q: torch.Tensor, cu_k: torch.Tensor, max_lq, max_lk):
+    """Host upper bounds of the sequence lengths; read from the device (a synchronising
+    copy) only when the caller gives none."""
+    if max_lq is None or max_lk is None:
+        lq = (cu_q[1:] - cu_q[:-1]).max().item() if cu_q.numel() > 1 else 0
+        lk = (cu_k[1:] - cu_k[:-1]).max().item() if cu_k.numel() > 1 else 0
+        max_lq = lq if max_lq is None else max_lq
+        max_lk = lk if max_lk is None else max_lk
+    return int(max_lq), int(max_lk)
+
+
+class VarlenPlan:
+    """Outputs and workspace for packed (THD) prefill batches within given bounds."""
+
+    def __init__(self, batch, total_q, max_lq, max_lk, hq, d, d_idx, budget, *, r=4,
+                 row_chunk=None, device="cuda"):
+        dev = torch.device(device)
+        # about 16K score rows per selection chunk, whatever the batch
+        self.row_chunk = row_chunk if row_chunk else max(64, 16384 // max(batch, 1))
+        self.shape = (batch, total_q, max_lq, max_lk, budget, r)
+        self.sel = torch.empty((total_q, budget // r), dtype=torch.int32, device=dev)
+        self.out = torch.empty((total_q, hq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev)
+        self.k_pooled = torch.empty((batch, max_lk // r, d_idx), dtype=torch.bfloat16,
+                                    device=dev)
+        nbytes = _lib.load().qsa_prefill_varlen_workspace_bytes(batch, max_lq, max_lk, r, budget,
+                                                                self.row_chunk)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        self.ws_bytes = nbytes
+
+
+def qsa_prefill_varlen_forward(q, k, v, q_idx, w, k_idx, cu_seqlens_q, cu_seqlens_k, *,
+                               budget: int, max_lq: Optional[int] = None,
+                               max_lk: Optional[int] = None, scale: Optional[float] = None,
+                               r: int = 4, row_chunk: Optional[int] = None,
+                               plan: Optional[VarlenPlan] = None):
+    """Whole prefill of a packed batch. q [Tq,Hq,d], k/v [Tk,Hkv,d], q_idx [Tq,H_I,d_I],
+    w [Tq,H_I], k_idx [Tk,d_I]; cu_seqlens_q/k int32 [B+1] on the device. Each sequence's
+    queries are its last tokens. Returns (out, lse, sel with per-sequence block ids,
+    k_pooled [B, max_lk/r, d_I])."""
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("q_idx", q_idx, torch.bfloat16),
+                        ("w", w, torch.float32), ("k_idx", k_idx, torch.bfloat16),
+                        ("cu_seqlens_q", cu_seqlens_q, torch.int32),
+                        ("cu_seqlens_k", cu_seqlens_k, torch.int32)):
+        _need(t, name, dt, q.device)
+    batch = cu_seqlens_q.numel() - 1
+    total_q, hq, d = q.shape
+    _, hkv, _ = k.shape
+    _, h_idx, d_idx = q_idx.shape
+    max_lq, max_lk = _bounds(cu_seqlens_q, cu_seqlens_k, max_lq, max_lk)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if plan is None:
+        plan = VarlenPlan(batch, total_q, max_lq, max_lk, hq, d, d_idx, budget, r=r,
+                          row_chunk=row_chunk, device=q.device)
+    _call("qsa_prefill_varlen_forward", batch, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), total_q,
+          max_lq, max_lk, hq, hkv, d, h_idx, d_idx, r, budget, _ptr(q), _ptr(k), _ptr(v),
+          _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(plan.k_pooled), scale, _ptr(plan.sel),
+          _ptr(plan.out), _ptr(plan.lse), plan.row_chunk, _ptr(plan.ws), plan.ws_bytes,
+          _stream(q))
+    return plan.out, plan.lse, plan.sel, plan.k_pooled
+
+
+def qsa_sparse_attn_varlen_fwd(q, k, v, sel, cu_seqlens_q, cu_seqlens_k, *,
+                               scale: Optional[float] = None, r: int = 4,
+                               out: Optional[torch.Tensor] = None,
+                               lse: Optional[torch.Tensor] = None):
+    """Attention of a packed batch over per-sequence selections sel [Tq, n_sel]."""
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("sel", sel, torch.int32),
+                        ("cu_seqlens_q", cu_seqlens_q, torch.int32),
+                        ("cu_seqlens_k", cu_seqlens_k, torch.int32)):
+        _need(t, name, dt, q.device)
+    total_q, hq, d = q.shape
+    _, hkv, _ = k.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _call("qsa_sparse_attn_varlen_fwd", cu_seqlens_q.numel() - 1, _ptr(cu_seqlens_q),
+          _ptr(cu_seqlens_k), total_q, hq, hkv, d, r, sel.shape[1], _ptr(q), _ptr(k), _ptr(v),
+          _ptr(sel), scale, _ptr(out), _ptr(lse), _stream(q))
+    return out, lse
+
+
 class DecodePlan:
     """Preallocated outputs and workspace for repeated decode steps of one shape."""
 

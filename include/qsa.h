@@ -267,6 +267,53 @@ qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, i
                                void* stream);
 
 /*
+ * Packed variable-length batches (THD) [MR5]: `batch` sequences packed along the token
+ * axis. Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q, q_idx,
+ * w, sel, out and lse, and key tokens cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k, v
+ * and k_idx; its queries are its LAST lq_b = cu_q[b+1]-cu_q[b] tokens, so query row
+ * i of the sequence sits at position lk_b - lq_b + i among its own lk_b keys (a
+ * sequence with lq_b = lk_b is a plain prefill, lq_b < lk_b a chunk after a prefix
+ * whose keys are packed in too). Every step is the single-sequence one applied to
+ * each sequence on its own: no block, score or key crosses a sequence boundary.
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [batch + 1], non-decreasing from 0;
+ *                cu_k[b+1]-cu_k[b] >= cu_q[b+1]-cu_q[b] for every b
+ *   max_lq, max_lk  host upper bounds of lq_b and lk_b (they size grids and the
+ *                padded pooled-key buffer; a longer sequence is not detected and is
+ *                processed only up to the bounds)
+ *   total_q      host copy of cu_seqlens_q[batch]
+ *   k_pooled     output bf16 [batch][max_lk/r][d_idx]: sequence b's complete blocks
+ *                in its slot (the rest of the slot is left as it was)
+ *   sel          int32 [total_q][K/r]: block ids LOCAL to each row's sequence,
+ *                ascending, -1 padded, as stage 3 writes them for one sequence
+ * The selection runs in chunks of row_chunk local rows of every sequence at once
+ * (the workspace holds batch x row_chunk score rows). The attention launches one
+ * resident generation of rows at a time over the packed rows, sequences mixed.
+ */
+size_t qsa_prefill_varlen_workspace_bytes(int batch, int64_t max_lq, int64_t max_lk, int r,
+                                          int budget_tokens, int64_t row_chunk);
+qsa_status qsa_prefill_varlen_select(int batch, const int32_t* cu_seqlens_q,
+                                     const int32_t* cu_seqlens_k, int64_t max_lq,
+                                     int64_t max_lk, int h_idx, int d_idx, int r,
+                                     int budget_tokens, const void* q_idx, const float* w,
+                                     const void* k_idx, void* k_pooled, int32_t* sel,
+                                     int64_t row_chunk, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+qsa_status qsa_sparse_attn_varlen_fwd(int batch, const int32_t* cu_seqlens_q,
+                                      const int32_t* cu_seqlens_k, int64_t total_q, int hq,
+                                      int hkv, int d, int r, int n_sel, const void* q,
+                                      const void* k, const void* v, const int32_t* sel,
+                                      float softmax_scale, void* out, float* lse, void* stream);
+qsa_status qsa_prefill_varlen_forward(int batch, const int32_t* cu_seqlens_q,
+                                      const int32_t* cu_seqlens_k, int64_t total_q,
+                                      int64_t max_lq, int64_t max_lk, int hq, int hkv, int d,
+                                      int h_idx, int d_idx, int r, int budget_tokens,
+                                      const void* q, const void* k, const void* v,
+                                      const void* q_idx, const float* w, const void* k_idx,
+                                      void* k_pooled, float softmax_scale, int32_t* sel,
+                                      void* out, float* lse, int64_t row_chunk,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Whole decode step for `batch` sequences: scores against the pooled-key cache,
  * top-k, split attention and combine. Inputs as in stages 2-4'; q_idx
  * [batch][h_idx][d_idx], w [batch][h_idx], k_pooled [batch][lmax/r][d_idx]

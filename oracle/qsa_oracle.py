@@ -377,6 +377,40 @@ def forward_prefill(q_bits, k_bits, v_bits, q_idx_bits, w, k_idx_bits, *, r: int
             "out": outs, "lse": lses}
 
 
+def forward_prefill_varlen(q_bits, k_bits, v_bits, q_idx_bits, w, k_idx_bits, cu_q, cu_k, *,
+                           r: int, budget: int, scale: Optional[float] = None,
+                           rows: Optional[Sequence[int]] = None) -> dict:
+    """QSA prefill of a packed batch ([MR] section 5.3 "Rollout & SGLang": packed THD
+    tensors). Sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 and key tokens
+    cu_k[b] .. cu_k[b+1]-1; its queries are its last tokens (row i of the sequence
+    at position lk_b - lq_b + i). Each sequence is an independent prefill: its blocks,
+    scores, selection (ids local to the sequence) and attention see only its own keys.
+    ``rows`` are packed query rows (default all). Returns the pooled keys of each
+    sequence and, per requested row in order: scores, selection, output and lse.
+    """
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    total_q = int(cu_q[-1])
+    rows = np.arange(total_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    seq_of = np.searchsorted(cu_q, rows, side="right") - 1
+    hq, d = q_bits.shape[1:]
+    n_sel = budget // r
+    out = {"pooled": [], "scores": [None] * len(rows), "sel": np.zeros((len(rows), n_sel), np.int64),
+           "out": np.zeros((len(rows), hq, d)), "lse": np.zeros((len(rows), hq))}
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        mine = np.nonzero(seq_of == b)[0]
+        res = forward_prefill(q_bits[q0:q1], k_bits[k0:k1], v_bits[k0:k1], q_idx_bits[q0:q1],
+                              np.asarray(w)[q0:q1], k_idx_bits[k0:k1], r=r, budget=budget,
+                              q_pos0=int((k1 - k0) - (q1 - q0)), scale=scale,
+                              rows=rows[mine] - q0)
+        out["pooled"].append(res["pooled"])
+        for j, m in enumerate(mine):
+            out["scores"][m] = res["scores"][j]
+            out["sel"][m], out["out"][m], out["lse"][m] = res["sel"][j], res["out"][j], res["lse"][j]
+    return out
+
+
 def forward_decode(q_bits, q_idx_bits, w, k_pooled_bits, seq_lens, fetch_kv, *, r: int,
                    budget: int, scale: Optional[float] = None) -> dict:
     """QSA decode: one new query token per sequence, at position seq_lens[b] - 1.

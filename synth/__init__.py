@@ -9,5 +9,7 @@ from .workloads import (  # noqa: F401
     Workload,
     bf16_bits,
     generate,
+    generate_varlen,
+    serving_lengths,
     workload,
 )

@@ -113,6 +113,8 @@ def _chunk_seed(ss: np.random.SeedSequence, chunk: int) -> int:
 
 def _fill_normal(out: torch.Tensor, ss: np.random.SeedSequence, scale: float) -> None:
     """Fill a bf16 tensor with bf16(N(0,1) * scale), one seeded draw per row chunk."""
+    if out.numel() == 0:
+        return
     flat = out.view(out.shape[0], -1) if out.dim() > 1 else out.view(1, -1)
     rows, cols = flat.shape
     rows_per_chunk = max(1, CHUNK_ELEMS // max(cols, 1))
@@ -228,4 +230,45 @@ def generate(wl: Workload, device="cpu", seq_lens=None) -> dict:
         seq_lens = [wl.lk] * b
     sl = torch.tensor(list(seq_lens), dtype=torch.int32, device=device)
     out.update(q=q, k_cache=kc, v_cache=vc, q_idx=q_idx, w=w, k_pooled=kp, seq_lens=sl)
+    return out
+
+
+def serving_lengths(n_seqs: int, total: int, lo: int, seed: int) -> list:
+    """A seeded length mix for a packed prefill batch: n_seqs lengths, each at least
+    ``lo``, summing to ``total``: Dirichlet(1, ..., 1) shares of the tokens above the
+    floor, rounded down, the remainder given to the last sequence."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    share = rng.dirichlet(np.ones(n_seqs))
+    extra = np.floor(share * (total - n_seqs * lo)).astype(np.int64)
+    lens = lo + extra
+    lens[-1] += total - int(lens.sum())
+    return [int(x) for x in lens]
+
+
+def generate_varlen(wl: Workload, lens, device="cpu") -> dict:
+    """Draw a packed (THD) batch: sequence b has lens[b] = (lq_b, lk_b), its queries
+    being its last lq_b tokens. Each sequence is drawn by ``generate`` as a prefill
+    workload of its own shapes (seed wl.seed * 1000 + b, no pooled prefix), and the
+    tensors are concatenated along the token axis. Returns q, k, v, q_idx, w, k_idx,
+    cu_q and cu_k (int32, on ``device``), the lengths, and each sequence's needle
+    rows as packed row indices."""
+    parts = []
+    for b, (lq, lk) in enumerate(lens):
+        wb = dataclasses.replace(wl, kind="prefill", batch=1, lq=int(lq), lk=int(lk),
+                                 q_pos0=int(lk) - int(lq), seed=wl.seed * 1000 + b,
+                                 pooled_prefix_blocks=0,
+                                 needle_spacing=(wl.needle_spacing
+                                                 if wl.needle_spacing and lk >= wl.needle_spacing
+                                                 else 0))
+        parts.append(generate(wb, device=device))
+    cu_q = np.concatenate([[0], np.cumsum([lq for lq, _ in lens])]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum([lk for _, lk in lens])]).astype(np.int32)
+    out = {name: torch.cat([p[name] for p in parts], dim=0)
+           for name in ("q", "k", "v", "q_idx", "w", "k_idx")}
+    out["cu_q"] = torch.from_numpy(cu_q).to(device)
+    out["cu_k"] = torch.from_numpy(cu_k).to(device)
+    out["lens"] = [(int(a), int(b)) for a, b in lens]
+    out["aligned_rows"] = np.concatenate(
+        [p["aligned_rows"] + cu_q[b] for b, p in enumerate(parts)]).astype(np.int64)
+    out["aligned_blocks"] = np.concatenate([p["aligned_blocks"] for p in parts]).astype(np.int64)
     return out

@@ -166,3 +166,37 @@ def test_warmup_validation(lib):
                                     FAKE, FAKE, FAKE, None, 0, None) == 1
     assert lib.qsa_index_scores_bwd(10, 4, 128, 4, FAKE, FAKE, FAKE, 25, 0, FAKE, 22, FAKE,
                                     FAKE, FAKE, None, 0, None) == 1  # ld < nblk
+
+
+def test_varlen_validation_and_workspace(lib):
+    f = ctypes.c_float(0.0625)
+
+    def sel_call(batch=2, cu_q=FAKE, cu_k=FAKE, max_lq=100, max_lk=200, h=4, di=128, r=4,
+                 budget=256, ws_bytes=1 << 40, kp=FAKE):
+        return lib.qsa_prefill_varlen_select(batch, cu_q, cu_k, max_lq, max_lk, h, di, r, budget,
+                                             FAKE, FAKE, FAKE, kp, FAKE, 64, FAKE, ws_bytes, None)
+
+    assert sel_call(batch=0) == 1
+    assert sel_call(cu_q=None) == 1 and "cu_seqlens" in _err(lib)
+    assert sel_call(max_lq=300) == 1                   # max_lq > max_lk
+    assert sel_call(r=3) == 2
+    assert sel_call(h=5) == 2
+    assert sel_call(budget=258) == 1
+    assert sel_call(kp=MISALIGNED) == 1 and "aligned" in _err(lib)
+    assert sel_call(max_lk=1 << 24) == 2               # 2^22 blocks and more
+    need = lib.qsa_prefill_varlen_workspace_bytes(2, 100, 200, 4, 256, 64)
+    # two sequences x 64 rows of 50 block scores (ld 52), fp32
+    assert need >= 2 * 64 * 52 * 4
+    assert sel_call(ws_bytes=need - 1) == 3 and "workspace" in _err(lib)
+
+    def attn_call(batch=2, total_q=100, hq=24, hkv=2, d=256, n_sel=64, scale=f, out=FAKE):
+        return lib.qsa_sparse_attn_varlen_fwd(batch, FAKE, FAKE, total_q, hq, hkv, d, 4, n_sel,
+                                              FAKE, FAKE, FAKE, FAKE, scale, out, None, None)
+
+    assert attn_call(hkv=5) == 1
+    assert attn_call(d=192) == 2
+    assert attn_call(n_sel=2048) == 2
+    assert attn_call(total_q=-1) == 1
+    assert attn_call(scale=ctypes.c_float(float("nan"))) == 1
+    assert attn_call(out=MISALIGNED) == 1
+    assert attn_call(total_q=0) == 0                   # nothing to do

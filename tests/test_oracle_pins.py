@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from oracle import qsa_oracle as O
-from synth import bf16_bits, generate, workload
+from synth import bf16_bits, generate, generate_varlen, workload
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -329,6 +329,73 @@ def test_chunked_prefill_equals_full_prefill_rows():
                               rows=np.arange(0, L - prefix, 5))
     np.testing.assert_array_equal(chunk["sel"], full["sel"])
     np.testing.assert_allclose(chunk["out"], full["out"], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------
+# Packed variable-length batches
+# ------------------------------------------------------------------------------------
+
+
+def _varlen_oracle(inp, budget, **kw):
+    return O.forward_prefill_varlen(
+        bf16_bits(inp["q"]), bf16_bits(inp["k"]), bf16_bits(inp["v"]), bf16_bits(inp["q_idx"]),
+        inp["w"].numpy(), bf16_bits(inp["k_idx"]), inp["cu_q"].numpy(), inp["cu_k"].numpy(),
+        r=4, budget=budget, **kw)
+
+
+def test_varlen_full_budget_equals_dense_attention_per_sequence():
+    # Budget above every length: each sequence is dense attention over its own keys,
+    # queries aligned to its last tokens (a prefix packed in for the second one).
+    lens = [(37, 37), (20, 53), (65, 65), (1, 6)]
+    wl = workload("tiny", hq=4, hkv=2, d=16, d_i=16, budget=256, seed=3, needle_spacing=0)
+    inp = generate_varlen(wl, lens)
+    res = _varlen_oracle(inp, 256)
+    q, k, v = (torch.from_numpy(O.bf16_to_f64(bf16_bits(inp[n]))) for n in ("q", "k", "v"))
+    cq, ck = inp["cu_q"].numpy(), inp["cu_k"].numpy()
+    scale = 1.0 / math.sqrt(wl.d)
+    for b, (lq, lk) in enumerate(lens):
+        qs = q[cq[b]:cq[b + 1]].permute(1, 0, 2)
+        ks = k[ck[b]:ck[b + 1]].permute(1, 0, 2).repeat_interleave(2, dim=0)
+        vs = v[ck[b]:ck[b + 1]].permute(1, 0, 2).repeat_interleave(2, dim=0)
+        allow = torch.arange(lk)[None, :] <= (lk - lq + torch.arange(lq))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, attn_mask=allow,
+                                                               scale=scale)
+        logits = torch.where(allow, scale * qs @ ks.transpose(1, 2), -torch.inf)
+        np.testing.assert_allclose(res["out"][cq[b]:cq[b + 1]], ref.permute(1, 0, 2).numpy(),
+                                   rtol=0, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][cq[b]:cq[b + 1]],
+                                   torch.logsumexp(logits, -1).T.numpy(), rtol=0, atol=1e-12)
+
+
+def test_varlen_sequences_are_isolated_and_rows_valid():
+    # Under a budget (selection active), changing every input of sequence 0 leaves the
+    # other sequences' results bit-identical; every row's selection is a valid one of
+    # its own sequence (local ids, own block, size, order).
+    lens = [(40, 40), (24, 64), (33, 33)]
+    wl = workload("tiny", hq=4, hkv=2, d=16, d_i=16, budget=16, seed=4, needle_spacing=0)
+    inp = generate_varlen(wl, lens)
+    res = _varlen_oracle(inp, 16)
+    alt = dict(inp)
+    g = torch.Generator().manual_seed(99)
+    for n in ("q", "k", "v", "q_idx", "k_idx"):
+        t = inp[n].clone()
+        end = int(inp["cu_q" if n in ("q", "q_idx") else "cu_k"][1])
+        t[:end] = torch.randn(t[:end].shape, generator=g).to(t.dtype)
+        alt[n] = t
+    res2 = _varlen_oracle(alt, 16)
+    first = int(inp["cu_q"][1])
+    assert not np.array_equal(res["out"][:first], res2["out"][:first])
+    np.testing.assert_array_equal(res["sel"][first:], res2["sel"][first:])
+    np.testing.assert_array_equal(res["out"][first:], res2["out"][first:])
+    cq = inp["cu_q"].numpy()
+    for b, (lq, lk) in enumerate(lens):
+        for i in range(lq):
+            t = lk - lq + i
+            own = t // 4
+            row = res["sel"][cq[b] + i]
+            kept = row[row >= 0]
+            assert len(kept) == min(4, own + 1) and kept[-1] == own
+            assert np.all(np.diff(kept) > 0) and np.all(row[len(kept):] == -1)
 
 
 # ------------------------------------------------------------------------------------
