@@ -38,6 +38,8 @@ def parse_args():
                    help="skip the sparse-attention backward measurement")
     p.add_argument("--no-warmup", action="store_true",
                    help="skip the indexer KL warm-up measurement")
+    p.add_argument("--no-paged", action="store_true",
+                   help="skip the decode step over a paged K/V cache")
     p.add_argument("--no-varlen", action="store_true",
                    help="skip the packed variable-length prefill batch")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -215,12 +217,40 @@ def bench_backward(torch, Q, wl, inp, plan, reps=2):
     return ms
 
 
-def bench_decode(args, torch, Q, wl, inp):
+def paged_copy(torch, kc, vc, page_size, seed=1):
+    """The caches [B, L, Hkv, d] scattered into pools of shuffled pages (the layout a
+    serving engine's page allocator leaves), and the block table."""
+    bsz, L, hkv, d = kc.shape
+    n_per = L // page_size
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    table = torch.randperm(bsz * n_per, generator=g).view(bsz, n_per).to(torch.int32)
+    table = table.to(kc.device)
+    slots = (table.long()[:, :, None] * page_size
+             + torch.arange(page_size, device=kc.device)).reshape(-1)
+    pools = []
+    for c in (kc, vc):
+        pool = torch.empty((bsz * L, hkv, d), dtype=c.dtype, device=c.device)
+        pool[slots] = c.reshape(-1, hkv, d)
+        pools.append(pool)
+    del slots
+    return pools[0], pools[1], table
+
+
+def bench_decode(args, torch, Q, wl, inp, paged=None):
+    """Seconds per decode step; with paged = (k_pool, v_pool, table, page_size) the
+    step reads K/V through the block table."""
     plan = Q.DecodePlan(wl.batch, wl.hq, wl.d, wl.lk, wl.budget, device=inp["q"].device)
 
     def step():
-        Q.qsa_decode_forward(inp["q"], inp["q_idx"], inp["w"], inp["k_pooled"], inp["k_cache"],
-                             inp["v_cache"], inp["seq_lens"], budget=wl.budget, plan=plan)
+        if paged is None:
+            Q.qsa_decode_forward(inp["q"], inp["q_idx"], inp["w"], inp["k_pooled"],
+                                 inp["k_cache"], inp["v_cache"], inp["seq_lens"],
+                                 budget=wl.budget, plan=plan)
+        else:
+            Q.qsa_decode_forward_paged(inp["q"], inp["q_idx"], inp["w"], inp["k_pooled"],
+                                       paged[0], paged[1], paged[2], inp["seq_lens"],
+                                       budget=wl.budget, page_size=paged[3], lmax=wl.lk,
+                                       plan=plan)
 
     for _ in range(5):
         step()
@@ -489,6 +519,22 @@ def main():
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": d_bytes / s_dec / 1e9 / HBM_PEAK_GBS,
                                        "algorithmic_bytes_per_step": d_bytes}}
+        if not args.no_paged:
+            P = 64
+            kp, vp, table = paged_copy(torch, dinp["k_cache"], dinp["v_cache"], P)
+            del dinp["k_cache"], dinp["v_cache"]
+            torch.cuda.empty_cache()
+            s_pg = bench_decode(args, torch, Q, dwl, dinp, paged=(kp, vp, table, P))
+            progress(f"paged decode: {s_pg * 1e6:.1f} us per step")
+            line["decode_paged"] = {
+                "workload": f"{dwl.name}, K/V in shuffled pages of {P} tokens",
+                "page_size": P, "value": dwl.batch / s_pg, "unit": "tokens/s",
+                "ms_per_step": s_pg * 1e3,
+                "roofline": {"bound": "hbm", "achieved": d_bytes / s_pg / 1e9,
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": d_bytes / s_pg / 1e9 / HBM_PEAK_GBS,
+                             "algorithmic_bytes_per_step": d_bytes}}
+            del kp, vp, table
         del dinp
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -11,6 +11,7 @@ from .ops import (  # noqa: F401
     QSAError,
     abi_version,
     qsa_decode_forward,
+    qsa_decode_forward_paged,
     qsa_index_scores,
     qsa_index_scores_bwd,
     qsa_indexer_kl_loss,

@@ -49,6 +49,10 @@ SIGNATURES = {
                                         _P, _P, _P]),
     "qsa_prefill_varlen_forward": (_I, [_I, _P, _P, _L, _L, _L, _I, _I, _I, _I, _I, _I, _I, _P,
                                         _P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _L, _P, _Z, _P]),
+    "qsa_sparse_attn_decode_paged": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _L, _I, _P, _L,
+                                          _L, _P, _P, _F, _P, _P, _P, _Z, _P]),
+    "qsa_decode_forward_paged": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _L, _P,
+                                      _P, _L, _I, _P, _L, _L, _P, _F, _P, _P, _P, _P, _Z, _P]),
     "qsa_probe_gather": (_I, [_P, _Z, _P, _L, _I, _P, _P]),
     "qsa_decode_workspace_bytes": (_Z, [_I, _I, _I, _L, _I, _I]),
     "qsa_decode_forward": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _L, _P, _P, _L,

@@ -60,26 +60,41 @@ __device__ __forceinline__ int pick4(int b0, int b1, int b2, int b3, int i) {
   return i == 0 ? b0 : (i == 1 ? b1 : (i == 2 ? b2 : b3));
 }
 
+// Row of kb/vb holding token `i` (0..3) of kept block b: the token clamped to the
+// query's position t, at that block's place p (in units of 4 rows) in a paged pool, or
+// at its own position in a contiguous cache. Padding (b < 0) reads row 0. For a paged
+// pool the offset stays inside the block, so a block after t (not a valid selection)
+// still reads inside the pool.
+__device__ __forceinline__ int64_t attn_row(int b, int p, int i, int64_t t, bool paged) {
+  if (b < 0) return 0;
+  const int64_t tl = min((int64_t)b * 4 + i, t);
+  if (!paged) return tl;
+  const int64_t off = tl - (int64_t)b * 4;
+  return (int64_t)p * 4 + (off < 0 ? 0 : off);
+}
+
 // Issues the loads of one step. Block ids < 0 (padding) and keys after position t
-// read an in-bounds row that the softmax masks.
+// read an in-bounds row that the softmax masks. b4 holds the kept blocks' ids (token
+// positions); with a paged pool, p4 holds their places in it (units of 4 rows).
 template <int D>
 __device__ __forceinline__ void attn_load_step(AttnStep<D>& st, const int (&b4)[4],
+                                               const int (&p4)[4], bool paged,
                                                const uint16_t* kb, const uint16_t* vb,
                                                int64_t kstride, int g, int64_t t, int c16,
                                                int quad) {
   // K rows: key (c16) = token (c16 & 3) of block slot (c16 >> 2).
   const int bk = pick4(b4[0], b4[1], b4[2], b4[3], c16 >> 2);
-  int64_t tk = (int64_t)bk * 4 + (c16 & 3);
-  tk = bk < 0 ? 0 : min(tk, t);
+  const int pk = pick4(p4[0], p4[1], p4[2], p4[3], c16 >> 2);
+  const int64_t tk = attn_row(bk, pk, c16 & 3, t, paged);
   const uint16_t* kp = kb + tk * kstride + g * D + quad * 8;
 #pragma unroll
   for (int c = 0; c < AttnStep<D>::NC; ++c) st.Kc[c] = ld16(kp + c * 32);
   // V rows: this lane's 4 keys are the 4 tokens of block slot `quad`.
   const int bv = pick4(b4[0], b4[1], b4[2], b4[3], quad);
+  const int pv = pick4(p4[0], p4[1], p4[2], p4[3], quad);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    int64_t tv = (int64_t)bv * 4 + kk;
-    tv = bv < 0 ? 0 : min(tv, t);
+    const int64_t tv = attn_row(bv, pv, kk, t, paged);
     const uint16_t* vp = vb + tv * kstride + g * D + c16 * 8;
 #pragma unroll
     for (int hf = 0; hf < AttnStep<D>::NH; ++hf) st.Vr[kk][hf] = ld16(vp + hf * 128);
@@ -201,7 +216,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
     for (int j = 0; j < 4; ++j) b4[j] = (4 * s + j < a.n_sel) ? srow[4 * s + j] : -1;
     if (b4[0] < 0) break;  // -1 padding reached
     AttnStep<D> st;
-    attn_load_step<D>(st, b4, kb, vb, kstride, g, t, c16, quad);
+    attn_load_step<D>(st, b4, b4, false, kb, vb, kstride, g, t, c16, quad);
     attn_compute_step<D>(st, b4, Qc, O, m_run, l_run, a.scale_log2, t, quad);
   }
 
@@ -258,20 +273,40 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(AttnArgs a) {
   const int g = rem / a.n_split;
   const int wg_split = rem - g * a.n_split;
   const int64_t t = (int64_t)a.seq_lens[row] - 1;
-  const uint16_t* kb = a.k + row * a.cache_bs;
-  const uint16_t* vb = a.v + row * a.cache_bs;
+  const bool paged = a.block_table != nullptr;
+  const uint16_t* kb = paged ? a.k : a.k + row * a.cache_bs;
+  const uint16_t* vb = paged ? a.v : a.v + row * a.cache_bs;
   const int32_t* srow = a.sel + row * a.n_sel;
   const int64_t kstride = (int64_t)a.hkv * D;
   const int s_begin = (wg_split * 4 + wave) * SPS;
 
-  int ids[SPS][4];
+  // ids: the kept blocks; pids: where their rows sit (paged: page from the block table,
+  // clamped to the table and the pool, times blocks per page, plus the block's offset).
+  int ids[SPS][4], pids[SPS][4];
 #pragma unroll
   for (int si = 0; si < SPS; ++si)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = 4 * (s_begin + si) + j;
       ids[si][j] = (t >= 0 && k < a.n_sel) ? srow[k] : -1;
+      pids[si][j] = ids[si][j];
     }
+  if (paged) {
+    const int32_t* trow = a.block_table + row * a.table_stride;
+    const int pb = a.page_blocks;
+#pragma unroll
+    for (int si = 0; si < SPS; ++si)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int b = ids[si][j];
+        if (b >= 0) {
+          const int pi = b / pb;
+          int pg = trow[pi < a.table_stride ? pi : a.table_stride - 1];
+          pg = pg < 0 ? 0 : (pg < a.num_pages ? pg : a.num_pages - 1);
+          pids[si][j] = pg * pb + (b - pi * pb);
+        }
+      }
+  }
 
   uint4 Qc[D / 32];
   attn_load_q<D>(Qc, a.q + row * (int64_t)a.hq * D, g, G, c16, quad);
@@ -283,13 +318,17 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(AttnArgs a) {
   // Loads are issued for every step (padding reads an in-bounds row); a step whose
   // first block is padding is skipped (the padding is at the end of the row).
   AttnStep<D> A, B;
-  attn_load_step<D>(A, ids[0], kb, vb, kstride, g, t, c16, quad);
+  attn_load_step<D>(A, ids[0], pids[0], paged, kb, vb, kstride, g, t, c16, quad);
 #pragma unroll
   for (int si = 0; si < SPS; si += 2) {
-    if (si + 1 < SPS) attn_load_step<D>(B, ids[si + 1], kb, vb, kstride, g, t, c16, quad);
+    if (si + 1 < SPS)
+      attn_load_step<D>(B, ids[si + 1], pids[si + 1], paged, kb, vb, kstride, g, t, c16,
+                        quad);
     if (ids[si][0] >= 0)
       attn_compute_step<D>(A, ids[si], Qc, O, m_run, l_run, a.scale_log2, t, quad);
-    if (si + 2 < SPS) attn_load_step<D>(A, ids[si + 2], kb, vb, kstride, g, t, c16, quad);
+    if (si + 2 < SPS)
+      attn_load_step<D>(A, ids[si + 2], pids[si + 2], paged, kb, vb, kstride, g, t, c16,
+                        quad);
     if (si + 1 < SPS && ids[si + 1][0] >= 0)
       attn_compute_step<D>(B, ids[si + 1], Qc, O, m_run, l_run, a.scale_log2, t, quad);
   }

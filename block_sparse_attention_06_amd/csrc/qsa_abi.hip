@@ -402,12 +402,38 @@ size_t qsa_sparse_attn_decode_workspace_bytes(int batch, int hq, int d, int n_se
   return align256(slots * d * sizeof(float)) + align256(slots * 2 * sizeof(float));
 }
 
-qsa_status qsa_sparse_attn_decode(int batch, int hq, int hkv, int d, int r, int n_sel,
-                                  const void* q, const void* k_cache, const void* v_cache,
-                                  int64_t cache_batch_stride, int64_t lmax,
-                                  const int32_t* seq_lens, const int32_t* sel,
-                                  float softmax_scale, void* out, float* lse, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+namespace {
+
+// A paged K/V cache: pools of num_pages pages of page_size tokens ([slot][hkv][d],
+// slot = page * page_size + offset); page p of sequence s is table[s * table_stride + p].
+struct PagedKV {
+  const int32_t* table;
+  int64_t table_stride;
+  int page_size;
+  int64_t num_pages;
+};
+
+qsa_status check_paged(const PagedKV& p, int r, int64_t lmax) {
+  QSA_REQUIRE(p.table, QSA_ERR_INVALID_ARGUMENT, "null block table");
+  QSA_REQUIRE(p.page_size >= r && p.page_size % r == 0 && p.page_size <= (1 << 20),
+              QSA_ERR_UNSUPPORTED, "page_size=%d: a multiple of r=%d up to 2^20 (a block of r "
+              "tokens must not straddle pages)", p.page_size, r);
+  QSA_REQUIRE(p.num_pages >= 1 && p.num_pages * (p.page_size / r) < ((int64_t)1 << 31),
+              QSA_ERR_INVALID_ARGUMENT, "num_pages=%lld", (long long)p.num_pages);
+  QSA_REQUIRE(p.table_stride >= (lmax + p.page_size - 1) / p.page_size,
+              QSA_ERR_INVALID_ARGUMENT,
+              "table_stride=%lld holds fewer pages than lmax=%lld tokens need",
+              (long long)p.table_stride, (long long)lmax);
+  return QSA_OK;
+}
+
+qsa_status sparse_attn_decode_impl(int batch, int hq, int hkv, int d, int r, int n_sel,
+                                   const void* q, const void* k_cache, const void* v_cache,
+                                   int64_t cache_batch_stride, int64_t lmax,
+                                   const PagedKV* paged, const int32_t* seq_lens,
+                                   const int32_t* sel, float softmax_scale, void* out,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
   QSA_TRY(check_r(r));
   QSA_TRY(check_attn_shape(hq, hkv, d));
   QSA_REQUIRE(n_sel >= 1 && n_sel <= 1024, QSA_ERR_UNSUPPORTED, "n_sel=%d: supported 1..1024",
@@ -419,9 +445,14 @@ qsa_status qsa_sparse_attn_decode(int batch, int hq, int hkv, int d, int r, int 
               "null tensor pointer");
   QSA_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out),
               QSA_ERR_INVALID_ARGUMENT, "q, caches and out must be 16-byte aligned");
-  QSA_REQUIRE(batch == 1 || (cache_batch_stride % 8 == 0 &&
-                             cache_batch_stride >= lmax * (int64_t)hkv * d),
-              QSA_ERR_INVALID_ARGUMENT, "cache_batch_stride=%lld", (long long)cache_batch_stride);
+  if (paged) {
+    QSA_TRY(check_paged(*paged, r, lmax));
+  } else {
+    QSA_REQUIRE(batch == 1 || (cache_batch_stride % 8 == 0 &&
+                               cache_batch_stride >= lmax * (int64_t)hkv * d),
+                QSA_ERR_INVALID_ARGUMENT, "cache_batch_stride=%lld",
+                (long long)cache_batch_stride);
+  }
   const size_t need = qsa_sparse_attn_decode_workspace_bytes(batch, hq, d, n_sel);
   QSA_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), QSA_ERR_WORKSPACE,
               "decode workspace: need %zu bytes (16-byte aligned), got %zu", need,
@@ -449,8 +480,41 @@ qsa_status qsa_sparse_attn_decode(int batch, int hq, int hkv, int d, int r, int 
                                        align256(slots * d * sizeof(float)));
   a.n_split = ns;
   a.steps_per_split = qsa::decode_steps_per_split(n_sel);
+  if (paged) {
+    a.block_table = paged->table;
+    a.table_stride = paged->table_stride;
+    a.page_blocks = paged->page_size / r;
+    a.num_pages = (int)paged->num_pages;
+  }
   return hip_status(qsa::launch_sparse_attn_decode(a, static_cast<hipStream_t>(stream)),
-                    "qsa_sparse_attn_decode launch");
+                    "decode attention launch");
+}
+
+}  // namespace
+
+qsa_status qsa_sparse_attn_decode(int batch, int hq, int hkv, int d, int r, int n_sel,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  int64_t cache_batch_stride, int64_t lmax,
+                                  const int32_t* seq_lens, const int32_t* sel,
+                                  float softmax_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return sparse_attn_decode_impl(batch, hq, hkv, d, r, n_sel, q, k_cache, v_cache,
+                                 cache_batch_stride, lmax, nullptr, seq_lens, sel,
+                                 softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+qsa_status qsa_sparse_attn_decode_paged(int batch, int hq, int hkv, int d, int r, int n_sel,
+                                        const void* q, const void* k_pool, const void* v_pool,
+                                        int64_t num_pages, int page_size,
+                                        const int32_t* block_table, int64_t table_stride,
+                                        int64_t lmax, const int32_t* seq_lens,
+                                        const int32_t* sel, float softmax_scale, void* out,
+                                        float* lse, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  const PagedKV pk{block_table, table_stride, page_size, num_pages};
+  return sparse_attn_decode_impl(batch, hq, hkv, d, r, n_sel, q, k_pool, v_pool, 0, lmax, &pk,
+                                 seq_lens, sel, softmax_scale, out, lse, workspace,
+                                 workspace_bytes, stream);
 }
 
 // ---- whole prefill path ----
@@ -705,15 +769,22 @@ size_t qsa_decode_workspace_bytes(int batch, int hq, int d, int64_t lmax, int r,
   return sc + tk + qsa_sparse_attn_decode_workspace_bytes(batch, hq, d, budget_tokens / r);
 }
 
-qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int d_idx, int r,
-                              int budget_tokens, const void* q, const void* q_idx,
-                              const float* w, const void* k_pooled,
-                              int64_t k_pooled_batch_stride, const void* k_cache,
-                              const void* v_cache, int64_t cache_batch_stride, int64_t lmax,
-                              const int32_t* seq_lens, float softmax_scale, int32_t* sel,
-                              void* out, float* lse, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+namespace {
+
+qsa_status decode_forward_impl(int batch, int hq, int hkv, int d, int h_idx, int d_idx, int r,
+                               int budget_tokens, const void* q, const void* q_idx,
+                               const float* w, const void* k_pooled,
+                               int64_t k_pooled_batch_stride, const void* k_cache,
+                               const void* v_cache, int64_t cache_batch_stride,
+                               const PagedKV* paged, int64_t lmax, const int32_t* seq_lens,
+                               float softmax_scale, int32_t* sel, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   QSA_TRY(check_r(r));
+  if (paged) QSA_TRY(check_paged(*paged, r, lmax));
+  QSA_REQUIRE(q && k_cache && v_cache && out && aligned16(q) && aligned16(k_cache) &&
+                  aligned16(v_cache) && aligned16(out),
+              QSA_ERR_INVALID_ARGUMENT, "q, caches and out must be non-null and 16-byte aligned");
+  QSA_REQUIRE(isfinite(softmax_scale), QSA_ERR_INVALID_ARGUMENT, "softmax_scale not finite");
   QSA_TRY(check_budget(budget_tokens, r));
   QSA_TRY(check_indexer_shape(h_idx, d_idx));
   QSA_TRY(check_attn_shape(hq, hkv, d));
@@ -755,9 +826,46 @@ qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int 
     QSA_TRY(hip_status(qsa::launch_index_scores(sa, s), "decode score scan launch"));
     QSA_TRY(hip_status(qsa::launch_topk_blocks(ta, tk, s), "decode top-k launch"));
   }
-  return qsa_sparse_attn_decode(batch, hq, hkv, d, r, budget_tokens / r, q, k_cache, v_cache,
-                                cache_batch_stride, lmax, seq_lens, sel, softmax_scale, out, lse,
-                                tk + tk_bytes, workspace_bytes - sc_bytes - tk_bytes, stream);
+  return sparse_attn_decode_impl(batch, hq, hkv, d, r, budget_tokens / r, q, k_cache, v_cache,
+                                 cache_batch_stride, lmax, paged, seq_lens, sel, softmax_scale,
+                                 out, lse, tk + tk_bytes, workspace_bytes - sc_bytes - tk_bytes,
+                                 stream);
+}
+
+}  // namespace
+
+qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int d_idx, int r,
+                              int budget_tokens, const void* q, const void* q_idx,
+                              const float* w, const void* k_pooled,
+                              int64_t k_pooled_batch_stride, const void* k_cache,
+                              const void* v_cache, int64_t cache_batch_stride, int64_t lmax,
+                              const int32_t* seq_lens, float softmax_scale, int32_t* sel,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (batch > 1)
+    QSA_REQUIRE(cache_batch_stride % 8 == 0 && cache_batch_stride >= lmax * (int64_t)hkv * d,
+                QSA_ERR_INVALID_ARGUMENT, "cache_batch_stride=%lld",
+                (long long)cache_batch_stride);
+  return decode_forward_impl(batch, hq, hkv, d, h_idx, d_idx, r, budget_tokens, q, q_idx, w,
+                             k_pooled, k_pooled_batch_stride, k_cache, v_cache,
+                             cache_batch_stride, nullptr, lmax, seq_lens, softmax_scale, sel,
+                             out, lse, workspace, workspace_bytes, stream);
+}
+
+qsa_status qsa_decode_forward_paged(int batch, int hq, int hkv, int d, int h_idx, int d_idx,
+                                    int r, int budget_tokens, const void* q, const void* q_idx,
+                                    const float* w, const void* k_pooled,
+                                    int64_t k_pooled_batch_stride, const void* k_pool,
+                                    const void* v_pool, int64_t num_pages, int page_size,
+                                    const int32_t* block_table, int64_t table_stride,
+                                    int64_t lmax, const int32_t* seq_lens, float softmax_scale,
+                                    int32_t* sel, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const PagedKV pk{block_table, table_stride, page_size, num_pages};
+  return decode_forward_impl(batch, hq, hkv, d, h_idx, d_idx, r, budget_tokens, q, q_idx, w,
+                             k_pooled, k_pooled_batch_stride, k_pool, v_pool, 0, &pk, lmax,
+                             seq_lens, softmax_scale, sel, out, lse, workspace, workspace_bytes,
+                             stream);
 }
 
 // ---- measurement aid ----

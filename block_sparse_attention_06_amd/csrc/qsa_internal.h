@@ -131,6 +131,12 @@ struct AttnArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int batch_vl;
+  // decode from a paged cache: k / v are pools of num_pages pages of page_blocks
+  // 4-token blocks; page p of sequence s is block_table[s * table_stride + p]
+  const int32_t* block_table;
+  int64_t table_stride;
+  int page_blocks;
+  int num_pages;
 };
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream);
 // Rows per launch of launch_sparse_attn_fwd on the current device; -1 if unknown.

@@ -471,6 +471,36 @@ def qsa_decode_forward(q, q_idx, w, k_pooled, k_cache, v_cache, seq_lens, *, bud
     return plan.out, plan.lse, plan.sel
 
 
+def qsa_decode_forward_paged(q, q_idx, w, k_pooled, k_pool, v_pool, block_table, seq_lens, *,
+                             budget: int, page_size: int, lmax: Optional[int] = None,
+                             scale: Optional[float] = None, r: int = 4,
+                             plan: Optional[DecodePlan] = None):
+    """Whole decode step over a paged K/V cache. k_pool/v_pool [num_pages*page_size,Hkv,d],
+    block_table int32 [B, pages per sequence] (page ids), k_pooled [B,Lmax/r,d_I];
+    lmax defaults to page_size * block_table.shape[1]. Returns (out, lse, sel)."""
+    q_idx = q_idx.reshape(q_idx.shape[0], q_idx.shape[-2], q_idx.shape[-1])
+    w = w.reshape(w.shape[0], w.shape[-1])
+    for name, t, dt in (("q", q, torch.bfloat16), ("q_idx", q_idx, torch.bfloat16),
+                        ("w", w, torch.float32), ("k_pooled", k_pooled, torch.bfloat16),
+                        ("k_pool", k_pool, torch.bfloat16), ("v_pool", v_pool, torch.bfloat16),
+                        ("block_table", block_table, torch.int32),
+                        ("seq_lens", seq_lens, torch.int32)):
+        _need(t, name, dt, q.device)
+    bsz, hq, d = q.shape
+    slots, hkv, _ = k_pool.shape
+    _, h_idx, d_idx = q_idx.shape
+    lmax = page_size * block_table.shape[1] if lmax is None else lmax
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if plan is None:
+        plan = DecodePlan(bsz, hq, d, lmax, budget, r=r, device=q.device)
+    _call("qsa_decode_forward_paged", bsz, hq, hkv, d, h_idx, d_idx, r, budget, _ptr(q),
+          _ptr(q_idx), _ptr(w), _ptr(k_pooled), k_pooled.stride(0), _ptr(k_pool), _ptr(v_pool),
+          slots // page_size, page_size, _ptr(block_table), block_table.stride(0), lmax,
+          _ptr(seq_lens), scale, _ptr(plan.sel), _ptr(plan.out), _ptr(plan.lse), _ptr(plan.ws),
+          plan.ws_bytes, _stream(q))
+    return plan.out, plan.lse, plan.sel
+
+
 def qsa_probe_gather(buf: torch.Tensor, block_ids: torch.Tensor, steps: int, sink: torch.Tensor):
     """Measurement aid: read random (or given) 4 KiB blocks of `buf` (see include/qsa.h).
 

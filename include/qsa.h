@@ -331,6 +331,40 @@ qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int 
                               void* stream);
 
 /*
+ * Decode from a PAGED K/V cache (serving engines keep the cache in fixed-size pages
+ * [MR5]): the same computation as qsa_sparse_attn_decode / qsa_decode_forward, with
+ * the K/V rows of token j of sequence s at pool slot
+ *   block_table[s * table_stride + j / page_size] * page_size + j % page_size.
+ *   k_pool, v_pool  bf16 [num_pages * page_size][hkv][d]
+ *   page_size       tokens per page, a multiple of r (a block never straddles pages)
+ *   block_table     device int32 [batch][table_stride], table_stride >=
+ *                   ceil(lmax / page_size); entries outside [0, num_pages) are clamped
+ *                   into it (wrong but in-bounds reads: the caller keeps them valid)
+ * The pooled-key cache keeps its per-sequence layout ([batch][lmax/r][d_idx] with
+ * k_pooled_batch_stride). Each kept block's page is looked up once, when the decode
+ * attention reads its block ids; every other argument, the workspace and the errors
+ * are those of the contiguous calls, plus QSA_ERR_UNSUPPORTED for a page size that is
+ * not a multiple of r.
+ */
+qsa_status qsa_sparse_attn_decode_paged(int batch, int hq, int hkv, int d, int r, int n_sel,
+                                        const void* q, const void* k_pool, const void* v_pool,
+                                        int64_t num_pages, int page_size,
+                                        const int32_t* block_table, int64_t table_stride,
+                                        int64_t lmax, const int32_t* seq_lens,
+                                        const int32_t* sel, float softmax_scale, void* out,
+                                        float* lse, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+qsa_status qsa_decode_forward_paged(int batch, int hq, int hkv, int d, int h_idx, int d_idx,
+                                    int r, int budget_tokens, const void* q, const void* q_idx,
+                                    const float* w, const void* k_pooled,
+                                    int64_t k_pooled_batch_stride, const void* k_pool,
+                                    const void* v_pool, int64_t num_pages, int page_size,
+                                    const int32_t* block_table, int64_t table_stride,
+                                    int64_t lmax, const int32_t* seq_lens, float softmax_scale,
+                                    int32_t* sel, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * Measurement aid, not part of QSA: the gather ceiling of the memory system for the
  * access pattern of the attention stage. n_waves waves each read `steps` x 4 blocks
  * of 4 KiB from buf, block j of wave w step s at buf + 4096 * block_ids[(w*steps+s)*4+j];

@@ -411,6 +411,19 @@ def forward_prefill_varlen(q_bits, k_bits, v_bits, q_idx_bits, w, k_idx_bits, cu
     return out
 
 
+def paged_fetcher(k_pool_bits, v_pool_bits, block_table, page_size: int):
+    """``fetch_kv(b, tokens)`` for a paged K/V cache: token j of sequence b sits at pool
+    slot block_table[b][j // page_size] * page_size + j % page_size (pools
+    [n_slots, Hkv, d] of raw bf16 bits)."""
+    table = np.asarray(block_table, dtype=np.int64)
+
+    def fetch(b: int, tokens: np.ndarray):
+        tokens = np.asarray(tokens, dtype=np.int64)
+        slots = table[b, tokens // page_size] * page_size + tokens % page_size
+        return bf16_to_f64(k_pool_bits[slots]), bf16_to_f64(v_pool_bits[slots])
+    return fetch
+
+
 def forward_decode(q_bits, q_idx_bits, w, k_pooled_bits, seq_lens, fetch_kv, *, r: int,
                    budget: int, scale: Optional[float] = None) -> dict:
     """QSA decode: one new query token per sequence, at position seq_lens[b] - 1.

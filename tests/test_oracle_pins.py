@@ -398,6 +398,40 @@ def test_varlen_sequences_are_isolated_and_rows_valid():
             assert np.all(np.diff(kept) > 0) and np.all(row[len(kept):] == -1)
 
 
+def test_paged_fetcher_matches_contiguous_cache():
+    # Scatter a contiguous cache into randomly ordered pages (spare pages hold noise):
+    # the paged fetcher returns the contiguous rows, and decode through it is identical.
+    rng = np.random.default_rng(8)
+    bsz, lmax, hkv, d, P = 3, 96, 2, 8, 16
+    kc = _bits(rng.standard_normal((bsz, lmax, hkv, d)))
+    vc = _bits(rng.standard_normal((bsz, lmax, hkv, d)))
+    n_pages = bsz * lmax // P + 5
+    perm = rng.permutation(n_pages)[: bsz * lmax // P].reshape(bsz, lmax // P)
+    kp_pool = _bits(rng.standard_normal((n_pages * P, hkv, d)))
+    vp_pool = _bits(rng.standard_normal((n_pages * P, hkv, d)))
+    for b in range(bsz):
+        for p in range(lmax // P):
+            kp_pool[perm[b, p] * P:(perm[b, p] + 1) * P] = kc[b, p * P:(p + 1) * P]
+            vp_pool[perm[b, p] * P:(perm[b, p] + 1) * P] = vc[b, p * P:(p + 1) * P]
+    fetch = O.paged_fetcher(kp_pool, vp_pool, perm, P)
+    toks = rng.choice(lmax, 40, replace=False)
+    for b in range(bsz):
+        kr, vr = fetch(b, toks)
+        np.testing.assert_array_equal(kr, O.bf16_to_f64(kc[b, toks]))
+        np.testing.assert_array_equal(vr, O.bf16_to_f64(vc[b, toks]))
+    q = _bits(rng.standard_normal((bsz, 4, d)))
+    qi = _bits(rng.standard_normal((bsz, 2, 8)))
+    w = rng.uniform(size=(bsz, 2))
+    kpool = _bits(rng.standard_normal((bsz, lmax // 4, 8)))
+    lens = np.array([96, 61, 7])
+    ref = O.forward_decode(q, qi, w, kpool, lens,
+                           lambda b, t: (O.bf16_to_f64(kc[b, t]), O.bf16_to_f64(vc[b, t])),
+                           r=4, budget=32)
+    got = O.forward_decode(q, qi, w, kpool, lens, fetch, r=4, budget=32)
+    np.testing.assert_array_equal(got["sel"], ref["sel"])
+    np.testing.assert_array_equal(got["out"], ref["out"])
+
+
 # ------------------------------------------------------------------------------------
 # Backward of the sparse attention over a fixed selection
 # ------------------------------------------------------------------------------------
