@@ -355,6 +355,35 @@ def bench_varlen(torch, Q, n_seqs=16, total=131072, floor=2048, reps=3):
                                    "algorithmic_bytes_per_call": a_bytes}}
 
 
+def bench_pool_encoding(torch, Q, n_tok=1 << 20, d_i=128, rope_dim=64, reps=5):
+    """Pooling of 1M raw indexer keys (262144 blocks), plain and with the rotary
+    encoding of the pooled keys fused in; HBM roofline on read + write bytes."""
+    import torch as _t
+    g = _t.Generator(device="cuda").manual_seed(17)
+    k = (_t.randn((n_tok, d_i), generator=g, device="cuda") / math.sqrt(d_i)).to(_t.bfloat16)
+    out = _t.empty((n_tok // 4, d_i), dtype=_t.bfloat16, device="cuda")
+    ms = {}
+    for name, pe in (("plain", None), ("encoded", (rope_dim, 1.0e6))):
+        Q.qsa_pool_keys(k, out=out, pe=pe)
+        _t.cuda.synchronize()
+        a, b = _t.cuda.Event(enable_timing=True), _t.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            Q.qsa_pool_keys(k, out=out, pe=pe)
+        b.record()
+        _t.cuda.synchronize()
+        ms[name] = a.elapsed_time(b) / reps
+    nbytes = n_tok * d_i * 2 + (n_tok // 4) * d_i * 2
+    del k, out
+    return {"workload": f"{n_tok} raw indexer keys, d_I {d_i}, r 4; encoding rope_dim "
+                        f"{rope_dim}", "plain_us": ms["plain"] * 1e3,
+            "encoded_us": ms["encoded"] * 1e3,
+            "roofline": {"bound": "hbm", "achieved": nbytes / ms["encoded"] / 1e6,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": nbytes / ms["encoded"] / 1e6 / HBM_PEAK_GBS,
+                         "algorithmic_bytes_per_call": nbytes}}
+
+
 def cpu_baseline(wl, inp, budget_s):
     """The oracle, as it stands, on evenly spread query rows of the same workload."""
     import numpy as np
@@ -500,6 +529,9 @@ def main():
     if not args.no_warmup:
         line["indexer_warmup"] = bench_warmup(torch, Q)
         progress("indexer warm-up done")
+    line["pool_encoding"] = bench_pool_encoding(torch, Q)
+    progress(f"pooling: {line['pool_encoding']['plain_us']:.1f} us plain, "
+             f"{line['pool_encoding']['encoded_us']:.1f} us encoded")
     if not args.no_varlen:
         line["varlen"] = bench_varlen(torch, Q)
         progress(f"varlen: {line['varlen']['ms']:.2f} ms per packed batch")

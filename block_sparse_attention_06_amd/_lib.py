@@ -20,6 +20,7 @@ SIGNATURES = {
     "qsa_abi_version": (_I, []),
     "qsa_last_error": (ctypes.c_char_p, []),
     "qsa_pool_keys": (_I, [_P, _L, _L, _I, _I, _P, _L, _P]),
+    "qsa_pool_keys_pe": (_I, [_P, _L, _L, _I, _I, _L, _P, _P, _L, _P]),
     "qsa_index_scores": (_I, [_I, _L, _I, _I, _I, _P, _L, _P, _L, _P, _L, _L, _L, _P, _P, _L,
                               _L, _P]),
     "qsa_topk_workspace_bytes": (_Z, [_I, _L, _L, _I, _I]),
@@ -39,16 +40,17 @@ SIGNATURES = {
                                     _P, _P, _Z, _P]),
     "qsa_prefill_workspace_bytes": (_Z, [_L, _L, _I, _I, _L]),
     "qsa_prefill_select": (_I, [_L, _L, _L, _I, _I, _I, _I, _P, _P, _P, _L, _P, _P, _P, _L, _P,
-                                _Z, _P]),
+                                _Z, _P, _P]),
     "qsa_prefill_forward": (_I, [_L, _L, _L, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
-                                 _L, _P, _P, _F, _P, _P, _P, _L, _P, _Z, _P]),
+                                 _L, _P, _P, _F, _P, _P, _P, _L, _P, _Z, _P, _P]),
     "qsa_prefill_varlen_workspace_bytes": (_Z, [_I, _L, _L, _I, _I, _L]),
     "qsa_prefill_varlen_select": (_I, [_I, _P, _P, _L, _L, _I, _I, _I, _I, _P, _P, _P, _P, _P,
-                                       _L, _P, _Z, _P]),
+                                       _L, _P, _Z, _P, _P]),
     "qsa_sparse_attn_varlen_fwd": (_I, [_I, _P, _P, _L, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F,
                                         _P, _P, _P]),
     "qsa_prefill_varlen_forward": (_I, [_I, _P, _P, _L, _L, _L, _I, _I, _I, _I, _I, _I, _I, _P,
-                                        _P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _L, _P, _Z, _P]),
+                                        _P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _L, _P, _Z, _P,
+                                        _P]),
     "qsa_sparse_attn_decode_paged": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _L, _I, _P, _L,
                                           _L, _P, _P, _F, _P, _P, _P, _Z, _P]),
     "qsa_decode_forward_paged": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _L, _P,

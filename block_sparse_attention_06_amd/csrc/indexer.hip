@@ -27,45 +27,100 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
   return __float_as_uint((float)y) >> 16;  // y is exact in bf16, hence in fp32
 }
 
-// 8 columns c..c+7 of pooled block b: the mean of keys b*r .. b*r+r-1 (row stride ks).
-__device__ __forceinline__ void pool_block8(const uint16_t* __restrict__ k, int64_t ks, int64_t b,
-                                            int c, int r, uint16_t* __restrict__ dst) {
-  double acc[8];
+// fp64 means of columns c..c+7 of pooled block b: keys b*r .. b*r+r-1 (row stride ks),
+// summed exactly (each bf16 value and every partial sum fit fp64 without rounding).
+__device__ __forceinline__ void pool_mean8(const uint16_t* __restrict__ k, int64_t ks, int64_t b,
+                                           int c, int r, double (&m)[8]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  for (int e = 0; e < 8; ++e) m[e] = 0.0;
   for (int j = 0; j < r; ++j) {
     const uint4 x = ld16(k + (b * r + j) * ks + c);
     const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += (double)bf16_bits_to_f32(w4[e] & 0xffffu);
-      acc[2 * e + 1] += (double)bf16_bits_to_f32(w4[e] >> 16);
+      m[2 * e] += (double)bf16_bits_to_f32(w4[e] & 0xffffu);
+      m[2 * e + 1] += (double)bf16_bits_to_f32(w4[e] >> 16);
     }
   }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] /= r;
+}
+
+__device__ __forceinline__ void store_bf16x8(const double (&m)[8], uint16_t* __restrict__ dst) {
   uint32_t o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    o[e] = f64_to_bf16_bits(acc[2 * e] / r) | (f64_to_bf16_bits(acc[2 * e + 1] / r) << 16);
+    o[e] = f64_to_bf16_bits(m[2 * e]) | (f64_to_bf16_bits(m[2 * e + 1]) << 16);
   *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Columns c..c+7 of pooled block b of a sequence (keys k, row stride ks) into row dst.
+// With rope_dim > 0 the leading rope_dim columns are rotated at the block's position
+// pos = (first_block + b) * r in the half-split convention: column i < h = rope_dim/2
+// pairs with i + h at angle pos * theta^(-2i/rope_dim); the thread of columns c < h
+// writes both halves of its pairs, the threads of columns h <= c < rope_dim nothing.
+// Mean, rotation and angle are fp64; the result is rounded once to bf16.
+constexpr int kMaxRopeHalf = 2048;  // rope_dim <= d_idx <= 4096
+
+// inv[i] = theta^(-2i / rope_dim) for i < rope_dim / 2, once per workgroup in LDS.
+__device__ __forceinline__ void rope_freqs(double* inv, int rope_dim, double theta) {
+  for (int i = threadIdx.x; i < (rope_dim >> 1); i += blockDim.x)
+    inv[i] = pow(theta, -2.0 * (double)i / (double)rope_dim);
+  __syncthreads();
+}
+
+__device__ __forceinline__ void pool_block8(const uint16_t* __restrict__ k, int64_t ks, int64_t b,
+                                            int c, int r, int64_t first_block, int rope_dim,
+                                            const double* inv, uint16_t* __restrict__ dst_row) {
+  const int h = rope_dim >> 1;
+  if (c >= rope_dim) {
+    double m[8];
+    pool_mean8(k, ks, b, c, r, m);
+    store_bf16x8(m, dst_row + c);
+    return;
+  }
+  if (c >= h) return;
+  double x1[8], x2[8];
+  pool_mean8(k, ks, b, c, r, x1);
+  pool_mean8(k, ks, b, c + h, r, x2);
+  const double pos = (double)((first_block + b) * r);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    double sn, cs;
+    sincos(pos * inv[c + e], &sn, &cs);
+    const double a = x1[e], bb = x2[e];
+    x1[e] = a * cs - bb * sn;
+    x2[e] = bb * cs + a * sn;
+  }
+  store_bf16x8(x1, dst_row + c);
+  store_bf16x8(x2, dst_row + c + h);
 }
 
 __global__ __launch_bounds__(256) void pool_keys_kernel(const uint16_t* __restrict__ k,
                                                         int64_t ks, int64_t nb, int d, int r,
-                                                        uint16_t* __restrict__ p, int64_t ps) {
+                                                        uint16_t* __restrict__ p, int64_t ps,
+                                                        int64_t first_block, int rope_dim,
+                                                        double theta) {
+  __shared__ double inv[kMaxRopeHalf];
+  if (rope_dim) rope_freqs(inv, rope_dim, theta);
   const int vec = d >> 3;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t b = gid / vec;
   if (b >= nb) return;
   const int c = (int)(gid - b * vec) * 8;
-  pool_block8(k, ks, b, c, r, p + b * ps + c);
+  pool_block8(k, ks, b, c, r, first_block, rope_dim, inv, p + b * ps);
 }
 
 // Packed sequences: sequence blockIdx.y pools its complete blocks (at most max_nb) from
-// its own key tokens into its slot of the padded output p[batch][max_nb][d].
+// its own key tokens into its slot of the padded output p[batch][max_nb][d]; block
+// positions count from the sequence's first token.
 __global__ __launch_bounds__(256) void pool_keys_varlen_kernel(const uint16_t* __restrict__ k,
                                                                const int32_t* __restrict__ cu_k,
                                                                int64_t max_nb, int d, int r,
-                                                               uint16_t* __restrict__ p) {
+                                                               uint16_t* __restrict__ p,
+                                                               int rope_dim, double theta) {
+  __shared__ double inv[kMaxRopeHalf];
+  if (rope_dim) rope_freqs(inv, rope_dim, theta);
   const int vec = d >> 3;
   const int bi = blockIdx.y;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -74,26 +129,28 @@ __global__ __launch_bounds__(256) void pool_keys_varlen_kernel(const uint16_t* _
   const int64_t nb = min(((int64_t)cu_k[bi + 1] - k0) / r, max_nb);
   if (b >= nb) return;
   const int c = (int)(gid - b * vec) * 8;
-  pool_block8(k + k0 * d, d, b, c, r, p + ((int64_t)bi * max_nb + b) * d + c);
+  pool_block8(k + k0 * d, d, b, c, r, 0, rope_dim, inv, p + ((int64_t)bi * max_nb + b) * d);
 }
 
 hipError_t launch_pool_keys(const uint16_t* k_idx, int64_t k_stride, int64_t n_blocks, int d_idx,
-                            int r, uint16_t* k_pooled, int64_t p_stride, hipStream_t stream) {
+                            int r, uint16_t* k_pooled, int64_t p_stride, const PooledPe& pe,
+                            hipStream_t stream) {
   if (n_blocks <= 0) return hipSuccess;
   const int64_t threads = n_blocks * (d_idx / 8);
   const int64_t grid = (threads + 255) / 256;
   hipLaunchKernelGGL(pool_keys_kernel, dim3((unsigned)grid), dim3(256), 0, stream, k_idx,
-                     k_stride, n_blocks, d_idx, r, k_pooled, p_stride);
+                     k_stride, n_blocks, d_idx, r, k_pooled, p_stride, pe.first_block,
+                     pe.rope_dim, pe.theta);
   return hipGetLastError();
 }
 
 hipError_t launch_pool_keys_varlen(const uint16_t* k_idx, const int32_t* cu_k, int batch,
                                    int64_t max_nb, int d_idx, int r, uint16_t* k_pooled,
-                                   hipStream_t stream) {
+                                   const PooledPe& pe, hipStream_t stream) {
   if (max_nb <= 0 || batch <= 0) return hipSuccess;
   const int64_t grid = (max_nb * (d_idx / 8) + 255) / 256;
   hipLaunchKernelGGL(pool_keys_varlen_kernel, dim3((unsigned)grid, (unsigned)batch), dim3(256), 0,
-                     stream, k_idx, cu_k, max_nb, d_idx, r, k_pooled);
+                     stream, k_idx, cu_k, max_nb, d_idx, r, k_pooled, pe.rope_dim, pe.theta);
   return hipGetLastError();
 }
 

@@ -75,6 +75,20 @@ size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 int64_t score_ld(int64_t nblk) { return (nblk + 3) & ~int64_t(3); }
 
+// The pooled-key encoding of a call: none for NULL or rope_dim 0.
+qsa_status pooled_pe(const qsa_pooled_pe* pe, int d_idx, qsa::PooledPe* out) {
+  *out = qsa::PooledPe{0, 0.0, 0};
+  if (!pe || pe->rope_dim == 0) return QSA_OK;
+  QSA_REQUIRE(pe->rope_dim % 16 == 0 && pe->rope_dim >= 16 && pe->rope_dim <= d_idx,
+              QSA_ERR_UNSUPPORTED, "rope_dim=%d: a multiple of 16 in 16..d_idx=%d, or 0",
+              pe->rope_dim, d_idx);
+  QSA_REQUIRE(isfinite(pe->rope_theta) && pe->rope_theta > 1.f, QSA_ERR_INVALID_ARGUMENT,
+              "rope_theta=%g must be finite and > 1", (double)pe->rope_theta);
+  out->rope_dim = pe->rope_dim;
+  out->theta = (double)pe->rope_theta;
+  return QSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,8 +116,39 @@ qsa_status qsa_pool_keys(const void* k_idx, int64_t k_idx_row_stride, int64_t n_
   return hip_status(
       qsa::launch_pool_keys(static_cast<const uint16_t*>(k_idx), k_idx_row_stride, n_blocks,
                             d_idx, r, static_cast<uint16_t*>(k_pooled), k_pooled_row_stride,
-                            static_cast<hipStream_t>(stream)),
+                            qsa::PooledPe{0, 0.0, 0}, static_cast<hipStream_t>(stream)),
       "qsa_pool_keys launch");
+}
+
+qsa_status qsa_pool_keys_pe(const void* k_idx, int64_t k_idx_row_stride, int64_t n_blocks,
+                            int d_idx, int r, int64_t first_block, const qsa_pooled_pe* pe,
+                            void* k_pooled, int64_t k_pooled_row_stride, void* stream) {
+  qsa::PooledPe p{};
+  QSA_TRY(pooled_pe(pe, d_idx, &p));
+  QSA_REQUIRE(first_block >= 0, QSA_ERR_INVALID_ARGUMENT, "first_block=%lld < 0",
+              (long long)first_block);
+  p.first_block = first_block;
+  if (p.rope_dim == 0)
+    return qsa_pool_keys(k_idx, k_idx_row_stride, n_blocks, d_idx, r, k_pooled,
+                         k_pooled_row_stride, stream);
+  QSA_TRY(check_r(r));
+  QSA_REQUIRE(n_blocks >= 0, QSA_ERR_INVALID_ARGUMENT, "n_blocks=%lld < 0", (long long)n_blocks);
+  QSA_REQUIRE(d_idx > 0 && d_idx % 8 == 0 && d_idx <= 4096, QSA_ERR_UNSUPPORTED,
+              "d_idx=%d must be a multiple of 8 in 8..4096", d_idx);
+  if (n_blocks == 0) return QSA_OK;
+  QSA_REQUIRE(k_idx && k_pooled, QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  QSA_REQUIRE(aligned16(k_idx) && aligned16(k_pooled), QSA_ERR_INVALID_ARGUMENT,
+              "k_idx and k_pooled must be 16-byte aligned");
+  QSA_REQUIRE(k_idx_row_stride >= d_idx && k_idx_row_stride % 8 == 0 &&
+                  k_pooled_row_stride >= d_idx && k_pooled_row_stride % 8 == 0,
+              QSA_ERR_INVALID_ARGUMENT,
+              "row strides (%lld, %lld) must be >= d_idx and multiples of 8 elements",
+              (long long)k_idx_row_stride, (long long)k_pooled_row_stride);
+  return hip_status(
+      qsa::launch_pool_keys(static_cast<const uint16_t*>(k_idx), k_idx_row_stride, n_blocks,
+                            d_idx, r, static_cast<uint16_t*>(k_pooled), k_pooled_row_stride, p,
+                            static_cast<hipStream_t>(stream)),
+      "qsa_pool_keys_pe launch");
 }
 
 qsa_status qsa_index_scores(int batch, int64_t lq, int h_idx, int d_idx, int r,
@@ -532,8 +577,10 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
                               const void* k_idx, int64_t first_raw_token,
                               const void* k_pooled_prefix, void* k_pooled, int32_t* sel,
                               int64_t row_chunk, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              const qsa_pooled_pe* pe, void* stream) {
   QSA_TRY(check_r(r));
+  qsa::PooledPe ppe{};
+  QSA_TRY(pooled_pe(pe, d_idx, &ppe));
   QSA_TRY(check_budget(budget_tokens, r));
   QSA_TRY(check_indexer_shape(h_idx, d_idx));
   QSA_REQUIRE(lq >= 0 && lk >= 1 && q_pos0 >= 0 && q_pos0 + lq <= lk, QSA_ERR_INVALID_ARGUMENT,
@@ -564,9 +611,9 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
   }
   const int64_t new_blocks = nblk - prefix_blocks;
   if (new_blocks > 0)
-    QSA_TRY(qsa_pool_keys(k_idx, d_idx, new_blocks, d_idx, r,
-                          static_cast<uint16_t*>(k_pooled) + prefix_blocks * d_idx, d_idx,
-                          stream));
+    QSA_TRY(qsa_pool_keys_pe(k_idx, d_idx, new_blocks, d_idx, r, prefix_blocks, pe,
+                             static_cast<uint16_t*>(k_pooled) + prefix_blocks * d_idx, d_idx,
+                             stream));
   if (lq == 0) return QSA_OK;
   const int64_t ld = score_ld(nblk);
   float* sc = static_cast<float*>(workspace);
@@ -591,13 +638,14 @@ qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, i
                                const void* k_idx, int64_t first_raw_token,
                                const void* k_pooled_prefix, void* k_pooled, float softmax_scale,
                                int32_t* sel, void* out, float* lse, int64_t row_chunk,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               void* workspace, size_t workspace_bytes,
+                               const qsa_pooled_pe* pe, void* stream) {
   QSA_TRY(check_budget(budget_tokens, r));
   QSA_TRY(check_attn_fwd(lq, lk, hq, hkv, d, r, budget_tokens / r, q, k, v, sel, q_pos0,
                          softmax_scale, out));
   QSA_TRY(qsa_prefill_select(lq, lk, q_pos0, h_idx, d_idx, r, budget_tokens, q_idx, w, k_idx,
                              first_raw_token, k_pooled_prefix, k_pooled, sel, row_chunk,
-                             workspace, workspace_bytes, stream));
+                             workspace, workspace_bytes, pe, stream));
   return qsa_sparse_attn_fwd(lq, lk, hq, hkv, d, r, budget_tokens / r, q, k, v, sel, q_pos0,
                              softmax_scale, out, lse, stream);
 }
@@ -653,10 +701,12 @@ qsa_status qsa_prefill_varlen_select(int batch, const int32_t* cu_seqlens_q,
                                      int budget_tokens, const void* q_idx, const float* w,
                                      const void* k_idx, void* k_pooled, int32_t* sel,
                                      int64_t row_chunk, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+                                     const qsa_pooled_pe* pe, void* stream) {
   QSA_TRY(check_varlen(batch, cu_seqlens_q, cu_seqlens_k, max_lq, max_lk, r));
   QSA_TRY(check_budget(budget_tokens, r));
   QSA_TRY(check_indexer_shape(h_idx, d_idx));
+  qsa::PooledPe ppe{};
+  QSA_TRY(pooled_pe(pe, d_idx, &ppe));
   const int64_t nblk = max_lk / r;
   QSA_REQUIRE(k_pooled && (k_idx || nblk == 0), QSA_ERR_INVALID_ARGUMENT,
               "null k_pooled or k_idx");
@@ -675,7 +725,7 @@ qsa_status qsa_prefill_varlen_select(int batch, const int32_t* cu_seqlens_q,
   hipStream_t s = static_cast<hipStream_t>(stream);
   QSA_TRY(hip_status(qsa::launch_pool_keys_varlen(static_cast<const uint16_t*>(k_idx),
                                                   cu_seqlens_k, batch, nblk, d_idx, r,
-                                                  static_cast<uint16_t*>(k_pooled), s),
+                                                  static_cast<uint16_t*>(k_pooled), ppe, s),
                      "varlen pooling launch"));
   if (max_lq == 0) return QSA_OK;
   const int64_t rc = varlen_row_chunk(max_lq, row_chunk);
@@ -742,7 +792,8 @@ qsa_status qsa_prefill_varlen_forward(int batch, const int32_t* cu_seqlens_q,
                                       const void* q_idx, const float* w, const void* k_idx,
                                       void* k_pooled, float softmax_scale, int32_t* sel,
                                       void* out, float* lse, int64_t row_chunk,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+                                      void* workspace, size_t workspace_bytes,
+                                      const qsa_pooled_pe* pe, void* stream) {
   QSA_TRY(check_budget(budget_tokens, r));
   QSA_TRY(check_attn_shape(hq, hkv, d));
   QSA_REQUIRE(total_q >= 0 && total_q < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT,
@@ -753,7 +804,7 @@ qsa_status qsa_prefill_varlen_forward(int batch, const int32_t* cu_seqlens_q,
               QSA_ERR_INVALID_ARGUMENT, "q, k, v and out must be non-null and 16-byte aligned");
   QSA_TRY(qsa_prefill_varlen_select(batch, cu_seqlens_q, cu_seqlens_k, max_lq, max_lk, h_idx,
                                     d_idx, r, budget_tokens, q_idx, w, k_idx, k_pooled, sel,
-                                    row_chunk, workspace, workspace_bytes, stream));
+                                    row_chunk, workspace, workspace_bytes, pe, stream));
   return qsa_sparse_attn_varlen_fwd(batch, cu_seqlens_q, cu_seqlens_k, total_q, hq, hkv, d, r,
                                     budget_tokens / r, q, k, v, sel, softmax_scale, out, lse,
                                     stream);

@@ -30,13 +30,22 @@ __device__ __forceinline__ SeqRows varlen_rows(const Varlen& v, int bi, int64_t 
 }
 
 // ---- stage 1 ----
+// Positional encoding of the pooled keys: RoPE on the leading rope_dim columns (0: none)
+// at the block's position (first_block + b) * r.
+struct PooledPe {
+  int rope_dim;
+  double theta;
+  int64_t first_block;
+};
 hipError_t launch_pool_keys(const uint16_t* k_idx, int64_t k_stride, int64_t n_blocks, int d_idx,
-                            int r, uint16_t* k_pooled, int64_t p_stride, hipStream_t stream);
+                            int r, uint16_t* k_pooled, int64_t p_stride, const PooledPe& pe,
+                            hipStream_t stream);
 // Packed sequences (keys cu_k[b] .. cu_k[b+1]-1 of k_idx [.][d_idx]) into the padded
 // k_pooled [batch][max_nb][d_idx]; blocks past a sequence's complete blocks are untouched.
+// Block positions count from each sequence's first token (pe.first_block unused).
 hipError_t launch_pool_keys_varlen(const uint16_t* k_idx, const int32_t* cu_k, int batch,
                                    int64_t max_nb, int d_idx, int r, uint16_t* k_pooled,
-                                   hipStream_t stream);
+                                   const PooledPe& pe, hipStream_t stream);
 
 // Two-level top-k: per segment of kTopkWaveSeg candidates, the kTopkWaveKeep best as
 // (score, id) pairs (id -1: empty) and the worst kept one when the segment had more.

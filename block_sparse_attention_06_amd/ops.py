@@ -67,8 +67,24 @@ def abi_version() -> int:
 # ------------------------------------------------------------------------------------
 
 
-def qsa_pool_keys(k_idx: torch.Tensor, r: int = 4, out: Optional[torch.Tensor] = None):
-    """Mean-pool [n_tok, d_I] bf16 indexer keys into [n_tok // r, d_I] (complete blocks)."""
+class _PooledPe(ctypes.Structure):
+    _fields_ = [("rope_dim", ctypes.c_int), ("rope_theta", ctypes.c_float)]
+
+
+def _pe_arg(pe):
+    """(rope_dim, rope_theta) or None -> a pointer to the C struct (kept alive by the
+    returned holder) or NULL."""
+    if pe is None:
+        return None, None
+    st = _PooledPe(int(pe[0]), float(pe[1]))
+    return st, ctypes.cast(ctypes.pointer(st), ctypes.c_void_p)
+
+
+def qsa_pool_keys(k_idx: torch.Tensor, r: int = 4, out: Optional[torch.Tensor] = None, *,
+                  pe=None, first_block: int = 0):
+    """Mean-pool [n_tok, d_I] bf16 indexer keys into [n_tok // r, d_I] (complete blocks).
+    pe = (rope_dim, rope_theta) also encodes each block at position
+    (first_block + b) * r (see include/qsa.h)."""
     _need(k_idx, "k_idx", torch.bfloat16, contiguous=False)
     if k_idx.dim() != 2 or k_idx.stride(1) != 1:
         raise ValueError("k_idx must be [n_tokens, d_idx] with unit column stride")
@@ -78,8 +94,14 @@ def qsa_pool_keys(k_idx: torch.Tensor, r: int = 4, out: Optional[torch.Tensor] =
     _need(out, "out", torch.bfloat16, k_idx.device, contiguous=False)
     if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] < nb or out.shape[1] != d_i:
         raise ValueError("out must be [>= n_tokens // r, d_idx] with unit column stride")
-    _call("qsa_pool_keys", _ptr(k_idx), k_idx.stride(0), nb, d_i, r, _ptr(out), out.stride(0),
-          _stream(k_idx))
+    if pe is None:
+        _call("qsa_pool_keys", _ptr(k_idx), k_idx.stride(0), nb, d_i, r, _ptr(out),
+              out.stride(0), _stream(k_idx))
+    else:
+        keep, pp = _pe_arg(pe)
+        _call("qsa_pool_keys_pe", _ptr(k_idx), k_idx.stride(0), nb, d_i, r, first_block, pp,
+              _ptr(out), out.stride(0), _stream(k_idx))
+        del keep
     return out
 
 
@@ -307,7 +329,7 @@ def _prefill_args(q_idx, w, k_idx, k_pooled_prefix, r, lk):
 
 def qsa_prefill_select(q_idx, w, k_idx, *, lk: int, budget: int, q_pos0: int = 0,
                        k_pooled_prefix: Optional[torch.Tensor] = None, r: int = 4,
-                       row_chunk: int = 4096, plan: Optional[PrefillPlan] = None):
+                       row_chunk: int = 4096, plan: Optional[PrefillPlan] = None, pe=None):
     """Selection half of prefill: pool the new blocks, score + top-k in row chunks.
     Returns (sel, k_pooled)."""
     lq, h_idx, d_idx = q_idx.shape
@@ -315,16 +337,18 @@ def qsa_prefill_select(q_idx, w, k_idx, *, lk: int, budget: int, q_pos0: int = 0
     if plan is None:
         plan = PrefillPlan(lq, lk, 1, 1, 128, h_idx, d_idx, budget, r=r, row_chunk=row_chunk,
                            device=q_idx.device, with_attention=False)
+    keep, pp = _pe_arg(pe)
     _call("qsa_prefill_select", lq, lk, q_pos0, h_idx, d_idx, r, budget, _ptr(q_idx), _ptr(w),
           _ptr(k_idx), prefix_blocks * r, _ptr(k_pooled_prefix), _ptr(plan.k_pooled),
-          _ptr(plan.sel), plan.row_chunk, _ptr(plan.ws), plan.ws_bytes, _stream(q_idx))
+          _ptr(plan.sel), plan.row_chunk, _ptr(plan.ws), plan.ws_bytes, pp, _stream(q_idx))
+    del keep
     return plan.sel, plan.k_pooled
 
 
 def qsa_prefill_forward(q, k, v, q_idx, w, k_idx, *, budget: int, q_pos0: int = 0,
                         k_pooled_prefix: Optional[torch.Tensor] = None,
                         scale: Optional[float] = None, r: int = 4, row_chunk: int = 4096,
-                        plan: Optional[PrefillPlan] = None):
+                        plan: Optional[PrefillPlan] = None, pe=None):
     """Whole prefill: pool the new blocks, score + top-k in row chunks, attention.
 
     q [Lq,Hq,d], k/v [Lk,Hkv,d], q_idx [Lq,H_I,d_I], w [Lq,H_I]; k_idx holds the raw
@@ -341,10 +365,12 @@ def qsa_prefill_forward(q, k, v, q_idx, w, k_idx, *, budget: int, q_pos0: int = 
     if plan is None:
         plan = PrefillPlan(lq, lk, hq, hkv, d, h_idx, d_idx, budget, r=r, row_chunk=row_chunk,
                            device=q.device)
+    keep, pp = _pe_arg(pe)
     _call("qsa_prefill_forward", lq, lk, q_pos0, hq, hkv, d, h_idx, d_idx, r, budget, _ptr(q),
           _ptr(k), _ptr(v), _ptr(q_idx), _ptr(w), _ptr(k_idx), prefix_blocks * r,
           _ptr(k_pooled_prefix), _ptr(plan.k_pooled), scale, _ptr(plan.sel), _ptr(plan.out),
-          _ptr(plan.lse), plan.row_chunk, _ptr(plan.ws), plan.ws_bytes, _stream(q))
+          _ptr(plan.lse), plan.row_chunk, _ptr(plan.ws), plan.ws_bytes, pp, _stream(q))
+    del keep
     return plan.out, plan.lse, plan.sel, plan.k_pooled
 
 
@@ -383,7 +409,7 @@ def qsa_prefill_varlen_forward(q, k, v, q_idx, w, k_idx, cu_seqlens_q, cu_seqlen
                                budget: int, max_lq: Optional[int] = None,
                                max_lk: Optional[int] = None, scale: Optional[float] = None,
                                r: int = 4, row_chunk: Optional[int] = None,
-                               plan: Optional[VarlenPlan] = None):
+                               plan: Optional[VarlenPlan] = None, pe=None):
     """Whole prefill of a packed batch. q [Tq,Hq,d], k/v [Tk,Hkv,d], q_idx [Tq,H_I,d_I],
     w [Tq,H_I], k_idx [Tk,d_I]; cu_seqlens_q/k int32 [B+1] on the device. Each sequence's
     queries are its last tokens. Returns (out, lse, sel with per-sequence block ids,
@@ -403,11 +429,13 @@ def qsa_prefill_varlen_forward(q, k, v, q_idx, w, k_idx, cu_seqlens_q, cu_seqlen
     if plan is None:
         plan = VarlenPlan(batch, total_q, max_lq, max_lk, hq, d, d_idx, budget, r=r,
                           row_chunk=row_chunk, device=q.device)
+    keep, pp = _pe_arg(pe)
     _call("qsa_prefill_varlen_forward", batch, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), total_q,
           max_lq, max_lk, hq, hkv, d, h_idx, d_idx, r, budget, _ptr(q), _ptr(k), _ptr(v),
           _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(plan.k_pooled), scale, _ptr(plan.sel),
           _ptr(plan.out), _ptr(plan.lse), plan.row_chunk, _ptr(plan.ws), plan.ws_bytes,
-          _stream(q))
+          pp, _stream(q))
+    del keep
     return plan.out, plan.lse, plan.sel, plan.k_pooled
 
 

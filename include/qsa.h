@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -67,14 +67,41 @@ const char* qsa_last_error(void);
  * summed in fp64 (exact for bf16 keys), divided by r and rounded once to nearest
  * even. Only complete blocks are
  * passed: the caller points k_idx at the first token of the first block to pool and
- * k_pooled at that block's row. No positional encoding is added here; a caller that
- * wants one applies it to k_pooled afterwards.
+ * k_pooled at that block's row. qsa_pool_keys adds no positional encoding;
+ * qsa_pool_keys_pe adds the one below.
  *   k_idx     bf16 [r*n_blocks rows][d_idx], row i at k_idx + i*k_idx_row_stride
  *   k_pooled  bf16 [n_blocks][d_idx],        row b at k_pooled + b*k_pooled_row_stride
  */
 qsa_status qsa_pool_keys(const void* k_idx, int64_t k_idx_row_stride, int64_t n_blocks,
                          int d_idx, int r, void* k_pooled, int64_t k_pooled_row_stride,
                          void* stream);
+
+/*
+ * Positional encoding of the pooled keys [DR]: the keys are mean-pooled first and the
+ * position is encoded afterwards (the pages name no form; the reading here is the
+ * partial rotary encoding of the model's attention): the leading rope_dim columns of
+ * kbar[b] are rotated at the block's position p = (first_block + b) * r, the position
+ * of its first token, in the half-split convention: for i < h = rope_dim / 2,
+ *   a = p * rope_theta^(-2i / rope_dim)
+ *   kbar[i]     <- kbar[i] cos a - kbar[i+h] sin a
+ *   kbar[i + h] <- kbar[i+h] cos a + kbar[i] sin a
+ * The mean, the angle and the rotation are fp64; the result is rounded once to bf16.
+ * The indexer queries are expected rotated the same way at their own positions (the
+ * caller's projection does that, as for q and k of the attention), so that a score
+ * depends on the query's offset from the block. rope_dim = 0 (or a NULL pointer
+ * wherever a qsa_pooled_pe* is taken) means no encoding.
+ *   rope_dim    multiple of 16 with 16 <= rope_dim <= d_idx, or 0
+ *   rope_theta  rotary base, finite and > 1
+ * qsa_pool_keys_pe: as qsa_pool_keys; first_block is the index of the first pooled
+ * block within its sequence (nonzero when pooling the tail of a cached prefix).
+ */
+typedef struct qsa_pooled_pe {
+  int rope_dim;
+  float rope_theta;
+} qsa_pooled_pe;
+qsa_status qsa_pool_keys_pe(const void* k_idx, int64_t k_idx_row_stride, int64_t n_blocks,
+                            int d_idx, int r, int64_t first_block, const qsa_pooled_pe* pe,
+                            void* k_pooled, int64_t k_pooled_row_stride, void* stream);
 
 /*
  * Stage 2 -- light MQA indexer block scores [DR], [RA] (DSA-style reading):
@@ -242,6 +269,9 @@ qsa_status qsa_sparse_attn_decode(int batch, int hq, int hkv, int d, int r, int 
  * NULL when first_raw_token == 0). Outputs: k_pooled [lk/r][d_idx] (prefix rows
  * copied, new rows pooled) and sel [lq][K/r]. Query row i sits at q_pos0 + i.
  * workspace: qsa_prefill_workspace_bytes() bytes (one chunk's scores + top-k space).
+ * pe: positional encoding of the new pooled rows (see qsa_pool_keys_pe; their first
+ * block is first_raw_token / r), or NULL for none. Prefix rows are copied as given,
+ * so a prefix pooled with the same encoding stays consistent.
  */
 size_t qsa_prefill_workspace_bytes(int64_t lq, int64_t lk, int r, int budget_tokens,
                                    int64_t row_chunk);
@@ -250,7 +280,7 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
                               const void* k_idx, int64_t first_raw_token,
                               const void* k_pooled_prefix, void* k_pooled, int32_t* sel,
                               int64_t row_chunk, void* workspace, size_t workspace_bytes,
-                              void* stream);
+                              const qsa_pooled_pe* pe, void* stream);
 
 /*
  * Whole prefill path: qsa_prefill_select followed by qsa_sparse_attn_fwd on the same
@@ -264,7 +294,7 @@ qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, i
                                const void* k_pooled_prefix, void* k_pooled,
                                float softmax_scale, int32_t* sel, void* out, float* lse,
                                int64_t row_chunk, void* workspace, size_t workspace_bytes,
-                               void* stream);
+                               const qsa_pooled_pe* pe, void* stream);
 
 /*
  * Packed variable-length batches (THD) [MR5]: `batch` sequences packed along the token
@@ -286,7 +316,8 @@ qsa_status qsa_prefill_forward(int64_t lq, int64_t lk, int64_t q_pos0, int hq, i
  *   sel          int32 [total_q][K/r]: block ids LOCAL to each row's sequence,
  *                ascending, -1 padded, as stage 3 writes them for one sequence
  * The selection runs in chunks of row_chunk local rows of every sequence at once
- * (the workspace holds batch x row_chunk score rows). The attention launches one
+ * (the workspace holds batch x row_chunk score rows). pe (or NULL) encodes each
+ * sequence's pooled keys at positions counted from the sequence's first token. The attention launches one
  * resident generation of rows at a time over the packed rows, sequences mixed.
  */
 size_t qsa_prefill_varlen_workspace_bytes(int batch, int64_t max_lq, int64_t max_lk, int r,
@@ -297,7 +328,7 @@ qsa_status qsa_prefill_varlen_select(int batch, const int32_t* cu_seqlens_q,
                                      int budget_tokens, const void* q_idx, const float* w,
                                      const void* k_idx, void* k_pooled, int32_t* sel,
                                      int64_t row_chunk, void* workspace, size_t workspace_bytes,
-                                     void* stream);
+                                     const qsa_pooled_pe* pe, void* stream);
 qsa_status qsa_sparse_attn_varlen_fwd(int batch, const int32_t* cu_seqlens_q,
                                       const int32_t* cu_seqlens_k, int64_t total_q, int hq,
                                       int hkv, int d, int r, int n_sel, const void* q,
@@ -311,7 +342,8 @@ qsa_status qsa_prefill_varlen_forward(int batch, const int32_t* cu_seqlens_q,
                                       const void* q_idx, const float* w, const void* k_idx,
                                       void* k_pooled, float softmax_scale, int32_t* sel,
                                       void* out, float* lse, int64_t row_chunk,
-                                      void* workspace, size_t workspace_bytes, void* stream);
+                                      void* workspace, size_t workspace_bytes,
+                                      const qsa_pooled_pe* pe, void* stream);
 
 /*
  * Whole decode step for `batch` sequences: scores against the pooled-key cache,

@@ -26,8 +26,9 @@ Readings where the pages leave a step open (each is stated where it is used):
 * Score (DSA reading): s[t,b] = sum_h w[t,h] * max(0, qI[t,h] . kbar[b]); no extra
   global scale (a positive scale cannot change a ranking).
 * Pooling is the mean over the r keys of a complete block, rounded once to bf16;
-  a trailing partial block is never pooled. No positional encoding is added inside
-  the path (the caller may add one to the pooled keys before scoring).
+  a trailing partial block is never pooled. The positional encoding [DR] adds after
+  pooling is optional: a partial rotary encoding of the pooled key at its block's
+  first-token position (``rope_rotate``; the pages give no form).
 * Only complete blocks strictly before the query's own block b(t) = t // r are
   scored; the own block is always kept and counts toward the budget, so
   n_sel = K // r blocks are kept in all. Ties go to the lower block index; -0.0
@@ -76,15 +77,39 @@ def f64_to_bf16(x: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 
 
-def pool_keys(k_idx_bits: np.ndarray, r: int) -> np.ndarray:
-    """Mean-pool r consecutive indexer keys per complete block, rounded to bf16.
+def rope_rotate(x: np.ndarray, pos: np.ndarray, rope_dim: int, theta: float) -> np.ndarray:
+    """Rotary encoding of rows x [n, d] at positions pos [n] (fp64), half-split form:
+    for i < h = rope_dim / 2 the pair (x[i], x[i + h]) turns by pos * theta^(-2i/rope_dim);
+    columns from rope_dim on are unchanged. (Reading of [DR]'s unnamed positional
+    encoding: the partial rotary encoding of the model's attention.)"""
+    y = np.array(x, dtype=np.float64, copy=True)
+    if rope_dim == 0:
+        return y
+    h = rope_dim // 2
+    inv = np.power(float(theta), -2.0 * np.arange(h, dtype=np.float64) / rope_dim)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = y[:, :h].copy(), y[:, h:rope_dim].copy()
+    y[:, :h] = a * c - b * s
+    y[:, h:rope_dim] = b * c + a * s
+    return y
+
+
+def pool_keys(k_idx_bits: np.ndarray, r: int, pe=None, first_block: int = 0) -> np.ndarray:
+    """Mean-pool r consecutive indexer keys per complete block, rounded to bf16 [DR].
 
     k_idx_bits: [n_tokens, d_I] bf16 bits. Returns [n_tokens // r, d_I] bf16 bits.
+    With pe = (rope_dim, theta) the mean is first encoded at the block's position
+    (first_block + b) * r, the position of its first token ([DR]: keys are pooled
+    first, then the position is encoded); mean and rotation in fp64, one rounding.
     """
     x = bf16_to_f64(k_idx_bits)
     nb = x.shape[0] // r
     blocks = x[: nb * r].reshape(nb, r, x.shape[1])
-    return f64_to_bf16(blocks.sum(axis=1) / r)
+    m = blocks.sum(axis=1) / r
+    if pe is not None and pe[0]:
+        m = rope_rotate(m, (first_block + np.arange(nb)) * r, int(pe[0]), float(pe[1]))
+    return f64_to_bf16(m)
 
 
 # --------------------------------------------------------------------------------------
@@ -333,7 +358,8 @@ def forward_prefill(q_bits, k_bits, v_bits, q_idx_bits, w, k_idx_bits, *, r: int
                     q_pos0: int = 0, scale: Optional[float] = None,
                     k_pooled_prefix_bits: Optional[np.ndarray] = None,
                     rows: Optional[Sequence[int]] = None, n_keys: Optional[int] = None,
-                    fetch_kv: Optional[Callable] = None, row_chunk: int = 2048) -> dict:
+                    fetch_kv: Optional[Callable] = None, row_chunk: int = 2048,
+                    pe=None) -> dict:
     """QSA prefill for query rows ``rows`` (default: all).
 
     q_bits [Lq, Hq, d]; k_bits/v_bits [Lk, Hkv, d] (or ``fetch_kv(tokens)`` returning
@@ -341,7 +367,7 @@ def forward_prefill(q_bits, k_bits, v_bits, q_idx_bits, w, k_idx_bits, *, r: int
     k_idx_bits holds the raw indexer keys of the tokens after the pooled prefix
     (k_pooled_prefix_bits, [P, d_I], or none). Query row i is at position q_pos0 + i.
     Returns the pooled keys of the new blocks, and per row: scores, selection,
-    output and lse.
+    output and lse. pe = (rope_dim, theta) encodes the new pooled keys (see pool_keys).
     """
     lq, hq, d = q_bits.shape
     scale = 1.0 / np.sqrt(d) if scale is None else scale
@@ -349,7 +375,8 @@ def forward_prefill(q_bits, k_bits, v_bits, q_idx_bits, w, k_idx_bits, *, r: int
     if fetch_kv is None:
         fetch_kv = _rows_fetcher(k_bits, v_bits)
         n_keys = k_bits.shape[0]
-    pooled_new = pool_keys(k_idx_bits, r)
+    n_prefix = 0 if k_pooled_prefix_bits is None else len(k_pooled_prefix_bits)
+    pooled_new = pool_keys(k_idx_bits, r, pe, first_block=n_prefix)
     if k_pooled_prefix_bits is not None and len(k_pooled_prefix_bits):
         pooled_all = np.concatenate([k_pooled_prefix_bits, pooled_new], axis=0)
     else:
@@ -379,7 +406,7 @@ def forward_prefill(q_bits, k_bits, v_bits, q_idx_bits, w, k_idx_bits, *, r: int
 
 def forward_prefill_varlen(q_bits, k_bits, v_bits, q_idx_bits, w, k_idx_bits, cu_q, cu_k, *,
                            r: int, budget: int, scale: Optional[float] = None,
-                           rows: Optional[Sequence[int]] = None) -> dict:
+                           rows: Optional[Sequence[int]] = None, pe=None) -> dict:
     """QSA prefill of a packed batch ([MR] section 5.3 "Rollout & SGLang": packed THD
     tensors). Sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 and key tokens
     cu_k[b] .. cu_k[b+1]-1; its queries are its last tokens (row i of the sequence
@@ -403,7 +430,7 @@ def forward_prefill_varlen(q_bits, k_bits, v_bits, q_idx_bits, w, k_idx_bits, cu
         res = forward_prefill(q_bits[q0:q1], k_bits[k0:k1], v_bits[k0:k1], q_idx_bits[q0:q1],
                               np.asarray(w)[q0:q1], k_idx_bits[k0:k1], r=r, budget=budget,
                               q_pos0=int((k1 - k0) - (q1 - q0)), scale=scale,
-                              rows=rows[mine] - q0)
+                              rows=rows[mine] - q0, pe=pe)
         out["pooled"].append(res["pooled"])
         for j, m in enumerate(mine):
             out["scores"][m] = res["scores"][j]

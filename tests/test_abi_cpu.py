@@ -24,7 +24,7 @@ def test_every_header_function_is_exported_and_declared(lib):
     assert sorted(_lib.SIGNATURES) == names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.qsa_abi_version() == 1
+    assert lib.qsa_abi_version() == 2
 
 
 P = ctypes.c_void_p
@@ -174,7 +174,8 @@ def test_varlen_validation_and_workspace(lib):
     def sel_call(batch=2, cu_q=FAKE, cu_k=FAKE, max_lq=100, max_lk=200, h=4, di=128, r=4,
                  budget=256, ws_bytes=1 << 40, kp=FAKE):
         return lib.qsa_prefill_varlen_select(batch, cu_q, cu_k, max_lq, max_lk, h, di, r, budget,
-                                             FAKE, FAKE, FAKE, kp, FAKE, 64, FAKE, ws_bytes, None)
+                                             FAKE, FAKE, FAKE, kp, FAKE, 64, FAKE, ws_bytes, None,
+                                             None)
 
     assert sel_call(batch=0) == 1
     assert sel_call(cu_q=None) == 1 and "cu_seqlens" in _err(lib)
@@ -200,3 +201,24 @@ def test_varlen_validation_and_workspace(lib):
     assert attn_call(scale=ctypes.c_float(float("nan"))) == 1
     assert attn_call(out=MISALIGNED) == 1
     assert attn_call(total_q=0) == 0                   # nothing to do
+
+
+def test_pooled_key_encoding_validation(lib):
+    from block_sparse_attention_06_amd.ops import _PooledPe
+
+    def pool(rope_dim, theta, d=128, first=0):
+        st = _PooledPe(rope_dim, theta)
+        return lib.qsa_pool_keys_pe(FAKE, d, 10, d, 4, first, ctypes.byref(st), FAKE, d, None)
+
+    assert pool(24, 1e4) == 2 and "rope_dim" in _err(lib)    # not a multiple of 16
+    assert pool(256, 1e4) == 2                                # wider than d_idx
+    assert pool(64, 1.0) == 1 and "rope_theta" in _err(lib)
+    assert pool(64, float("inf")) == 1
+    assert pool(64, 1e4, first=-1) == 1
+    assert pool(64, 1e4, d=60) == 2                           # d_idx not a multiple of 8
+    st = _PooledPe(64, 1e4)
+    assert lib.qsa_pool_keys_pe(FAKE, 128, 0, 128, 4, 0, ctypes.byref(st), FAKE, 128, None) == 0
+    # the whole-path drivers check the encoding before launching anything
+    bad = _PooledPe(20, 1e4)
+    assert lib.qsa_prefill_select(64, 64, 0, 4, 128, 4, 256, FAKE, FAKE, FAKE, 0, None, FAKE,
+                                  FAKE, 64, FAKE, 1 << 40, ctypes.byref(bad), None) == 2

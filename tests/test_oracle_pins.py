@@ -332,6 +332,72 @@ def test_chunked_prefill_equals_full_prefill_rows():
 
 
 # ------------------------------------------------------------------------------------
+# Positional encoding of the pooled keys
+# ------------------------------------------------------------------------------------
+
+
+def _torch_rope_complex(x: np.ndarray, pos: np.ndarray, rope_dim: int, theta: float):
+    """The same rotation written as complex multiplication (torch, fp64)."""
+    h = rope_dim // 2
+    t = torch.from_numpy(np.array(x, dtype=np.float64))
+    inv = torch.tensor(float(theta), dtype=torch.float64) ** (
+        -2.0 * torch.arange(h, dtype=torch.float64) / rope_dim)
+    ang = torch.from_numpy(np.asarray(pos, dtype=np.float64))[:, None] * inv[None, :]
+    z = torch.complex(t[:, :h], t[:, h:rope_dim]) * torch.polar(torch.ones_like(ang), ang)
+    out = t.clone()
+    out[:, :h], out[:, h:rope_dim] = z.real, z.imag
+    return out.numpy()
+
+
+@pytest.mark.parametrize("rope_dim,first_block", [(16, 0), (64, 7), (128, 1000)])
+def test_pooled_encoding_against_torch_complex_rotation(rope_dim, first_block):
+    rng = np.random.default_rng(rope_dim)
+    k = _bits(rng.standard_normal((4 * 300 + 3, 128)) / math.sqrt(128))
+    got = O.pool_keys(k, 4, (rope_dim, 1e4), first_block=first_block)
+    mean = torch.from_numpy(O.bf16_to_f64(k)[:1200]).reshape(300, 4, 128).mean(dim=1).numpy()
+    ref = _torch_rope_complex(mean, (first_block + np.arange(300)) * 4, rope_dim, 1e4)
+    np.testing.assert_array_equal(got, O.f64_to_bf16(ref))
+    # columns past rope_dim are the plain mean; position 0 is the identity
+    np.testing.assert_array_equal(got[:, rope_dim:], O.pool_keys(k, 4)[:, rope_dim:])
+    if first_block == 0:
+        np.testing.assert_array_equal(got[0], O.pool_keys(k, 4)[0])
+
+
+def test_rotary_scores_depend_on_offset_only():
+    # Rotating the query at t and the key at p keeps norms and gives a dot product that
+    # depends on t - p only (shifting both by 1000 changes nothing), for every pair.
+    rng = np.random.default_rng(11)
+    q, k = rng.standard_normal((50, 64)), rng.standard_normal((50, 64))
+    t, p = rng.integers(0, 5000, 50), rng.integers(0, 5000, 50)
+    for rd in (16, 64):
+        qr, kr = O.rope_rotate(q, t, rd, 1e6), O.rope_rotate(k, p, rd, 1e6)
+        qs, ks = O.rope_rotate(q, t + 1000, rd, 1e6), O.rope_rotate(k, p + 1000, rd, 1e6)
+        np.testing.assert_allclose((qr * kr).sum(1), (qs * ks).sum(1), rtol=1e-9, atol=1e-9)
+        np.testing.assert_allclose(np.linalg.norm(qr, axis=1), np.linalg.norm(q, axis=1),
+                                   rtol=1e-12)
+    np.testing.assert_array_equal(O.rope_rotate(q, t, 0, 1e4), q)
+
+
+def test_encoded_chunked_prefill_equals_full_prefill_rows():
+    # With the encoding, a prefix pooled earlier (its blocks at their own positions) and
+    # the chunk's new blocks pooled from first_block on give the full prefill's rows.
+    L, prefix, pe = 768, 512, (16, 1e4)
+    wl, inp = _small_prefill(L=L, budget=64, seed=9)
+    full = _run_oracle(wl, inp, rows=np.arange(prefix, L, 5), pe=pe)
+    kb = bf16_bits(inp["k_idx"])
+    pooled_prefix = O.pool_keys(kb[:prefix], 4, pe)
+    chunk = O.forward_prefill(bf16_bits(inp["q"])[prefix:], bf16_bits(inp["k"]),
+                              bf16_bits(inp["v"]), bf16_bits(inp["q_idx"])[prefix:],
+                              inp["w"].numpy()[prefix:], kb[prefix:], r=4, budget=64,
+                              q_pos0=prefix, k_pooled_prefix_bits=pooled_prefix,
+                              rows=np.arange(0, L - prefix, 5), pe=pe)
+    np.testing.assert_array_equal(chunk["sel"], full["sel"])
+    np.testing.assert_allclose(chunk["out"], full["out"], rtol=0, atol=1e-13)
+    plain = _run_oracle(wl, inp, rows=np.arange(prefix, L, 5))
+    assert not np.array_equal(plain["sel"], full["sel"])  # the encoding changes selections
+
+
+# ------------------------------------------------------------------------------------
 # Packed variable-length batches
 # ------------------------------------------------------------------------------------
 
