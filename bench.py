@@ -217,6 +217,19 @@ def bench_backward(torch, Q, wl, inp, plan, reps=2):
     return ms
 
 
+def time_calls(torch, f, reps):
+    """Average seconds of f() over reps calls after one untimed call (HIP events)."""
+    f()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        f()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps * 1e-3
+
+
 def paged_copy(torch, kc, vc, page_size, seed=1):
     """The caches [B, L, Hkv, d] scattered into pools of shuffled pages (the layout a
     serving engine's page allocator leaves), and the block table."""
@@ -541,9 +554,22 @@ def main():
         torch.cuda.synchronize()
         s_dec = bench_decode(args, torch, Q, dwl, dinp)
         progress(f"decode: {s_dec * 1e6:.1f} us per step")
+        # The MTP layer reuses the main layer's selection: its step is the decode
+        # attention alone (its own cache; the same bytes are read here).
+        mtp_plan = Q.DecodePlan(dwl.batch, dwl.hq, dwl.d, dwl.lk, dwl.budget, device=dev)
+        Q.qsa_decode_forward(dinp["q"], dinp["q_idx"], dinp["w"], dinp["k_pooled"],
+                             dinp["k_cache"], dinp["v_cache"], dinp["seq_lens"],
+                             budget=dwl.budget, plan=mtp_plan)
+        mtp_s = time_calls(torch, lambda: Q.qsa_sparse_attn_decode(
+            dinp["q"], dinp["k_cache"], dinp["v_cache"], dinp["seq_lens"], mtp_plan.sel), 20)
+        progress(f"MTP decode attention over the reused selection: {mtp_s * 1e6:.1f} us")
         own = (dwl.lk - 1) // dwl.r
         d_bytes = dwl.batch * (own * dwl.d_i * 2 + dwl.budget * dwl.hkv * 2 * dwl.d * 2 +
                                dwl.hq * dwl.d * 2 * 2)
+        line["mtp_reuse"] = {
+            "what": "MTP layer attending over the main layer's selections (no indexer)",
+            "prefill128k_ms": attn_ms, "prefill128k_main_step_ms": ms_step,
+            "decode1m_us": mtp_s * 1e6, "decode1m_main_step_us": s_dec * 1e6}
         line["decode"] = {"workload": dwl.name, "batch": dwl.batch, "context": dwl.lk,
                           "value": dwl.batch / s_dec, "unit": "tokens/s", "ms_per_step": s_dec * 1e3,
                           "steps": args.decode_steps,

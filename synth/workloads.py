@@ -54,6 +54,7 @@ class Workload:
     needle_spacing: int  # 0: no needles
     pooled_prefix_blocks: int  # leading blocks whose pooled keys arrive as a cache
     aligned_fraction: float = 0.10
+    smooth: int = 0  # prefill: > 0 correlates q_idx and w along the tokens over ~smooth tokens
 
     @property
     def n_sel(self) -> int:
@@ -127,6 +128,23 @@ def _fill_normal(out: torch.Tensor, ss: np.random.SeedSequence, scale: float) ->
         flat[r0:r1].copy_(x)  # fp32 -> bf16 rounds to nearest even
 
 
+def _smoothed_normal(shape, ss: np.random.SeedSequence, span: int, device) -> torch.Tensor:
+    """fp32 draws with N(0, 1) marginals, correlated along axis 0: white N(0, 1) noise
+    filtered by a causal exponential window (weights a^k, a = 1 - 1/span, k < 4 span),
+    normalised to unit variance; the lag-l correlation is about a^l."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(_chunk_seed(ss, 0))
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    a = 1.0 - 1.0 / span
+    taps = 4 * span
+    kern = a ** torch.arange(taps, device=device, dtype=torch.float32)
+    kern = kern / kern.square().sum().sqrt()
+    flat = x.reshape(shape[0], -1).T.unsqueeze(1)  # [channels, 1, tokens]
+    y = torch.nn.functional.conv1d(torch.nn.functional.pad(flat, (taps - 1, 0)),
+                                   kern.flip(0).view(1, 1, taps))
+    return y.squeeze(1).T.reshape(shape)
+
+
 def _fill_uniform(out: torch.Tensor, ss: np.random.SeedSequence) -> None:
     gen = torch.Generator(device=out.device)
     gen.manual_seed(_chunk_seed(ss, 0))
@@ -197,9 +215,16 @@ def generate(wl: Workload, device="cpu", seq_lens=None) -> dict:
         _fill_normal(q, seeds["q"], sd)
         _fill_normal(k, seeds["k"], sd)
         _fill_normal(v, seeds["v"], sd)
-        _fill_normal(q_idx, seeds["q_idx"], sdi)
         _fill_normal(k_idx, seeds["k_idx"], sdi)
-        _fill_uniform(w, seeds["w"])
+        if wl.smooth:
+            # Neighbouring queries alike (real selections overlap): the same marginals,
+            # correlated along the tokens; w through the normal CDF stays U(0, 1).
+            q_idx.copy_(_smoothed_normal(q_idx.shape, seeds["q_idx"], wl.smooth, device) * sdi)
+            z = _smoothed_normal(w.shape, seeds["w"], wl.smooth, device)
+            w.copy_(0.5 * (1.0 + torch.erf(z / math.sqrt(2.0))))
+        else:
+            _fill_normal(q_idx, seeds["q_idx"], sdi)
+            _fill_uniform(w, seeds["w"])
         kp = None
         if wl.pooled_prefix_blocks:
             kp = torch.empty((wl.pooled_prefix_blocks, wl.d_i), dtype=bf, device=device)
