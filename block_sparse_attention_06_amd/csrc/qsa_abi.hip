@@ -377,6 +377,8 @@ qsa_status qsa_indexer_kl_target(int64_t lq, int64_t lk, int hq, int hkv, int d,
                                  void* stream) {
   QSA_TRY(check_r(r));
   QSA_TRY(check_attn_shape(hq, hkv, d));
+  QSA_REQUIRE(hkv <= qsa::kKlMaxGroups, QSA_ERR_UNSUPPORTED,
+              "hkv=%d: the dense KL passes take up to %d KV groups", hkv, qsa::kKlMaxGroups);
   QSA_REQUIRE(lq >= 0 && lq < ((int64_t)1 << 31) && lk >= 1, QSA_ERR_INVALID_ARGUMENT,
               "lq=%lld lk=%lld", (long long)lq, (long long)lk);
   QSA_REQUIRE(q_pos0 >= 0 && q_pos0 + lq <= lk, QSA_ERR_INVALID_ARGUMENT,

@@ -187,6 +187,7 @@ hipError_t launch_sparse_attn_bwd(BwdArgs a, char* ws, size_t ws_bytes, hipStrea
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 
 // ---- indexer warm-up (KL distillation) ----
+constexpr int kKlMaxGroups = 4;  // KV groups the dense KL passes hold in one wave
 struct KlArgs {
   const uint16_t* q;  // [lq][hq][d]
   const uint16_t* k;  // [lk][hkv][d]

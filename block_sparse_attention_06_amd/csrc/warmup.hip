@@ -10,13 +10,11 @@
 // constant.
 //
 // Kernels:
-//  * kl_lse_kernel: dense causal lse of every (query row, head), one wave per (row,
-//    KV group) over keys 0..t in tiles of 16 (S^T = K.Q^T on v_mfma_f32_16x16x32_bf16,
-//    online max and sum as in the sparse forward), two tiles in flight.
-//  * kl_target_kernel: one wave per row over the keys of its scored blocks: both
-//    groups' probabilities, summed over the heads (a reduction across the 16 lanes of
-//    a quad group), then the max over each block's 4 keys; writes the unnormalised
-//    pooled values.
+//  * kl_dense_kernel<TARGET = false>: dense causal lse of every (query row, head);
+//    kl_dense_kernel<TARGET = true>: per scored block, the max over its 4 keys of the
+//    head-summed probabilities exp(S - lse) (unnormalised). Both walk the keys in
+//    steps shared by a workgroup's rows through LDS (S = Q.K^T on
+//    v_mfma_f32_16x16x32_bf16).
 //  * kl_loss_kernel: one workgroup per row: normalises the target, the scores'
 //    log-softmax, the KL value and dL/ds = softmax(s) - target, sums in fp64.
 //  * index_scores_bwd_dq_kernel / _dk_kernel: the gradients of the scores with
@@ -52,129 +50,200 @@ __device__ __forceinline__ uint2 w_repack(const uint4 (&r)[4], int e) {
 
 }  // namespace
 
-// ---- dense lse ------------------------------------------------------------------------
+// ---- dense passes over shared key tiles --------------------------------------------------
+//
+// Both passes read every key before the query. A workgroup of 8 waves takes 8 * RPW
+// consecutive query rows (RPW per wave, all KV groups of a row in one wave, so the
+// target's head sum stays in the wave) and walks the keys its rows need in steps of KS:
+// the step's keys (every group) are loaded once, cooperatively, into a double-buffered
+// LDS tile, two steps ahead in registers, and every wave reads them from there as the
+// B operand of S = Q.K^T for each of its rows. The lse pass keeps the online max and
+// sum of every (row, head); the target pass sums exp(S - lse) over the heads and takes
+// the max over each block's 4 keys.
 
-template <int D>
-__global__ __launch_bounds__(256) void kl_lse_kernel(KlArgs a) {
+constexpr int kKlWaves = 8;
+// Start of the running max: finite, so that x - m is never inf - inf, and far below any
+// score, so that 2^(m - x) is 0 for the first real one.
+constexpr float kKlNoMax = -1e30f;
+
+template <int D, bool TARGET, int KS, int NG, int RPW>
+__global__ __launch_bounds__(512) void kl_dense_kernel(KlArgs a) {
   constexpr int NC = D / 32;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int VPR = D / 8;     // 16-byte vectors of one key row of one group
+  constexpr int KROW = VPR + 1;  // padded LDS row
+  constexpr int TILE_ROWS = kKlWaves * RPW;
+  constexpr int LPT = (KS * NG * VPR + 511) / 512;  // 16-byte loads per thread per step
+  __shared__ uint4 kt[2][NG][KS][KROW];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15;
   const int quad = lane >> 4;
-  const int G = a.hq / a.hkv;
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t row = item / a.hkv;
-  const int g = (int)(item - row * a.hkv);
-  if (row >= a.lq) return;
-  const int64_t t = a.q_pos0 + row;
-  const int64_t kstride = (int64_t)a.hkv * D;
-  const bool hv = c16 < G;
-  uint4 Qc[NC];
-  {
-    const uint16_t* qp = a.q + (row * a.hq + g * G + (hv ? c16 : 0)) * (int64_t)D + quad * 8;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) Qc[c] = hv ? ld16(qp + c * 32) : make_uint4(0, 0, 0, 0);
-  }
-  const int n_tiles = (int)(t / 16) + 1;  // keys 0..t
-  auto load = [&](uint4 (&K)[NC], int tile) {
-    const int64_t j = min((int64_t)tile * 16 + c16, t);  // past t: an in-bounds row, masked
-    const uint16_t* kp = a.k + j * kstride + g * D + quad * 8;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) K[c] = ld16(kp + c * 32);
-  };
-  float m_run = -INFINITY, l_run = 0.f;
-  auto step = [&](const uint4 (&K)[NC], int tile) {
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NC; ++c) S = mfma_16x16x32(K[c], Qc[c], S);
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      x[i] = ((int64_t)tile * 16 + 4 * quad + i <= t) ? S[i] * a.scale_log2 : -INFINITY;
-    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = wave_xor_max(mt, 16);
-    mt = wave_xor_max(mt, 32);
-    const float m_new = fmaxf(m_run, mt);  // finite: key tile*16 <= t is never masked
-    l_run = l_run * exp2f(m_run - m_new) + (exp2f(x[0] - m_new) + exp2f(x[1] - m_new)) +
-            (exp2f(x[2] - m_new) + exp2f(x[3] - m_new));
-    m_run = m_new;
-  };
-  uint4 K0[NC], K1[NC];
-  load(K0, 0);
-  for (int tile = 0; tile < n_tiles; tile += 2) {
-    load(K1, min(tile + 1, n_tiles - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    step(K0, tile);
-    load(K0, min(tile + 2, n_tiles - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    if (tile + 1 < n_tiles) step(K1, tile + 1);
-  }
-  float l_tot = wave_xor_sum(l_run, 16);
-  l_tot = wave_xor_sum(l_tot, 32);
-  if (quad == 0 && hv) a.lse[row * a.hq + g * G + c16] = m_run * kLn2W + logf(l_tot);
-}
+  const int H = a.hkv;
+  const int G = a.hq / H;
+  const bool hv = c16 < G;  // the Q operand's row c16 is a head of the group
+  const int64_t row0 = (int64_t)blockIdx.x * TILE_ROWS;
+  const int64_t t_last = a.q_pos0 + min(row0 + TILE_ROWS, a.lq) - 1;
+  // Keys the workgroup needs: 0..t_last (lse), or the last row's scored blocks (target).
+  const int64_t kend = TARGET ? min(t_last / a.r, a.nblk) * a.r : t_last + 1;
+  if (kend <= 0) return;
+  const int nsteps = (int)((kend + KS - 1) / KS);
+  const int64_t kstride = (int64_t)H * D;
 
-// ---- pooled target --------------------------------------------------------------------
-
-template <int D>
-__global__ __launch_bounds__(256) void kl_target_kernel(KlArgs a) {
-  constexpr int NC = D / 32;
-  constexpr int kMaxGroups = 2;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c16 = lane & 15;
-  const int quad = lane >> 4;
-  const int G = a.hq / a.hkv;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= a.lq) return;
-  const int64_t t = a.q_pos0 + row;
-  const int64_t own = min(t / a.r, a.nblk);  // scored blocks 0 .. own-1
-  if (own <= 0) return;
-  const int64_t kstride = (int64_t)a.hkv * D;
-  const bool hv = c16 < G;
-  float* trow = a.target + row * a.ld;
-  const int n_tiles = (int)((own + 3) / 4);  // 16 keys = 4 blocks per tile
-  for (int g0 = 0; g0 < a.hkv; g0 += kMaxGroups) {
-    const int ng = min(kMaxGroups, a.hkv - g0);
-    uint4 Qc[kMaxGroups][NC];
-    float L2[kMaxGroups];
+  int64_t row[RPW], lim[RPW];  // lim: the row's keys are 0 .. lim-1
+  bool rv[RPW];
+  uint4 Qc[RPW][NG][NC];
+  float L2v[RPW][NG][4], m_run[RPW][NG][4], l_run[RPW][NG][4];  // heads 4*quad + i
 #pragma unroll
-    for (int gi = 0; gi < kMaxGroups; ++gi) {
-      const int g = g0 + (gi < ng ? gi : 0);
-      const bool ok = hv && gi < ng;
-      const uint16_t* qp = a.q + (row * a.hq + g * G + (hv ? c16 : 0)) * (int64_t)D + quad * 8;
+  for (int p = 0; p < RPW; ++p) {
+    row[p] = row0 + wave * RPW + p;
+    rv[p] = row[p] < a.lq;
+    const int64_t t = a.q_pos0 + (rv[p] ? row[p] : 0);
+    lim[p] = !rv[p] ? 0 : (TARGET ? min(t / a.r, a.nblk) * a.r : t + 1);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) Qc[gi][c] = ok ? ld16(qp + c * 32) : make_uint4(0, 0, 0, 0);
-      L2[gi] = ok ? a.lse[row * a.hq + g * G + c16] * kLog2eW : 0.f;
-    }
-    for (int tile = 0; tile < n_tiles; ++tile) {
-      const int64_t j = (int64_t)tile * 16 + c16;  // key row of this lane
-      const int64_t jc = min(j, own * a.r - 1);
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < NG; ++g) {
+      const bool ok = rv[p] && hv && g < H;
+      const uint16_t* qp =
+          a.q + ((rv[p] ? row[p] : 0) * a.hq + (g < H ? g : 0) * G + (hv ? c16 : 0)) * (int64_t)D +
+          quad * 8;
 #pragma unroll
-      for (int gi = 0; gi < kMaxGroups; ++gi) {
-        if (gi >= ng) break;
-        const uint16_t* kp = a.k + jc * kstride + (g0 + gi) * D + quad * 8;
-        f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NC; ++c) S = mfma_16x16x32(ld16(kp + c * 32), Qc[gi][c], S);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = hv && (int64_t)tile * 16 + 4 * quad + i < own * a.r;
-          acc[i] += ok ? exp2f(S[i] * a.scale_log2 - L2[gi]) : 0.f;
-        }
-      }
-      // Sum over the heads (the 16 lanes of this quad group), then the max over the
-      // block's 4 keys: block 4*tile + quad.
+      for (int c = 0; c < NC; ++c) Qc[p][g][c] = ok ? ld16(qp + c * 32) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) acc[i] += __shfl_xor(acc[i], d, 64);
+        const int h = 4 * quad + i;
+        L2v[p][g][i] = !TARGET ? 0.f
+                       : (rv[p] && g < H && h < G) ? a.lse[row[p] * a.hq + g * G + h] * kLog2eW
+                                                   : INFINITY;
+        m_run[p][g][i] = kKlNoMax;
+        l_run[p][g][i] = 0.f;
       }
-      const float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-      const int64_t b = (int64_t)tile * 4 + quad;
-      if (c16 == 0 && b < own) trow[b] = g0 == 0 ? mx : trow[b] + mx;
     }
+  }
+
+  // Step loads: vector e = (key, group, v) of the 16 keys, every group.
+  auto issue = [&](uint4 (&R)[LPT], int s) {
+#pragma unroll
+    for (int l = 0; l < LPT; ++l) {
+      const int e = tid + 512 * l;
+      const int key = e / (NG * VPR), g = (e / VPR) % NG, v = e % VPR;
+      const int64_t j = min((int64_t)s * KS + key, kend - 1);
+      // Unconditional (a group past the last reads the last one, never used), so that
+      // the waits count loads exactly.
+      R[l] = ld16(a.k + j * kstride + min(g, H - 1) * D + v * 8);
+    }
+  };
+  auto store = [&](const uint4 (&R)[LPT], int slot) {
+#pragma unroll
+    for (int l = 0; l < LPT; ++l) {
+      const int e = tid + 512 * l;
+      const int key = e / (NG * VPR), g = (e / VPR) % NG, v = e % VPR;
+      if (e < KS * NG * VPR) kt[slot][g][key][v] = R[l];
+    }
+  };
+  // S = Q.K^T on the same operands (heads as MFMA rows, keys as columns): lane c16
+  // holds key j0 + c16, rows 4*quad + i are the heads. The lse pass keeps running
+  // (max, sum) per lane and head over the lane's keys (no cross-lane work per step);
+  // the target pass sums a lane's heads in registers, then across the quads, and takes
+  // each block's max over 4 neighbouring lanes.
+  auto compute = [&](int s, int slot) {
+#pragma unroll
+    for (int u = 0; u < KS / 16; ++u) {
+      const int64_t j0 = (int64_t)s * KS + u * 16;
+      const int64_t key = j0 + c16;
+      float acc[RPW];
+#pragma unroll
+      for (int p = 0; p < RPW; ++p) acc[p] = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g >= H) break;
+        uint4 Kc[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) Kc[c] = kt[slot][g][u * 16 + c16][quad + 4 * c];
+#pragma unroll
+        for (int p = 0; p < RPW; ++p) {
+          if (j0 >= lim[p]) continue;
+          f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NC; ++c) S = mfma_16x16x32(Qc[p][g][c], Kc[c], S);
+          if constexpr (TARGET) {
+            // Padding heads carry L2 = +inf, so they add exp2(-inf) = 0.
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[p] += __builtin_amdgcn_exp2f(S[i] * a.scale_log2 - L2v[p][g][i]);
+          } else {
+            // Online (max, sum) with one exponential per score: e = 2^-|x - m| is the
+            // factor for the old sum when x is the new max, else the new term.
+            const bool kok = key < lim[p];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = kok ? S[i] * a.scale_log2 : -INFINITY;
+              const float dlt = x - m_run[p][g][i];
+              const float e = __builtin_amdgcn_exp2f(-fabsf(dlt));
+              const bool up = dlt > 0.f;
+              l_run[p][g][i] = up ? fmaf(l_run[p][g][i], e, 1.f) : l_run[p][g][i] + e;
+              m_run[p][g][i] = up ? x : m_run[p][g][i];
+            }
+          }
+        }
+      }
+      if constexpr (TARGET) {
+#pragma unroll
+        for (int p = 0; p < RPW; ++p) {
+          if (j0 >= lim[p]) continue;
+          float v = key < lim[p] ? acc[p] : 0.f;
+          v += __shfl_xor(v, 16, 64);
+          v += __shfl_xor(v, 32, 64);  // key j0 + c16, summed over every head
+          v = fmaxf(v, __shfl_xor(v, 1, 64));
+          v = fmaxf(v, __shfl_xor(v, 2, 64));  // max over the block's 4 keys
+          const int64_t b = key / 4;
+          if (quad == 0 && (c16 & 3) == 0 && b * a.r < lim[p]) a.target[row[p] * a.ld + b] = v;
+        }
+      }
+    }
+  };
+
+  // Two steps of loads in flight: unconditional (past the end they repeat the last
+  // step), so that every wait is for exactly one step's loads.
+  uint4 R0[LPT], R1[LPT];
+  issue(R0, 0);
+  issue(R1, min(1, nsteps - 1));
+  store(R0, 0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    issue(R0, min(s + 2, nsteps - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s, 0);
+    if (s + 1 < nsteps) store(R1, 1);
+    __syncthreads();
+    if (s + 1 >= nsteps) break;
+    issue(R1, min(s + 3, nsteps - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s + 1, 1);
+    if (s + 2 < nsteps) store(R0, 0);
+    __syncthreads();
+  }
+
+  if constexpr (!TARGET) {
+    // Combine the 16 key lanes' (max, sum) of each head.
+#pragma unroll
+    for (int p = 0; p < RPW; ++p)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g >= H) break;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float m = m_run[p][g][i], l = l_run[p][g][i];
+#pragma unroll
+          for (int dd = 1; dd < 16; dd <<= 1) {
+            const float mo = __shfl_xor(m, dd, 64), lo = __shfl_xor(l, dd, 64);
+            const float mn = fmaxf(m, mo);
+            l = l * exp2f(m - mn) + lo * exp2f(mo - mn);
+            m = mn;
+          }
+          const int h = 4 * quad + i;
+          if (rv[p] && c16 == 0 && h < G) a.lse[row[p] * a.hq + g * G + h] = m * kLn2W + logf(l);
+        }
+      }
   }
 }
 
@@ -414,16 +483,29 @@ __global__ __launch_bounds__(256) void pool_keys_bwd_kernel(IdxBwdArgs a) {
 
 // ---- host side ------------------------------------------------------------------------
 
+namespace {
+
+// Both passes of one shape: rows per workgroup = 8 waves * RPW.
+template <int D, int KS, int NG, int RPW>
+void launch_kl_pair(const KlArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.lq + kKlWaves * RPW - 1) / (kKlWaves * RPW)));
+  hipLaunchKernelGGL((kl_dense_kernel<D, false, KS, NG, RPW>), grid, dim3(512), 0, stream, a);
+  hipLaunchKernelGGL((kl_dense_kernel<D, true, KS, NG, RPW>), grid, dim3(512), 0, stream, a);
+}
+
+}  // namespace
+
 hipError_t launch_kl_target(const KlArgs& a, hipStream_t stream) {
   if (a.lq <= 0) return hipSuccess;
-  const dim3 g1((unsigned)((a.lq * a.hkv + 3) / 4));
-  const dim3 g2((unsigned)((a.lq + 3) / 4));
-  if (a.d == 256) {
-    hipLaunchKernelGGL(kl_lse_kernel<256>, g1, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(kl_target_kernel<256>, g2, dim3(256), 0, stream, a);
+  if (a.hkv > kKlMaxGroups) return hipErrorInvalidValue;
+  // Up to 2 groups: 2 rows per wave, 32 keys per step; 3 or 4 groups: 1 row per wave
+  // (the same Q registers), 16 keys per step (the same LDS).
+  if (a.hkv <= 2) {
+    if (a.d == 256) launch_kl_pair<256, 32, 2, 2>(a, stream);
+    else launch_kl_pair<128, 32, 2, 2>(a, stream);
   } else {
-    hipLaunchKernelGGL(kl_lse_kernel<128>, g1, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(kl_target_kernel<128>, g2, dim3(256), 0, stream, a);
+    if (a.d == 256) launch_kl_pair<256, 16, 4, 1>(a, stream);
+    else launch_kl_pair<128, 16, 4, 1>(a, stream);
   }
   return hipGetLastError();
 }

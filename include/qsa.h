@@ -213,7 +213,8 @@ qsa_status qsa_sparse_attn_bwd(int64_t lq, int64_t lk, int hq, int hkv, int d, i
  *   lse[i][h] = ln sum_{j <= t_i} exp(scale q[i][h] . k[j][g]), fp32 [lq][hq];
  *   target[i][b] = max_{j in block b} sum_h exp(scale q[i][h] . k[j][g] - lse[i][h])
  *   for b < B_i (unnormalised), fp32 [lq][ld] (ld >= lk / r, ld % 4 == 0; entries
- *   b >= B_i are not written). q, k as for qsa_sparse_attn_fwd.
+ *   b >= B_i are not written). q, k as for qsa_sparse_attn_fwd; hkv <= 4
+ *   (QSA_ERR_UNSUPPORTED otherwise: the head sum of a row stays in one wave).
  * qsa_indexer_kl_loss: from the indexer scores s [lq][ld] (stage 2) and target,
  *   loss[i] = KL(p_i || softmax(s_i)) with p_i = target_i / sum_b target_i[b] (0 when
  *   B_i = 0), fp32 [lq]; dscores[i][b] = softmax(s_i)[b] - p_i[b] for b < B_i,

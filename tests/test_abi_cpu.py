@@ -145,6 +145,8 @@ def test_warmup_validation(lib):
                                      None) == 1
     assert lib.qsa_indexer_kl_target(10, 100, 24, 2, 192, 4, FAKE, FAKE, 0, f, FAKE, FAKE, 28,
                                      None) == 2
+    assert lib.qsa_indexer_kl_target(10, 100, 24, 6, 256, 4, FAKE, FAKE, 0, f, FAKE, FAKE, 28,
+                                     None) == 2 and "hkv" in _err(lib)  # > 4 KV groups
     assert lib.qsa_indexer_kl_target(10, 100, 24, 2, 256, 4, FAKE, FAKE, 95, f, FAKE, FAKE, 28,
                                      None) == 1
     assert lib.qsa_indexer_kl_target(10, 100, 24, 2, 256, 4, FAKE, FAKE, 0, f, FAKE, FAKE, 24,

@@ -64,6 +64,13 @@ def test_kl_target_model_shape_and_peaky():
     _target_case(lq=96, lk=700, q_pos0=604, hq=6, hkv=2, d=128, seed=62, unscaled=True)
 
 
+def test_kl_target_more_groups():
+    # 3 and 4 KV groups take the one-row-per-wave shape; 1 group the two-row one.
+    _target_case(lq=37, lk=300, q_pos0=263, hq=12, hkv=3, d=256, seed=67)
+    _target_case(lq=70, lk=150, q_pos0=80, hq=16, hkv=4, d=128, seed=68)
+    _target_case(lq=33, lk=33, q_pos0=0, hq=16, hkv=1, d=128, seed=69)
+
+
 def test_kl_loss_and_score_gradient():
     # The loss kernel on the GPU's own scores and target, against the oracle on the same
     # numbers; then end to end against the oracle's own scores and target.
