@@ -297,22 +297,28 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
 
 // ------------------------------------------------------------------------------------
 // Stage 2 for a few query rows per sequence (decode): a streaming scan of the pooled
-// keys. One wave per (sequence, row, range of blocks), no LDS and no barriers: the
-// wave keeps its token's 4 heads as the A operand (rows 0-3 of the MFMA tile, the rest
-// zero) and loads pooled keys straight into B operands, two 64-block tiles in flight
-// (the next tile is loaded before the current one is multiplied). Same column
-// permutation and 16-byte stores as the GEMM above.
+// keys. One wave per (sequence, row, range of blocks), no barriers: the wave keeps its
+// token's 4 heads as the A operand (rows 0-3 of the MFMA tile, the rest zero). A tile
+// of 64 pooled keys is read from memory contiguously (instruction u, lane L: bytes
+// 1024 u + 16 L of the tile for d_I = 128, whole rows per 16 lanes) and turned into B
+// operands (lane (c16, quad) of column set j needs chunk quad + 4c of row 16 j + c16)
+// through a wave-private LDS half tile whose 16-byte chunks are XOR-swizzled by the
+// row, so that both the contiguous writes and the strided reads hit distinct banks.
+// Two tiles are in flight: a tile's loads are issued before the previous one is staged
+// and multiplied.
 // ------------------------------------------------------------------------------------
 
 template <int DI, bool CAND>
-__global__ __launch_bounds__(256) void index_scores_scan_kernel(ScoreArgs a, int n_ranges,
+__global__ __launch_bounds__(256, 2) void index_scores_scan_kernel(ScoreArgs a, int n_ranges,
                                                                 int blocks_per_wave) {
   // With CAND, a wave's range is one top-k segment (kTopkWaveSeg blocks, tiles of 64):
-  // each tile's rank keys are parked in LDS (one per lane), and at the end the wave
-  // extracts the segment's kTopkWaveKeep best for the top-k merge.
+  // each tile's scores wait in LDS (one per lane and tile), and at the end the wave
+  // writes them and extracts the segment's kTopkWaveKeep best for the top-k merge.
   constexpr int kSegTiles = kTopkWaveSeg / 64;
-  __shared__ uint64_t rk_lds[CAND ? 4 : 1][CAND ? kTopkWaveSeg : 1];
   constexpr int NC = DI / 32;
+  constexpr int CPR = DI / 8;  // 16-byte chunks per pooled key = loads per lane per tile
+  __shared__ uint4 stage[4][32 * CPR];  // half a tile per wave
+  __shared__ float scores_lds[4][kSegTiles * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;
@@ -356,88 +362,111 @@ __global__ __launch_bounds__(256) void index_scores_scan_kernel(ScoreArgs a, int
   for (int h = 0; h < 4; ++h)
     W[h] = h < a.h_idx ? a.w[(int64_t)bi * a.w_bs + row * a.h_idx + h] : 0.f;
 
-  uint4 B0[4][NC], B1[4][NC];
-  auto load = [&](uint4 (&B)[4][NC], int64_t nb) {
+  uint4* st = stage[wave];
+  uint4 R0[CPR], R1[CPR];
+  // Unconditional loads (rows past the range clamp to its last one, never used), so
+  // that every wait counts exactly one tile.
+  auto load = [&](uint4 (&R)[CPR], int64_t nb) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t blk = min(nb + 4 * c16 + j, n1 - 1);  // clamped; extra columns unused
-      const uint16_t* p = kpb + blk * DI + quad * 8;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) B[j][c] = ld16_stream(p + c * 32);  // read once per pass
+    for (int u = 0; u < CPR; ++u) {
+      const int e = u * 64 + lane;
+      const int64_t blk = min(nb + e / CPR, n1 - 1);
+      R[u] = ld16_stream(kpb + blk * DI + (e % CPR) * 8);  // read once per pass
     }
   };
-  auto compute = [&](const uint4 (&B)[4][NC], int64_t nb) {
-    float s[4];
+  // Stage a tile and multiply it, half a tile (32 rows, two MFMA column sets) at a time:
+  // returns the scores of blocks nb + 16 j + c16 (valid in the quad-0 lanes).
+  auto compute = [&](const uint4 (&R)[CPR], float (&s)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc = mfma_16x16x32(A[c], B[j][c], acc);
-      s[j] = W[0] * fmaxf(acc[0], 0.f) + W[1] * fmaxf(acc[1], 0.f) + W[2] * fmaxf(acc[2], 0.f) +
-             W[3] * fmaxf(acc[3], 0.f);
-    }
-    const int64_t blk0 = nb + 4 * c16;
-    if (!CAND && quad == 0 && blk0 < n1)
-      *reinterpret_cast<float4*>(orow + blk0) = make_float4(s[0], s[1], s[2], s[3]);
-    if constexpr (CAND) {
-      // Lane L takes block nb + L: element L % 4 of quad-0 lane L / 4.
-      float v[4];
+      for (int u = h * CPR / 2; u < (h + 1) * CPR / 2; ++u) {
+        const int e = u * 64 + lane;
+        const int r = e / CPR - 32 * h, ch = e % CPR;
+        st[r * CPR + (ch ^ (r & (CPR - 1)))] = R[u];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = __shfl(s[j], lane >> 2, 64);
-      const int j = lane & 3;
-      const float mine = j == 0 ? v[0] : (j == 1 ? v[1] : (j == 2 ? v[2] : v[3]));
-      const int64_t blk = nb + lane;
-      const int it = (int)((nb - n0) >> 6);
-      rk_lds[wave][it * 64 + lane] = blk < n1 ? rank_key(mine, (int32_t)blk) : 0ull;
+      for (int jj = 0; jj < 2; ++jj) {
+        const int r = 16 * jj + c16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          acc = mfma_16x16x32(A[c], st[r * CPR + ((quad + 4 * c) ^ (r & (CPR - 1)))], acc);
+        s[2 * h + jj] = W[0] * fmaxf(acc[0], 0.f) + W[1] * fmaxf(acc[1], 0.f) +
+                        W[2] * fmaxf(acc[2], 0.f) + W[3] * fmaxf(acc[3], 0.f);
+      }
+      // The next half's stores must not pass these reads.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   };
   const int n_tiles = (int)((n1 - n0 + 63) / 64);
-  // Each tile's loads are issued before the previous tile's MFMAs: the prefetches are
-  // unconditional (addresses past the range clamp to its last block) and a scheduling
-  // barrier keeps the compiler from sinking them below the MFMAs, which would leave a
-  // wave only one tile in flight while it waits.
-  load(B0, n0);
-  for (int it = 0; it < n_tiles; it += 2) {
-    const int64_t nb = n0 + (int64_t)it * 64;
-    load(B1, nb + 64);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(B0, nb);
-    load(B0, nb + 128);
-    __builtin_amdgcn_sched_barrier(0);
-    if (it + 1 < n_tiles) compute(B1, nb + 64);
-  }
-  if constexpr (CAND) {
-    const int n_valid = (int)(n1 - n0);
-    // The segment's scores leave in one burst of coalesced float4 stores after its
-    // loads (stores interleaved with the key stream cost HBM read/write turnarounds);
-    // the rank keys in LDS carry each score, a -0 coming back as +0.
-    const uint64_t* seg = rk_lds[wave];
+
+  // Lane L's score: block nb + L of the tile (element L / 16 of quad-0 lane L % 16).
+  auto lane_score = [&](const uint4 (&R)[CPR]) -> float {
+    float s[4];
+    compute(R, s);
+    float v[4];
 #pragma unroll
-    for (int q = 0; q < kTopkWaveSeg / 256; ++q) {
-      const int p = q * 256 + 4 * lane;
-      if (p < n_valid) {
-        float f[4];
+    for (int j = 0; j < 4; ++j) v[j] = __shfl(s[j], c16, 64);
+    return quad == 0 ? v[0] : (quad == 1 ? v[1] : (quad == 2 ? v[2] : v[3]));
+  };
+
+  // Streams up to kSegTiles tiles from block c0 with two tiles in flight, parking one
+  // score per lane and tile in the wave's LDS slots (no global stores in the stream: a
+  // store among the loads would make every wait a full drain).
+  float* sc = scores_lds[wave];
+  auto stream = [&](int64_t c0, int nt) {
+    load(R0, c0);
+    load(R1, c0 + 64);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = key_to_float((uint32_t)(seg[p + e] >> 32));
-        if (p + 4 <= n_valid) {
-          *reinterpret_cast<float4*>(orow + n0 + p) = make_float4(f[0], f[1], f[2], f[3]);
-        } else {
-          for (int e = 0; e < n_valid - p; ++e) orow[n0 + p + e] = f[e];
-        }
-      }
+    for (int it = 0; it < kSegTiles; it += 2) {
+      if (it >= nt) break;
+      const int64_t nb = c0 + (int64_t)it * 64;
+      sc[it * 64 + lane] = lane_score(R0);
+      if (it + 2 < kSegTiles) load(R0, nb + 128);
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + 1 < nt) sc[(it + 1) * 64 + lane] = lane_score(R1);
+      if (it + 3 < kSegTiles) load(R1, nb + 192);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  if constexpr (!CAND) {
+    // Chunks of kSegTiles tiles, each streamed, then stored in one burst.
+    for (int64_t c0 = n0; c0 < n1; c0 += 64 * kSegTiles) {
+      const int nv = (int)min(n1 - c0, (int64_t)64 * kSegTiles);
+      stream(c0, (nv + 63) / 64);
+#pragma unroll
+      for (int i = 0; i < kSegTiles; ++i)
+        if (i * 64 + lane < nv) orow[c0 + i * 64 + lane] = sc[i * 64 + lane];  // own slots
+    }
+  } else {
+    stream(n0, n_tiles);
+    const int n_valid = (int)(n1 - n0);
+    // The segment's scores leave in one burst of coalesced stores after its loads
+    // (stores interleaved with the key stream cost HBM read/write turnarounds); a -0
+    // leaves as +0, as the rank keys see it.
     uint64_t rk[kSegTiles];
 #pragma unroll
-    for (int i = 0; i < kSegTiles; ++i) rk[i] = i < n_tiles ? seg[i * 64 + lane] : 0ull;
+    for (int i = 0; i < kSegTiles; ++i) {
+      const int p = i * 64 + lane;
+      rk[i] = p < n_valid ? rank_key(sc[p], (int32_t)(n0 + p)) : 0ull;
+      if (p < n_valid) orow[n0 + p] = key_to_float((uint32_t)(rk[i] >> 32));
+    }
     const int keep = min(n_valid, kTopkWaveKeep);
     float* cv = a.cand.cand_val + cslot * kTopkWaveKeep;
     int32_t* ci = a.cand.cand_idx + cslot * kTopkWaveKeep;
-    // The extraction packs its survivors into the first 64 slots of this wave's keys,
-    // which are all in registers by now.
-    const uint64_t last = wave_extract_top<kSegTiles>(rk, keep, rk_lds[wave], [&](int k, uint64_t w) {
-      cv[k] = key_to_float((uint32_t)(w >> 32));
-      ci[k] = rank_key_id(w);
-    });
+    // The extraction packs its survivors into 64 wave-private slots: the staging tile.
+    const uint64_t last =
+        wave_extract_top<kSegTiles>(rk, keep, reinterpret_cast<uint64_t*>(st), [&](int k, uint64_t w) {
+          cv[k] = key_to_float((uint32_t)(w >> 32));
+          ci[k] = rank_key_id(w);
+        });
     if (lane == 0) {
       for (int k = keep; k < kTopkWaveKeep; ++k) {
         cv[k] = __builtin_nanf("");

@@ -116,6 +116,33 @@ def test_index_scores_batched_seq_lens():
             assert np.all(np.abs(got[i, :own] - ref[i, :own]) <= 2e-5 * bound[i, :own] + 1e-30)
 
 
+@pytest.mark.parametrize("d_i,h_i,lq,seq", [(128, 4, 4, [800_003, 333_337, 4093, 5]),
+                                             (64, 3, 1, [262_147, 1_000_000, 65, 4])])
+def test_index_scores_streaming_scan(d_i, h_i, lq, seq):
+    """Few rows per sequence take the streaming scan: long ranges split into several
+    chunks per wave, ragged ends, rows with no block to score."""
+    bsz = len(seq)
+    nblk = max(seq) // 4
+    _say(f"scores scan lq={lq} d_i={d_i} seq_lens={seq}")
+    q = _randn_bf16((bsz, lq, h_i, d_i), 6, 1 / math.sqrt(d_i))
+    kp = _randn_bf16((bsz, nblk, d_i), 7, 1 / math.sqrt(d_i))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(8)
+    w = torch.rand((bsz, lq, h_i), generator=g, device=DEV) - 0.3
+    sl = torch.tensor(seq, dtype=torch.int32, device=DEV)
+    s = Q.qsa_index_scores(q, w, kp, seq_lens=sl)
+    torch.cuda.synchronize()
+    for b in range(bsz):
+        pos = seq[b] - lq + np.arange(lq)
+        qf, kf, wf = O.bf16_to_f64(bits(q[b])), O.bf16_to_f64(bits(kp[b])), w[b].double().cpu().numpy()
+        ref = O.index_scores(qf, wf, kf, pos, 4)
+        bound = _score_bound(qf, wf, kf)
+        got = s[b].double().cpu().numpy()[:, :nblk]
+        for i in range(lq):
+            own = max(0, min(pos[i] // 4, nblk)) if pos[i] >= 0 else 0
+            assert np.all(np.abs(got[i, :own] - ref[i, :own]) <= 2e-5 * bound[i, :own] + 1e-30)
+
+
 # ------------------------------------------------------------------------------------
 # Stage 3: top-k on given scores (same fp32 inputs on both sides: exact equality)
 # ------------------------------------------------------------------------------------
