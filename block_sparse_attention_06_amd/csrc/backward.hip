@@ -23,7 +23,9 @@
 // do not depend on scheduling). Per row: S = Q.K^T and dP = dO.V^T with the block's 4
 // keys as MFMA columns (12 of 16 rows are heads, 4 of 16 columns are keys), so P and
 // dS land in the A-operand layout of dV = P^T.dO and dK = dS^T.Q, whose B operands
-// are the row's dO and q with 4 heads per lane.
+// are the row's dO and q with 4 heads per lane. A row's q and dO are read from memory
+// once, two rows ahead, and staged in the wave's LDS tile, from which both layouts are
+// read; the block's K and V sit in LDS too.
 
 #include <cstring>  // rocPRIM's host code uses memset
 
@@ -234,14 +236,19 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_dkdv_kernel(BwdArgs a) {
   const int64_t kstride = (int64_t)a.hkv * D;
 
   // The block's 4 keys as B columns (k = dims 32c + 8*quad + [0..7]); other columns 0.
-  const int64_t tok = kb * 4 + c16;
-  const bool kv = c16 < 4 && tok < a.lk;
-  uint4 Kb[NC], Vb[NC];
+  __shared__ uint4 bwd_tile_q[4][16 * D / 8], bwd_tile_do[4][16 * D / 8];
+  __shared__ uint4 bwd_tile_kv[4][2][4 * D / 8];
+  // The block's 4 keys (K, then V) in the wave's LDS, chunks XOR-swizzled by the key:
+  // B columns c16 read key c16 % 4 (columns past the 4 keys are masked out of P and dS
+  // later; keys past lk read the last key, also masked).
+  uint4* tkv = &bwd_tile_kv[wave][0][0];
+  {
+    const int64_t tok = min(kb * 4 + (lane & 3), a.lk - 1);
+    const int part = (lane >> 2) & 1;  // 0: K, 1: V
+    const uint16_t* src = (part ? a.v : a.k) + tok * kstride + g * D;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int64_t off = (kv ? tok : 0) * kstride + g * D + quad * 8 + c * 32;
-    Kb[c] = kv ? ld16(a.k + off) : make_uint4(0, 0, 0, 0);
-    Vb[c] = kv ? ld16(a.v + off) : make_uint4(0, 0, 0, 0);
+    for (int u = lane >> 3; u < D / 8; u += 8)
+      tkv[(part * 4 + (lane & 3)) * (D / 8) + (u ^ (lane & 3))] = ld16(src + u * 8);
   }
 
   f32x4 dK[NT], dV[NT];
@@ -254,81 +261,125 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_dkdv_kernel(BwdArgs a) {
   const int32_t p0 = a.start[kb], p1 = a.start[kb + 1];
   const bool hv = c16 < G;  // A rows: head c16
 
-  // Software pipeline over the rows: a row's q and dO of head c16 (A operands, k =
-  // dims 32c + 8*quad + [0..7]) with its lse and D of heads 4*quad + i are loaded one
-  // row ahead, into the registers the previous row's S and dP MFMAs have just read.
-  // They cover every line of the row's q and dO for the group, so the second layout
-  // (4 heads per lane, 8 dims each: the B operands of dV and dK), loaded after the
-  // MFMAs of S and dP, comes from cache.
-  uint4 Qa[NC], dOa[NC];
-  float L2[4], Dh[4];
-  int64_t row = 0;
-  auto load_first = [&](int32_t p) {
-    row = a.pair_rows[p];
-    const int64_t hbase = (row * a.hq + g * G) * (int64_t)D;
+  // Rows are loaded two ahead into registers: a row's q and dO of head c16 (k = dims
+  // 32c + 8*quad + [0..7]) with its lse and D of heads 4*quad + i. On arrival they go
+  // to the wave's LDS tile ([head][16-byte chunk], chunks XOR-swizzled by head & 7 so
+  // that all three access shapes are free of bank conflicts), the registers take the
+  // row after next, and the row is computed from the tile: the A operands of S and dP
+  // (the layout it was written in) and the B operands of dV and dK (4 heads per lane,
+  // 8 dims each). The tile is private to the wave: no workgroup barrier.
+  struct RowBuf {
+    uint4 Qa[NC], dOa[NC];
+    float L2[4], Dh[4];
+    int64_t row;
+  };
+  // Every load is unconditional (lanes past the group's heads read its last head: their
+  // S and dP rows are masked out of P and dS, and P and dS are zero on those heads), so
+  // that the waits count loads exactly.
+  // The pair list is read-only here and p is uniform: scalar loads, which the vector
+  // loads in flight need not wait for.
+  const auto* prow = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(a.pair_rows));
+  auto load_row = [&](RowBuf& rb, int32_t p) {
+    rb.row = prow[p];
+    const int64_t hbase = (rb.row * a.hq + g * G) * (int64_t)D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int64_t off = hbase + (int64_t)(hv ? c16 : 0) * D + quad * 8 + c * 32;
-      Qa[c] = hv ? ld16(a.q + off) : make_uint4(0, 0, 0, 0);
-      dOa[c] = hv ? ld16(a.dout + off) : make_uint4(0, 0, 0, 0);
+      const int64_t off = hbase + (int64_t)min(c16, G - 1) * D + quad * 8 + c * 32;
+      rb.Qa[c] = ld16(a.q + off);
+      rb.dOa[c] = ld16(a.dout + off);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = 4 * quad + i;
-      L2[i] = h < G ? a.lse[row * a.hq + g * G + h] * kLog2e : 0.f;
-      Dh[i] = h < G ? a.dbuf[row * a.hq + g * G + h] : 0.f;
+      const int h = min(4 * quad + i, G - 1);
+      rb.L2[i] = a.lse[rb.row * a.hq + g * G + h] * kLog2e;
+      rb.Dh[i] = a.dbuf[rb.row * a.hq + g * G + h];
     }
   };
-  if (p0 < p1) load_first(p0);
-  for (int32_t p = p0; p < p1; ++p) {
+  uint4* tq = bwd_tile_q[wave];
+  uint4* tdo = bwd_tile_do[wave];
+  struct RowState {
+    float l2[4], dh[4];
+    int64_t t;
+  };
+  auto stage = [&](const RowBuf& rb, RowState& rs) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ch = (quad + 4 * c) ^ (c16 & 7);
+      tq[c16 * (D / 8) + ch] = rb.Qa[c];
+      tdo[c16 * (D / 8) + ch] = rb.dOa[c];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rs.l2[i] = rb.L2[i];
+      rs.dh[i] = rb.Dh[i];
+    }
+    rs.t = a.q_pos0 + rb.row;
+  };
+  auto compute = [&](const RowState& rs) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      S = mfma_16x16x32(Qa[c], Kb[c], S);
-      dP = mfma_16x16x32(dOa[c], Vb[c], dP);
+      const int ch = (quad + 4 * c) ^ (c16 & 7);
+      const int kch = (quad + 4 * c) ^ (c16 & 3);
+      S = mfma_16x16x32(tq[c16 * (D / 8) + ch], tkv[(c16 & 3) * (D / 8) + kch], S);
+      dP = mfma_16x16x32(tdo[c16 * (D / 8) + ch], tkv[(4 + (c16 & 3)) * (D / 8) + kch], dP);
     }
-    const int64_t t = a.q_pos0 + row;
-    const int64_t hbase = (row * a.hq + g * G) * (int64_t)D;
-    float l2[4], dh[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      l2[i] = L2[i];
-      dh[i] = Dh[i];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // The next row (past the list: the last row again, in bounds).
-    load_first(min(p + 1, p1 - 1));
-    uint4 Qr[NH][4], dOr[NH][4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int h = 4 * quad + kk;
-      const bool ok = h < G;
-      const int64_t off = hbase + (int64_t)(ok ? h : 0) * D + c16 * 8;
-#pragma unroll
-      for (int hf = 0; hf < NH; ++hf) {
-        Qr[hf][kk] = ok ? ld16(a.q + off + hf * 128) : make_uint4(0, 0, 0, 0);
-        dOr[hf][kk] = ok ? ld16(a.dout + off + hf * 128) : make_uint4(0, 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
     // Row 4*quad+i is head 4*quad+i; column c16 is token kb*4 + c16.
     float pv[4], ds[4];
-    const bool key_ok = c16 < 4 && kb * 4 + c16 <= t && kb * 4 + c16 < a.lk;
+    const bool key_ok = c16 < 4 && kb * 4 + c16 <= rs.t && kb * 4 + c16 < a.lk;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = key_ok && 4 * quad + i < G;
-      pv[i] = ok ? exp2f(S[i] * sl2 - l2[i]) : 0.f;
-      ds[i] = pv[i] * (dP[i] - dh[i]);
+      pv[i] = ok ? exp2f(S[i] * sl2 - rs.l2[i]) : 0.f;
+      ds[i] = pv[i] * (dP[i] - rs.dh[i]);
     }
     const uint2 Ap = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
     const uint2 As = make_uint2(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]));
 #pragma unroll
-    for (int hf = 0; hf < NH; ++hf)
+    for (int hf = 0; hf < NH; ++hf) {
+      uint4 Rr[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        dV[hf * 8 + e] = mfma_16x16x16(Ap, bwd_repack(dOr[hf], e), dV[hf * 8 + e]);
-        dK[hf * 8 + e] = mfma_16x16x16(As, bwd_repack(Qr[hf], e), dK[hf * 8 + e]);
+      for (int kk = 0; kk < 4; ++kk) {
+        const int h = 4 * quad + kk;
+        Rr[kk] = tdo[h * (D / 8) + ((c16 + 16 * hf) ^ (h & 7))];
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dV[hf * 8 + e] = mfma_16x16x16(Ap, bwd_repack(Rr, e), dV[hf * 8 + e]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int h = 4 * quad + kk;
+        Rr[kk] = tq[h * (D / 8) + ((c16 + 16 * hf) ^ (h & 7))];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dK[hf * 8 + e] = mfma_16x16x16(As, bwd_repack(Rr, e), dK[hf * 8 + e]);
+    }
+    // The next row's tile stores must not pass these reads.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  if (p0 < p1) {
+    // Loads are unconditional (past the list: the last row again, in bounds), so that
+    // every wait counts exactly one row's loads.
+    RowBuf B0, B1;
+    RowState st;
+    load_row(B0, p0);
+    load_row(B1, min(p0 + 1, p1 - 1));
+    for (int32_t p = p0; p < p1; p += 2) {
+      stage(B0, st);
+      load_row(B0, min(p + 2, p1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st);
+      stage(B1, st);
+      load_row(B1, min(p + 3, p1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      if (p + 1 < p1) compute(st);
+    }
   }
 
   // Rows 0..3 of the accumulators are the block's keys (quad 0 lanes): dims
