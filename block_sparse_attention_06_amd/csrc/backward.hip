@@ -116,47 +116,54 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_dq_kernel(BwdArgs a) {
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.scale_log2;
 
-  for (int s = 0; s < n_steps; ++s) {
+  // Steps of 4 kept blocks, two in flight: a step's block ids are scalar loads (the
+  // selection row is read-only here and uniform per wave), its K and V rows are
+  // unconditional vector loads (padding reads token 0, masked), so the waits count
+  // exactly one step's loads.
+  const auto* ssel = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(srow));
+  struct Step {
+    uint4 Kc[NC], Vc[NC];  // key c16 = token (c16 & 3) of block slot (c16 >> 2)
+    uint4 Kr[NH][4];       // the tokens of block slot `quad`, 8 dims each
+    int first, bq;         // block of slot 0 (-1: padding reached), block of slot `quad`
+  };
+  auto issue = [&](Step& st, int s) {
     int b4[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b4[j] = (4 * s + j < a.n_sel) ? srow[4 * s + j] : -1;
-    if (b4[0] < 0) break;  // -1 padding reached
-
-    // K and V rows, key c16 = token (c16 & 3) of block slot (c16 >> 2).
+    for (int j = 0; j < 4; ++j) b4[j] = (4 * s + j < a.n_sel) ? ssel[4 * s + j] : -1;
+    st.first = b4[0];
     const int bk = c16 < 4 ? b4[0] : (c16 < 8 ? b4[1] : (c16 < 12 ? b4[2] : b4[3]));
     int64_t tk = (int64_t)bk * 4 + (c16 & 3);
     tk = bk < 0 ? 0 : min(tk, t);
     const uint16_t* kp = a.k + tk * kstride + g * D + quad * 8;
     const uint16_t* vp = a.v + tk * kstride + g * D + quad * 8;
-    uint4 Kc[NC], Vc[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      Kc[c] = ld16(kp + c * 32);
-      Vc[c] = ld16(vp + c * 32);
+      st.Kc[c] = ld16(kp + c * 32);
+      st.Vc[c] = ld16(vp + c * 32);
     }
-    // K again with 4 keys per lane (the tokens of block slot `quad`), 8 dims each.
-    const int bq = quad == 0 ? b4[0] : (quad == 1 ? b4[1] : (quad == 2 ? b4[2] : b4[3]));
-    uint4 Kr[NH][4];
+    st.bq = quad == 0 ? b4[0] : (quad == 1 ? b4[1] : (quad == 2 ? b4[2] : b4[3]));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      int64_t tv = (int64_t)bq * 4 + kk;
-      tv = bq < 0 ? 0 : min(tv, t);
+      int64_t tv = (int64_t)st.bq * 4 + kk;
+      tv = st.bq < 0 ? 0 : min(tv, t);
       const uint16_t* p = a.k + tv * kstride + g * D + c16 * 8;
 #pragma unroll
-      for (int hf = 0; hf < NH; ++hf) Kr[hf][kk] = ld16(p + hf * 128);
+      for (int hf = 0; hf < NH; ++hf) st.Kr[hf][kk] = ld16(p + hf * 128);
     }
-
+  };
+  auto compute = [&](const Step& st) {
     f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      S = mfma_16x16x32(Kc[c], Qc[c], S);
-      dP = mfma_16x16x32(Vc[c], dOc[c], dP);
+      S = mfma_16x16x32(st.Kc[c], Qc[c], S);
+      dP = mfma_16x16x32(st.Vc[c], dOc[c], dP);
     }
     // Row 4*quad+i of S^T is token bq*4 + i; column c16 is head c16.
     float ds[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = hv && bq >= 0 && (int64_t)bq * 4 + i <= t;
+      const bool ok = hv && st.bq >= 0 && (int64_t)st.bq * 4 + i <= t;
       const float p = ok ? exp2f(S[i] * sl2 - L2) : 0.f;
       ds[i] = p * (dP[i] - Dh);
     }
@@ -165,7 +172,20 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_dq_kernel(BwdArgs a) {
     for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        acc[hf * 8 + e] = mfma_16x16x16(A, bwd_repack(Kr[hf], e), acc[hf * 8 + e]);
+        acc[hf * 8 + e] = mfma_16x16x16(A, bwd_repack(st.Kr[hf], e), acc[hf * 8 + e]);
+  };
+  Step A0, A1;
+  issue(A0, 0);
+  issue(A1, 1);
+  for (int s = 0; s < n_steps; s += 2) {
+    if (A0.first < 0) break;  // -1 padding reached
+    compute(A0);
+    issue(A0, s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 >= n_steps || A1.first < 0) break;
+    compute(A1);
+    issue(A1, s + 3);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // dq = scale * dS.K; lane holds heads 4*quad + i, dims hf*128 + 8*c16 + e.
