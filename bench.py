@@ -31,7 +31,7 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="prefill128k",
                    choices=["prefill128k", "prefill32k", "chunked1m", "tiny"])
-    p.add_argument("--row-chunk", type=int, default=4096)
+    p.add_argument("--row-chunk", type=int, default=16384)
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-backward", action="store_true",
@@ -42,6 +42,8 @@ def parse_args():
                    help="skip the decode step over a paged K/V cache")
     p.add_argument("--no-varlen", action="store_true",
                    help="skip the packed variable-length prefill batch")
+    p.add_argument("--no-other", action="store_true",
+                   help="skip the 32K and chunked-1M prefill steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -146,7 +148,9 @@ def bench_prefill(args, torch, Q, wl, inp):
                          row_chunk=args.row_chunk, device=dev)
     scale = 1.0 / math.sqrt(wl.d)
 
-    def step(ev_a=None, ev_b=None):
+    def step(ev_s=None, ev_a=None, ev_b=None):
+        if ev_s is not None:
+            ev_s.record()
         Q.qsa_prefill_select(inp["q_idx"], inp["w"], inp["k_idx"], lk=wl.lk, budget=wl.budget,
                              q_pos0=wl.q_pos0, k_pooled_prefix=inp["k_pooled_prefix"], plan=plan)
         if ev_a is not None:
@@ -159,15 +163,40 @@ def bench_prefill(args, torch, Q, wl, inp):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
            for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for a, b in evs:
-        step(a, b)
+    for s_, a, b in evs:
+        step(s_, a, b)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    attn_ms = sum(a.elapsed_time(b) for _, a, b in evs) / len(evs)
+    bench_prefill.step_ms = sorted(s_.elapsed_time(b) for s_, _, b in evs)
     return wall, attn_ms, plan
+
+
+def percentiles(xs):
+    """p10 / p50 / p90 of a sorted list (nearest rank)."""
+    n = len(xs)
+    pick = lambda q: xs[min(n - 1, max(0, int(math.ceil(q * n)) - 1))]
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
+
+def bench_other_prefill(torch, Q, name, steps=5):
+    """A whole prefill step (select + attention) on another workload: tokens/s."""
+    import types
+    from synth import generate, workload
+    owl = workload(name)
+    oinp = generate(owl, device="cuda")
+    torch.cuda.synchronize()
+    args = types.SimpleNamespace(row_chunk=min(16384, owl.lq), warmup=1, steps=steps)
+    wall, attn_ms, plan = bench_prefill(args, torch, Q, owl, oinp)
+    step_ms = bench_prefill.step_ms
+    del oinp, plan
+    torch.cuda.empty_cache()
+    return {"query_tokens": owl.lq, "context": owl.lk, "q_pos0": owl.q_pos0,
+            "tokens_per_s": owl.lq * steps / wall, "ms_per_step": wall / steps * 1e3,
+            "attention_ms": attn_ms, "step_ms": percentiles(step_ms), "steps": steps}
 
 
 def backward_bytes(wl, t):
@@ -516,6 +545,7 @@ def main():
                      "algorithmic_bytes_per_launch": a_bytes / n_launch,
                      "avg_launch_ms": attn_ms / n_launch},
         "stages_ms": {"select (pool + scores + top-k)": ms_step - attn_ms, "attention": attn_ms},
+        "step_ms_events": percentiles(bench_prefill.step_ms),
         "score_gemm_flops_per_step": score_flops(wl, t),
     }
     kv_mib = (2 * wl.lk * wl.hkv * wl.d * 2) >> 20
@@ -595,6 +625,11 @@ def main():
             del kp, vp, table
         del dinp
         torch.cuda.empty_cache()
+    if not args.no_other and wl.name == "prefill128k":
+        line["other_prefill"] = {n: bench_other_prefill(torch, Q, n)
+                                 for n in ("prefill32k", "chunked1m")}
+        progress("other prefill workloads: " + ", ".join(
+            f"{n} {v['ms_per_step']:.2f} ms" for n, v in line["other_prefill"].items()))
     if not args.no_cpu_baseline:
         inp = generate(wl, device=dev)
         line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
