@@ -112,8 +112,9 @@ __device__ __forceinline__ uint64_t wave_extract_top_iter(uint64_t (&rk)[SLOTS],
 
 // Same contract as wave_extract_top_iter for keep <= 16, in three wave-wide passes
 // instead of one reduction per key:
-//  1. the keep-th largest of the 64 lane maxima, thr, is a lower bound of the keep-th
-//     largest key (the keep lane maxima >= thr are distinct keys);
+//  1. the keep-th largest high word (the score's order key) of the 64 lane maxima,
+//     found bit by bit with ballots, gives thr: every key whose high word reaches it
+//     is a candidate, and there are at least keep of them (one per such lane);
 //  2. the keys >= thr (at least keep of them) are packed into `scratch`, 64 wave-private
 //     LDS slots (more than 64 of them, possible only when the largest keys crowd into
 //     few lanes, falls back to the repeated maxima);
@@ -127,12 +128,15 @@ __device__ __forceinline__ uint64_t wave_extract_top(uint64_t (&rk)[SLOTS], int 
   uint64_t mx = rk[0];
 #pragma unroll
   for (int i = 1; i < SLOTS; ++i) mx = rk[i] > mx ? rk[i] : mx;
-  int above = 0;
+  const uint32_t mhi = (uint32_t)(mx >> 32);
+  uint32_t pre = 0;  // the largest v with at least keep lanes' high words >= v
 #pragma unroll
-  for (int j = 0; j < 64; ++j) above += readlane_u64(mx, j) > mx ? 1 : 0;
-  const uint64_t hit = __ballot(mx != 0 && above == keep - 1);
-  // Fewer than keep nonempty lanes: every nonzero key is a candidate.
-  const uint64_t thr = hit ? readlane_u64(mx, __builtin_ctzll(hit)) : 1ull;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = pre | (1u << b);
+    if (__popcll(__ballot(mhi >= cand)) >= keep) pre = cand;
+  }
+  // Fewer than keep nonempty lanes leave pre = 0: every nonzero key is a candidate.
+  const uint64_t thr = pre ? ((uint64_t)pre << 32) : 1ull;
   int total = 0;
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) {

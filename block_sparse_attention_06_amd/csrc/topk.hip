@@ -870,57 +870,126 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
   }
 }
 
-// First pass over long rows: wave w of the launch takes segment (row, seg) of
-// kWaveSeg scores, each lane holding kWaveSeg / 64 of them, and extracts its kWaveKeep best
-// (score, id) rank keys.
+// First pass over long rows: each wave takes kSegsPerWave consecutive segments (row,
+// seg) of kWaveSeg scores, each lane holding kWaveSeg / 64 of them, and extracts each
+// segment's kWaveKeep best (score, id) rank keys. The next segment's scores are loaded
+// before the current one is ranked; the winners wait in LDS and leave in one burst of
+// coalesced stores at the end (a store among the loads would drain every wait).
+constexpr int kSegsPerWave = 4;
+
 __global__ __launch_bounds__(256) void topk_wave_segments_kernel(TopkLaunch L) {
+  constexpr int kQ = kWaveSeg / 256;  // float4 loads per lane
+  constexpr int kOut = kSegsPerWave * kWaveKeep;
+  static_assert(kOut == 64, "one candidate per lane in the final stores");
   __shared__ uint64_t scratch[4][64];
+  __shared__ float out_v[4][kOut];
+  __shared__ int32_t out_i[4][kOut];
+  __shared__ float out_bv[4][kSegsPerWave];
+  __shared__ int32_t out_bi[4][kSegsPerWave];
   const TopkArgs& a = L.a;
   const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t rows = (int64_t)a.batch * a.lq;
-  const int64_t crow = item / L.n_seg;
-  if (crow >= rows) return;
-  const int seg_id = (int)(item - crow * L.n_seg);
-  const int bi = (int)(crow / a.lq);
-  const int64_t row = crow - (int64_t)bi * a.lq;
-  int64_t t, own, C;
-  int m;
-  if (!row_geometry(a, row, bi, t, own, C, m)) return;
-  float* cv = L.cand_val + (crow * L.n_seg + seg_id) * kWaveKeep;
-  int32_t* ci = L.cand_idx + (crow * L.n_seg + seg_id) * kWaveKeep;
-  if (t < 0 || m == C) return;  // the merge writes such rows without reading candidates
-  const int lo = seg_id * kWaveSeg;
-  const int n = (int)max((int64_t)0, min(C - lo, (int64_t)kWaveSeg));
-  const float* src = a.scores + (int64_t)bi * a.s_bs + row * a.ld + lo;
-  // lane holds positions 4*(lane + 64*q) + e, q < kWaveSeg / 256
-  constexpr int kQ = kWaveSeg / 256;
-  uint64_t rk[4 * kQ];
+  const int wave = threadIdx.x >> 6;
+  const int64_t n_items = (int64_t)a.batch * a.lq * L.n_seg;  // item = row * n_seg + seg
+  const int64_t item0 = ((int64_t)blockIdx.x * 4 + wave) * kSegsPerWave;
+  if (item0 >= n_items) return;
+
+  struct Seg {
+    const float* src;  // the segment's first score (a valid address when not live)
+    int n, lo;         // scores in the segment, first block id
+    bool live;         // the merge reads this segment's candidates
+  };
+  auto geom = [&](int64_t item) {
+    Seg sg{a.scores, 0, 0, false};
+    if (item >= n_items) return sg;
+    const int64_t crow = item / L.n_seg;
+    const int seg_id = (int)(item - crow * L.n_seg);
+    const int bi = (int)(crow / a.lq);
+    const int64_t row = crow - (int64_t)bi * a.lq;
+    int64_t t, own, C;
+    int m;
+    if (!row_geometry(a, row, bi, t, own, C, m)) return sg;
+    if (t < 0 || m == C) return sg;  // the merge writes such rows without candidates
+    sg.live = true;
+    sg.lo = seg_id * kWaveSeg;
+    sg.n = (int)max((int64_t)0, min(C - sg.lo, (int64_t)kWaveSeg));
+    sg.src = a.scores + (int64_t)bi * a.s_bs + row * a.ld + sg.lo;
+    return sg;
+  };
+  // lane holds positions 4*(lane + 64*q) + e; loads past the segment's scores read its
+  // last aligned float4 (inside the row: ld % 4 == 0), so every load is unconditional.
+  auto load = [&](const Seg& sg, float4 (&v)[kQ]) {
+    const int pmax = sg.n > 0 ? ((sg.n - 1) & ~3) : 0;
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) {
-    const int p = 4 * (lane + 64 * q);
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (p < n) v = *reinterpret_cast<const float4*>(src + p);  // inside the row: ld % 4 == 0
-    const float xs[4] = {v.x, v.y, v.z, v.w};
+    for (int q = 0; q < kQ; ++q)
+      v[q] = *reinterpret_cast<const float4*>(sg.src + min(4 * (lane + 64 * q), pmax));
+  };
+  auto rank = [&](const Seg& sg, const float4 (&v)[kQ], int k) {
+    uint64_t rk[4 * kQ];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rk[4 * q + e] = p + e < n ? rank_key(xs[e], lo + p + e) : 0ull;
-  }
-  const int keep = min(n, kWaveKeep);
-  const uint64_t last = wave_extract_top<4 * kQ>(rk, keep, scratch[threadIdx.x >> 6],
-                                                 [&](int k, uint64_t w) {
-    const int32_t id = rank_key_id(w);
-    cv[k] = src[id - lo];
-    ci[k] = id;
-  });
-  if (lane == 0) {
-    for (int k = keep; k < kWaveKeep; ++k) {
-      cv[k] = __builtin_nanf("");
-      ci[k] = -1;
+    for (int q = 0; q < kQ; ++q) {
+      const int p = 4 * (lane + 64 * q);
+      const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rk[4 * q + e] = p + e < sg.n ? rank_key(xs[e], sg.lo + p + e) : 0ull;
     }
-    const bool truncated = n > keep;
-    L.bnd_val[crow * L.n_seg + seg_id] =
-        truncated ? a.scores[(int64_t)bi * a.s_bs + row * a.ld + rank_key_id(last)] : 0.f;
-    L.bnd_idx[crow * L.n_seg + seg_id] = truncated ? rank_key_id(last) : -1;
+    const int keep = min(sg.n, kWaveKeep);
+    // Empty slots first (the extraction fills 0..keep-1), then the winners; a -0 score
+    // comes back as +0, which ranks the same.
+    if (lane < kWaveKeep) {
+      out_v[wave][k * kWaveKeep + lane] = __builtin_nanf("");
+      out_i[wave][k * kWaveKeep + lane] = -1;
+    }
+    const uint64_t last = wave_extract_top<4 * kQ>(rk, keep, scratch[wave], [&](int r, uint64_t w) {
+      out_v[wave][k * kWaveKeep + r] = key_to_float((uint32_t)(w >> 32));
+      out_i[wave][k * kWaveKeep + r] = rank_key_id(w);
+    });
+    if (lane == 0) {
+      const bool truncated = sg.n > keep;
+      out_bv[wave][k] = truncated ? key_to_float((uint32_t)(last >> 32)) : 0.f;
+      out_bi[wave][k] = truncated ? rank_key_id(last) : -1;
+    }
+    // The next extraction reuses the scratch slots.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  bool live[kSegsPerWave];
+  Seg cur = geom(item0);
+  float4 vc[kQ], vn[kQ];
+  load(cur, vc);
+#pragma unroll
+  for (int k = 0; k < kSegsPerWave; ++k) {
+    const Seg nxt = geom(item0 + k + 1);
+    if (k + 1 < kSegsPerWave) load(nxt, vn);
+    __builtin_amdgcn_sched_barrier(0);
+    live[k] = cur.live;
+    if (cur.live) rank(cur, vc, k);
+    cur = nxt;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) vc[q] = vn[q];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // Consecutive items have consecutive candidate slots: lane L stores candidate L % 16
+  // of segment L / 16.
+  const int k = lane / kWaveKeep;
+  bool mine = false;
+#pragma unroll
+  for (int j = 0; j < kSegsPerWave; ++j) mine = j == k ? live[j] : mine;
+  if (mine) {
+    L.cand_val[item0 * kWaveKeep + lane] = out_v[wave][lane];
+    L.cand_idx[item0 * kWaveKeep + lane] = out_i[wave][lane];
+  }
+  if (lane < kSegsPerWave) {
+    bool lv = false;
+#pragma unroll
+    for (int j = 0; j < kSegsPerWave; ++j) lv = j == lane ? live[j] : lv;
+    if (lv) {
+      L.bnd_val[item0 + lane] = out_bv[wave][lane];
+      L.bnd_idx[item0 + lane] = out_bi[wave][lane];
+    }
   }
 }
 
@@ -989,8 +1058,9 @@ hipError_t launch_topk_blocks(const TopkArgs& a, void* ws, hipStream_t stream) {
   }
   const TopkLaunch L = merge_launch(a, ws);
   const size_t segs = (size_t)a.batch * a.lq * L.n_seg;
-  hipLaunchKernelGGL(topk_wave_segments_kernel, dim3((unsigned)((segs + 3) / 4)), dim3(256), 0,
-                     stream, L);
+  const size_t per_wg = 4 * kSegsPerWave;
+  hipLaunchKernelGGL(topk_wave_segments_kernel, dim3((unsigned)((segs + per_wg - 1) / per_wg)),
+                     dim3(256), 0, stream, L);
   hipLaunchKernelGGL(topk_kernel<kMerge>, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
                      dim3(kTkThreads), 0, stream, L);
   return hipGetLastError();
