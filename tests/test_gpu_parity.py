@@ -345,10 +345,15 @@ def test_sparse_attn_fwd_softmax_stress():
     _attn_case(600, 600, 0, 24, 2, 256, 512, seed=77, unscaled=True)
 
 
-def test_sparse_attn_decode():
-    bsz, lmax, hq, hkv, d, budget = 3, 5000, 24, 2, 256, 2048
-    seq = [5000, 4093, 17]
-    _say(f"decode attn seq={seq}")
+@pytest.mark.parametrize("lmax,hq,hkv,d,budget,seq", [
+    (5000, 24, 2, 256, 2048, [5000, 4093, 17]),      # model shape: 2 steps per wave
+    (3000, 16, 1, 128, 256, [3000, 1499, 2]),        # 16 heads per group, 1 step per wave
+    (20000, 8, 2, 128, 4096, [20000, 16387, 4101]),  # 4 steps per wave
+    (9000, 12, 1, 256, 4096, [8999, 600]),           # fewer kept blocks than places
+])
+def test_sparse_attn_decode(lmax, hq, hkv, d, budget, seq):
+    bsz = len(seq)
+    _say(f"decode attn seq={seq} heads={hq}/{hkv} d={d} K={budget}")
     q = _randn_bf16((bsz, hq, d), 31, 1 / math.sqrt(d))
     kc = _randn_bf16((bsz, lmax, hkv, d), 32, 1 / math.sqrt(d))
     vc = _randn_bf16((bsz, lmax, hkv, d), 33, 1 / math.sqrt(d))
