@@ -238,7 +238,8 @@ __global__ __launch_bounds__(256) void bwd_starts_kernel(const int32_t* __restri
 
 // ---- key side: dK and dV --------------------------------------------------------------
 
-template <int D>
+// NL: 1 KiB loads that cover a row's G heads of one group, ceil(G * D / 512).
+template <int D, int NL>
 __global__ __launch_bounds__(256) void sparse_attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NC = D / 32;
   constexpr int NH = D / 128;
@@ -281,34 +282,42 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_dkdv_kernel(BwdArgs a) {
   const int32_t p0 = a.start[kb], p1 = a.start[kb + 1];
   const bool hv = c16 < G;  // A rows: head c16
 
-  // Rows are loaded two ahead into registers: a row's q and dO of head c16 (k = dims
-  // 32c + 8*quad + [0..7]) with its lse and D of heads 4*quad + i. On arrival they go
-  // to the wave's LDS tile ([head][16-byte chunk], chunks XOR-swizzled by head & 7 so
-  // that all three access shapes are free of bank conflicts), the registers take the
-  // row after next, and the row is computed from the tile: the A operands of S and dP
-  // (the layout it was written in) and the B operands of dV and dK (4 heads per lane,
-  // 8 dims each). The tile is private to the wave: no workgroup barrier.
+  // Rows are loaded two ahead into registers: a row's q and dO of the group's heads
+  // (contiguous chunks) with its lse and D of heads 4*quad + i. On arrival they go to
+  // the wave's LDS tile ([head][16-byte chunk], chunks XOR-swizzled by head & 7 so that
+  // all three access shapes are free of bank conflicts), the registers take the row
+  // after next, and the row is computed from the tile: the A operands of S and dP (head
+  // c16, k = dims 32c + 8*quad + [0..7]) and the B operands of dV and dK (4 heads per
+  // lane, 8 dims each). The tile is private to the wave: no workgroup barrier.
   struct RowBuf {
-    uint4 Qa[NC], dOa[NC];
+    uint4 Qa[NL], dOa[NL];
     float L2[4], Dh[4];
     int64_t row;
   };
-  // Every load is unconditional (lanes past the group's heads read its last head: their
-  // S and dP rows are masked out of P and dS, and P and dS are zero on those heads), so
-  // that the waits count loads exactly.
+  // Every load is unconditional (past the group's heads: its last head again; those
+  // S and dP rows are masked out of P and dS), so that the waits count loads exactly.
   // The pair list is read-only here and p is uniform: scalar loads, which the vector
   // loads in flight need not wait for.
   const auto* prow = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
       reinterpret_cast<uintptr_t>(a.pair_rows));
+  // The group's G heads of a row are G * D contiguous bf16 in q and in dout: load u,
+  // lane L takes 16-byte chunk 64u + L of them (whole 1 KiB per instruction; chunks past
+  // the group's last re-read it).
+  constexpr int CPR = D / 8;  // 16-byte chunks per head
+  const int n_chunks = G * CPR;
   auto load_row = [&](RowBuf& rb, int32_t p) {
     rb.row = prow[p];
     const int64_t hbase = (rb.row * a.hq + g * G) * (int64_t)D;
+    const uint16_t* qp = a.q + hbase + lane * 8;
+    const uint16_t* dp = a.dout + hbase + lane * 8;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int64_t off = hbase + (int64_t)min(c16, G - 1) * D + quad * 8 + c * 32;
-      rb.Qa[c] = ld16(a.q + off);
-      rb.dOa[c] = ld16(a.dout + off);
+    for (int u = 0; u < NL - 1; ++u) {
+      rb.Qa[u] = ld16(qp + u * 512);
+      rb.dOa[u] = ld16(dp + u * 512);
     }
+    const int64_t last = (int64_t)min(64 * (NL - 1) + lane, n_chunks - 1) * 8;
+    rb.Qa[NL - 1] = ld16(a.q + hbase + last);
+    rb.dOa[NL - 1] = ld16(a.dout + hbase + last);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = min(4 * quad + i, G - 1);
@@ -318,16 +327,23 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_dkdv_kernel(BwdArgs a) {
   };
   uint4* tq = bwd_tile_q[wave];
   uint4* tdo = bwd_tile_do[wave];
+  for (int c = 64 * NL + lane; c < 16 * CPR; c += 64) {
+    tq[c] = make_uint4(0, 0, 0, 0);
+    tdo[c] = make_uint4(0, 0, 0, 0);
+  }
   struct RowState {
     float l2[4], dh[4];
     int64_t t;
   };
   auto stage = [&](const RowBuf& rb, RowState& rs) {
+    // Rows past the group's heads that the last load reaches get copies of its last
+    // chunk (finite; they meet P = dS = 0); the rest were zeroed at the start.
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int ch = (quad + 4 * c) ^ (c16 & 7);
-      tq[c16 * (D / 8) + ch] = rb.Qa[c];
-      tdo[c16 * (D / 8) + ch] = rb.dOa[c];
+    for (int u = 0; u < NL; ++u) {
+      const int c = 64 * u + lane;
+      const int h = c / CPR, ch = c % CPR;
+      tq[h * CPR + (ch ^ (h & 7))] = rb.Qa[u];
+      tdo[h * CPR + (ch ^ (h & 7))] = rb.dOa[u];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -516,12 +532,26 @@ hipError_t launch_sparse_attn_bwd(BwdArgs a, char* ws, size_t ws_bytes, hipStrea
                      stream, kd.current(), n_pairs, (int32_t)a.n_kb, a.start);
   const dim3 gq((unsigned)((a.lq * a.hkv + 3) / 4));
   const dim3 gk((unsigned)((a.n_kb * a.hkv + 3) / 4));
+  const int nl = (a.hq / a.hkv * a.d + 511) / 512;  // 1 KiB loads per row and group
   if (a.d == 256) {
     hipLaunchKernelGGL(sparse_attn_bwd_dq_kernel<256>, gq, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(sparse_attn_bwd_dkdv_kernel<256>, gk, dim3(256), 0, stream, a);
+    switch (nl) {
+#define QSA_DKDV(N) \
+  case N: hipLaunchKernelGGL((sparse_attn_bwd_dkdv_kernel<256, N>), gk, dim3(256), 0, stream, a); break;
+      QSA_DKDV(1) QSA_DKDV(2) QSA_DKDV(3) QSA_DKDV(4) QSA_DKDV(5) QSA_DKDV(6) QSA_DKDV(7)
+      QSA_DKDV(8)
+#undef QSA_DKDV
+      default: return hipErrorInvalidValue;
+    }
   } else {
     hipLaunchKernelGGL(sparse_attn_bwd_dq_kernel<128>, gq, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(sparse_attn_bwd_dkdv_kernel<128>, gk, dim3(256), 0, stream, a);
+    switch (nl) {
+#define QSA_DKDV(N) \
+  case N: hipLaunchKernelGGL((sparse_attn_bwd_dkdv_kernel<128, N>), gk, dim3(256), 0, stream, a); break;
+      QSA_DKDV(1) QSA_DKDV(2) QSA_DKDV(3) QSA_DKDV(4)
+#undef QSA_DKDV
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }

@@ -85,3 +85,10 @@ def test_backward_softmax_stress():
     # Unscaled N(0,1) q and k: peaky softmax rows.
     _case(lq=200, lk=1200, q_pos0=1000, hq=6, hkv=2, d=128, budget=256, seed=43,
           unscaled=True)
+
+
+@pytest.mark.parametrize("hq,hkv", [(10, 2), (16, 1)])
+def test_backward_head_group_sizes(hq, hkv):
+    # 5 heads per group: a row's group spans 2.5 KiB, the last 1 KiB load half used;
+    # 16 heads: every tile row is a real head.
+    _case(lq=160, lk=900, q_pos0=740, hq=hq, hkv=hkv, d=256, budget=512, seed=44 + hq)
