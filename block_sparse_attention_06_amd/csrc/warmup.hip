@@ -395,67 +395,103 @@ __global__ __launch_bounds__(256) void index_scores_bwd_dq_kernel(IdxBwdArgs a) 
   }
 }
 
-// Block-major: a wave owns 16 pooled keys and walks the query rows that score any of
-// them, 4 tokens (16 (token, head) rows) at a time: z = q.kbar^T (A = q, B = pooled
-// keys), so a lane holds block c16 and rows 4*quad + i (token quad's heads); dz is the
-// A operand of dkbar = dz^T.q (k = rows), B = the token's 4 heads x 8 dims.
+// Block-major: a workgroup owns 16 pooled keys; its 4 waves split the query rows that
+// score any of them, 4 tokens (16 (token, head) rows) per step, wave v taking steps v,
+// v + 4, ... : z = q.kbar^T (A = q, B = pooled keys), so a lane holds block c16 and rows
+// 4*quad + i (token quad's heads); dz is the A operand of dkbar = dz^T.q (k = rows), B =
+// the token's 4 heads x 8 dims. Every load is unconditional (clamped rows, heads and
+// dims meet dz = 0 or are never stored) and a wave's next step is loaded before the
+// current one is multiplied. The 4 partial sums are added in LDS in a fixed order.
 template <int DI>
 __global__ __launch_bounds__(256) void index_scores_bwd_dk_kernel(IdxBwdArgs a) {
   constexpr int NC = DI / 32;
   constexpr int NT = 8;
+  __shared__ float part[3][NT * 4][64];  // waves 1..3: acc[e][i] of each lane
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;
   const int quad = lane >> 4;
-  const int64_t b0 = ((int64_t)blockIdx.x * 4 + wave) * 16;
-  if (b0 >= a.nblk) return;
+  const int64_t b0 = (int64_t)blockIdx.x * 16;
+  if (b0 >= a.nblk) return;  // uniform over the workgroup
   const int64_t blk = b0 + c16;
   const bool bv = blk < a.nblk;
+  const int64_t blk_c = bv ? blk : a.nblk - 1;
   uint4 Kc[NC];
   {
-    const uint16_t* kp = a.kp + (bv ? blk : 0) * DI + quad * 8;
+    const uint16_t* kp = a.kp + blk_c * DI + quad * 8;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) Kc[c] = bv ? ld16(kp + c * 32) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < NC; ++c) Kc[c] = ld16(kp + c * 32);
   }
   // Rows that score block b0: t / r > b0, i.e. t >= r * (b0 + 1).
   const int64_t t_first = (int64_t)a.r * (b0 + 1);
-  const int64_t tok_begin = max((int64_t)0, t_first - a.q_pos0);
+  const int64_t tok_base = max((int64_t)0, t_first - a.q_pos0) / 4 * 4;
+  const int64_t n_steps = a.lq > tok_base ? (a.lq - tok_base + 3) / 4 : 0;
+  const int hmax = a.h_idx - 1;
+  const int dmax = DI / 8 - 1;
+
+  struct In {
+    uint4 Aq[NC];  // q of (token tok0 + (c16 >> 2), head c16 & 3), dims quad*8 + 32c
+    uint4 Qr[4];   // q of (token tok0 + quad, head kk), dims 8*c16 ..
+    float g, w[4];
+  };
+  auto fetch = [&](In& in, int64_t s) {
+    const int64_t tok0 = tok_base + 4 * s;
+    const int64_t tka = min(tok0 + (c16 >> 2), a.lq - 1);
+    const uint16_t* qp = a.q_idx + (tka * a.h_idx + min(c16 & 3, hmax)) * DI + quad * 8;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) in.Aq[c] = ld16(qp + c * 32);
+    const int64_t tk = min(tok0 + quad, a.lq - 1);
+    in.g = a.dscores[tk * a.ld + blk_c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) in.w[i] = a.w[tk * a.h_idx + min(i, hmax)];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      in.Qr[kk] = ld16(a.q_idx + (tk * a.h_idx + min(kk, hmax)) * DI + min(c16, dmax) * 8);
+  };
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t tok0 = tok_begin / 4 * 4; tok0 < a.lq; tok0 += 4) {
-    // A: row c16 = (token tok0 + (c16 >> 2), head c16 & 3).
-    const int64_t tka = tok0 + (c16 >> 2);
-    const int ha = c16 & 3;
-    const bool ra = tka < a.lq && ha < a.h_idx;
-    const uint16_t* qp =
-        a.q_idx + ((ra ? tka : 0) * a.h_idx + (ra ? ha : 0)) * DI + quad * 8;
+  auto step = [&](const In& in, int64_t s) {
     f32x4 Z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      Z = mfma_16x16x32(ra ? ld16(qp + c * 32) : make_uint4(0, 0, 0, 0), Kc[c], Z);
+    for (int c = 0; c < NC; ++c) Z = mfma_16x16x32(in.Aq[c], Kc[c], Z);
     // Output rows 4*quad + i: token tok0 + quad, head i; column c16: block blk.
-    const int64_t tk = tok0 + quad;
+    const int64_t tk = tok_base + 4 * s + quad;
     const bool tv = tk < a.lq;
     const int64_t own = tv ? min((a.q_pos0 + tk) / a.r, a.nblk) : 0;
-    const float g = (tv && bv && blk < own) ? a.dscores[tk * a.ld + blk] : 0.f;
+    const float g = (tv && bv && blk < own) ? in.g : 0.f;
     float dz[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float wi = (tv && i < a.h_idx) ? a.w[tk * a.h_idx + i] : 0.f;
-      dz[i] = Z[i] > 0.f ? g * wi : 0.f;
-    }
+    for (int i = 0; i < 4; ++i) dz[i] = (Z[i] > 0.f && i < a.h_idx) ? g * in.w[i] : 0.f;
     const uint2 A = make_uint2(pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3]));
-    // B: token tok0 + quad, heads kk (k = rows 4*quad + kk), dims 8*c16 .. + 7.
-    uint4 Qr[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bool ok = tv && kk < a.h_idx && c16 < DI / 8;
-      Qr[kk] = ok ? ld16(a.q_idx + (tk * a.h_idx + kk) * DI + c16 * 8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < NT; ++e) acc[e] = mfma_16x16x16(A, w_repack(Qr, e), acc[e]);
+    for (int e = 0; e < NT; ++e) acc[e] = mfma_16x16x16(A, w_repack(in.Qr, e), acc[e]);
+  };
+  In i0, i1;
+  fetch(i0, wave);
+  fetch(i1, wave + 4);
+  for (int64_t s = wave; s < n_steps; s += 8) {
+    step(i0, s);
+    fetch(i0, s + 8);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 4 < n_steps) step(i1, s + 4);
+    fetch(i1, s + 12);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < NT; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[wave - 1][e * 4 + i][lane] = acc[e][i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int e = 0; e < NT; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[e][i] += part[w][e * 4 + i][lane];
   // acc[e][i]: block b0 + 4*quad + i, dim 8*c16 + e.
   if (c16 < DI / 8) {
 #pragma unroll
@@ -525,7 +561,7 @@ hipError_t launch_index_scores_bwd(const IdxBwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(index_scores_bwd_dq_kernel<64>, gq, dim3(256), 0, stream, a);
   }
   if (a.nblk > 0) {
-    const dim3 gk((unsigned)((a.nblk + 63) / 64));
+    const dim3 gk((unsigned)((a.nblk + 15) / 16));
     if (a.d_idx == 128)
       hipLaunchKernelGGL(index_scores_bwd_dk_kernel<128>, gk, dim3(256), 0, stream, a);
     else
