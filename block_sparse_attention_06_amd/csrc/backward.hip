@@ -116,48 +116,59 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_dq_kernel(BwdArgs a) {
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.scale_log2;
 
-  // Steps of 4 kept blocks, two in flight: a step's block ids are scalar loads (the
-  // selection row is read-only here and uniform per wave), its K and V rows are
-  // unconditional vector loads (padding reads token 0, masked), so the waits count
-  // exactly one step's loads.
+  // Steps of 4 kept blocks (16 keys: key x = token x % 4 of block slot x / 4), two in
+  // flight. A step's block ids are scalar loads (the selection row is read-only here
+  // and uniform per wave); its K and V rows are read whole (load u, lane L: 16-byte
+  // chunk L % 32 of key 2u + L / 32, padding reads token 0, masked) and staged in the
+  // wave's LDS tiles ([key][chunk], chunks XOR-swizzled by key & 7), which give the A
+  // operands of S^T = K.Q^T and dP^T = V.dO^T (key c16, chunk quad + 4c) and the B
+  // operand of dQ = dS.K (4 keys per lane, 8 dims each): K is read from memory once.
+  constexpr int CPK = D / 8;         // 16-byte chunks per key row
+  constexpr int LPS = 16 * CPK / 64;  // loads per lane per step, each of K and V
+  __shared__ uint4 dq_tile_k[4][16 * CPK], dq_tile_v[4][16 * CPK];
+  uint4* tk_ = dq_tile_k[wave];
+  uint4* tv_ = dq_tile_v[wave];
   const auto* ssel = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
       reinterpret_cast<uintptr_t>(srow));
   struct Step {
-    uint4 Kc[NC], Vc[NC];  // key c16 = token (c16 & 3) of block slot (c16 >> 2)
-    uint4 Kr[NH][4];       // the tokens of block slot `quad`, 8 dims each
-    int first, bq;         // block of slot 0 (-1: padding reached), block of slot `quad`
+    uint4 Kr[LPS], Vr[LPS];
+    int first, bq;  // block of slot 0 (-1: padding reached), block of slot `quad`
   };
   auto issue = [&](Step& st, int s) {
     int b4[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) b4[j] = (4 * s + j < a.n_sel) ? ssel[4 * s + j] : -1;
     st.first = b4[0];
-    const int bk = c16 < 4 ? b4[0] : (c16 < 8 ? b4[1] : (c16 < 12 ? b4[2] : b4[3]));
-    int64_t tk = (int64_t)bk * 4 + (c16 & 3);
-    tk = bk < 0 ? 0 : min(tk, t);
-    const uint16_t* kp = a.k + tk * kstride + g * D + quad * 8;
-    const uint16_t* vp = a.v + tk * kstride + g * D + quad * 8;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      st.Kc[c] = ld16(kp + c * 32);
-      st.Vc[c] = ld16(vp + c * 32);
-    }
     st.bq = quad == 0 ? b4[0] : (quad == 1 ? b4[1] : (quad == 2 ? b4[2] : b4[3]));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      int64_t tv = (int64_t)st.bq * 4 + kk;
-      tv = st.bq < 0 ? 0 : min(tv, t);
-      const uint16_t* p = a.k + tv * kstride + g * D + c16 * 8;
-#pragma unroll
-      for (int hf = 0; hf < NH; ++hf) st.Kr[hf][kk] = ld16(p + hf * 128);
+    for (int u = 0; u < LPS; ++u) {
+      const int key = u * (64 / CPK) + lane / CPK;
+      const int slot = key >> 2;
+      const int bk = slot == 0 ? b4[0] : (slot == 1 ? b4[1] : (slot == 2 ? b4[2] : b4[3]));
+      int64_t tok = (int64_t)bk * 4 + (key & 3);
+      tok = bk < 0 ? 0 : min(tok, t);
+      const int64_t off = tok * kstride + g * D + (lane % CPK) * 8;
+      st.Kr[u] = ld16(a.k + off);
+      st.Vr[u] = ld16(a.v + off);
     }
   };
   auto compute = [&](const Step& st) {
+#pragma unroll
+    for (int u = 0; u < LPS; ++u) {
+      const int key = u * (64 / CPK) + lane / CPK;
+      const int ch = (lane % CPK) ^ (key & 7);
+      tk_[key * CPK + ch] = st.Kr[u];
+      tv_[key * CPK + ch] = st.Vr[u];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      S = mfma_16x16x32(st.Kc[c], Qc[c], S);
-      dP = mfma_16x16x32(st.Vc[c], dOc[c], dP);
+      const int ch = (quad + 4 * c) ^ (c16 & 7);
+      S = mfma_16x16x32(tk_[c16 * CPK + ch], Qc[c], S);
+      dP = mfma_16x16x32(tv_[c16 * CPK + ch], dOc[c], dP);
     }
     // Row 4*quad+i of S^T is token bq*4 + i; column c16 is head c16.
     float ds[4];
@@ -169,10 +180,21 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_dq_kernel(BwdArgs a) {
     }
     const uint2 A = make_uint2(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]));
 #pragma unroll
-    for (int hf = 0; hf < NH; ++hf)
+    for (int hf = 0; hf < NH; ++hf) {
+      uint4 Kq[4];  // the tokens of block slot `quad`, dims hf*128 + 8*c16 ..
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int key = 4 * quad + kk;
+        Kq[kk] = tk_[key * CPK + ((c16 + 16 * hf) ^ (key & 7))];
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        acc[hf * 8 + e] = mfma_16x16x16(A, bwd_repack(st.Kr[hf], e), acc[hf * 8 + e]);
+        acc[hf * 8 + e] = mfma_16x16x16(A, bwd_repack(Kq, e), acc[hf * 8 + e]);
+    }
+    // The next step's tile stores must not pass these reads.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
   Step A0, A1;
   issue(A0, 0);
