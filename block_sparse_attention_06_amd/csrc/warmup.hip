@@ -10,11 +10,12 @@
 // constant.
 //
 // Kernels:
-//  * kl_dense_kernel<TARGET = false>: dense causal lse of every (query row, head);
-//    kl_dense_kernel<TARGET = true>: per scored block, the max over its 4 keys of the
-//    head-summed probabilities exp(S - lse) (unnormalised). Both walk the keys in
+//  * kl_split_kernel / kl_dense_kernel <TARGET = false>: dense causal lse of every
+//    (query row, head); <TARGET = true>: per scored block, the max over its 4 keys of
+//    the head-summed probabilities exp(S - lse) (unnormalised). Both walk the keys in
 //    steps shared by a workgroup's rows through LDS (S = Q.K^T on
-//    v_mfma_f32_16x16x32_bf16).
+//    v_mfma_f32_16x16x32_bf16); the split kernel (up to 2 KV groups) gives each group
+//    its own waves, the dense one (3 or 4 groups) keeps a row's groups in one wave.
 //  * kl_loss_kernel: one workgroup per row: normalises the target, the scores'
 //    log-softmax, the KL value and dL/ds = softmax(s) - target, sums in fp64.
 //  * index_scores_bwd_dq_kernel / _dk_kernel: the gradients of the scores with
@@ -507,6 +508,185 @@ __global__ __launch_bounds__(256) void index_scores_bwd_dk_kernel(IdxBwdArgs a) 
   }
 }
 
+// The same passes with the KV groups split over the waves (up to 2 groups): 8 / H waves
+// per group, 4 rows each, so a workgroup takes 4 * 8 / H rows and a wave reads only its
+// own group's keys from the shared tile, each key fragment serving 4 rows (the kernel
+// above reads both groups' keys for 2 rows). The target pass adds the groups' head
+// sums through LDS: every wave parks its per-(row, key) sums, and after the step's
+// barrier the waves of group 0 add them up and take each block's max.
+template <int D, bool TARGET, int KS, int H>
+__global__ __launch_bounds__(512) void kl_split_kernel(KlArgs a) {
+  constexpr int NC = D / 32;
+  constexpr int VPR = D / 8;
+  constexpr int KROW = VPR + 1;
+  constexpr int RPW = 4;
+  constexpr int WPG = kKlWaves / H;     // waves per group
+  constexpr int TILE_ROWS = WPG * RPW;  // rows per workgroup
+  constexpr int LPT = (KS * H * VPR + 511) / 512;
+  __shared__ uint4 kt[2][H][KS][KROW];
+  __shared__ float xch[2][H][TARGET ? TILE_ROWS : 1][TARGET ? KS : 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15;
+  const int quad = lane >> 4;
+  const int grp = wave / WPG, wr = wave % WPG;
+  const int G = a.hq / H;
+  const bool hv = c16 < G;  // the Q operand's row c16 is a head of the group
+  const int64_t row0 = (int64_t)blockIdx.x * TILE_ROWS;
+  const int64_t t_last = a.q_pos0 + min(row0 + TILE_ROWS, a.lq) - 1;
+  const int64_t kend = TARGET ? min(t_last / a.r, a.nblk) * a.r : t_last + 1;
+  if (kend <= 0) return;
+  const int nsteps = (int)((kend + KS - 1) / KS);
+  const int64_t kstride = (int64_t)H * D;
+
+  int64_t row[RPW], lim[RPW];
+  bool rv[RPW];
+  uint4 Qc[RPW][NC];
+  float L2v[RPW][4], m_run[RPW][4], l_run[RPW][4];  // heads 4*quad + i
+#pragma unroll
+  for (int p = 0; p < RPW; ++p) {
+    row[p] = row0 + wr * RPW + p;
+    rv[p] = row[p] < a.lq;
+    const int64_t t = a.q_pos0 + (rv[p] ? row[p] : 0);
+    lim[p] = !rv[p] ? 0 : (TARGET ? min(t / a.r, a.nblk) * a.r : t + 1);
+    const bool ok = rv[p] && hv;
+    const uint16_t* qp =
+        a.q + ((rv[p] ? row[p] : 0) * a.hq + grp * G + (hv ? c16 : 0)) * (int64_t)D + quad * 8;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) Qc[p][c] = ok ? ld16(qp + c * 32) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * quad + i;
+      L2v[p][i] = !TARGET ? 0.f
+                  : (rv[p] && h < G) ? a.lse[row[p] * a.hq + grp * G + h] * kLog2eW : INFINITY;
+      m_run[p][i] = kKlNoMax;
+      l_run[p][i] = 0.f;
+    }
+  }
+
+  auto issue = [&](uint4 (&R)[LPT], int s) {
+#pragma unroll
+    for (int l = 0; l < LPT; ++l) {
+      const int e = tid + 512 * l;
+      const int key = e / (H * VPR), g = (e / VPR) % H, v = e % VPR;
+      const int64_t j = min((int64_t)s * KS + min(key, KS - 1), kend - 1);
+      R[l] = ld16(a.k + j * kstride + g * D + v * 8);
+    }
+  };
+  auto store = [&](const uint4 (&R)[LPT], int slot) {
+#pragma unroll
+    for (int l = 0; l < LPT; ++l) {
+      const int e = tid + 512 * l;
+      const int key = e / (H * VPR), g = (e / VPR) % H, v = e % VPR;
+      if (e < KS * H * VPR) kt[slot][g][key][v] = R[l];
+    }
+  };
+  auto compute = [&](int s, int slot) {
+#pragma unroll
+    for (int u = 0; u < KS / 16; ++u) {
+      const int64_t j0 = (int64_t)s * KS + u * 16;
+      const int64_t key = j0 + c16;
+      uint4 Kc[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) Kc[c] = kt[slot][grp][u * 16 + c16][quad + 4 * c];
+#pragma unroll
+      for (int p = 0; p < RPW; ++p) {
+        float acc = 0.f;
+        if (j0 < lim[p]) {
+          f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NC; ++c) S = mfma_16x16x32(Qc[p][c], Kc[c], S);
+          if constexpr (TARGET) {
+            // Padding heads carry L2 = +inf, so they add exp2(-inf) = 0.
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc += __builtin_amdgcn_exp2f(S[i] * a.scale_log2 - L2v[p][i]);
+          } else {
+            // One exponential per score: e = 2^-|x - m| is the old sum's factor when x
+            // is the new max, else the new term.
+            const bool kok = key < lim[p];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = kok ? S[i] * a.scale_log2 : -INFINITY;
+              const float dlt = x - m_run[p][i];
+              const float e = __builtin_amdgcn_exp2f(-fabsf(dlt));
+              const bool up = dlt > 0.f;
+              l_run[p][i] = up ? fmaf(l_run[p][i], e, 1.f) : l_run[p][i] + e;
+              m_run[p][i] = up ? x : m_run[p][i];
+            }
+          }
+        }
+        if constexpr (TARGET) {
+          float v = key < lim[p] ? acc : 0.f;
+          v += __shfl_xor(v, 16, 64);
+          v += __shfl_xor(v, 32, 64);  // key j0 + c16, summed over the group's heads
+          if (quad == 0) xch[slot][grp][wr * RPW + p][u * 16 + c16] = v;
+        }
+      }
+    }
+  };
+  // After the step's barrier: the group-0 waves add the groups' sums of their rows (row
+  // wr * 4 + quad) and write each scored block's max over its 4 keys.
+  auto finalize = [&](int s, int slot) {
+    if constexpr (TARGET) {
+      if (grp != 0) return;
+      const int lr = wr * RPW + quad;
+      const int64_t rq = row0 + lr;
+      const int64_t lq_ = quad == 0 ? lim[0] : (quad == 1 ? lim[1] : (quad == 2 ? lim[2] : lim[3]));
+#pragma unroll
+      for (int u = 0; u < KS / 16; ++u) {
+        const int64_t key = (int64_t)s * KS + u * 16 + c16;
+        float v = xch[slot][0][lr][u * 16 + c16];
+        if (H == 2) v += xch[slot][H - 1][lr][u * 16 + c16];
+        v = fmaxf(v, __shfl_xor(v, 1, 64));
+        v = fmaxf(v, __shfl_xor(v, 2, 64));  // max over the block's 4 keys
+        const int64_t b = key / 4;
+        if ((c16 & 3) == 0 && rq < a.lq && b * a.r < lq_) a.target[rq * a.ld + b] = v;
+      }
+    }
+  };
+
+  uint4 R0[LPT], R1[LPT];
+  issue(R0, 0);
+  issue(R1, min(1, nsteps - 1));
+  store(R0, 0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    issue(R0, min(s + 2, nsteps - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s, 0);
+    if (s + 1 < nsteps) store(R1, 1);
+    __syncthreads();
+    finalize(s, 0);
+    if (s + 1 >= nsteps) break;
+    issue(R1, min(s + 3, nsteps - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s + 1, 1);
+    if (s + 2 < nsteps) store(R0, 0);
+    __syncthreads();
+    finalize(s + 1, 1);
+  }
+
+  if constexpr (!TARGET) {
+#pragma unroll
+    for (int p = 0; p < RPW; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = m_run[p][i], l = l_run[p][i];
+#pragma unroll
+        for (int dd = 1; dd < 16; dd <<= 1) {
+          const float mo = __shfl_xor(m, dd, 64), lo = __shfl_xor(l, dd, 64);
+          const float mn = fmaxf(m, mo);
+          l = l * exp2f(m - mn) + lo * exp2f(mo - mn);
+          m = mn;
+        }
+        const int h = 4 * quad + i;
+        if (rv[p] && c16 == 0 && h < G) a.lse[row[p] * a.hq + grp * G + h] = m * kLn2W + logf(l);
+      }
+  }
+}
+
 // dk_idx[j] = dk_pooled[j / r] / r for tokens of complete blocks, 0 for the rest.
 __global__ __launch_bounds__(256) void pool_keys_bwd_kernel(IdxBwdArgs a) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -529,6 +709,15 @@ void launch_kl_pair(const KlArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((kl_dense_kernel<D, true, KS, NG, RPW>), grid, dim3(512), 0, stream, a);
 }
 
+// Both passes with the groups split over the waves: rows per workgroup = 4 * 8 / H.
+template <int D, int KS, int H>
+void launch_kl_split(const KlArgs& a, hipStream_t stream) {
+  constexpr int rows = 4 * kKlWaves / H;
+  const dim3 grid((unsigned)((a.lq + rows - 1) / rows));
+  hipLaunchKernelGGL((kl_split_kernel<D, false, KS, H>), grid, dim3(512), 0, stream, a);
+  hipLaunchKernelGGL((kl_split_kernel<D, true, KS, H>), grid, dim3(512), 0, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_kl_target(const KlArgs& a, hipStream_t stream) {
@@ -537,8 +726,13 @@ hipError_t launch_kl_target(const KlArgs& a, hipStream_t stream) {
   // Up to 2 groups: 2 rows per wave, 32 keys per step; 3 or 4 groups: 1 row per wave
   // (the same Q registers), 16 keys per step (the same LDS).
   if (a.hkv <= 2) {
-    if (a.d == 256) launch_kl_pair<256, 32, 2, 2>(a, stream);
-    else launch_kl_pair<128, 32, 2, 2>(a, stream);
+    if (a.hkv == 2) {
+      if (a.d == 256) launch_kl_split<256, 32, 2>(a, stream);
+      else launch_kl_split<128, 32, 2>(a, stream);
+    } else {
+      if (a.d == 256) launch_kl_split<256, 32, 1>(a, stream);
+      else launch_kl_split<128, 32, 1>(a, stream);
+    }
   } else {
     if (a.d == 256) launch_kl_pair<256, 16, 4, 1>(a, stream);
     else launch_kl_pair<128, 16, 4, 1>(a, stream);
