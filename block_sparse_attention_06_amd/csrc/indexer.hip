@@ -132,10 +132,128 @@ __global__ __launch_bounds__(256) void pool_keys_varlen_kernel(const uint16_t* _
   pool_block8(k + k0 * d, d, b, c, r, 0, rope_dim, inv, p + ((int64_t)bi * max_nb + b) * d);
 }
 
+// Wave-row pooling, used when a row's d/8 threads (TPR) are a power of two <= 64, so no
+// row straddles a wave, and r = 4. Compared with the per-thread form above: the four
+// loads of a thread are issued together, a workgroup
+// strides over the blocks, and with an encoding the angles of the wave's rows are
+// spread over all 64 lanes (their sines and cosines go through wave-private LDS) while
+// every lane rotates and stores its own 8 columns, taking its partner columns' means
+// (c +- rope_dim/2, in the same row) from the partner lane. Arithmetic and rounding
+// are those of pool_block8, value for value.
+struct PoolWaveArgs {
+  const uint16_t* k;
+  int64_t ks;
+  int64_t nb;  // blocks (plain); max blocks per sequence (packed)
+  int d, r;
+  uint16_t* p;
+  int64_t ps;
+  int64_t first_block;
+  int rope_dim;
+  double theta;
+  const int32_t* cu_k;  // packed sequences (blockIdx.y) or null
+};
+
+constexpr int kPoolWaveMaxD = 512;  // TPR <= 64
+
+// pool_mean8 with the r = 4 loads issued together.
+__device__ __forceinline__ void pool_mean8_r4(const uint16_t* __restrict__ k, int64_t ks,
+                                              int64_t b, int c, double (&m)[8]) {
+  uint4 x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = ld16(k + (b * 4 + j) * ks + c);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w4[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m[2 * e] += (double)bf16_bits_to_f32(w4[e] & 0xffffu);
+      m[2 * e + 1] += (double)bf16_bits_to_f32(w4[e] >> 16);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] /= 4;
+}
+
+__global__ __launch_bounds__(256) void pool_keys_wave_kernel(PoolWaveArgs a) {
+  __shared__ double inv[kPoolWaveMaxD / 2];
+  __shared__ double2 sc_all[4][kWave * 4];  // per wave: rows_per_wave * rope_dim/2 <= 256
+  const uint16_t* k = a.k;
+  uint16_t* p = a.p;
+  int64_t nb = a.nb, first_block = a.first_block;
+  if (a.cu_k) {  // packed: sequence blockIdx.y, positions from its first token
+    const int64_t k0 = a.cu_k[blockIdx.y];
+    k += k0 * a.ks;
+    nb = min(((int64_t)a.cu_k[blockIdx.y + 1] - k0) / a.r, a.nb);
+    p += (int64_t)blockIdx.y * a.nb * a.ps;
+    first_block = 0;
+  }
+  const int rope_dim = a.rope_dim, h = rope_dim >> 1;
+  if (rope_dim) rope_freqs(inv, rope_dim, a.theta);
+  const int tpr = a.d >> 3, rpw = kWave / tpr, rpi = 4 * rpw;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int rw = lane / tpr, c = (lane & (tpr - 1)) * 8;
+  const bool rot = c < rope_dim, first_half = c < h;
+  const int partner = rot ? lane + (first_half ? (h >> 3) : -(h >> 3)) : lane;
+  const int ai = rw * h + (first_half ? c : c - h);  // this lane's first (sin, cos) entry
+  double2* sc = sc_all[wave];
+  for (int64_t base = (int64_t)blockIdx.x * rpi; base < nb; base += (int64_t)gridDim.x * rpi) {
+    const int64_t row0 = base + wave * rpw;
+    const int64_t b = row0 + rw, bl = min(b, nb - 1);
+    double x[8];
+    pool_mean8_r4(k, a.ks, bl, c, x);
+    if (rope_dim) {
+      for (int t = lane; t < rpw * h; t += kWave) {
+        const int row = t / h, i = t - row * h;
+        const int64_t bb = min(row0 + row, nb - 1);
+        double sn, cs;
+        sincos((double)((first_block + bb) * a.r) * inv[i], &sn, &cs);
+        sc[t] = make_double2(sn, cs);
+      }
+      double y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = __shfl(x[e], partner);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (rot) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double2 v = sc[ai + e];
+          // first half: a*cos - b*sin with b the partner; second half: b*cos + a*sin
+          x[e] = first_half ? x[e] * v.y - y[e] * v.x : x[e] * v.y + y[e] * v.x;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (b < nb) store_bf16x8(x, p + b * a.ps + c);
+  }
+}
+
+static bool pool_wave_fits(int d, int r) {
+  const int tpr = d >> 3;
+  return r == 4 && d <= kPoolWaveMaxD && (tpr & (tpr - 1)) == 0;
+}
+
+static hipError_t launch_pool_wave(const PoolWaveArgs& a, int64_t rows, int batch,
+                                   hipStream_t stream) {
+  const int rpi = 4 * (kWave / (a.d >> 3));
+  const int64_t passes = (rows + rpi - 1) / rpi;
+  const int64_t cap = (int64_t)256 * 5 / batch + 1;  // 5 resident workgroups per CU
+  const unsigned grid = (unsigned)(passes < cap ? passes : cap);
+  hipLaunchKernelGGL(pool_keys_wave_kernel, dim3(grid, (unsigned)batch), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_pool_keys(const uint16_t* k_idx, int64_t k_stride, int64_t n_blocks, int d_idx,
                             int r, uint16_t* k_pooled, int64_t p_stride, const PooledPe& pe,
                             hipStream_t stream) {
   if (n_blocks <= 0) return hipSuccess;
+  if (pool_wave_fits(d_idx, r))
+    return launch_pool_wave({k_idx, k_stride, n_blocks, d_idx, r, k_pooled, p_stride, pe.first_block,
+                          pe.rope_dim, pe.theta, nullptr},
+                         n_blocks, 1, stream);
   const int64_t threads = n_blocks * (d_idx / 8);
   const int64_t grid = (threads + 255) / 256;
   hipLaunchKernelGGL(pool_keys_kernel, dim3((unsigned)grid), dim3(256), 0, stream, k_idx,
@@ -148,6 +266,10 @@ hipError_t launch_pool_keys_varlen(const uint16_t* k_idx, const int32_t* cu_k, i
                                    int64_t max_nb, int d_idx, int r, uint16_t* k_pooled,
                                    const PooledPe& pe, hipStream_t stream) {
   if (max_nb <= 0 || batch <= 0) return hipSuccess;
+  if (pool_wave_fits(d_idx, r))
+    return launch_pool_wave({k_idx, d_idx, max_nb, d_idx, r, k_pooled, d_idx, 0, pe.rope_dim, pe.theta,
+                          cu_k},
+                         max_nb, batch, stream);
   const int64_t grid = (max_nb * (d_idx / 8) + 255) / 256;
   hipLaunchKernelGGL(pool_keys_varlen_kernel, dim3((unsigned)grid, (unsigned)batch), dim3(256), 0,
                      stream, k_idx, cu_k, max_nb, d_idx, r, k_pooled, pe.rope_dim, pe.theta);

@@ -59,6 +59,17 @@ def test_pool_keys_bit_exact(n_tok, d_i, row_stride):
     np.testing.assert_array_equal(bits(out), O.pool_keys(bits(k), 4))
 
 
+@pytest.mark.parametrize("n_tok,d_i", [(4 * 300 + 3, 256), (4 * 200, 512), (4 * 513 + 2, 96),
+                                      (4 * 100 + 1, 1024), (4 * 50, 8), (4 * 70, 32)])
+def test_pool_keys_other_widths(n_tok, d_i):
+    # widths whose rows fill whole waves (8..512) and widths that do not (96, 1024)
+    _say(f"pool n_tok={n_tok} d_i={d_i}")
+    k = _randn_bf16((n_tok, d_i), seed=n_tok + d_i, scale=1 / math.sqrt(d_i))
+    out = Q.qsa_pool_keys(k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out), O.pool_keys(bits(k), 4))
+
+
 # ------------------------------------------------------------------------------------
 # Stage 2: scores
 # ------------------------------------------------------------------------------------

@@ -34,6 +34,21 @@ def test_pool_with_encoding_bit_exact(n_tok, d_i, rope_dim, first_block):
     np.testing.assert_array_equal(bits(got), ref)
 
 
+@pytest.mark.parametrize("n_tok,d_i,rope_dim,first_block",
+                         [(4 * 3001, 256, 48, 77), (4 * 999 + 1, 512, 512, 5),
+                          (4 * 300, 64, 64, 0), (4 * 500, 96, 32, 9), (4 * 123, 1024, 80, 1)])
+def test_pool_with_encoding_other_shapes(n_tok, d_i, rope_dim, first_block):
+    # partner columns rope_dim/2 apart that are not a power of two (48, 80), a whole-row
+    # rotation, and widths taking the per-thread form (96, 1024)
+    _say(f"encoded pool n_tok={n_tok} d_i={d_i} rope_dim={rope_dim}")
+    g = torch.Generator(device=DEV).manual_seed(n_tok + d_i)
+    k = (torch.randn((n_tok, d_i), generator=g, device=DEV) / math.sqrt(d_i)).to(torch.bfloat16)
+    got = Q.qsa_pool_keys(k, pe=(rope_dim, 1.0e4), first_block=first_block)
+    torch.cuda.synchronize()
+    ref = O.pool_keys(bits(k), 4, (rope_dim, 1.0e4), first_block=first_block)
+    np.testing.assert_array_equal(bits(got), ref)
+
+
 def _check_rows(inp, wl, out, sel, kp, rows, pe, q_pos0, prefix_bits=None):
     res = O.forward_prefill(bits(inp["q"]), bits(inp["k"]), bits(inp["v"]), bits(inp["q_idx"]),
                             inp["w"].cpu().numpy(), bits(inp["k_idx"]), r=4, budget=wl.budget,
