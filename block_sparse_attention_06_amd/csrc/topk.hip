@@ -7,15 +7,22 @@
 // blocks, ranked by score (descending) then block id (ascending); emit the kept ids
 // in ascending order, padded with -1.
 //
-// One workgroup per row (or per row segment), reading the row about once:
-//   1. a sample of the row (every k-th run of 32 consecutive scores) gives a value
-//      bin above which roughly 2m candidates are expected;
-//   2. one streaming pass appends every candidate at or above that bin (an upper set
-//      of the value order, so if it holds at least m candidates it holds the m best)
-//      to an LDS list;
-//   3. the exact selection below runs on that list -- or, if the list came out
-//      shorter than m or overflowed, on the whole row (same result, more passes).
-// Exact selection of the m best among n candidates:
+// Rows of at most kSegMax candidates: one wave per row (topk_wave_rows_kernel below),
+// reading the row about once -- a sample sets a key threshold, one streaming pass
+// collects the scores at or above it into a wave-private list, and a radix select on
+// (score, id) ranks finds the m best in it; a list that overflowed or came out short
+// sends the wave through the whole row instead.
+// Rows longer than kSegMax candidates use two launches: one wave per segment of
+// kWaveSeg scores keeps its kWaveKeep best (wave-wide passes, no barriers)
+// and reports the worst of them; the merge (one workgroup per row) selects the m best
+// of all kept candidates, which is the row's answer when every truncated segment's
+// reported worst ranks at or after the m-th selected (nothing left behind could rank
+// higher); otherwise the merge repeats the exact selection over the whole row. The
+// merge's selection of the m best among n candidates:
+//   0. for a long list, a sample (every k-th run of 32 consecutive scores) gives a
+//      value bin above which roughly 2m candidates are expected, and one streaming
+//      pass appends every candidate at or above it to an LDS list (an upper set of the
+//      value order: if it holds at least m candidates it holds the m best);
 //   a. min / max, then a histogram over kLinBins equal-width value bins; the map
 //      x -> floor((x - min) * bins / (max - min)) is monotone and sends equal values
 //      (and -0.0 / +0.0) to one bin, so every candidate in a bin above the bin B that
@@ -24,15 +31,7 @@
 //   c. candidates above the final bucket are kept; the bucket is sorted in LDS by
 //      (key desc, id asc) -- or, when more than kTieCap candidates share one exact
 //      key, a radix select on the id keeps the lowest ids.
-// Rows longer than kSegMax candidates use two launches: one wave per segment of
-// kWaveSeg scores keeps its kWaveKeep best (wave-wide passes, no barriers)
-// and reports the worst of them; the merge selects the m best of all kept candidates,
-// which is the row's answer when every truncated segment's reported worst ranks at
-// or after the m-th selected (nothing left behind could rank higher); otherwise the
-// merge repeats the exact selection over the whole row.
 // No floating-point atomics; results do not depend on scheduling.
-
-#include <type_traits>
 
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -52,7 +51,6 @@ constexpr int kSampleMax = 4096;
 constexpr int kWaveSeg = kTopkWaveSeg;    // scores per wave in the first pass
 constexpr int kWaveKeep = kTopkWaveKeep;  // candidates kept per wave segment
 
-enum TopkMode { kRows = 0, kMerge = 2 };
 
 template <int LIST, int BWORDS>
 struct TkSharedT {
@@ -69,7 +67,6 @@ struct TkSharedT {
   float wred[2 * kWaves];
   int32_t misc[8];
 };
-using TkRowsShared = TkSharedT<kListCap, kSegMax / 32>;       // ~37 KB
 using TkMergeShared = TkSharedT<2 * kListCap, 262144 / 32>;   // ~82 KB
 
 // ---- block-level primitives ---------------------------------------------------------
@@ -516,7 +513,7 @@ __device__ void select_row(SM& sm, const float* row, const int32_t* ids, int lo,
 
 struct TopkLaunch {
   TopkArgs a;
-  int seg;          // segment length (kSegments / kMerge)
+  int seg;          // segment length
   int n_seg;        // segments per row
   float* cand_val;  // [rows][n_seg][kseg], NaN where absent
   int32_t* cand_idx;
@@ -752,9 +749,11 @@ __device__ __forceinline__ int merge_segments_fast(SM& sm, MergeRegs& r, int m, 
   return 0;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
-  using SM = typename std::conditional<MODE == kRows, TkRowsShared, TkMergeShared>::type;
+// Merge of the segment winners of long rows (one workgroup per row): check that no
+// truncated segment could hide a better candidate (else redo the selection on the
+// whole row), write the ids ascending.
+__global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(TopkLaunch L) {
+  using SM = TkMergeShared;
   __shared__ SM sm;
   const TopkArgs& a = L.a;
   const int tid = threadIdx.x;
@@ -762,7 +761,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
   const int bi = blockIdx.z;
   const int64_t crow = (int64_t)bi * a.lq + row;
   MergeRegs mr;
-  const bool fast_merge = MODE == kMerge && L.n_seg <= kTkThreads * kMergeSPT;
+  const bool fast_merge = L.n_seg <= kTkThreads * kMergeSPT;
   if (fast_merge) merge_fetch(sm, L, crow, mr);
   int64_t t, own, C;
   int m;
@@ -776,19 +775,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkLaunch L) {
     return;
   }
 
-  if constexpr (MODE == kRows) {
-    // C <= kSegMax: kept ids go to a bitmap, written out in ascending order.
-    const int n = (int)C;
-    const int words = (n + 31) / 32;
-    for (int i = tid; i < words; i += kTkThreads) sm.bitmap[i] = 0u;
-    __syncthreads();
-    select_row(sm, srow, nullptr, 0, n, m,
-               [&](int id, float) { atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31)); });
-    write_bitmap_ids(sm, words, out);
-    for (int k = m + tid; k < a.n_sel; k += kTkThreads) out[k] = k == m ? (int32_t)own : -1;
-  } else {
-    // Merge the segment winners, check that no truncated segment could hide a better
-    // candidate (else redo the selection on the whole row), write the ids ascending.
+  {
     int fast = 1;
     if (fast_merge) {
       fast = merge_segments_fast(sm, mr, m, out);
@@ -993,6 +980,325 @@ __global__ __launch_bounds__(256) void topk_wave_segments_kernel(TopkLaunch L) {
   }
 }
 
+// ---- one wave per row ----------------------------------------------------------------
+// Rows of at most kSegMax candidates, one wave each and no workgroup barriers, so that
+// many rows are in flight per CU:
+//   1. a row longer than the list (cap entries) is sampled at 64 evenly spaced runs of
+//      32 scores (one 128-byte line each); the k-th largest sample, k aiming at
+//      sqrt(m * cap) list entries over the whole row, is the key threshold. Shorter
+//      rows take every score;
+//   2. one streaming pass appends each score at or above the threshold, as (order key,
+//      position), to a wave-private LDS list in position order: a lane's 0..4 entries
+//      of a float4 are placed by three ballots of its count's bits;
+//   3. the list is held in registers as 48-bit ranks (key, then 0xffff - position:
+//      larger ranks first, all distinct) and a radix select with 8-bit digits finds the
+//      m-th rank; the entries at or above it are written in list order, which is
+//      ascending id order.
+// A list that overflowed or came out shorter than m runs step 3 over the whole row,
+// streamed from memory once per digit. NaN scores are absent, as in the rest of this
+// file. The result is the same as the workgroup kernel's for any row.
+constexpr int kWrCap = 2048;              // list entries per wave, at most
+constexpr int kWrCapSmall = 1664;         // for m <= 511: 4 workgroups per CU
+constexpr int kWrSlots = kWrCap / kWave;  // list entries per lane, at most
+constexpr int kWrSampleSlots = 32;        // sampled scores per lane (2048 a wave)
+constexpr int kWrVec = 8;                 // float4 loads in flight per lane while streaming
+constexpr int kWrRowsPerWg = 4;
+
+// A wave's LDS: key[cap] then pos[cap]; the 256-bin histogram of the radix select
+// reuses key[0..256), which holds nothing live while a histogram is in use (the list
+// is read into registers before its selection).
+struct WrLds {
+  uint32_t* key;
+  uint16_t* pos;
+  uint32_t* hist;
+  int cap;
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t y = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o, kWave) << 32) |
+                       (uint32_t)__shfl_xor((int)(uint32_t)v, o, kWave);
+    v = y < v ? y : v;
+  }
+  return v;
+}
+
+// The need-th largest of the BITS-wide values that each(f) presents (f(v) once per
+// present value, on the lane holding it), found digit by digit from the top, starting
+// below the bits that all values share. Returns the prefix fixed so far and its width
+// in pbits: the values whose top pbits bits are at or above the prefix are the need
+// largest (with ties, when every bit is fixed, the values equal to the need-th largest
+// may add more). need is clamped to the number of present values.
+template <int BITS, class Each>
+__device__ __forceinline__ uint64_t wave_radix_select(uint32_t* hist, uint32_t need, Each each,
+                                                      int& pbits) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t lo = ~0ull, nhi = ~0ull;  // min and (complemented) max
+  uint32_t total = 0;
+  each([&](uint64_t v) {
+    lo = v < lo ? v : lo;
+    nhi = ~v < nhi ? ~v : nhi;
+    ++total;
+  });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) total += (uint32_t)__shfl_xor((int)total, o, kWave);
+  need = min(need, total);
+  pbits = 0;
+  if (need == 0) return 0;
+  lo = wave_min_u64(lo);
+  const uint64_t hi = ~wave_min_u64(nhi);
+  if (lo == hi) {
+    pbits = BITS;
+    return hi;
+  }
+  const int diff = 64 - __clzll((long long)(lo ^ hi));  // width of the differing low part
+  pbits = BITS - diff;
+  uint64_t prefix = hi >> diff;
+  while (pbits < BITS) {
+    const int w = min(8, BITS - pbits);
+    const int shift = BITS - pbits - w;
+    *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_sync();
+    each([&](uint64_t v) {
+      if ((v >> (shift + w)) == prefix)
+        atomicAdd(&hist[(uint32_t)(v >> shift) & ((1u << w) - 1u)], 1u);
+    });
+    wave_lds_sync();
+    const uint4 h = *reinterpret_cast<const uint4*>(hist + 4 * lane);
+    const uint32_t s = h.x + h.y + h.z + h.w;
+    uint32_t suf = s;  // values in the bins of lanes >= this one
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t y = __shfl_down(suf, o, kWave);
+      if (lane + o < kWave) suf += y;
+    }
+    // bin 4*lane + e holds h_e values, with a_e values in the bins above it
+    const uint32_t a3 = suf - s, a2 = a3 + h.w, a1 = a2 + h.z, a0 = a1 + h.y;
+    int e = -1;
+    uint32_t above = 0, cnt = 0;
+    if (a3 < need && need <= a3 + h.w) {
+      e = 3; above = a3; cnt = h.w;
+    } else if (a2 < need && need <= a2 + h.z) {
+      e = 2; above = a2; cnt = h.z;
+    } else if (a1 < need && need <= a1 + h.y) {
+      e = 1; above = a1; cnt = h.y;
+    } else if (a0 < need && need <= a0 + h.x) {
+      e = 0; above = a0; cnt = h.x;
+    }
+    const uint64_t hit = __ballot(e >= 0);
+    const int src = (int)__ffsll((unsigned long long)hit) - 1;  // exactly one bin holds it
+    const int digit = __shfl(4 * lane + e, src, kWave);
+    need -= (uint32_t)__shfl((int)above, src, kWave);
+    const uint32_t in_bin = (uint32_t)__shfl((int)cnt, src, kWave);
+    prefix = (prefix << w) | (uint32_t)digit;
+    pbits += w;
+    if (in_bin == need) break;  // the whole bin is kept
+    wave_lds_sync();
+  }
+  return prefix;
+}
+
+// Appends the flagged entries of a lane's float4 (ids p0..p0+3) in id order, after
+// `count` entries so far; returns this float4's entry total (wave-uniform).
+template <class Put>
+__device__ __forceinline__ uint32_t wave_append4(const bool (&f)[4], uint32_t count, Put put) {
+  const int k = (int)f[0] + (int)f[1] + (int)f[2] + (int)f[3];
+  const uint64_t b0 = __ballot(k & 1), b1 = __ballot(k & 2), b2 = __ballot(k & 4);
+  uint32_t p = count + (uint32_t)(lane_prefix(b0) + 2 * lane_prefix(b1) + 4 * lane_prefix(b2));
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (f[e]) put(p++, e);
+  return (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
+}
+
+__device__ __forceinline__ uint64_t wr_rank(uint32_t key, int pos) {
+  return ((uint64_t)key << 16) | (uint64_t)(0xffffu - (uint32_t)pos);
+}
+
+// Float4 q of the streaming chunk at c0 (clamped into the row; positions >= n absent).
+__device__ __forceinline__ float4 wr_load(const float* row, int c0, int q, int n) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = min(c0 + (q * kWave + lane) * 4, (n - 1) & ~3);
+  return *reinterpret_cast<const float4*>(row + i);
+}
+
+__device__ void wave_select_row(const WrLds L, const float* row, int n, int m, int32_t* out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int kChunk = kWave * 4 * kWrVec;
+  // 1. Threshold key (0 admits every score).
+  uint32_t tau = 0;
+  const int cap = L.cap;
+  if (n > cap) {
+    // 64 runs of 32 consecutive scores (8 float4, 128 bytes), evenly spaced: a
+    // lane reads float4 (lane & 7) of run s * 8 + (lane >> 3).
+    const int n_runs = (n >> 2) >> 3;  // complete runs, >= 64 here
+    uint32_t sk[kWrSampleSlots];
+#pragma unroll
+    for (int s = 0; s < kWrSampleSlots / 4; ++s) {
+      const int run = (int)((int64_t)(s * 8 + (lane >> 3)) * n_runs / 64);
+      const int i = (run * 8 + (lane & 7)) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(row + i);
+      const float xs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sk[4 * s + e] = xs[e] == xs[e] ? order_key(xs[e]) : 0u;
+    }
+    uint32_t nv = 0;
+#pragma unroll
+    for (int j = 0; j < kWrSampleSlots; ++j) nv += sk[j] != 0u;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) nv += __shfl_xor(nv, o, kWave);
+    if (nv > 0) {
+      // aim at the geometric mean of m and cap: the count's error is a factor
+      const int64_t tgt = (int64_t)sqrtf((float)m * (float)cap);
+      const uint32_t k = (uint32_t)max<int64_t>(1, (tgt * nv + n - 1) / n);
+      int pb;
+      const uint64_t pre = wave_radix_select<32>(
+          L.hist, k,
+          [&](auto&& f) {
+#pragma unroll
+            for (int j = 0; j < kWrSampleSlots; ++j)
+              if (sk[j]) f((uint64_t)sk[j]);
+          },
+          pb);
+      tau = (uint32_t)(pre << (32 - pb));
+    }
+    wave_lds_sync();
+  }
+  // 2. Stream the row into the list, the next chunk's loads in flight meanwhile. The
+  // key threshold is compared as the least float whose key reaches it.
+  const float tf = tau <= 0x007fffffu ? -INFINITY : key_to_float(tau);
+  uint32_t count = 0;
+  auto take = [&](const float4 (&v)[kWrVec], int c0) {
+#pragma unroll
+    for (int q = 0; q < kWrVec; ++q) {
+      const int i = c0 + (q * kWave + lane) * 4;
+      const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+      bool f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = xs[e] >= tf && i + e < n;  // NaN: false
+      if (__ballot(f[0] || f[1] || f[2] || f[3]) == 0ull) continue;
+      count += wave_append4(f, count, [&](uint32_t p, int e) {
+        if (p < (uint32_t)cap) {
+          L.key[p] = order_key(xs[e]);
+          L.pos[p] = (uint16_t)(i + e);
+        }
+      });
+    }
+  };
+  // Loads are issued unconditionally (clamped into the row), so that waiting for one
+  // buffer never waits for the other.
+  float4 va[kWrVec], vb[kWrVec];
+#pragma unroll
+  for (int q = 0; q < kWrVec; ++q) va[q] = wr_load(row, 0, q, n);
+  for (int c0 = 0; c0 < n; c0 += 2 * kChunk) {
+#pragma unroll
+    for (int q = 0; q < kWrVec; ++q) vb[q] = wr_load(row, c0 + kChunk, q, n);
+    take(va, c0);
+#pragma unroll
+    for (int q = 0; q < kWrVec; ++q) va[q] = wr_load(row, c0 + 2 * kChunk, q, n);
+    if (c0 + kChunk < n) take(vb, c0 + kChunk);
+  }
+  wave_lds_sync();
+  uint32_t written = 0;
+  if (count >= (uint32_t)m && count <= (uint32_t)cap) {
+    // 3. Select on the list, in registers.
+    uint64_t rk[kWrSlots];
+#pragma unroll
+    for (int j = 0; j < kWrSlots; ++j) {
+      const uint32_t p = (uint32_t)(j * kWave + lane);
+      rk[j] = p < count ? wr_rank(L.key[p], L.pos[p]) : 0ull;
+    }
+    int pb;
+    const uint64_t pre = wave_radix_select<48>(
+        L.hist, (uint32_t)m,
+        [&](auto&& f) {
+#pragma unroll
+          for (int j = 0; j < kWrSlots; ++j)
+            if (rk[j]) f(rk[j]);
+        },
+        pb);
+#pragma unroll
+    for (int j = 0; j < kWrSlots; ++j) {
+      const bool kp = rk[j] != 0ull && (rk[j] >> (48 - pb)) >= pre;
+      const uint64_t b = __ballot(kp);
+      const uint32_t p = written + (uint32_t)lane_prefix(b);
+      if (kp && p < (uint32_t)m) out[p] = (int32_t)(0xffffu - (uint32_t)(rk[j] & 0xffffu));
+      written += (uint32_t)__popcll(b);
+    }
+    written = min(written, (uint32_t)m);
+  } else {
+    // The whole row, one streaming pass per digit, then one to write the kept ids.
+    auto each_row = [&](auto&& f) {
+      for (int c0 = 0; c0 < n; c0 += kChunk) {
+        float4 v[kWrVec];
+#pragma unroll
+        for (int q = 0; q < kWrVec; ++q) v[q] = wr_load(row, c0, q, n);
+#pragma unroll
+        for (int q = 0; q < kWrVec; ++q) {
+          const int i = c0 + (q * kWave + lane) * 4;
+          const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (i + e < n && xs[e] == xs[e]) f(wr_rank(order_key(xs[e]), i + e));
+        }
+      }
+    };
+    int pb;
+    const uint64_t pre = wave_radix_select<48>(L.hist, (uint32_t)m, each_row, pb);
+    for (int c0 = 0; c0 < n; c0 += kChunk) {
+      float4 v[kWrVec];
+#pragma unroll
+      for (int q = 0; q < kWrVec; ++q) v[q] = wr_load(row, c0, q, n);
+#pragma unroll
+      for (int q = 0; q < kWrVec; ++q) {
+        const int i = c0 + (q * kWave + lane) * 4;
+        const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+        bool f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          f[e] = i + e < n && xs[e] == xs[e] &&
+                 (wr_rank(order_key(xs[e]), i + e) >> (48 - pb)) >= pre;
+        written += wave_append4(f, written, [&](uint32_t p, int e) {
+          if (p < (uint32_t)m) out[p] = i + e;
+        });
+      }
+    }
+    written = min(written, (uint32_t)m);
+  }
+  for (int k = (int)written + lane; k < m; k += kWave) out[k] = -1;  // only with NaN scores
+}
+
+__global__ __launch_bounds__(kWrRowsPerWg * kWave) void topk_wave_rows_kernel(TopkArgs a,
+                                                                              int cap) {
+  extern __shared__ uint32_t wr_smem[];  // kWrRowsPerWg * cap * 6 bytes
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kWrRowsPerWg + wave;
+  const int bi = blockIdx.z;
+  if (row >= a.lq) return;
+  int64_t t, own, C;
+  int m;
+  int32_t* out = row_geometry(a, row, bi, t, own, C, m);
+  if (!out) return;
+  if (t < 0 || m == C) {
+    for (int k = lane; k < a.n_sel; k += kWave)
+      out[k] = t < 0 ? -1 : (k < C ? k : (k == C ? (int32_t)own : -1));
+    return;
+  }
+  if (m > 0)
+    wave_select_row(WrLds{wr_smem + wave * cap,
+                          reinterpret_cast<uint16_t*>(wr_smem + kWrRowsPerWg * cap) + wave * cap,
+                          wr_smem + wave * cap, cap},
+                    a.scores + (int64_t)bi * a.s_bs + row * a.ld, (int)C, m, out);
+  for (int k = m + lane; k < a.n_sel; k += kWave) out[k] = k == m ? (int32_t)own : -1;
+}
+
 // ---- host side ----------------------------------------------------------------------
 
 static int64_t max_candidates(const TopkArgs& a) {
@@ -1043,7 +1349,7 @@ static TopkLaunch merge_launch(const TopkArgs& a, void* ws) {
 
 hipError_t launch_topk_merge(const TopkArgs& a, void* ws, hipStream_t stream) {
   if (a.lq <= 0 || a.batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel<kMerge>, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
                      dim3(kTkThreads), 0, stream, merge_launch(a, ws));
   return hipGetLastError();
 }
@@ -1051,9 +1357,12 @@ hipError_t launch_topk_merge(const TopkArgs& a, void* ws, hipStream_t stream) {
 hipError_t launch_topk_blocks(const TopkArgs& a, void* ws, hipStream_t stream) {
   if (a.lq <= 0 || a.batch <= 0) return hipSuccess;
   if (max_candidates(a) <= kSegMax) {
-    TopkLaunch L{a, 0, 0, nullptr, nullptr, nullptr, nullptr, 0};
-    hipLaunchKernelGGL(topk_kernel<kRows>, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
-                       dim3(kTkThreads), 0, stream, L);
+    const int cap = a.n_sel <= 512 ? kWrCapSmall : kWrCap;
+    hipLaunchKernelGGL(topk_wave_rows_kernel,
+                       dim3((unsigned)((a.lq + kWrRowsPerWg - 1) / kWrRowsPerWg), 1,
+                            (unsigned)a.batch),
+                       dim3(kWrRowsPerWg * kWave), (size_t)kWrRowsPerWg * cap * 6, stream, a,
+                       cap);
     return hipGetLastError();
   }
   const TopkLaunch L = merge_launch(a, ws);
@@ -1061,7 +1370,7 @@ hipError_t launch_topk_blocks(const TopkArgs& a, void* ws, hipStream_t stream) {
   const size_t per_wg = 4 * kSegsPerWave;
   hipLaunchKernelGGL(topk_wave_segments_kernel, dim3((unsigned)((segs + per_wg - 1) / per_wg)),
                      dim3(256), 0, stream, L);
-  hipLaunchKernelGGL(topk_kernel<kMerge>, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)a.lq, 1, (unsigned)a.batch),
                      dim3(kTkThreads), 0, stream, L);
   return hipGetLastError();
 }

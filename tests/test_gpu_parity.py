@@ -236,24 +236,47 @@ def test_topk_huge_tie_set_takes_lowest_ids():
     _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
 
 
+@pytest.mark.parametrize("pattern", ["runs32_every16", "runs32_every8"])
 @pytest.mark.parametrize("sampled_high", [True, False])
-def test_topk_adversarial_sample(sampled_high):
-    # The kernel estimates its threshold from every 8th run of 32 scores (rows of
-    # 32768 candidates). Large values only in the sampled runs make the estimate too
-    # high (fewer than m candidates pass); only outside them, too low (the candidate
-    # list overflows). Both must fall back to the exact selection over the whole row.
+def test_topk_adversarial_sample(pattern, sampled_high):
+    # A row of 32768 candidates is sampled at 64 evenly spaced runs of 32 scores (every
+    # 16th run). Large values only in the sampled runs make the threshold too high
+    # (fewer than m candidates pass); only outside them, too low (the candidate list
+    # overflows). Both must fall back to the exact selection over the whole row. The
+    # runs32_every8 pattern (a superset of the sampled runs) is a second spacing.
     rng = np.random.default_rng(15 + sampled_high)
     lq, budget = 3, 2048
     q_pos0 = 4 * 32768
     nblk = 32768 + 4
     x = rng.random((lq, nblk)).astype(np.float32)
-    runs = np.arange(nblk) // 32
-    sampled = runs % 8 == 0
+    if pattern == "runs32_every16":
+        sampled = (np.arange(nblk) // 32) % 16 == 0
+    else:
+        sampled = (np.arange(nblk) // 32) % 8 == 0
     hi = sampled if sampled_high else ~sampled
     x[:, hi] += 10.0
-    _say(f"topk adversarial sampled_high={sampled_high}")
+    _say(f"topk adversarial pattern={pattern} sampled_high={sampled_high}")
     sel = _run_topk(_nan_tail(x, q_pos0), q_pos0, nblk, budget)
     _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
+
+
+@pytest.mark.parametrize("budget", [2048, 4096, 64])
+@pytest.mark.parametrize("kind", ["normal", "quantized"])
+def test_topk_row_lengths_around_the_list_size(budget, kind):
+    # Rows just below, at and above the list size (1664 entries for budgets up to
+    # 2048, else 2048: every score is a list entry up to that; longer rows are sampled),
+    # a ragged length and the 32768 maximum, with distinct scores and with heavy ties
+    # (quantized to halves).
+    rng = np.random.default_rng(budget + len(kind))
+    for c0 in (1662, 1664, 2046, 2047, 2048, 2049, 5001, 32760):
+        q_pos0, lq = 4 * c0 + 1, 8
+        nblk = min((q_pos0 + lq) // 4 + 1, 32768)
+        x = rng.standard_normal((lq, nblk)).astype(np.float32)
+        if kind == "quantized":
+            x = np.round(x * 2) / 2
+        _say(f"topk rows from {c0} blocks, budget {budget}, {kind}")
+        sel = _run_topk(_nan_tail(x, q_pos0), q_pos0, nblk, budget)
+        _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
 
 
 def test_topk_long_rows_concentrated_best():
