@@ -12,7 +12,11 @@
 // collects the scores at or above it into a wave-private list, and a radix select on
 // (score, id) ranks finds the m best in it; a list that overflowed or came out short
 // sends the wave through the whole row instead.
-// Rows longer than kSegMax candidates use two launches: one wave per segment of
+// Rows longer than kSegMax candidates, when there are many: one wave per kSegMax-score
+// segment keeps the segment's m best with that same selection, and one wave per row
+// selects the m best of what its segments kept (topk_long_segments_kernel,
+// topk_long_merge_kernel). Few long rows (decode) use two launches with more, smaller
+// pieces: one wave per segment of
 // kWaveSeg scores keeps its kWaveKeep best (wave-wide passes, no barriers)
 // and reports the worst of them; the merge (one workgroup per row) selects the m best
 // of all kept candidates, which is the row's answer when every truncated segment's
@@ -1129,7 +1133,20 @@ __device__ __forceinline__ float4 wr_load(const float* row, int c0, int q, int n
   return *reinterpret_cast<const float4*>(row + i);
 }
 
-__device__ void wave_select_row(const WrLds L, const float* row, int n, int m, int32_t* out) {
+// This wave's part of the dynamic LDS of a launch with list size cap.
+__device__ __forceinline__ WrLds wr_lds(uint32_t* smem, int cap) {
+  const int wave = threadIdx.x >> 6;
+  return WrLds{smem + wave * cap,
+               reinterpret_cast<uint16_t*>(smem + kWrRowsPerWg * cap) + wave * cap,
+               smem + wave * cap, cap};
+}
+
+// Selects the m best of row[0..n) (positions as ids; NaN absent) and calls emit(k, pos,
+// value) for the k-th kept in ascending position order (k < m), then pad(k) for the
+// places a row with fewer than m present scores leaves empty.
+template <class Emit, class Pad>
+__device__ void wave_select_row(const WrLds L, const float* row, int n, int m, Emit emit,
+                                Pad pad) {
   const int lane = threadIdx.x & (kWave - 1);
   constexpr int kChunk = kWave * 4 * kWrVec;
   // 1. Threshold key (0 admits every score).
@@ -1229,7 +1246,8 @@ __device__ void wave_select_row(const WrLds L, const float* row, int n, int m, i
       const bool kp = rk[j] != 0ull && (rk[j] >> (48 - pb)) >= pre;
       const uint64_t b = __ballot(kp);
       const uint32_t p = written + (uint32_t)lane_prefix(b);
-      if (kp && p < (uint32_t)m) out[p] = (int32_t)(0xffffu - (uint32_t)(rk[j] & 0xffffu));
+      if (kp && p < (uint32_t)m)
+        emit(p, (int)(0xffffu - (uint32_t)(rk[j] & 0xffffu)), key_to_float((uint32_t)(rk[j] >> 16)));
       written += (uint32_t)__popcll(b);
     }
     written = min(written, (uint32_t)m);
@@ -1266,13 +1284,13 @@ __device__ void wave_select_row(const WrLds L, const float* row, int n, int m, i
           f[e] = i + e < n && xs[e] == xs[e] &&
                  (wr_rank(order_key(xs[e]), i + e) >> (48 - pb)) >= pre;
         written += wave_append4(f, written, [&](uint32_t p, int e) {
-          if (p < (uint32_t)m) out[p] = i + e;
+          if (p < (uint32_t)m) emit(p, i + e, xs[e]);
         });
       }
     }
     written = min(written, (uint32_t)m);
   }
-  for (int k = (int)written + lane; k < m; k += kWave) out[k] = -1;  // only with NaN scores
+  for (int k = (int)written + lane; k < m; k += kWave) pad(k);  // only with NaN scores
 }
 
 __global__ __launch_bounds__(kWrRowsPerWg * kWave) void topk_wave_rows_kernel(TopkArgs a,
@@ -1292,10 +1310,97 @@ __global__ __launch_bounds__(kWrRowsPerWg * kWave) void topk_wave_rows_kernel(To
     return;
   }
   if (m > 0)
-    wave_select_row(WrLds{wr_smem + wave * cap,
-                          reinterpret_cast<uint16_t*>(wr_smem + kWrRowsPerWg * cap) + wave * cap,
-                          wr_smem + wave * cap, cap},
-                    a.scores + (int64_t)bi * a.s_bs + row * a.ld, (int)C, m, out);
+    wave_select_row(wr_lds(wr_smem, cap), a.scores + (int64_t)bi * a.s_bs + row * a.ld, (int)C,
+                    m, [&](uint32_t k, int pos, float) { out[k] = pos; },
+                    [&](int k) { out[k] = -1; });
+  for (int k = m + lane; k < a.n_sel; k += kWave) out[k] = k == m ? (int32_t)own : -1;
+}
+
+// ---- long rows by waves ----------------------------------------------------------------
+// Rows of more than kSegMax candidates, when there are enough (row, segment) items to
+// fill the GPU: pass 1 selects the m best of each kSegMax-score segment of a row with
+// the one-wave selection and stores them in ascending id order as (score, id) in the
+// segment's ks slots (NaN / -1 after them); pass 2 runs the same selection over the
+// row's stored slots, whose order is id order, so ties still go to the lower id. A
+// segment keeps its m best and the row keeps m, so nothing a segment dropped can be
+// among the row's m best: the result is exact.
+struct TopkLong {
+  TopkArgs a;
+  int n_wseg;  // segments of kSegMax scores per row
+  int ks;      // candidate slots per segment (n_sel rounded up to 4)
+  float* cand_val;  // [batch * lq][n_wseg][ks]
+  int32_t* cand_idx;
+  int cap;
+};
+
+__global__ __launch_bounds__(kWrRowsPerWg * kWave) void topk_long_segments_kernel(TopkLong T) {
+  extern __shared__ uint32_t wr_smem[];  // kWrRowsPerWg * cap * 6 bytes
+  const TopkArgs& a = T.a;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int64_t item = (int64_t)blockIdx.x * kWrRowsPerWg + wave;
+  if (item >= a.lq * T.n_wseg) return;
+  const int64_t row = item / T.n_wseg;
+  const int seg = (int)(item - row * T.n_wseg);
+  const int bi = blockIdx.z;
+  int64_t t, own, C;
+  int m;
+  if (!row_geometry(a, row, bi, t, own, C, m) || t < 0 || m == C) return;  // no candidates
+  const int64_t slot0 = (((int64_t)bi * a.lq + row) * T.n_wseg + seg) * T.ks;
+  float* cv = T.cand_val + slot0;
+  int32_t* ci = T.cand_idx + slot0;
+  const int64_t lo = (int64_t)seg * kSegMax;
+  const int ns = (int)max<int64_t>(0, min<int64_t>(kSegMax, C - lo));
+  const float* srow = a.scores + (int64_t)bi * a.s_bs + row * a.ld + lo;
+  int kept;
+  if (ns > m) {
+    if (m > 0)
+      wave_select_row(wr_lds(wr_smem, T.cap), srow, ns, m,
+                      [&](uint32_t k, int pos, float v) {
+                        cv[k] = v;
+                        ci[k] = (int32_t)(lo + pos);
+                      },
+                      [&](int k) {
+                        cv[k] = __builtin_nanf("");
+                        ci[k] = -1;
+                      });
+    kept = m;
+  } else {
+    for (int k = lane; k < ns; k += kWave) {
+      cv[k] = srow[k];
+      ci[k] = (int32_t)(lo + k);
+    }
+    kept = ns;
+  }
+  for (int k = kept + lane; k < T.ks; k += kWave) {
+    cv[k] = __builtin_nanf("");
+    ci[k] = -1;
+  }
+}
+
+__global__ __launch_bounds__(kWrRowsPerWg * kWave) void topk_long_merge_kernel(TopkLong T) {
+  extern __shared__ uint32_t wr_smem[];
+  const TopkArgs& a = T.a;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kWrRowsPerWg + wave;
+  const int bi = blockIdx.z;
+  if (row >= a.lq) return;
+  int64_t t, own, C;
+  int m;
+  int32_t* out = row_geometry(a, row, bi, t, own, C, m);
+  if (!out) return;
+  if (t < 0 || m == C) {
+    for (int k = lane; k < a.n_sel; k += kWave)
+      out[k] = t < 0 ? -1 : (k < C ? k : (k == C ? (int32_t)own : -1));
+    return;
+  }
+  if (m > 0) {
+    const int64_t slot0 = ((int64_t)bi * a.lq + row) * T.n_wseg * T.ks;
+    const int32_t* ci = T.cand_idx + slot0;
+    const int n2 = (int)((C + kSegMax - 1) / kSegMax) * T.ks;  // this row's segments
+    wave_select_row(wr_lds(wr_smem, T.cap), T.cand_val + slot0, n2, m,
+                    [&](uint32_t k, int pos, float) { out[k] = ci[pos]; },
+                    [&](int k) { out[k] = -1; });
+  }
   for (int k = m + lane; k < a.n_sel; k += kWave) out[k] = k == m ? (int32_t)own : -1;
 }
 
@@ -1314,11 +1419,30 @@ static int n_wave_segs(const TopkArgs& a) {
 
 static size_t align_up(size_t n) { return (n + 255) & ~size_t(255); }
 
+static int n_long_segs(const TopkArgs& a) {
+  return (int)((max_candidates(a) + kSegMax - 1) / kSegMax);
+}
+
+static int long_slots(const TopkArgs& a) { return (a.n_sel + 3) & ~3; }
+
+// Long rows by waves when there are at least 2048 (row, segment) items and a row's
+// stored candidates fit one wave selection; else segments of kWaveSeg and the merge.
+static bool long_by_waves(const TopkArgs& a) {
+  if (max_candidates(a) <= kSegMax) return false;
+  const int64_t items = (int64_t)a.batch * a.lq * n_long_segs(a);
+  return items >= 2048 && (int64_t)n_long_segs(a) * long_slots(a) <= kSegMax;
+}
+
+// Either layout fits (the launch may pick the other one when its rows turn out shorter
+// than the sizing assumed).
 size_t topk_workspace_bytes(const TopkArgs& a) {
   if (max_candidates(a) <= kSegMax) return 0;
   const size_t rows = (size_t)a.batch * a.lq;
   const size_t segs = rows * n_wave_segs(a);
-  return 2 * align_up(segs * kWaveKeep * 4) + 2 * align_up(segs * 4);
+  const size_t seg_layout = 2 * align_up(segs * kWaveKeep * 4) + 2 * align_up(segs * 4);
+  const size_t slots = rows * n_long_segs(a) * long_slots(a);
+  const size_t wave_layout = 2 * align_up(slots * 4);
+  return seg_layout > wave_layout ? seg_layout : wave_layout;
 }
 
 bool topk_supported(const TopkArgs& a) {
@@ -1363,6 +1487,25 @@ hipError_t launch_topk_blocks(const TopkArgs& a, void* ws, hipStream_t stream) {
                             (unsigned)a.batch),
                        dim3(kWrRowsPerWg * kWave), (size_t)kWrRowsPerWg * cap * 6, stream, a,
                        cap);
+    return hipGetLastError();
+  }
+  if (long_by_waves(a)) {
+    const int n_wseg = n_long_segs(a), ks = long_slots(a);
+    const size_t slots = (size_t)a.batch * a.lq * n_wseg * ks;
+    float* cv = static_cast<float*>(ws);
+    int32_t* ci = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(slots * 4));
+    const int cap = a.n_sel <= 512 ? kWrCapSmall : kWrCap;
+    const TopkLong T{a, n_wseg, ks, cv, ci, cap};
+    const size_t lds = (size_t)kWrRowsPerWg * cap * 6;
+    const int64_t items = a.lq * n_wseg;
+    hipLaunchKernelGGL(topk_long_segments_kernel,
+                       dim3((unsigned)((items + kWrRowsPerWg - 1) / kWrRowsPerWg), 1,
+                            (unsigned)a.batch),
+                       dim3(kWrRowsPerWg * kWave), lds, stream, T);
+    hipLaunchKernelGGL(topk_long_merge_kernel,
+                       dim3((unsigned)((a.lq + kWrRowsPerWg - 1) / kWrRowsPerWg), 1,
+                            (unsigned)a.batch),
+                       dim3(kWrRowsPerWg * kWave), lds, stream, T);
     return hipGetLastError();
   }
   const TopkLaunch L = merge_launch(a, ws);

@@ -279,6 +279,23 @@ def test_topk_row_lengths_around_the_list_size(budget, kind):
         _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
 
 
+@pytest.mark.parametrize("q_blk,lq,nblk,budget,kind",
+                         [(69000, 700, 70000, 2048, "normal"), (69000, 700, 70000, 4096, "quantized"),
+                          (32500, 2100, 33100, 2048, "quantized")])
+def test_topk_long_rows_by_waves(q_blk, lq, nblk, budget, kind):
+    # Enough rows of more than 32768 candidates to take the two wave passes (best of
+    # each 32768-score segment, then best of the kept): three segments with a ragged
+    # last one, heavy ties, and rows on both sides of 32768 candidates in one launch.
+    rng = np.random.default_rng(q_blk + budget)
+    q_pos0 = 4 * q_blk + 3
+    x = rng.standard_normal((lq, nblk)).astype(np.float32)
+    if kind == "quantized":
+        x = np.round(x * 2) / 2
+    _say(f"topk long rows by waves: rows {lq}, from {q_blk} blocks, budget {budget}, {kind}")
+    sel = _run_topk(_nan_tail(x, q_pos0), q_pos0, nblk, budget)
+    _check_topk_exact(x, sel, q_pos0, nblk, budget // 4)
+
+
 def test_topk_long_rows_concentrated_best():
     # Rows longer than one workgroup's 32768 candidates are split into segments that
     # each keep only a few candidates. Here every one of the best blocks sits in one
