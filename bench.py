@@ -514,7 +514,7 @@ def main():
     achieved = a_bytes / (attn_ms * 1e-3) / 1e9
     rows_pl = Q.qsa_sparse_attn_fwd_rows_per_launch(wl.hkv, wl.d)
     rows_pl = rows_pl if rows_pl > 0 else wl.lq
-    n_launch = -(-wl.lq // rows_pl)
+    n_launch = -(-wl.lq // rows_pl) * wl.hkv  # one KV group per launch
     traffic = counted_traffic()
     line = {
         "metric": METRIC,
@@ -539,7 +539,7 @@ def main():
                      "hbm_frac_from_traffic": (traffic / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
                                                if traffic else None),
                      "per": f"one qsa_sparse_attn_fwd call over all {wl.lq} rows = "
-                            f"{n_launch} launches of {rows_pl} rows",
+                            f"{n_launch} launches of {rows_pl} rows of one KV group",
                      "launches_per_call": n_launch,
                      "algorithmic_bytes_per_call": a_bytes, "avg_call_ms": attn_ms,
                      "algorithmic_bytes_per_launch": a_bytes / n_launch,

@@ -13,7 +13,8 @@
 // gathers its own K/V straight from global memory into MFMA operands -- no LDS round
 // trip and no cross-wave synchronisation. Blocks that many rows keep are shared
 // through L2 instead: the launcher starts the rows one resident generation at a
-// time, so that rows in flight walk their ascending block lists in step.
+// time, so that rows in flight walk their ascending block lists in step, and one KV
+// group at a time, so that the group's K/V stays in the last-level cache.
 //
 //   S^T[16 keys x 16 heads] = K[16 x d] . Q^T        8 x v_mfma_f32_16x16x32_bf16
 //     lane l: key row (l%16) -> 16 B of that key; output: head (l%16), keys 4*(l/16)+i
@@ -176,9 +177,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
   const int quad = lane >> 4;
   const int G = a.hq / a.hkv;
 
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t lrow = item / a.hkv;
-  const int g = (int)(item - lrow * a.hkv);
+  const int64_t lrow = (int64_t)blockIdx.x * 4 + wave;
+  const int g = a.kv_group;
   if (lrow >= a.lq) return;
   const int64_t row = a.row_begin + lrow;      // row of q, sel, out and lse
   const int64_t kstride = (int64_t)a.hkv * D;  // elements between consecutive tokens
@@ -460,37 +460,45 @@ const void* sparse_attn_fn(int d) {
 
 }  // namespace
 
-// One resident generation of 256-thread workgroups, each taking 4 (row, KV group)
-// waves; -1 when the occupancy is unknown.
+// One resident generation of 256-thread workgroups of 4 waves, each wave one row of
+// the launch's KV group; -1 when the occupancy is unknown.
 int64_t sparse_attn_fwd_rows_per_launch(int hkv, int d) {
+  (void)hkv;
   const int64_t gen = resident_workgroups(sparse_attn_fn(d), 256);
   if (gen <= 0) return -1;
-  const int64_t rows = (gen * 4 + hkv - 1) / hkv;
-  return rows > 0 ? rows : 1;
+  return gen * 4;
 }
 
-// The rows are launched one generation at a time: as many workgroups as the device
-// holds at once. Rows that start together walk their ascending kept-block lists at
-// the same pace, so a block that several of them kept is read by all of them within
-// a short time and comes from L2 after the first read. In one grid over all rows the
-// resident workgroups drift apart as they finish at different times, and such
-// blocks come from beyond L2 again. At 128K tokens (24/2 heads, d=256, K=2048) on
-// MI355X: one grid 66.8 ms, L2 hit rate 10 %; generations of 512 workgroups
-// 44.1 ms, L2 hit rate 53 %, half the bytes fetched. Each row's sums run in the
-// same order either way, so the outputs are identical.
+// The rows are launched one KV group at a time and, within a group, one generation at
+// a time: as many workgroups as the device holds at once.
+// - Generations: rows that start together walk their ascending kept-block lists at
+//   the same pace, so a block that several of them kept is read by all of them within
+//   a short time and comes from L2 after the first read. In one grid over all rows
+//   the resident workgroups drift apart as they finish at different times, and such
+//   blocks come from beyond L2 again. At 128K tokens (24/2 heads, d=256, K=2048) on
+//   MI355X: one grid 66.8 ms, L2 hit rate 10 %; generations of 512 workgroups
+//   44.1 ms, L2 hit rate 53 %, half the bytes fetched.
+// - One group at a time: a group's K and V of a 128K context take 128 MB, which the
+//   256 MB last-level cache (MALL) keeps across the generations, while both groups'
+//   256 MB do not: 44.0 ms with the two groups of a row in one generation, 39.2 ms
+//   group by group.
+// Each row's sums run in the same order either way, so the outputs are identical.
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream) {
   if (a.lq <= 0) return hipSuccess;
   int64_t rows = sparse_attn_fwd_rows_per_launch(a.hkv, a.d);
   if (rows <= 0) rows = a.lq;
-  for (int64_t c0 = 0; c0 < a.lq; c0 += rows) {
-    AttnArgs c = a;
-    c.lq = a.lq - c0 < rows ? a.lq - c0 : rows;
-    c.row_begin = a.row_begin + c0;
-    const dim3 grid((unsigned)((c.lq * c.hkv + 3) / 4));
-    if (a.d == 256)
-      hipLaunchKernelGGL(sparse_attn_kernel<256>, grid, dim3(256), 0, stream, c);
-    else
-      hipLaunchKernelGGL(sparse_attn_kernel<128>, grid, dim3(256), 0, stream, c);
+  for (int g = 0; g < a.hkv; ++g) {
+    for (int64_t c0 = 0; c0 < a.lq; c0 += rows) {
+      AttnArgs c = a;
+      c.lq = a.lq - c0 < rows ? a.lq - c0 : rows;
+      c.row_begin = a.row_begin + c0;
+      c.kv_group = g;
+      const dim3 grid((unsigned)((c.lq + 3) / 4));
+      if (a.d == 256)
+        hipLaunchKernelGGL(sparse_attn_kernel<256>, grid, dim3(256), 0, stream, c);
+      else
+        hipLaunchKernelGGL(sparse_attn_kernel<128>, grid, dim3(256), 0, stream, c);
+    }
   }
   return hipGetLastError();
 }
