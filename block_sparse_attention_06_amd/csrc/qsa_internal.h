@@ -137,7 +137,7 @@ struct AttnArgs {
   // (device [batch + 1]) the rows and keys are packed sequences, each row's position
   // counted within its own sequence
   int64_t row_begin;
-  int kv_group;  // prefill: the KV group that every wave of the launch takes
+  int kv_group;  // prefill: the KV group every wave of the launch takes; -1: (row, group) pairs
   const int32_t* cu_q;
   const int32_t* cu_k;
   int batch_vl;

@@ -155,22 +155,24 @@ qsa_status qsa_topk_blocks(int batch, int64_t lq, int r, int budget_tokens,
  *   q    bf16 [lq][hq][d] (THD), k/v bf16 [lk][hkv][d] (THD), contiguous
  *   sel  int32 [lq][n_sel] as written by stage 3 (ascending ids, -1 padded)
  *   out  bf16 [lq][hq][d]; lse fp32 [lq][hq] or NULL
- * The rows go to the GPU one KV group at a time, in launches of
- * qsa_sparse_attn_fwd_rows_per_launch() rows of that group (hkv * ceil(lq / rows)
- * launches a call): one generation of the workgroups the device holds at once, so
- * that rows in flight walk their ascending block lists together and share the blocks
- * they have in common through L2, while one group's K/V stays in the last-level
- * cache. A row's result does not depend on how the rows are split.
+ * The rows go to the GPU in launches of one generation of the workgroups the device
+ * holds at once, so that rows in flight walk their ascending block lists together
+ * and share the blocks they have in common through L2. When the K/V of a sequence
+ * (lk * hkv * d * 4 bytes) exceed 128 MB, the launches take one KV group at a time,
+ * qsa_sparse_attn_fwd_rows_per_launch() rows of that group each (hkv * ceil(lq / rows)
+ * launches a call), so that a group's K/V stays in the last-level cache; otherwise
+ * each launch takes both groups of rows / hkv rows. A row's result does not depend on
+ * how the rows are split.
  */
 qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, int r, int n_sel,
                                const void* q, const void* k, const void* v,
                                const int32_t* sel, int64_t q_pos0, float softmax_scale,
                                void* out, float* lse, void* stream);
 /*
- * Rows per launch of qsa_sparse_attn_fwd on the current device (each launch takes one
- * KV group of its rows) for hkv KV heads and head dim d (128 or 256); 0 when the
+ * Rows per launch of qsa_sparse_attn_fwd on the current device when each launch takes
+ * one KV group of its rows (hkv KV heads, head dim d = 128 or 256); 0 when the
  * arguments are unsupported, -1 when the runtime cannot report the device's occupancy
- * (then all rows of a group go in one launch).
+ * (then all rows go in one launch).
  */
 int64_t qsa_sparse_attn_fwd_rows_per_launch(int hkv, int d);
 
