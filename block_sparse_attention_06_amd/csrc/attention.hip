@@ -489,7 +489,7 @@ constexpr int64_t kGroupOrderBytes = (int64_t)128 << 20;
 //   a row in one generation, 39.2 ms group by group (L2 hit rate 71 %). Packed short
 //   sequences (whose K/V fit the cache either way) keep the two groups together:
 //   36.9 against 37.9 ms for 16 prompts of 2K-24K tokens. For packed sequences the
-//   size is judged on the average sequence (rows / sequences).
+//   size is estimated from the average sequence (rows / sequences).
 // Each row's sums run in the same order either way, so the outputs are identical.
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream) {
   if (a.lq <= 0) return hipSuccess;
