@@ -390,6 +390,21 @@ def test_sparse_attn_fwd(lq, lk, q_pos0, hq, hkv, d, budget):
     _attn_case(lq, lk, q_pos0, hq, hkv, d, budget, seed=lq)
 
 
+@pytest.mark.parametrize("lq,lk,q_pos0,hq,hkv,d", [
+    (2500, 70000, 67500, 24, 2, 256),   # K/V 143 MB: one KV group per launch
+    (3000, 140000, 137000, 8, 2, 128),  # the same order at d = 128
+])
+def test_sparse_attn_fwd_group_by_group(lq, lk, q_pos0, hq, hkv, d):
+    # Contexts whose K/V exceed 128 MB run one KV group at a time, in launches of one
+    # resident generation of rows (2048 here): rows on both sides of a launch edge, the
+    # ragged last launch and random rows, checked against the oracle.
+    _say(f"attn by group lq={lq} lk={lk} hq={hq} hkv={hkv} d={d}")
+    rng = np.random.default_rng(lq)
+    rows = np.unique(np.concatenate([[0, 1, 2046, 2047, 2048, 2049, lq - 1],
+                                     rng.integers(0, lq, 25)]))
+    _attn_case(lq, lk, q_pos0, hq, hkv, d, 2048, seed=lq + 5, rows=rows)
+
+
 def test_sparse_attn_fwd_softmax_stress():
     # Unscaled N(0,1) q/k with scale 1/sqrt(d): peaky logits, exercises the rescaling.
     _say("attn softmax stress")
