@@ -109,12 +109,13 @@ def gather_ceiling(torch, Q, dev, mib, sequential, n_waves=65536, steps=32):
         g.manual_seed(7)
         ids = torch.randint(0, nblk, (n_ids,), generator=g, device=dev, dtype=torch.int32)
     sink = torch.zeros(1024, dtype=torch.int32, device=dev)
-    Q.qsa_probe_gather(buf, ids, steps, sink)
+    from block_sparse_attention_06_amd.probe import probe_gather
+    probe_gather(buf, ids, steps, sink)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(3)]
     for a, b in evs:
         a.record()
-        Q.qsa_probe_gather(buf, ids, steps, sink)
+        probe_gather(buf, ids, steps, sink)
         b.record()
     torch.cuda.synchronize()
     ms = min(a.elapsed_time(b) for a, b in evs)

@@ -20,7 +20,6 @@ from .ops import (  # noqa: F401
     qsa_prefill_forward,
     qsa_prefill_select,
     qsa_prefill_varlen_forward,
-    qsa_probe_gather,
     qsa_sparse_attn_bwd,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_fwd,

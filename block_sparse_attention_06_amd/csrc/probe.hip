@@ -1,14 +1,17 @@
-// Measurement aid (not part of the QSA computation): the memory-system ceiling that
-// the kept-token gather of the attention stage runs against. Each wave reads, per
-// step, four 4 KiB blocks whose indices come from `block_ids` (random for a gather,
-// consecutive for a stream) -- the access pattern of one 16-key step of the
-// attention kernel -- and folds the data into a value that is never used, so the
-// loads cannot be dropped.
+// Measurement aid, built as its own library (libqsa_probe.so), not part of the QSA
+// computation or of libqsa.so: the memory-system ceiling that the kept-token gather
+// of the attention stage runs against. Each wave reads, per step, four 4 KiB blocks
+// whose indices come from `block_ids` (random for a gather, consecutive for a
+// stream) -- the access pattern of one 16-key step of the attention kernel -- and
+// folds the data into a value that is never used, so the loads cannot be dropped.
 
-#include "qsa_device.h"
-#include "qsa_internal.h"
+#include <hip/hip_runtime.h>
 
-namespace qsa {
+#include <cstdint>
+
+#include "qsa_probe.h"
+
+namespace {
 
 __global__ __launch_bounds__(256) void probe_gather_kernel(const uint4* __restrict__ buf,
                                                            const int32_t* __restrict__ ids,
@@ -33,12 +36,16 @@ __global__ __launch_bounds__(256) void probe_gather_kernel(const uint4* __restri
   if (acc == 0x9e3779b9u) sink[wave & 1023] = acc;  // practically never taken
 }
 
-hipError_t launch_probe_gather(const void* buf, const int32_t* ids, int steps, int64_t n_waves,
-                               uint32_t* sink, hipStream_t stream) {
-  if (n_waves <= 0 || steps <= 0) return hipSuccess;
-  hipLaunchKernelGGL(probe_gather_kernel, dim3((unsigned)((n_waves + 3) / 4)), dim3(256), 0,
-                     stream, static_cast<const uint4*>(buf), ids, steps, n_waves, sink);
-  return hipGetLastError();
-}
+}  // namespace
 
-}  // namespace qsa
+extern "C" int qsa_probe_gather(const void* buf, size_t buf_bytes, const int32_t* block_ids,
+                                int64_t n_waves, int steps, uint32_t* sink, void* stream) {
+  if (!buf || !block_ids || !sink) return 1;
+  if ((reinterpret_cast<uintptr_t>(buf) & 15) || buf_bytes < 4096) return 1;
+  if (n_waves < 0 || steps < 0 || n_waves / 4 >= ((int64_t)1 << 31)) return 1;
+  if (n_waves == 0 || steps == 0) return 0;
+  hipLaunchKernelGGL(probe_gather_kernel, dim3((unsigned)((n_waves + 3) / 4)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf), block_ids,
+                     steps, n_waves, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}

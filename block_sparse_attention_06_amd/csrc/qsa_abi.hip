@@ -921,18 +921,4 @@ qsa_status qsa_decode_forward_paged(int batch, int hq, int hkv, int d, int h_idx
                              stream);
 }
 
-// ---- measurement aid ----
-
-qsa_status qsa_probe_gather(const void* buf, size_t buf_bytes, const int32_t* block_ids,
-                            int64_t n_waves, int steps, uint32_t* sink, void* stream) {
-  QSA_REQUIRE(buf && block_ids && sink, QSA_ERR_INVALID_ARGUMENT, "null pointer");
-  QSA_REQUIRE(aligned16(buf) && buf_bytes >= 4096, QSA_ERR_INVALID_ARGUMENT,
-              "buf must be 16-byte aligned and hold at least one 4 KiB block");
-  QSA_REQUIRE(n_waves >= 0 && steps >= 0 && n_waves / 4 < ((int64_t)1 << 31),
-              QSA_ERR_INVALID_ARGUMENT, "n_waves=%lld steps=%d", (long long)n_waves, steps);
-  return hip_status(qsa::launch_probe_gather(buf, block_ids, steps, n_waves, sink,
-                                             static_cast<hipStream_t>(stream)),
-                    "qsa_probe_gather launch");
-}
-
 }  // extern "C"

@@ -238,10 +238,6 @@ hipError_t launch_kl_target(const KlArgs& a, hipStream_t stream);
 hipError_t launch_kl_loss(const KlLossArgs& a, hipStream_t stream);
 hipError_t launch_index_scores_bwd(const IdxBwdArgs& a, hipStream_t stream);
 
-// ---- measurement aid ----
-hipError_t launch_probe_gather(const void* buf, const int32_t* ids, int steps, int64_t n_waves,
-                               uint32_t* sink, hipStream_t stream);
-
 // Decode split heuristic for a given n_sel: 4-block steps per wave (1, 2 or 4) and
 // workgroups of 4 waves (= partials) per (sequence, head).
 int decode_steps_per_split(int n_sel);

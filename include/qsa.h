@@ -402,20 +402,6 @@ qsa_status qsa_decode_forward_paged(int batch, int hq, int hkv, int d, int h_idx
                                     int32_t* sel, void* out, float* lse, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
-/*
- * Measurement aid, not part of QSA: the gather ceiling of the memory system for the
- * access pattern of the attention stage. n_waves waves each read `steps` x 4 blocks
- * of 4 KiB from buf, block j of wave w step s at buf + 4096 * block_ids[(w*steps+s)*4+j];
- * the data is folded into a value written to sink[0..1023] only in a never-taken case.
- *   buf        device buffer of buf_bytes bytes (16-byte aligned)
- *   block_ids  device int32 [n_waves * steps * 4]; every id must be < buf_bytes / 4096
- *              (the caller checks this: the kernel does not)
- *   sink       device uint32 [1024]
- * Bytes read per call: n_waves * steps * 16384.
- */
-qsa_status qsa_probe_gather(const void* buf, size_t buf_bytes, const int32_t* block_ids,
-                            int64_t n_waves, int steps, uint32_t* sink, void* stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -27,6 +27,21 @@ def test_every_header_function_is_exported_and_declared(lib):
     assert lib.qsa_abi_version() == 2
 
 
+def test_probe_library_is_separate():
+    # The benchmark's gather probe lives in its own library and header; libqsa.so
+    # exports only the QSA calls.
+    from block_sparse_attention_06_amd import probe
+    if not os.path.exists(probe.PROBE_LIB_PATH):
+        from block_sparse_attention_06_amd import build
+        build.build()
+    assert _lib.header_functions(probe.HEADER_PATH) == sorted(probe.SIGNATURES)
+    plib = probe.load()
+    assert hasattr(plib, "qsa_probe_gather")
+    qlib = _lib.load()
+    assert not hasattr(qlib, "qsa_probe_gather")
+    assert plib.qsa_probe_gather(None, 4096, None, 1, 1, None, None) == 1
+
+
 P = ctypes.c_void_p
 FAKE = P(0x1000)       # 16-byte aligned, never dereferenced: calls fail validation first
 MISALIGNED = P(0x1004)

@@ -11,12 +11,20 @@ import torch
 
 import block_sparse_attention_06_amd as Q
 from oracle import qsa_oracle as O
-from parity import bits, check_selection_row, compare_output, LSE_ABS
+from parity import bits, check_selection_row, compare_output, score_abs_tol, LSE_ABS, SCORE_REL
 from synth import generate, workload
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
+
+
+def _decode_tol(inp, b, t):
+    """fp32 score error floor of decode row b (query at position t)."""
+    own = t // 4
+    return float(score_abs_tol(O.bf16_to_f64(bits(inp["q_idx"][b, 0]))[None],
+                               inp["w"][b, 0].double().cpu().numpy()[None],
+                               O.bf16_to_f64(bits(inp["k_pooled"][b, :own])), [own])[0])
 
 
 def _say(*a):
@@ -103,7 +111,7 @@ def test_index_scores(lq, q_pos0, nblk, h_i, d_i):
     own = np.minimum(pos // 4, nblk)
     mask = np.arange(nblk)[None, :] < own[:, None]
     err = np.abs(got - np.nan_to_num(ref))[mask]
-    assert np.all(err <= 2e-5 * bound[mask] + 1e-30), f"max err {err.max()}"
+    assert np.all(err <= SCORE_REL * bound[mask] + 1e-30), f"max err {err.max()}"
 
 
 def test_index_scores_batched_seq_lens():
@@ -124,7 +132,7 @@ def test_index_scores_batched_seq_lens():
         got = s[b].double().cpu().numpy()[:, :nblk]
         for i in range(lq):
             own = max(0, min(pos[i] // 4, nblk)) if pos[i] >= 0 else 0
-            assert np.all(np.abs(got[i, :own] - ref[i, :own]) <= 2e-5 * bound[i, :own] + 1e-30)
+            assert np.all(np.abs(got[i, :own] - ref[i, :own]) <= SCORE_REL * bound[i, :own] + 1e-30)
 
 
 @pytest.mark.parametrize("d_i,h_i,lq,seq", [(128, 4, 4, [800_003, 333_337, 4093, 5]),
@@ -151,7 +159,7 @@ def test_index_scores_streaming_scan(d_i, h_i, lq, seq):
         got = s[b].double().cpu().numpy()[:, :nblk]
         for i in range(lq):
             own = max(0, min(pos[i] // 4, nblk)) if pos[i] >= 0 else 0
-            assert np.all(np.abs(got[i, :own] - ref[i, :own]) <= 2e-5 * bound[i, :own] + 1e-30)
+            assert np.all(np.abs(got[i, :own] - ref[i, :own]) <= SCORE_REL * bound[i, :own] + 1e-30)
 
 
 # ------------------------------------------------------------------------------------
@@ -455,7 +463,12 @@ class _Rows:
         return self._data[[self._at[int(i)] for i in idx]]
 
 
-def _prefill_parity(name, rows=None, row_chunk=4096, **over):
+def _prefill_parity(name, rows=None, row_chunk=4096, n_aligned=64, max_inexact=2, **over):
+    """The whole prefill path on the GPU against the oracle's whole path on `rows` (all
+    rows by default), plus the first `n_aligned` needle-aligned rows (all of them when
+    None) and the first and last rows. Selections must match (near-ties within the
+    band are counted, at most max_inexact rows), outputs are compared with the oracle's
+    attention over the GPU's own validated selection."""
     wl = workload(name, **over)
     _say(f"prefill {wl.name} lq={wl.lq} lk={wl.lk} q_pos0={wl.q_pos0} K={wl.budget} "
          f"row_chunk={row_chunk}")
@@ -466,7 +479,10 @@ def _prefill_parity(name, rows=None, row_chunk=4096, **over):
     torch.cuda.synchronize()
     if rows is None:
         rows = np.arange(wl.lq)
-    rows = np.unique(np.concatenate([np.asarray(rows), inp["aligned_rows"][:64], [0, wl.lq - 1]]))
+    al_rows, al_blocks = inp["aligned_rows"], inp["aligned_blocks"]
+    if n_aligned is not None:
+        al_rows, al_blocks = al_rows[:n_aligned], al_blocks[:n_aligned]
+    rows = np.unique(np.concatenate([np.asarray(rows), al_rows, [0, wl.lq - 1]])).astype(np.int64)
     rows_t = torch.from_numpy(rows).to(DEV)
 
     def fetch(toks):
@@ -477,21 +493,24 @@ def _prefill_parity(name, rows=None, row_chunk=4096, **over):
     # Oracle end to end (its own pooling, scores, selection, attention) on the rows.
     qb = _Rows((wl.lq, wl.hq, wl.d), rows, bits(inp["q"][rows_t]))
     qib = bits(inp["q_idx"])
-    res = O.forward_prefill(qb, None, None, qib, inp["w"].cpu().numpy(), bits(inp["k_idx"]),
+    w_np = inp["w"].cpu().numpy()
+    res = O.forward_prefill(qb, None, None, qib, w_np, bits(inp["k_idx"]),
                             r=wl.r, budget=wl.budget, q_pos0=wl.q_pos0,
                             k_pooled_prefix_bits=prefix, rows=rows, n_keys=wl.lk,
-                            fetch_kv=fetch)
+                            fetch_kv=fetch, row_chunk=512)
     # Pooled keys: bit-exact.
     np.testing.assert_array_equal(bits(kp[wl.pooled_prefix_blocks:]), res["pooled"])
+    kp_all = O.bf16_to_f64(bits(kp))
+    own = (wl.q_pos0 + rows) // wl.r
+    tol = score_abs_tol(O.bf16_to_f64(qib[rows]), w_np[rows], kp_all, own)
     sel_np = sel[rows_t].cpu().numpy()
     n_exact = 0
     for j, i in enumerate(rows):
-        t = wl.q_pos0 + int(i)
-        n_exact += check_selection_row(sel_np[j], res["scores"][j], t // 4, wl.n_sel,
-                                       f"{wl.name} row {i}")
+        n_exact += check_selection_row(sel_np[j], res["scores"][j], int(own[j]), wl.n_sel,
+                                       f"{wl.name} row {i}", abs_tol=tol[j])
     # Needle-aligned rows keep their needle.
-    for i, b in zip(inp["aligned_rows"][:64], inp["aligned_blocks"][:64]):
-        j = int(np.nonzero(rows == i)[0][0])
+    for i, b in zip(al_rows, al_blocks):
+        j = int(np.searchsorted(rows, i))
         assert b in sel_np[j], f"row {i} lost needle block {b}"
     # Output: oracle attention on the GPU's own selection.
     ref = np.zeros((len(rows), wl.hq, wl.d))
@@ -500,20 +519,26 @@ def _prefill_parity(name, rows=None, row_chunk=4096, **over):
         toks = O.kept_tokens(sel_np[j], t, wl.r, wl.lk)
         kr, vr = fetch(toks)
         ref[j], _ = O.attend(O.bf16_to_f64(qb[i]), kr, vr, 1 / math.sqrt(wl.d))
-    max_abs, rel = compare_output(out[rows_t], ref, wl.name)
-    _say(f"  rows={len(rows)} exact_sel={n_exact} max_abs={max_abs:.2e} rel_l2={rel:.2e}")
+    got = out[rows_t]
+    max_abs, rel = compare_output(got, ref, wl.name)
+    g64 = got.float().cpu().numpy().astype(np.float64)
+    row_rel = (np.linalg.norm((g64 - ref).reshape(len(rows), -1), axis=1)
+               / np.linalg.norm(ref.reshape(len(rows), -1), axis=1))
+    _say(f"  rows={len(rows)} (aligned {len(al_rows)}) exact_sel={n_exact} "
+         f"tie_band_rows={len(rows) - n_exact} max_abs={max_abs:.2e} rel_l2={rel:.2e} "
+         f"row_rel_l2: worst={row_rel.max():.2e} p99={np.quantile(row_rel, 0.99):.2e} "
+         f"(row {int(rows[np.argmax(row_rel)])})")
+    assert len(rows) - n_exact <= max_inexact, f"{len(rows) - n_exact} rows in the tie band"
     return n_exact, len(rows)
 
 
 def test_prefill_tiny_all_rows():
-    n_exact, n = _prefill_parity("tiny")
-    assert n_exact >= n - 2
+    _prefill_parity("tiny", n_aligned=None)
 
 
 def test_prefill_tiny_small_chunks_ragged():
     # Row chunks that do not divide Lq, Lq not a multiple of the 64-row tile.
-    n_exact, n = _prefill_parity("tiny", row_chunk=300, lq=1001, lk=1001)
-    assert n_exact >= n - 2
+    _prefill_parity("tiny", row_chunk=300, lq=1001, lk=1001, n_aligned=None)
 
 
 def test_prefill_generation_boundaries_against_oracle():
@@ -547,24 +572,29 @@ def test_attention_independent_of_row_split():
     assert torch.equal(o2, out) and torch.equal(l2, lse)
 
 
-# The full-size workloads in the selection chunks the benchmark uses (16384 rows).
+# The full-size workloads in the selection chunks the benchmark uses (16384 rows):
+# seeded random rows, needle-aligned rows (every one at 32K, 512 at 128K and on the
+# 1M context) and the first and last rows; at most 1 row in 500 may sit in the tie band.
 
+@pytest.mark.timeout(600)
 def test_prefill_32k_sampled():
     rng = np.random.default_rng(21)
-    rows = rng.choice(32768, 48, replace=False)
-    _prefill_parity("prefill32k", rows=rows, row_chunk=16384)
+    rows = rng.choice(32768, 2048, replace=False)
+    _prefill_parity("prefill32k", rows=rows, row_chunk=16384, n_aligned=None, max_inexact=10)
 
 
+@pytest.mark.timeout(600)
 def test_prefill_128k_sampled():
     rng = np.random.default_rng(22)
-    rows = rng.choice(131072, 24, replace=False)
-    _prefill_parity("prefill128k", rows=rows, row_chunk=16384)
+    rows = rng.choice(131072, 1536, replace=False)
+    _prefill_parity("prefill128k", rows=rows, row_chunk=16384, n_aligned=512, max_inexact=4)
 
 
+@pytest.mark.timeout(900)
 def test_chunked_prefill_1m_sampled():
     rng = np.random.default_rng(23)
-    rows = rng.choice(8192, 16, replace=False)
-    _prefill_parity("chunked1m", rows=rows, row_chunk=8192)
+    rows = rng.choice(8192, 1536, replace=False)
+    _prefill_parity("chunked1m", rows=rows, row_chunk=8192, n_aligned=512, max_inexact=4)
 
 
 def test_decode_forward_mixed_lengths_and_fallback():
@@ -599,7 +629,8 @@ def test_decode_forward_mixed_lengths_and_fallback():
     sel_np = sel.cpu().numpy()
     for b in range(len(seq)):
         t = seq[b] - 1
-        check_selection_row(sel_np[b], res["scores"][b], t // 4, wl.n_sel, f"decode b={b}")
+        check_selection_row(sel_np[b], res["scores"][b], t // 4, wl.n_sel, f"decode b={b}",
+                            abs_tol=_decode_tol(inp, b, t))
         toks = O.kept_tokens(sel_np[b], t, 4, t + 1)
         kr, vr = fetch(b, toks)
         ref, _ = O.attend(O.bf16_to_f64(bits(inp["q"][b])), kr, vr, 1 / math.sqrt(wl.d))
@@ -628,7 +659,8 @@ def test_decode_1m_full():
     sel_np = sel.cpu().numpy()
     for b in range(wl.batch):
         t = int(inp["seq_lens"][b]) - 1
-        check_selection_row(sel_np[b], res["scores"][b], t // 4, wl.n_sel, f"decode b={b}")
+        check_selection_row(sel_np[b], res["scores"][b], t // 4, wl.n_sel, f"decode b={b}",
+                            abs_tol=_decode_tol(inp, b, t))
         toks = O.kept_tokens(sel_np[b], t, 4, t + 1)
         kr, vr = fetch(b, toks)
         ref, ref_lse = O.attend(O.bf16_to_f64(bits(inp["q"][b])), kr, vr, 1 / math.sqrt(wl.d))

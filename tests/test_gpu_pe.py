@@ -9,7 +9,7 @@ import torch
 
 import block_sparse_attention_06_amd as Q
 from oracle import qsa_oracle as O
-from parity import bits, check_selection_row, compare_output
+from parity import bits, check_selection_row, compare_output, score_abs_tol
 from synth import generate, generate_varlen, workload
 
 pytestmark = pytest.mark.gpu
@@ -56,10 +56,15 @@ def _check_rows(inp, wl, out, sel, kp, rows, pe, q_pos0, prefix_bits=None):
     n_prefix = 0 if prefix_bits is None else len(prefix_bits)
     np.testing.assert_array_equal(bits(kp[n_prefix:]), res["pooled"])
     sel_np = sel.cpu().numpy()
+    kp_all = O.bf16_to_f64(res["pooled"] if prefix_bits is None
+                           else np.concatenate([prefix_bits, res["pooled"]]))
+    rr = np.asarray(rows)
+    tol = score_abs_tol(O.bf16_to_f64(bits(inp["q_idx"]))[rr], inp["w"].cpu().numpy()[rr],
+                        kp_all, (q_pos0 + rr) // 4)
     n_exact = 0
     for j, i in enumerate(rows):
         n_exact += check_selection_row(sel_np[i], res["scores"][j], (q_pos0 + i) // 4, wl.n_sel,
-                                       f"row {i}")
+                                       f"row {i}", abs_tol=tol[j])
     ref = np.zeros((len(rows), wl.hq, wl.d))
     kf, vf = O.bf16_to_f64(bits(inp["k"])), O.bf16_to_f64(bits(inp["v"]))
     qf = O.bf16_to_f64(bits(inp["q"]))

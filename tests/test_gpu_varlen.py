@@ -8,7 +8,7 @@ import torch
 
 import block_sparse_attention_06_amd as Q
 from oracle import qsa_oracle as O
-from parity import bits, check_selection_row, compare_output, LSE_ABS
+from parity import bits, check_selection_row, compare_output, score_abs_tol, LSE_ABS
 from synth import generate_varlen, workload
 
 pytestmark = pytest.mark.gpu
@@ -50,8 +50,11 @@ def _check_against_oracle(inp, wl, out, lse, sel, kp, rows):
         b = seq_of[j]
         lq, lk = inp["lens"][b]
         t = lk - lq + (i - cq[b])
+        tol = score_abs_tol(O.bf16_to_f64(bits(inp["q_idx"][i]))[None],
+                            inp["w"][i].double().cpu().numpy()[None],
+                            O.bf16_to_f64(res["pooled"][b]), [t // wl.r])[0]
         n_exact += check_selection_row(sel_np[i], res["scores"][j], t // wl.r, wl.n_sel,
-                                       f"seq {b} row {i}")
+                                       f"seq {b} row {i}", abs_tol=tol)
         toks = O.kept_tokens(sel_np[i], t, wl.r, lk) + ck[b]
         ref[j], ref_lse = O.attend(qf[i], kf[toks], vf[toks], 1 / math.sqrt(wl.d))
         assert np.abs(lse[i].cpu().numpy() - ref_lse).max() <= LSE_ABS

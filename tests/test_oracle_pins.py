@@ -699,7 +699,54 @@ def test_index_scores_backward_central_differences():
             fm = f(args["q"], args["w"], args["kp"])
             num = (fp - fm) / (2 * eps)
             assert abs(num - grad[idx]) <= 1e-7 * max(1.0, abs(num)), (name, idx, num, grad[idx])
-    # The pooling's gradient spreads each block's gradient over its r tokens / r.
-    g = O.pool_keys_backward(dkp, r, nblk * r + 2)
-    np.testing.assert_allclose(g[: nblk * r].reshape(nblk, r, di).sum(1), dkp, rtol=1e-14)
-    assert np.all(g[nblk * r:] == 0)
+
+
+def test_pool_keys_backward_against_autograd():
+    # The mean pooling's gradient, per token: torch's avg_pool1d (windows of r, stride
+    # r, a partial tail window dropped) differentiated by autograd in fp64. Every token
+    # of a complete block gets its block's gradient / r; the tail tokens get 0.
+    rng = np.random.default_rng(54)
+    assert np.all(O.pool_keys_backward(np.zeros((0, 4)), 4, 3) == 0)  # no complete block
+    for n_tokens, di, nblk in ((4 * 7 + 2, 6, 7), (4 * 5, 3, 5), (4 + 3, 4, 1)):
+        dkp = rng.standard_normal((nblk, di))
+        x = torch.from_numpy(rng.standard_normal((n_tokens, di))).requires_grad_()
+        pooled = torch.nn.functional.avg_pool1d(x.T[None], kernel_size=4, stride=4)[0].T
+        assert pooled.shape == (nblk, di)
+        (pooled * torch.from_numpy(dkp)).sum().backward()
+        got = O.pool_keys_backward(dkp, 4, n_tokens)
+        assert got.shape == (n_tokens, di)
+        np.testing.assert_allclose(got, x.grad.numpy(), rtol=1e-15, atol=0)
+
+
+def test_ranked_threshold_gap_hand_cases():
+    # Candidates ranked by score: 5, 3, 3, 1, 0.5 (blocks 0..4; the entries after the
+    # own block are not candidates). With n_sel places the row keeps m = n_sel - 1
+    # earlier blocks: the m-th and (m+1)-th ranked scores, written out by hand.
+    s = np.array([3.0, 5.0, 0.5, 3.0, 1.0, 99.0, 99.0])
+    own = 5
+    assert O.ranked_threshold_gap(s, own, 3) == (3.0, 3.0)   # m = 2: 5, [3], 3
+    assert O.ranked_threshold_gap(s, own, 4) == (3.0, 1.0)   # m = 3: 5, 3, [3], 1
+    assert O.ranked_threshold_gap(s, own, 5) == (1.0, 0.5)   # m = 4
+    assert O.ranked_threshold_gap(s, own, 2) == (5.0, 3.0)   # m = 1
+    assert O.ranked_threshold_gap(s, own, 6) is None         # m = 5: every candidate kept
+    assert O.ranked_threshold_gap(s, own, 40) is None
+    assert O.ranked_threshold_gap(s, own, 1) is None         # only the own block
+    assert O.ranked_threshold_gap(s, 0, 3) is None           # no candidate
+    # ReLU zeros and a signed zero: 2, 0, -0, 0 -> m = 2 gives (0, 0)
+    z = np.array([0.0, 2.0, -0.0, 0.0])
+    assert O.ranked_threshold_gap(z, 4, 3) == (0.0, 0.0)
+    assert O.ranked_threshold_gap(z, 4, 2) == (2.0, 0.0)
+
+
+def test_ranked_threshold_gap_brute_force():
+    # Against the brute-force ranking of select_blocks' own rule on random rows with
+    # ties: the m-th kept block's score and the best dropped block's score.
+    rng = np.random.default_rng(55)
+    for _ in range(200):
+        own = int(rng.integers(1, 40))
+        n_sel = int(rng.integers(1, 45))
+        s = rng.integers(0, 6, size=own + 3).astype(np.float64)
+        ranked = sorted(range(own), key=lambda b: (-s[b], b))
+        m = min(n_sel - 1, own)
+        want = None if (m == 0 or m >= own) else (s[ranked[m - 1]], s[ranked[m]])
+        assert O.ranked_threshold_gap(s, own, n_sel) == want
