@@ -137,6 +137,13 @@ def attention_bytes(wl, t):
     return gathered + len(t) * per_row
 
 
+def attention_flops(wl, t):
+    """Algorithmic flops of the attention over the kept tokens: per (row, head, kept
+    token) a d-long dot product for the score and a d-long P.V update, 2 flop per
+    multiply-add each."""
+    return int(kept_tokens(t, wl.n_sel).sum()) * wl.hq * wl.d * 4
+
+
 def score_flops(wl, t):
     """Algorithmic flops of the indexer score GEMM (2 * H_I * d_I per scored block)."""
     own = (t // wl.r).clip(max=wl.nblk)
@@ -174,6 +181,29 @@ def bench_prefill(args, torch, Q, wl, inp):
     attn_ms = sum(a.elapsed_time(b) for _, a, b in evs) / len(evs)
     bench_prefill.step_ms = sorted(s_.elapsed_time(b) for s_, _, b in evs)
     return wall, attn_ms, plan
+
+
+def bench_score_gemm(torch, Q, wl, inp, plan, row_chunk, reps=3):
+    """The indexer score GEMM alone over the same row chunks as the step (pooled keys
+    of the step's own pooling), into a chunk-sized scratch: ms per step's worth."""
+    kp = plan.k_pooled
+    nb_all = kp.shape[0]
+    scratch = torch.empty((min(row_chunk, wl.lq), Q.score_ld(nb_all)), dtype=torch.float32,
+                          device=kp.device)
+    chunks = []
+    for c0 in range(0, wl.lq, row_chunk):
+        c1 = min(wl.lq, c0 + row_chunk)
+        nb = min(nb_all, (wl.q_pos0 + c1 - 1) // wl.r)
+        chunks.append((c0, c1, nb))
+
+    def run():
+        for c0, c1, nb in chunks:
+            Q.qsa_index_scores(inp["q_idx"][c0:c1], inp["w"][c0:c1], kp, q_pos0=wl.q_pos0 + c0,
+                               nblk=nb, out=scratch[: c1 - c0, : Q.score_ld(nb)])
+
+    ms = time_calls(torch, run, reps) * 1e3
+    del scratch
+    return ms
 
 
 def percentiles(xs):
@@ -279,28 +309,32 @@ def paged_copy(torch, kc, vc, page_size, seed=1):
     return pools[0], pools[1], table
 
 
-def bench_decode(args, torch, Q, wl, inp, paged=None):
+def bench_decode(args, torch, Q, wl, inp, paged=None, query_sets=None):
     """Seconds per decode step; with paged = (k_pool, v_pool, table, page_size) the
-    step reads K/V through the block table."""
+    step reads K/V through the block table. With query_sets, step i takes set
+    i % len(query_sets) (new queries over the same caches), so that the blocks a step
+    selects and gathers differ from the previous step's."""
     plan = Q.DecodePlan(wl.batch, wl.hq, wl.d, wl.lk, wl.budget, device=inp["q"].device)
+    sets = query_sets or [{"q": inp["q"], "q_idx": inp["q_idx"], "w": inp["w"]}]
 
-    def step():
+    def step(i):
+        x = sets[i % len(sets)]
         if paged is None:
-            Q.qsa_decode_forward(inp["q"], inp["q_idx"], inp["w"], inp["k_pooled"],
+            Q.qsa_decode_forward(x["q"], x["q_idx"], x["w"], inp["k_pooled"],
                                  inp["k_cache"], inp["v_cache"], inp["seq_lens"],
                                  budget=wl.budget, plan=plan)
         else:
-            Q.qsa_decode_forward_paged(inp["q"], inp["q_idx"], inp["w"], inp["k_pooled"],
+            Q.qsa_decode_forward_paged(x["q"], x["q_idx"], x["w"], inp["k_pooled"],
                                        paged[0], paged[1], paged[2], inp["seq_lens"],
                                        budget=wl.budget, page_size=paged[3], lmax=wl.lk,
                                        plan=plan)
 
-    for _ in range(5):
-        step()
+    for i in range(5):
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.decode_steps):
-        step()
+    for i in range(args.decode_steps):
+        step(i)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / args.decode_steps
 
@@ -372,7 +406,8 @@ def bench_varlen(torch, Q, n_seqs=16, total=131072, floor=2048, reps=3):
 
     def attn():
         return Q.qsa_sparse_attn_varlen_fwd(inp["q"], inp["k"], inp["v"], plan.sel, inp["cu_q"],
-                                            inp["cu_k"], scale=scale, out=plan.out, lse=plan.lse)
+                                            inp["cu_k"], scale=scale, out=plan.out, lse=plan.lse,
+                                            max_lk=max_len)
 
     ms = {}
     for name, f in (("forward", run), ("attention", attn)):
@@ -386,16 +421,17 @@ def bench_varlen(torch, Q, n_seqs=16, total=131072, floor=2048, reps=3):
         torch.cuda.synchronize()
         ms[name] = a.elapsed_time(b) / reps
     t = np.concatenate([np.arange(n, dtype=np.int64) for n in lens])
-    a_bytes = attention_bytes(wl, t)
+    a_flops = attention_flops(wl, t)
     del inp, plan
     torch.cuda.empty_cache()
     return {"workload": f"{n_seqs} packed prompts of prefill128k shapes, {total} tokens",
             "lengths": lens, "row_chunk": 16384 // n_seqs, "ms": ms["forward"],
             "tokens_per_s": total / (ms["forward"] * 1e-3), "attention_ms": ms["attention"],
-            "attention_roofline": {"bound": "hbm", "achieved": a_bytes / ms["attention"] / 1e6,
-                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": a_bytes / ms["attention"] / 1e6 / HBM_PEAK_GBS,
-                                   "algorithmic_bytes_per_call": a_bytes}}
+            "attention_roofline": {"bound": "mfma",
+                                   "achieved": a_flops / ms["attention"] / 1e9,
+                                   "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                                   "frac": a_flops / ms["attention"] / 1e9 / MFMA_BF16_PEAK_TFS,
+                                   "algorithmic_flops_per_call": a_flops}}
 
 
 def bench_pool_encoding(torch, Q, n_tok=1 << 20, d_i=128, rope_dim=64, reps=5):
@@ -492,7 +528,7 @@ def main():
     import torch
 
     import block_sparse_attention_06_amd as Q
-    from synth import generate, workload
+    from synth import decode_query_sets, generate, workload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -512,11 +548,15 @@ def main():
     ms_step = wall / args.steps * 1e3
     t = wl.q_pos0 + np.arange(wl.lq, dtype=np.int64)
     a_bytes = attention_bytes(wl, t)
-    achieved = a_bytes / (attn_ms * 1e-3) / 1e9
+    a_flops = attention_flops(wl, t)
+    s_flops = score_flops(wl, t)
+    a_tfs = a_flops / (attn_ms * 1e-3) / 1e12
+    n_launch = Q.qsa_sparse_attn_fwd_launches(wl.lq, wl.lk, wl.hkv, wl.d)
     rows_pl = Q.qsa_sparse_attn_fwd_rows_per_launch(wl.hkv, wl.d)
-    rows_pl = rows_pl if rows_pl > 0 else wl.lq
-    n_launch = -(-wl.lq // rows_pl) * wl.hkv  # one KV group per launch
     traffic = counted_traffic()
+    score_ms = bench_score_gemm(torch, Q, wl, inp, plan, args.row_chunk)
+    progress(f"score GEMM alone: {score_ms:.2f} ms per step")
+    s_tfs = s_flops / (score_ms * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": wl.lq * args.steps / wall,
@@ -534,40 +574,62 @@ def main():
                    "q_pos0": wl.q_pos0, "heads": f"{wl.hq}q/{wl.hkv}kv", "head_dim": wl.d,
                    "indexer": f"{wl.h_i}x{wl.d_i}", "r": wl.r, "budget": wl.budget,
                    "row_chunk": args.row_chunk, "global_batch": 1, "parallelism": "single GPU"},
-        "roofline": {"kernel": "sparse_attn_kernel (kept-token gather + MFMA)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "hbm_frac_from_traffic": (traffic / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
-                                               if traffic else None),
+        # The dominant kernel (the attention) on its MFMA roofline: algorithmic flops
+        # (kept tokens x heads x d x 4) over the live HIP-event duration of the call.
+        "roofline": {"kernel": "sparse_attn_kernel (kept-token gather + MFMA)", "bound": "mfma",
+                     "achieved": a_tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": a_tfs / MFMA_BF16_PEAK_TFS,
+                     "traffic": traffic,
+                     "traffic_source": ("bytes beyond L2 per call (MALL or HBM), scaled "
+                                        "FETCH_SIZE + WRITE_SIZE from rocprofv3 --pmc runs in "
+                                        "profiles/sparse_attn_prefill128k_counters.md; null "
+                                        "when the attention sources changed since"),
                      "per": f"one qsa_sparse_attn_fwd call over all {wl.lq} rows = "
-                            f"{n_launch} launches of {rows_pl} rows of one KV group",
+                            f"{n_launch} launches of up to {rows_pl} (row, KV group) waves",
                      "launches_per_call": n_launch,
-                     "algorithmic_bytes_per_call": a_bytes, "avg_call_ms": attn_ms,
-                     "algorithmic_bytes_per_launch": a_bytes / n_launch,
+                     "algorithmic_flops_per_call": a_flops, "avg_call_ms": attn_ms,
+                     "algorithmic_flops_per_launch": a_flops / n_launch,
                      "avg_launch_ms": attn_ms / n_launch},
+        "mfma_fractions": {
+            "attention": a_tfs / MFMA_BF16_PEAK_TFS,
+            "score_gemm": s_tfs / MFMA_BF16_PEAK_TFS,
+            "prefill_step": (a_flops + s_flops) / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+            "score_gemm_ms": score_ms, "score_gemm_flops_per_step": s_flops,
+            "attention_flops_per_call": a_flops, "peak_TFLOPs": MFMA_BF16_PEAK_TFS},
         "stages_ms": {"select (pool + scores + top-k)": ms_step - attn_ms, "attention": attn_ms},
         "step_ms_events": percentiles(bench_prefill.step_ms),
-        "score_gemm_flops_per_step": score_flops(wl, t),
     }
     kv_mib = (2 * wl.lk * wl.hkv * wl.d * 2) >> 20
     ceil_rand = gather_ceiling(torch, Q, dev, kv_mib, sequential=False)
     ceil_seq = gather_ceiling(torch, Q, dev, 2048, sequential=True)
     progress(f"gather ceiling: {ceil_rand:.0f} GB/s random, {ceil_seq:.0f} GB/s sequential")
-    line["gather_ceiling"] = {
-        "random_4KiB_blocks_GBs": ceil_rand, "random_buffer_MiB": kv_mib,
+    beyond = traffic / (attn_ms * 1e-3) / 1e9 if traffic else None
+    line["gather"] = {
+        "algorithmic_bytes_per_call": a_bytes,
+        "effective_GBs": a_bytes / (attn_ms * 1e-3) / 1e9,
+        "effective_note": "kept K/V rows + q/out/sel/lse per call over its duration; counts "
+                          "L2 and MALL hits, so it is no HBM figure and has no fraction",
+        "beyond_l2_bytes_per_call": traffic, "beyond_l2_GBs": beyond,
+        "random_gather_ceiling_GBs": ceil_rand, "random_buffer_MiB": kv_mib,
         "sequential_stream_GBs": ceil_seq, "sequential_buffer_MiB": 2048,
-        "attention_frac_of_random_ceiling": achieved / ceil_rand}
+        "beyond_l2_frac_of_random_ceiling": beyond / ceil_rand if beyond else None}
     if not args.no_backward:
         b_ms = bench_backward(torch, Q, wl, inp, plan)
         b_bytes = backward_bytes(wl, t)
         b_gbs = b_bytes / (b_ms * 1e-3) / 1e9
         progress(f"backward: {b_ms:.1f} ms")
+        b_flops = a_flops * 5 // 2  # 5 products over the kept tokens: S, dP, dV, dQ, dK
+        b_tfs = b_flops / (b_ms * 1e-3) / 1e12
         line["backward"] = {
             "workload": wl.name, "what": "dq, dk, dv of the sparse attention (fp32) from out, "
             "lse and a random bf16 dout; inverse selection included",
             "ms": b_ms, "tokens_per_s": wl.lq / (b_ms * 1e-3),
-            "roofline": {"bound": "hbm", "achieved": b_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": b_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": b_bytes}}
+            "roofline": {"bound": "mfma", "achieved": b_tfs, "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": b_tfs / MFMA_BF16_PEAK_TFS,
+                         "algorithmic_flops_per_call": b_flops},
+            "moved_bytes_GBs": b_gbs, "moved_bytes_per_call": b_bytes,
+            "moved_bytes_note": "the design's own traffic (K/V rows, each (block, row) pair's "
+                                "q and dout, gradients), not algorithmic bytes; no fraction"}
     del inp, plan
     torch.cuda.empty_cache()
     if not args.no_warmup:
@@ -582,17 +644,29 @@ def main():
     if not args.no_decode:
         dwl = workload("decode1m")
         dinp = generate(dwl, device=dev)
+        qsets = decode_query_sets(dwl, 16, device=dev)
         torch.cuda.synchronize()
-        s_dec = bench_decode(args, torch, Q, dwl, dinp)
+        s_dec = bench_decode(args, torch, Q, dwl, dinp, query_sets=qsets)
+        s_dec_same = bench_decode(args, torch, Q, dwl, dinp)
         progress(f"decode: {s_dec * 1e6:.1f} us per step")
         # The MTP layer reuses the main layer's selection: its step is the decode
         # attention alone (its own cache; the same bytes are read here).
         mtp_plan = Q.DecodePlan(dwl.batch, dwl.hq, dwl.d, dwl.lk, dwl.budget, device=dev)
-        Q.qsa_decode_forward(dinp["q"], dinp["q_idx"], dinp["w"], dinp["k_pooled"],
-                             dinp["k_cache"], dinp["v_cache"], dinp["seq_lens"],
-                             budget=dwl.budget, plan=mtp_plan)
-        mtp_s = time_calls(torch, lambda: Q.qsa_sparse_attn_decode(
-            dinp["q"], dinp["k_cache"], dinp["v_cache"], dinp["seq_lens"], mtp_plan.sel), 20)
+        mtp_sels = []
+        for x in qsets:
+            Q.qsa_decode_forward(x["q"], x["q_idx"], x["w"], dinp["k_pooled"],
+                                 dinp["k_cache"], dinp["v_cache"], dinp["seq_lens"],
+                                 budget=dwl.budget, plan=mtp_plan)
+            mtp_sels.append(mtp_plan.sel.clone())
+        mtp_i = [0]
+
+        def mtp_call():
+            i = mtp_i[0] % len(qsets)
+            mtp_i[0] += 1
+            Q.qsa_sparse_attn_decode(qsets[i]["q"], dinp["k_cache"], dinp["v_cache"],
+                                     dinp["seq_lens"], mtp_sels[i])
+
+        mtp_s = time_calls(torch, mtp_call, 32)
         progress(f"MTP decode attention over the reused selection: {mtp_s * 1e6:.1f} us")
         own = (dwl.lk - 1) // dwl.r
         d_bytes = dwl.batch * (own * dwl.d_i * 2 + dwl.budget * dwl.hkv * 2 * dwl.d * 2 +
@@ -604,6 +678,9 @@ def main():
         line["decode"] = {"workload": dwl.name, "batch": dwl.batch, "context": dwl.lk,
                           "value": dwl.batch / s_dec, "unit": "tokens/s", "ms_per_step": s_dec * 1e3,
                           "steps": args.decode_steps,
+                          "queries": "16 seeded query sets in turn (each step selects and "
+                                     "gathers other blocks of the same caches)",
+                          "ms_per_step_same_query": s_dec_same * 1e3,
                           "roofline": {"bound": "hbm", "achieved": d_bytes / s_dec / 1e9,
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": d_bytes / s_dec / 1e9 / HBM_PEAK_GBS,
@@ -613,7 +690,8 @@ def main():
             kp, vp, table = paged_copy(torch, dinp["k_cache"], dinp["v_cache"], P)
             del dinp["k_cache"], dinp["v_cache"]
             torch.cuda.empty_cache()
-            s_pg = bench_decode(args, torch, Q, dwl, dinp, paged=(kp, vp, table, P))
+            s_pg = bench_decode(args, torch, Q, dwl, dinp, paged=(kp, vp, table, P),
+                                query_sets=qsets)
             progress(f"paged decode: {s_pg * 1e6:.1f} us per step")
             line["decode_paged"] = {
                 "workload": f"{dwl.name}, K/V in shuffled pages of {P} tokens",

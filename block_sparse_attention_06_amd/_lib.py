@@ -46,8 +46,9 @@ SIGNATURES = {
     "qsa_prefill_varlen_workspace_bytes": (_Z, [_I, _L, _L, _I, _I, _L]),
     "qsa_prefill_varlen_select": (_I, [_I, _P, _P, _L, _L, _I, _I, _I, _I, _P, _P, _P, _P, _P,
                                        _L, _P, _Z, _P, _P]),
-    "qsa_sparse_attn_varlen_fwd": (_I, [_I, _P, _P, _L, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F,
-                                        _P, _P, _P]),
+    "qsa_sparse_attn_varlen_fwd": (_I, [_I, _P, _P, _L, _L, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                                        _F, _P, _P, _P]),
+    "qsa_sparse_attn_fwd_launches": (_L, [_L, _L, _I, _I]),
     "qsa_prefill_varlen_forward": (_I, [_I, _P, _P, _L, _L, _L, _I, _I, _I, _I, _I, _I, _I, _P,
                                         _P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _L, _P, _Z, _P,
                                         _P]),

@@ -489,14 +489,38 @@ constexpr int64_t kGroupOrderBytes = (int64_t)128 << 20;
 //   a row in one generation, 39.2 ms group by group (L2 hit rate 71 %). Packed short
 //   sequences (whose K/V fit the cache either way) keep the two groups together:
 //   36.9 against 37.9 ms for 16 prompts of 2K-24K tokens. For packed sequences the
-//   size is estimated from the average sequence (rows / sequences).
+//   size is that of the longest sequence when the caller knows it (a chunk of new
+//   rows after a long cached prefix then runs group by group), else it is estimated
+//   from the average sequence (rows / sequences).
 // Each row's sums run in the same order either way, so the outputs are identical.
+namespace {
+
+bool fwd_by_group(int64_t keys, int hkv, int d) {
+  return keys * hkv * d * 4 > kGroupOrderBytes;  // K and V, bf16
+}
+
+// Rows per launch: a generation of (row, group) waves, one group or all of a row's.
+int64_t fwd_launch_rows(int64_t lq, bool by_group, int hkv, int d) {
+  const int64_t gen_rows = sparse_attn_fwd_rows_per_launch(hkv, d);
+  return gen_rows <= 0 ? lq : (by_group ? gen_rows : (gen_rows + hkv - 1) / hkv);
+}
+
+}  // namespace
+
+int64_t sparse_attn_fwd_launches(int64_t lq, int64_t keys, int hkv, int d) {
+  if (lq <= 0) return 0;
+  const bool by_group = fwd_by_group(keys, hkv, d);
+  const int64_t rows = fwd_launch_rows(lq, by_group, hkv, d);
+  return (by_group ? hkv : 1) * ((lq + rows - 1) / rows);
+}
+
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream) {
   if (a.lq <= 0) return hipSuccess;
-  int64_t gen_rows = sparse_attn_fwd_rows_per_launch(a.hkv, a.d);
-  const int64_t keys = a.cu_q ? a.lq / (a.batch_vl > 0 ? a.batch_vl : 1) : a.lk;
-  const bool by_group = keys * a.hkv * a.d * 4 > kGroupOrderBytes;  // K and V, bf16
-  int64_t rows = gen_rows <= 0 ? a.lq : (by_group ? gen_rows : (gen_rows + a.hkv - 1) / a.hkv);
+  const int64_t keys =
+      a.keys_hint > 0 ? a.keys_hint
+                      : (a.cu_q ? a.lq / (a.batch_vl > 0 ? a.batch_vl : 1) : a.lk);
+  const bool by_group = fwd_by_group(keys, a.hkv, a.d);
+  const int64_t rows = fwd_launch_rows(a.lq, by_group, a.hkv, a.d);
   for (int gp = 0; gp < (by_group ? a.hkv : 1); ++gp) {
     for (int64_t c0 = 0; c0 < a.lq; c0 += rows) {
       AttnArgs c = a;

@@ -305,6 +305,11 @@ int64_t qsa_sparse_attn_fwd_rows_per_launch(int hkv, int d) {
   return qsa::sparse_attn_fwd_rows_per_launch(hkv, d);
 }
 
+int64_t qsa_sparse_attn_fwd_launches(int64_t lq, int64_t lk, int hkv, int d) {
+  if (lq < 0 || lk < 0 || hkv < 1 || (d != 128 && d != 256)) return -1;
+  return qsa::sparse_attn_fwd_launches(lq, lk, hkv, d);
+}
+
 size_t qsa_sparse_attn_bwd_workspace_bytes(int64_t lq, int64_t lk, int hq, int r, int n_sel) {
   if (lq <= 0 || lk <= 0 || hq <= 0 || r <= 0 || n_sel <= 0) return 0;
   return qsa::bwd_layout(lq, lk, hq, n_sel, r).total;
@@ -749,10 +754,11 @@ qsa_status qsa_prefill_varlen_select(int batch, const int32_t* cu_seqlens_q,
 }
 
 qsa_status qsa_sparse_attn_varlen_fwd(int batch, const int32_t* cu_seqlens_q,
-                                      const int32_t* cu_seqlens_k, int64_t total_q, int hq,
-                                      int hkv, int d, int r, int n_sel, const void* q,
-                                      const void* k, const void* v, const int32_t* sel,
-                                      float softmax_scale, void* out, float* lse, void* stream) {
+                                      const int32_t* cu_seqlens_k, int64_t total_q,
+                                      int64_t max_lk, int hq, int hkv, int d, int r, int n_sel,
+                                      const void* q, const void* k, const void* v,
+                                      const int32_t* sel, float softmax_scale, void* out,
+                                      float* lse, void* stream) {
   QSA_TRY(check_r(r));
   QSA_TRY(check_attn_shape(hq, hkv, d));
   QSA_REQUIRE(batch >= 1 && batch <= 65535, QSA_ERR_INVALID_ARGUMENT, "batch=%d", batch);
@@ -761,6 +767,7 @@ qsa_status qsa_sparse_attn_varlen_fwd(int batch, const int32_t* cu_seqlens_q,
               n_sel);
   QSA_REQUIRE(total_q >= 0 && total_q < ((int64_t)1 << 31), QSA_ERR_INVALID_ARGUMENT,
               "total_q=%lld", (long long)total_q);
+  QSA_REQUIRE(max_lk >= 0, QSA_ERR_INVALID_ARGUMENT, "max_lk=%lld", (long long)max_lk);
   QSA_REQUIRE(isfinite(softmax_scale), QSA_ERR_INVALID_ARGUMENT, "softmax_scale not finite");
   if (total_q == 0) return QSA_OK;
   QSA_REQUIRE(q && k && v && sel && out, QSA_ERR_INVALID_ARGUMENT, "null tensor pointer");
@@ -782,6 +789,7 @@ qsa_status qsa_sparse_attn_varlen_fwd(int batch, const int32_t* cu_seqlens_q,
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.batch_vl = batch;
+  a.keys_hint = max_lk;
   return hip_status(qsa::launch_sparse_attn_fwd(a, static_cast<hipStream_t>(stream)),
                     "qsa_sparse_attn_varlen_fwd launch");
 }
@@ -807,9 +815,9 @@ qsa_status qsa_prefill_varlen_forward(int batch, const int32_t* cu_seqlens_q,
   QSA_TRY(qsa_prefill_varlen_select(batch, cu_seqlens_q, cu_seqlens_k, max_lq, max_lk, h_idx,
                                     d_idx, r, budget_tokens, q_idx, w, k_idx, k_pooled, sel,
                                     row_chunk, workspace, workspace_bytes, pe, stream));
-  return qsa_sparse_attn_varlen_fwd(batch, cu_seqlens_q, cu_seqlens_k, total_q, hq, hkv, d, r,
-                                    budget_tokens / r, q, k, v, sel, softmax_scale, out, lse,
-                                    stream);
+  return qsa_sparse_attn_varlen_fwd(batch, cu_seqlens_q, cu_seqlens_k, total_q, max_lk, hq,
+                                    hkv, d, r, budget_tokens / r, q, k, v, sel, softmax_scale,
+                                    out, lse, stream);
 }
 
 // ---- whole decode step ----

@@ -141,6 +141,9 @@ struct AttnArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int batch_vl;
+  // prefill: key count of the longest sequence, which chooses the launch order (one KV
+  // group at a time or both together); 0: lk, or for packed rows their average count
+  int64_t keys_hint;
   // decode from a paged cache: k / v are pools of num_pages pages of page_blocks
   // 4-token blocks; page p of sequence s is block_table[s * table_stride + p]
   const int32_t* block_table;
@@ -151,6 +154,9 @@ struct AttnArgs {
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream);
 // Rows per launch of launch_sparse_attn_fwd on the current device; -1 if unknown.
 int64_t sparse_attn_fwd_rows_per_launch(int hkv, int d);
+// Kernel launches of one launch_sparse_attn_fwd call over lq rows whose longest
+// sequence has `keys` keys (the same rule as the launcher); 0 if lq <= 0.
+int64_t sparse_attn_fwd_launches(int64_t lq, int64_t keys, int hkv, int d);
 hipError_t launch_sparse_attn_decode(const AttnArgs& a, hipStream_t stream);
 
 // ---- stage 4 backward ----

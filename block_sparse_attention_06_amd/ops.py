@@ -184,6 +184,13 @@ def qsa_sparse_attn_fwd_rows_per_launch(hkv: int, d: int, device=None) -> int:
         return int(_lib.load().qsa_sparse_attn_fwd_rows_per_launch(hkv, d))
 
 
+def qsa_sparse_attn_fwd_launches(lq: int, lk: int, hkv: int, d: int, device=None) -> int:
+    """Kernel launches one qsa_sparse_attn_fwd call issues for lq rows over lk keys on
+    `device` (the current device by default)."""
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        return int(_lib.load().qsa_sparse_attn_fwd_launches(lq, lk, hkv, d))
+
+
 def qsa_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor,
                         out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, *,
                         q_pos0: int = 0, scale: Optional[float] = None, r: int = 4,
@@ -442,8 +449,10 @@ def qsa_prefill_varlen_forward(q, k, v, q_idx, w, k_idx, cu_seqlens_q, cu_seqlen
 def qsa_sparse_attn_varlen_fwd(q, k, v, sel, cu_seqlens_q, cu_seqlens_k, *,
                                scale: Optional[float] = None, r: int = 4,
                                out: Optional[torch.Tensor] = None,
-                               lse: Optional[torch.Tensor] = None):
-    """Attention of a packed batch over per-sequence selections sel [Tq, n_sel]."""
+                               lse: Optional[torch.Tensor] = None, max_lk: int = 0):
+    """Attention of a packed batch over per-sequence selections sel [Tq, n_sel].
+    max_lk: the longest sequence's key count if known (0: unknown), which only
+    chooses the launch order."""
     for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
                         ("v", v, torch.bfloat16), ("sel", sel, torch.int32),
                         ("cu_seqlens_q", cu_seqlens_q, torch.int32),
@@ -455,8 +464,8 @@ def qsa_sparse_attn_varlen_fwd(q, k, v, sel, cu_seqlens_q, cu_seqlens_k, *,
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device) if lse is None else lse
     _call("qsa_sparse_attn_varlen_fwd", cu_seqlens_q.numel() - 1, _ptr(cu_seqlens_q),
-          _ptr(cu_seqlens_k), total_q, hq, hkv, d, r, sel.shape[1], _ptr(q), _ptr(k), _ptr(v),
-          _ptr(sel), scale, _ptr(out), _ptr(lse), _stream(q))
+          _ptr(cu_seqlens_k), total_q, max_lk, hq, hkv, d, r, sel.shape[1], _ptr(q), _ptr(k),
+          _ptr(v), _ptr(sel), scale, _ptr(out), _ptr(lse), _stream(q))
     return out, lse
 
 

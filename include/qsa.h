@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -175,6 +175,13 @@ qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, i
  * (then all rows go in one launch).
  */
 int64_t qsa_sparse_attn_fwd_rows_per_launch(int hkv, int d);
+/*
+ * Kernel launches one qsa_sparse_attn_fwd call issues for lq rows over a sequence of
+ * lk keys (for packed rows: the longest sequence's key count) on the current device,
+ * by the rule above; 0 for lq = 0, -1 for unsupported arguments. A measurement aid:
+ * the average launch duration is the call's duration over this count.
+ */
+int64_t qsa_sparse_attn_fwd_launches(int64_t lq, int64_t lk, int hkv, int d);
 
 /*
  * Stage 4 backward -- gradients of the stage-4 attention with respect to q, k and v
@@ -336,10 +343,11 @@ qsa_status qsa_prefill_varlen_select(int batch, const int32_t* cu_seqlens_q,
                                      int64_t row_chunk, void* workspace, size_t workspace_bytes,
                                      const qsa_pooled_pe* pe, void* stream);
 qsa_status qsa_sparse_attn_varlen_fwd(int batch, const int32_t* cu_seqlens_q,
-                                      const int32_t* cu_seqlens_k, int64_t total_q, int hq,
-                                      int hkv, int d, int r, int n_sel, const void* q,
-                                      const void* k, const void* v, const int32_t* sel,
-                                      float softmax_scale, void* out, float* lse, void* stream);
+                                      const int32_t* cu_seqlens_k, int64_t total_q,
+                                      int64_t max_lk, int hq, int hkv, int d, int r, int n_sel,
+                                      const void* q, const void* k, const void* v,
+                                      const int32_t* sel, float softmax_scale, void* out,
+                                      float* lse, void* stream);
 qsa_status qsa_prefill_varlen_forward(int batch, const int32_t* cu_seqlens_q,
                                       const int32_t* cu_seqlens_k, int64_t total_q,
                                       int64_t max_lq, int64_t max_lk, int hq, int hkv, int d,

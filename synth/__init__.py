@@ -8,6 +8,7 @@ from .workloads import (  # noqa: F401
     CONFIGS,
     Workload,
     bf16_bits,
+    decode_query_sets,
     generate,
     generate_varlen,
     serving_lengths,

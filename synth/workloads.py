@@ -297,3 +297,26 @@ def generate_varlen(wl: Workload, lens, device="cpu") -> dict:
         [p["aligned_rows"] + cu_q[b] for b, p in enumerate(parts)]).astype(np.int64)
     out["aligned_blocks"] = np.concatenate([p["aligned_blocks"] for p in parts]).astype(np.int64)
     return out
+
+
+def decode_query_sets(wl: Workload, n_sets: int, device="cpu") -> list:
+    """n_sets further draws of a decode workload's new-token inputs (q [B,Hq,d],
+    q_idx [B,1,H_I,d_I], w [B,1,H_I]) by the same recipe, set i from the seed
+    sequence (wl.seed, 1000 + i): successive decode steps then score, select and
+    gather different blocks of the same caches."""
+    assert wl.kind == "decode"
+    device = torch.device(device)
+    b, bf = wl.batch, torch.bfloat16
+    sets = []
+    for i in range(n_sets):
+        kids = dict(zip(("q", "q_idx", "w"),
+                        np.random.SeedSequence([wl.seed, 1000 + i]).spawn(3)))
+        q = torch.empty((b, wl.hq, wl.d), dtype=bf, device=device)
+        q_idx = torch.empty((b, 1, wl.h_i, wl.d_i), dtype=bf, device=device)
+        w = torch.empty((b, 1, wl.h_i), dtype=torch.float32, device=device)
+        _fill_normal(q, kids["q"], 1.0 / math.sqrt(wl.d))
+        _fill_normal(q_idx, kids["q_idx"], 1.0 / math.sqrt(wl.d_i))
+        _fill_uniform(w, kids["w"])
+        sets.append({"q": q, "q_idx": q_idx, "w": w})
+    return sets
+

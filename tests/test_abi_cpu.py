@@ -24,7 +24,7 @@ def test_every_header_function_is_exported_and_declared(lib):
     assert sorted(_lib.SIGNATURES) == names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.qsa_abi_version() == 2
+    assert lib.qsa_abi_version() == 3
 
 
 def test_probe_library_is_separate():
@@ -207,9 +207,11 @@ def test_varlen_validation_and_workspace(lib):
     assert need >= 2 * 64 * 52 * 4
     assert sel_call(ws_bytes=need - 1) == 3 and "workspace" in _err(lib)
 
-    def attn_call(batch=2, total_q=100, hq=24, hkv=2, d=256, n_sel=64, scale=f, out=FAKE):
-        return lib.qsa_sparse_attn_varlen_fwd(batch, FAKE, FAKE, total_q, hq, hkv, d, 4, n_sel,
-                                              FAKE, FAKE, FAKE, FAKE, scale, out, None, None)
+    def attn_call(batch=2, total_q=100, hq=24, hkv=2, d=256, n_sel=64, scale=f, out=FAKE,
+                  max_lk=0):
+        return lib.qsa_sparse_attn_varlen_fwd(batch, FAKE, FAKE, total_q, max_lk, hq, hkv, d, 4,
+                                              n_sel, FAKE, FAKE, FAKE, FAKE, scale, out, None,
+                                              None)
 
     assert attn_call(hkv=5) == 1
     assert attn_call(d=192) == 2
@@ -217,7 +219,17 @@ def test_varlen_validation_and_workspace(lib):
     assert attn_call(total_q=-1) == 1
     assert attn_call(scale=ctypes.c_float(float("nan"))) == 1
     assert attn_call(out=MISALIGNED) == 1
+    assert attn_call(max_lk=-1) == 1
     assert attn_call(total_q=0) == 0                   # nothing to do
+
+
+def test_attention_launch_count_query(lib):
+    # Unsupported arguments are -1; no rows are no launches. (With no GPU the occupancy
+    # is unknown and every row goes in one launch per KV-group pass.)
+    assert lib.qsa_sparse_attn_fwd_launches(10, 100, 0, 256) == -1
+    assert lib.qsa_sparse_attn_fwd_launches(10, 100, 2, 192) == -1
+    assert lib.qsa_sparse_attn_fwd_launches(0, 100, 2, 256) == 0
+    assert lib.qsa_sparse_attn_fwd_launches(10, 100, 2, 256) >= 1
 
 
 def test_pooled_key_encoding_validation(lib):
