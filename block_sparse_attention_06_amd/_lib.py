@@ -57,6 +57,8 @@ SIGNATURES = {
     "qsa_decode_forward_paged": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _L, _P,
                                       _P, _L, _I, _P, _L, _L, _P, _F, _P, _P, _P, _P, _Z, _P]),
     "qsa_decode_workspace_bytes": (_Z, [_I, _I, _I, _L, _I, _I]),
+    "qsa_decode_forward_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _L, _P,
+                                        _P, _L, _L, _P, _F, _P, _P, _P, _P]),
     "qsa_decode_forward": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _L, _P, _P, _L,
                                 _L, _P, _F, _P, _P, _P, _P, _Z, _P]),
 }

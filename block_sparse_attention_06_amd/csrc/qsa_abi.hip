@@ -7,8 +7,16 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "qsa.h"
 #include "qsa_internal.h"
+
+// Scratch of qsa_decode_forward_noalloc, for callers that cannot allocate: one copy on
+// every GPU the library runs on, held until the process ends. In host code its name
+// is a host-side stand-in; only the device address that hipGetSymbolAddress returns
+// (noalloc_scratch below) is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -39,6 +47,28 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
     const qsa_status st_ = (expr);       \
     if (st_ != QSA_OK) return st_;       \
   } while (0)
+
+// Device address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept.
+qsa_status noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (es != hipSuccess) return hip_status(es, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(QSA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return QSA_OK;
+}
 
 qsa_status check_r(int r) {
   QSA_REQUIRE(r == 4, QSA_ERR_UNSUPPORTED, "micro-block size r=%d: only r=4 is supported", r);
@@ -839,7 +869,8 @@ qsa_status decode_forward_impl(int batch, int hq, int hkv, int d, int h_idx, int
                                const void* v_cache, int64_t cache_batch_stride,
                                const PagedKV* paged, int64_t lmax, const int32_t* seq_lens,
                                float softmax_scale, int32_t* sel, void* out, float* lse,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               bool use_scratch = false) {
   QSA_TRY(check_r(r));
   if (paged) QSA_TRY(check_paged(*paged, r, lmax));
   QSA_REQUIRE(q && k_cache && v_cache && out && aligned16(q) && aligned16(k_cache) &&
@@ -861,6 +892,10 @@ qsa_status decode_forward_impl(int batch, int hq, int hkv, int d, int h_idx, int
               QSA_ERR_INVALID_ARGUMENT, "k_pooled_batch_stride=%lld",
               (long long)k_pooled_batch_stride);
   const size_t need = qsa_decode_workspace_bytes(batch, hq, d, lmax, r, budget_tokens);
+  if (use_scratch) {  // every argument checked: only now touch the device
+    QSA_TRY(noalloc_scratch(&workspace));
+    workspace_bytes = (size_t)QSA_NOALLOC_SCRATCH_BYTES;
+  }
   QSA_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), QSA_ERR_WORKSPACE,
               "decode workspace: need %zu bytes (16-byte aligned), got %zu", need,
               workspace_bytes);
@@ -911,6 +946,32 @@ qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int 
                              k_pooled, k_pooled_batch_stride, k_cache, v_cache,
                              cache_batch_stride, nullptr, lmax, seq_lens, softmax_scale, sel,
                              out, lse, workspace, workspace_bytes, stream);
+}
+
+qsa_status qsa_decode_forward_noalloc(int batch, int hq, int hkv, int d, int h_idx, int d_idx,
+                                      int r, int budget_tokens, const void* q,
+                                      const void* q_idx, const float* w, const void* k_pooled,
+                                      int64_t k_pooled_batch_stride, const void* k_cache,
+                                      const void* v_cache, int64_t cache_batch_stride,
+                                      int64_t lmax, const int32_t* seq_lens,
+                                      float softmax_scale, int32_t* sel, void* out, float* lse,
+                                      void* stream) {
+  QSA_REQUIRE(batch >= 1 && r > 0 && budget_tokens > 0 && lmax >= 0,
+              QSA_ERR_INVALID_ARGUMENT, "batch=%d r=%d budget=%d lmax=%lld", batch, r,
+              budget_tokens, (long long)lmax);
+  const size_t need = qsa_decode_workspace_bytes(batch, hq, d, lmax, r, budget_tokens);
+  QSA_REQUIRE(need <= (size_t)QSA_NOALLOC_SCRATCH_BYTES, QSA_ERR_WORKSPACE,
+              "qsa_decode_forward_noalloc: batch %d x lmax %lld needs %zu bytes of scratch; "
+              "the static scratch holds %zu (use qsa_decode_forward with a workspace)",
+              batch, (long long)lmax, need, (size_t)QSA_NOALLOC_SCRATCH_BYTES);
+  if (batch > 1)
+    QSA_REQUIRE(cache_batch_stride % 8 == 0 && cache_batch_stride >= lmax * (int64_t)hkv * d,
+                QSA_ERR_INVALID_ARGUMENT, "cache_batch_stride=%lld",
+                (long long)cache_batch_stride);
+  return decode_forward_impl(batch, hq, hkv, d, h_idx, d_idx, r, budget_tokens, q, q_idx, w,
+                             k_pooled, k_pooled_batch_stride, k_cache, v_cache,
+                             cache_batch_stride, nullptr, lmax, seq_lens, softmax_scale, sel,
+                             out, lse, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 qsa_status qsa_decode_forward_paged(int batch, int hq, int hkv, int d, int h_idx, int d_idx,

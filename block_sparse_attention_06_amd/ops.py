@@ -508,6 +508,35 @@ def qsa_decode_forward(q, q_idx, w, k_pooled, k_cache, v_cache, seq_lens, *, bud
     return plan.out, plan.lse, plan.sel
 
 
+def qsa_decode_forward_noalloc(q, q_idx, w, k_pooled, k_cache, v_cache, seq_lens, *,
+                               budget: int, scale: Optional[float] = None, r: int = 4,
+                               sel: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None,
+                               lse: Optional[torch.Tensor] = None):
+    """qsa_decode_forward without a workspace: the library's static device scratch
+    serves instead (calls overlapping on one GPU race). Outputs are the caller's
+    (allocated here when not given). Returns (out, lse, sel)."""
+    q_idx = q_idx.reshape(q_idx.shape[0], q_idx.shape[-2], q_idx.shape[-1])
+    w = w.reshape(w.shape[0], w.shape[-1])
+    for name, t, dt in (("q", q, torch.bfloat16), ("q_idx", q_idx, torch.bfloat16),
+                        ("w", w, torch.float32), ("k_pooled", k_pooled, torch.bfloat16),
+                        ("k_cache", k_cache, torch.bfloat16), ("v_cache", v_cache, torch.bfloat16),
+                        ("seq_lens", seq_lens, torch.int32)):
+        _need(t, name, dt, q.device)
+    bsz, hq, d = q.shape
+    _, lmax, hkv, _ = k_cache.shape
+    _, h_idx, d_idx = q_idx.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    sel = torch.empty((bsz, budget // r), dtype=torch.int32, device=q.device) if sel is None else sel
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _call("qsa_decode_forward_noalloc", bsz, hq, hkv, d, h_idx, d_idx, r, budget, _ptr(q),
+          _ptr(q_idx), _ptr(w), _ptr(k_pooled), k_pooled.stride(0), _ptr(k_cache),
+          _ptr(v_cache), k_cache.stride(0), lmax, _ptr(seq_lens), scale, _ptr(sel), _ptr(out),
+          _ptr(lse), _stream(q))
+    return out, lse, sel
+
+
 def qsa_decode_forward_paged(q, q_idx, w, k_pooled, k_pool, v_pool, block_table, seq_lens, *,
                              budget: int, page_size: int, lmax: Optional[int] = None,
                              scale: Optional[float] = None, r: int = 4,

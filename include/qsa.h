@@ -377,6 +377,29 @@ qsa_status qsa_decode_forward(int batch, int hq, int hkv, int d, int h_idx, int 
                               void* stream);
 
 /*
+ * qsa_decode_forward for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation and
+ * arguments without the workspace, which comes from a static device scratch of
+ * QSA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+ * process ends. The call allocates nothing. A step whose workspace
+ * (qsa_decode_workspace_bytes) exceeds the scratch returns QSA_ERR_WORKSPACE before
+ * anything is enqueued (at 1M-token caches, 24 heads, d = 256, K = 2048: up to 22
+ * sequences).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
+ * different streams or threads without ordering) race; calls ordered on one stream
+ * are safe. The caller still owns q, the caches, sel, out and lse.
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+qsa_status qsa_decode_forward_noalloc(int batch, int hq, int hkv, int d, int h_idx, int d_idx,
+                                      int r, int budget_tokens, const void* q,
+                                      const void* q_idx, const float* w, const void* k_pooled,
+                                      int64_t k_pooled_batch_stride, const void* k_cache,
+                                      const void* v_cache, int64_t cache_batch_stride,
+                                      int64_t lmax, const int32_t* seq_lens,
+                                      float softmax_scale, int32_t* sel, void* out, float* lse,
+                                      void* stream);
+
+/*
  * Decode from a PAGED K/V cache (serving engines keep the cache in fixed-size pages
  * [MR5]): the same computation as qsa_sparse_attn_decode / qsa_decode_forward, with
  * the K/V rows of token j of sequence s at pool slot

@@ -251,3 +251,21 @@ def test_pooled_key_encoding_validation(lib):
     bad = _PooledPe(20, 1e4)
     assert lib.qsa_prefill_select(64, 64, 0, 4, 128, 4, 256, FAKE, FAKE, FAKE, 0, None, FAKE,
                                   FAKE, 64, FAKE, 1 << 40, ctypes.byref(bad), None) == 2
+
+
+def test_decode_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    # The allocation-free decode step checks its workspace need against the static
+    # scratch on the host and returns QSA_ERR_WORKSPACE (3) before anything else.
+    args = (4, 24, 2, 256, 4, 128, 4, 2048, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0)
+    tail = (FAKE, ctypes.c_float(0.0625), FAKE, FAKE, None, None)
+    big = lib.qsa_decode_forward_noalloc(64, *args[1:], 1 << 20, *tail)
+    assert big == 3 and "scratch" in _err(lib)
+    assert lib.qsa_decode_workspace_bytes(64, 24, 256, 1 << 20, 4, 2048) > 32 << 20
+    # within the limit it gets past the size check (here to argument validation)
+    assert lib.qsa_decode_workspace_bytes(8, 24, 256, 1 << 20, 4, 2048) <= 32 << 20
+    stride = (1 << 20) * 2 * 256
+    assert lib.qsa_decode_forward_noalloc(8, 24, 2, 256, 4, 128, 3, 2048, FAKE, FAKE, FAKE, FAKE,
+                                          (1 << 18) * 128, FAKE, FAKE, stride, 1 << 20,
+                                          *tail) == 2  # r = 3
+    assert "r=3" in _err(lib)
+
