@@ -188,7 +188,7 @@ def bench_score_gemm(torch, Q, wl, inp, plan, row_chunk, reps=3):
     of the step's own pooling), into a chunk-sized scratch: ms per step's worth."""
     kp = plan.k_pooled
     nb_all = kp.shape[0]
-    scratch = torch.empty((min(row_chunk, wl.lq), Q.score_ld(nb_all)), dtype=torch.float32,
+    scratch = torch.empty(min(row_chunk, wl.lq) * Q.score_ld(nb_all), dtype=torch.float32,
                           device=kp.device)
     chunks = []
     for c0 in range(0, wl.lq, row_chunk):
@@ -198,8 +198,9 @@ def bench_score_gemm(torch, Q, wl, inp, plan, row_chunk, reps=3):
 
     def run():
         for c0, c1, nb in chunks:
+            ld = Q.score_ld(nb)
             Q.qsa_index_scores(inp["q_idx"][c0:c1], inp["w"][c0:c1], kp, q_pos0=wl.q_pos0 + c0,
-                               nblk=nb, out=scratch[: c1 - c0, : Q.score_ld(nb)])
+                               nblk=nb, out=scratch[: (c1 - c0) * ld].view(c1 - c0, ld))
 
     ms = time_calls(torch, run, reps) * 1e3
     del scratch

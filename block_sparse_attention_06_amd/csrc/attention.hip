@@ -130,15 +130,21 @@ __device__ __forceinline__ void attn_compute_step(const AttnStep<D>& st, const i
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = exp2f(x[i] - m_new);
   l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  const bool moved = m_new != m_run;
   m_run = m_new;
 
-  float ai[4];
+  // Rescale O only when some head's running max moved: otherwise every alpha is
+  // exactly 1 and the multiplies change nothing. After the first steps a new maximum
+  // is rare, so most steps skip the 64 multiplies (the result is bit-identical).
+  if (__any(moved)) {
+    float ai[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * quad + i, kWave);
+    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * quad + i, kWave);
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
+    for (int n = 0; n < NT; ++n) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) O[n][i] *= ai[i];
+      for (int i = 0; i < 4; ++i) O[n][i] *= ai[i];
+    }
   }
 
   const uint2 P = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
