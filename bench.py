@@ -32,6 +32,10 @@ def parse_args():
     p.add_argument("--workload", default="prefill128k",
                    choices=["prefill128k", "prefill32k", "chunked1m", "tiny"])
     p.add_argument("--row-chunk", type=int, default=16384)
+    p.add_argument("--select", choices=["auto", "fused", "plain"], default="auto",
+                   help="selection path of the step: the fused score/top-k, the two-kernel "
+                        "one (scores materialised, then top-k), or the library's default for "
+                        "the workload (auto)")
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-backward", action="store_true",
@@ -150,10 +154,18 @@ def score_flops(wl, t):
     return int(own.sum()) * 2 * wl.h_i * wl.d_i
 
 
-def bench_prefill(args, torch, Q, wl, inp):
+def select_path(Q, wl, select):
+    """'fused' or 'plain' for a --select choice on a workload."""
+    if select == "auto":
+        return "fused" if Q.prefer_fused_select(wl.lk, wl.r) else "plain"
+    return select
+
+
+def bench_prefill(args, torch, Q, wl, inp, fused=None):
     dev = inp["q"].device
+    fused = (select_path(Q, wl, args.select) == "fused") if fused is None else fused
     plan = Q.PrefillPlan(wl.lq, wl.lk, wl.hq, wl.hkv, wl.d, wl.h_i, wl.d_i, wl.budget,
-                         row_chunk=args.row_chunk, device=dev)
+                         row_chunk=args.row_chunk, device=dev, fused=fused)
     scale = 1.0 / math.sqrt(wl.d)
 
     def step(ev_s=None, ev_a=None, ev_b=None):
@@ -214,21 +226,32 @@ def percentiles(xs):
     return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
 
 
-def bench_other_prefill(torch, Q, name, steps=5):
-    """A whole prefill step (select + attention) on another workload: tokens/s."""
+def bench_other_prefill(torch, Q, name, select, steps=5):
+    """A whole prefill step (select + attention) on another workload: tokens/s, with
+    the step's selection path and, for comparison, the other one."""
     import types
     from synth import generate, workload
     owl = workload(name)
     oinp = generate(owl, device="cuda")
     torch.cuda.synchronize()
-    args = types.SimpleNamespace(row_chunk=min(16384, owl.lq), warmup=1, steps=steps)
-    wall, attn_ms, plan = bench_prefill(args, torch, Q, owl, oinp)
-    step_ms = bench_prefill.step_ms
-    del oinp, plan
+    select = select_path(Q, owl, select)
+    res = {"query_tokens": owl.lq, "context": owl.lk, "q_pos0": owl.q_pos0, "select": select}
+    for path in (select, "plain" if select == "fused" else "fused"):
+        args = types.SimpleNamespace(row_chunk=min(16384, owl.lq), warmup=1, steps=steps,
+                                     select=path)
+        wall, attn_ms, plan = bench_prefill(args, torch, Q, owl, oinp)
+        step_ms = bench_prefill.step_ms
+        del plan
+        torch.cuda.empty_cache()
+        if path == select:
+            res.update({"tokens_per_s": owl.lq * steps / wall, "ms_per_step": wall / steps * 1e3,
+                        "attention_ms": attn_ms, "step_ms": percentiles(step_ms),
+                        "steps": steps})
+        else:
+            res[f"ms_per_step_{path}_select"] = wall / steps * 1e3
+    del oinp
     torch.cuda.empty_cache()
-    return {"query_tokens": owl.lq, "context": owl.lk, "q_pos0": owl.q_pos0,
-            "tokens_per_s": owl.lq * steps / wall, "ms_per_step": wall / steps * 1e3,
-            "attention_ms": attn_ms, "step_ms": percentiles(step_ms), "steps": steps}
+    return res
 
 
 def backward_bytes(wl, t):
@@ -545,7 +568,16 @@ def main():
     torch.cuda.synchronize()
     progress(f"inputs of {wl.name} resident")
     wall, attn_ms, plan = bench_prefill(args, torch, Q, wl, inp)
-    progress(f"prefill: {wall / args.steps * 1e3:.2f} ms per step, attention {attn_ms:.2f} ms")
+    step_events = bench_prefill.step_ms
+    path = select_path(Q, wl, args.select)
+    progress(f"prefill ({path} selection): {wall / args.steps * 1e3:.2f} ms per step, "
+             f"attention {attn_ms:.2f} ms")
+    other = "plain" if path == "fused" else "fused"
+    o_wall, o_attn, o_plan = bench_prefill(args, torch, Q, wl, inp, fused=other == "fused")
+    del o_plan
+    torch.cuda.empty_cache()
+    other_ms = o_wall / args.steps * 1e3
+    progress(f"prefill ({other} selection): {other_ms:.2f} ms per step")
     ms_step = wall / args.steps * 1e3
     t = wl.q_pos0 + np.arange(wl.lq, dtype=np.int64)
     a_bytes = attention_bytes(wl, t)
@@ -598,7 +630,10 @@ def main():
             "score_gemm_ms": score_ms, "score_gemm_flops_per_step": s_flops,
             "attention_flops_per_call": a_flops, "peak_TFLOPs": MFMA_BF16_PEAK_TFS},
         "stages_ms": {"select (pool + scores + top-k)": ms_step - attn_ms, "attention": attn_ms},
-        "step_ms_events": percentiles(bench_prefill.step_ms),
+        "select_path": path,
+        "other_select_path": {"path": other, "ms_per_step": other_ms,
+                              "select_ms": other_ms - o_attn},
+        "step_ms_events": percentiles(step_events),
     }
     kv_mib = (2 * wl.lk * wl.hkv * wl.d * 2) >> 20
     ceil_rand = gather_ceiling(torch, Q, dev, kv_mib, sequential=False)
@@ -706,7 +741,7 @@ def main():
         del dinp
         torch.cuda.empty_cache()
     if not args.no_other and wl.name == "prefill128k":
-        line["other_prefill"] = {n: bench_other_prefill(torch, Q, n)
+        line["other_prefill"] = {n: bench_other_prefill(torch, Q, n, args.select)
                                  for n in ("prefill32k", "chunked1m")}
         progress("other prefill workloads: " + ", ".join(
             f"{n} {v['ms_per_step']:.2f} ms" for n, v in line["other_prefill"].items()))

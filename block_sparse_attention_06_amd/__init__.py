@@ -8,6 +8,7 @@ from .ops import (  # noqa: F401
     DecodePlan,
     PrefillPlan,
     VarlenPlan,
+    prefer_fused_select,
     QSAError,
     abi_version,
     qsa_decode_forward,

@@ -41,6 +41,9 @@ SIGNATURES = {
     "qsa_prefill_workspace_bytes": (_Z, [_L, _L, _I, _I, _L]),
     "qsa_prefill_select": (_I, [_L, _L, _L, _I, _I, _I, _I, _P, _P, _P, _L, _P, _P, _P, _L, _P,
                                 _Z, _P, _P]),
+    "qsa_prefill_fused_workspace_bytes": (_Z, [_L, _L, _I, _I, _L]),
+    "qsa_prefill_select_fused": (_I, [_L, _L, _L, _I, _I, _I, _I, _P, _P, _P, _L, _P, _P, _P,
+                                      _L, _P, _Z, _P, _P, _P]),
     "qsa_prefill_forward": (_I, [_L, _L, _L, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                                  _L, _P, _P, _F, _P, _P, _P, _L, _P, _Z, _P, _P]),
     "qsa_prefill_varlen_workspace_bytes": (_Z, [_I, _L, _L, _I, _I, _L]),

@@ -321,6 +321,11 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
   }
   const int64_t i0 = (int64_t)blockIdx.x * kScoreRows;
   if (i0 >= lq) return;
+  if (a.row_flags) {  // score only the tiles that hold a flagged row
+    const int64_t rr = i0 + threadIdx.x;
+    const int fl = (threadIdx.x < kScoreRows && rr < lq) ? a.row_flags[rr] : 0;
+    if (!__syncthreads_or(fl)) return;
+  }
   const int64_t t_last = base + min(i0 + kScoreRows - 1, lq - 1);
   if (t_last < 0) return;
   const int64_t nb_need = min(t_last / a.r, a.nblk);
@@ -406,9 +411,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
     for (int mt = 0; mt < 4; ++mt) {
       float s[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        s[j] = W[mt][0] * fmaxf(acc[mt][j][0], 0.f) + W[mt][1] * fmaxf(acc[mt][j][1], 0.f) +
-               W[mt][2] * fmaxf(acc[mt][j][2], 0.f) + W[mt][3] * fmaxf(acc[mt][j][3], 0.f);
+      for (int j = 0; j < 4; ++j) s[j] = score_of_heads(W[mt], acc[mt][j]);
       if (blk0 < lim[mt])
         *reinterpret_cast<float4*>(orow[mt] + blk0) = make_float4(s[0], s[1], s[2], s[3]);
     }
@@ -517,8 +520,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_scan_kernel(ScoreArgs a, 
 #pragma unroll
         for (int c = 0; c < NC; ++c)
           acc = mfma_16x16x32(A[c], st[r * CPR + ((quad + 4 * c) ^ (r & (CPR - 1)))], acc);
-        s[2 * h + jj] = W[0] * fmaxf(acc[0], 0.f) + W[1] * fmaxf(acc[1], 0.f) +
-                        W[2] * fmaxf(acc[2], 0.f) + W[3] * fmaxf(acc[3], 0.f);
+        s[2 * h + jj] = score_of_heads(W, acc);
       }
       // The next half's stores must not pass these reads.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -603,7 +605,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_scan_kernel(ScoreArgs a, 
 
 hipError_t launch_index_scores(const ScoreArgs& a, hipStream_t stream) {
   if (a.lq <= 0 || a.batch <= 0 || a.nblk <= 0) return hipSuccess;
-  if ((a.lq <= 4 || a.cand.cand_val) && !a.vl.cu_q) {
+  if ((a.lq <= 4 || a.cand.cand_val) && !a.vl.cu_q && !a.row_flags) {
     // About 2048 waves (two per SIMD): one round over the GPU, 64-block tiles. With
     // candidates, a wave covers exactly one top-k segment.
     const int64_t rows = (int64_t)a.batch * a.lq;

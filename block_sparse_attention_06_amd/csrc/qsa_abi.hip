@@ -609,12 +609,14 @@ size_t qsa_prefill_workspace_bytes(int64_t lq, int64_t lk, int r, int budget_tok
          qsa_topk_workspace_bytes(1, rc, lk / r, budget_tokens, r);
 }
 
-qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx, int d_idx,
-                              int r, int budget_tokens, const void* q_idx, const float* w,
-                              const void* k_idx, int64_t first_raw_token,
-                              const void* k_pooled_prefix, void* k_pooled, int32_t* sel,
-                              int64_t row_chunk, void* workspace, size_t workspace_bytes,
-                              const qsa_pooled_pe* pe, void* stream) {
+namespace {
+
+// Checks shared by both prefill selections, then the pooling of the new blocks (and
+// the copy of a pooled prefix into k_pooled).
+qsa_status prefill_pool(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx, int d_idx, int r,
+                        int budget_tokens, const void* k_idx, int64_t first_raw_token,
+                        const void* k_pooled_prefix, void* k_pooled, const qsa_pooled_pe* pe,
+                        size_t need, void* workspace, size_t workspace_bytes, void* stream) {
   QSA_TRY(check_r(r));
   qsa::PooledPe ppe{};
   QSA_TRY(pooled_pe(pe, d_idx, &ppe));
@@ -632,13 +634,11 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
               "null k_pooled or k_idx");
   QSA_REQUIRE(aligned16(k_pooled) && (!k_pooled_prefix || aligned16(k_pooled_prefix)),
               QSA_ERR_INVALID_ARGUMENT, "pooled-key buffers must be 16-byte aligned");
-  const int64_t nblk = lk / r;
-  const int64_t prefix_blocks = first_raw_token / r;
-  const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
-  const size_t need = qsa_prefill_workspace_bytes(lq, lk, r, budget_tokens, row_chunk);
   QSA_REQUIRE(lq == 0 || (workspace && workspace_bytes >= need && aligned16(workspace)),
               QSA_ERR_WORKSPACE, "prefill workspace: need %zu bytes (16-byte aligned), got %zu",
               need, workspace_bytes);
+  const int64_t nblk = lk / r;
+  const int64_t prefix_blocks = first_raw_token / r;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (prefix_blocks > 0 && k_pooled_prefix != k_pooled) {
     QSA_TRY(hip_status(hipMemcpyAsync(k_pooled, k_pooled_prefix,
@@ -651,7 +651,30 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
     QSA_TRY(qsa_pool_keys_pe(k_idx, d_idx, new_blocks, d_idx, r, prefix_blocks, pe,
                              static_cast<uint16_t*>(k_pooled) + prefix_blocks * d_idx, d_idx,
                              stream));
+  return QSA_OK;
+}
+
+// List entries of the fused selection's largest chunk: rows x pieces x piece capacity.
+size_t fused_list_bytes(int64_t lq, int64_t rc) {
+  const int64_t last = lq % rc == 0 ? rc : lq % rc;
+  const int64_t a = rc * qsa::fused_n_split(rc), b = last * qsa::fused_n_split(last);
+  return (size_t)(a > b ? a : b) * qsa::kFusedListCap * sizeof(uint64_t);
+}
+
+}  // namespace
+
+qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx, int d_idx,
+                              int r, int budget_tokens, const void* q_idx, const float* w,
+                              const void* k_idx, int64_t first_raw_token,
+                              const void* k_pooled_prefix, void* k_pooled, int32_t* sel,
+                              int64_t row_chunk, void* workspace, size_t workspace_bytes,
+                              const qsa_pooled_pe* pe, void* stream) {
+  const size_t need = qsa_prefill_workspace_bytes(lq, lk, r, budget_tokens, row_chunk);
+  QSA_TRY(prefill_pool(lq, lk, q_pos0, h_idx, d_idx, r, budget_tokens, k_idx, first_raw_token,
+                       k_pooled_prefix, k_pooled, pe, need, workspace, workspace_bytes, stream));
   if (lq == 0) return QSA_OK;
+  const int64_t nblk = lk / r;
+  const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
   const int64_t ld = score_ld(nblk);
   float* sc = static_cast<float*>(workspace);
   const size_t sc_bytes = align256((size_t)rc * (size_t)ld * sizeof(float));
@@ -665,6 +688,80 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
     QSA_TRY(qsa_topk_blocks(1, n, r, budget_tokens, sc, ld, 0, nblk, q_pos0 + c0, nullptr,
                             sel + c0 * n_sel, static_cast<char*>(workspace) + sc_bytes,
                             workspace_bytes - sc_bytes, stream));
+  }
+  return QSA_OK;
+}
+
+size_t qsa_prefill_fused_workspace_bytes(int64_t lq, int64_t lk, int r, int budget_tokens,
+                                         int64_t row_chunk) {
+  if (lq <= 0 || lk <= 0 || r <= 0) return 0;
+  const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
+  return align256((size_t)rc * (size_t)score_ld(lk / r) * sizeof(float)) +
+         align256(fused_list_bytes(lq, rc)) + align256((size_t)rc * 4 * sizeof(int32_t)) +
+         align256((size_t)rc * sizeof(int32_t));
+}
+
+qsa_status qsa_prefill_select_fused(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
+                                    int d_idx, int r, int budget_tokens, const void* q_idx,
+                                    const float* w, const void* k_idx, int64_t first_raw_token,
+                                    const void* k_pooled_prefix, void* k_pooled, int32_t* sel,
+                                    int64_t row_chunk, void* workspace, size_t workspace_bytes,
+                                    const qsa_pooled_pe* pe, const qsa_fused_tuning* tuning,
+                                    void* stream) {
+  const int64_t nblk = lk / r > 0 ? lk / r : 0;
+  QSA_REQUIRE(nblk < ((int64_t)1 << 24), QSA_ERR_UNSUPPORTED,
+              "%lld blocks: the fused selection takes fewer than 2^24", (long long)nblk);
+  const int n_sel = r > 0 ? budget_tokens / r : 0;
+  qsa_fused_tuning tn{2 * (n_sel > 1 ? n_sel - 1 : 1), 32, qsa::kFusedListCap};
+  if (tuning) {
+    if (tuning->target > 0) tn.target = tuning->target;
+    if (tuning->sample_k > 0) tn.sample_k = tuning->sample_k;
+    if (tuning->cap > 0) tn.cap = tuning->cap;
+  }
+  QSA_REQUIRE(tn.cap <= qsa::kFusedListCap, QSA_ERR_UNSUPPORTED, "cap=%d: at most %d", tn.cap,
+              qsa::kFusedListCap);
+  const size_t need = qsa_prefill_fused_workspace_bytes(lq, lk, r, budget_tokens, row_chunk);
+  QSA_TRY(prefill_pool(lq, lk, q_pos0, h_idx, d_idx, r, budget_tokens, k_idx, first_raw_token,
+                       k_pooled_prefix, k_pooled, pe, need, workspace, workspace_bytes, stream));
+  if (lq == 0) return QSA_OK;
+  QSA_REQUIRE(q_idx && w && sel && aligned16(q_idx), QSA_ERR_INVALID_ARGUMENT,
+              "null or misaligned q_idx, w or sel");
+  const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
+  const int64_t ld = score_ld(nblk);
+  char* ws = static_cast<char*>(workspace);
+  float* sc = reinterpret_cast<float*>(ws);
+  ws += align256((size_t)rc * (size_t)ld * sizeof(float));
+  uint64_t* lists = reinterpret_cast<uint64_t*>(ws);
+  ws += align256(fused_list_bytes(lq, rc));
+  int32_t* counts = reinterpret_cast<int32_t*>(ws);
+  ws += align256((size_t)rc * 4 * sizeof(int32_t));
+  int32_t* flags = reinterpret_cast<int32_t*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t c0 = 0; c0 < lq; c0 += rc) {
+    const int64_t n = (lq - c0) < rc ? (lq - c0) : rc;
+    qsa::FusedSelArgs f{};
+    f.q_idx = static_cast<const uint16_t*>(q_idx) + c0 * h_idx * d_idx;
+    f.w = w + c0 * h_idx;
+    f.kp = static_cast<const uint16_t*>(k_pooled);
+    f.nblk = nblk;
+    f.lq = n;
+    f.q_pos0 = q_pos0 + c0;
+    f.h_idx = h_idx;
+    f.d_idx = d_idx;
+    f.r = r;
+    f.n_sel = n_sel;
+    f.lists = lists;
+    f.counts = counts;
+    f.flags = flags;
+    f.n_split = qsa::fused_n_split(n);
+    f.split_cap = qsa::kFusedListCap;
+    f.cap = tn.cap;
+    f.target = tn.target;
+    f.sample_k = tn.sample_k;
+    f.scores = sc;
+    f.ld = ld;
+    f.sel = sel + c0 * n_sel;
+    QSA_TRY(hip_status(qsa::launch_select_fused(f, s), "fused selection launch"));
   }
   return QSA_OK;
 }

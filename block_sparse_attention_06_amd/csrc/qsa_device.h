@@ -39,6 +39,16 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(const uint2& a, const uint2& b, f
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+// One block score from the 4 per-head dot products of a token (MFMA accumulator
+// lanes): sum_h w_h * max(0, dot_h), always in this order, so that every kernel that
+// scores blocks produces the same fp32 value.
+__device__ __forceinline__ float score_of_heads(const float (&W)[4], const f32x4& acc) {
+  float s = W[0] * fmaxf(acc[0], 0.f);
+  s = fmaf(W[1], fmaxf(acc[1], 0.f), s);
+  s = fmaf(W[2], fmaxf(acc[2], 0.f), s);
+  return fmaf(W[3], fmaxf(acc[3], 0.f), s);
+}
+
 // Order-preserving map of a finite fp32 to uint32 (larger float -> larger key),
 // with -0.0 folded onto +0.0 so that the two compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {

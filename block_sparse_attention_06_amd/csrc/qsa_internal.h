@@ -84,8 +84,44 @@ struct ScoreArgs {
   int batch;
   TopkCandidates cand;  // optional (few rows per sequence): also emit segment candidates
   Varlen vl;            // packed sequences: q_idx / w rows packed, kp and scores per sequence
+  // optional [lq]: only the 64-row tiles holding a row whose flag is set are scored (the
+  // exact fallback of the fused selection); always the GEMM kernel
+  const int32_t* row_flags;
 };
 hipError_t launch_index_scores(const ScoreArgs& a, hipStream_t stream);
+
+// ---- stages 2 + 3 fused (prefill): scores go to short per-row lists, not to memory ----
+// Per row of a chunk: a threshold from a strided sample of its blocks' scores, then
+// every score at or above it appended (ascending block id) to the row's list; the m
+// best are selected from the list. Rows whose list came out shorter than m or longer
+// than the capacity are flagged and selected exactly from materialised scores.
+constexpr int kFusedListCap = 2048;  // list entries a row may hold in all (select in registers)
+struct FusedSelArgs {
+  const uint16_t* q_idx;  // the chunk's row 0: [lq][h_idx][d_idx]
+  const float* w;         // [lq][h_idx]
+  const uint16_t* kp;     // pooled keys [nblk][d_idx]
+  int64_t nblk;
+  int64_t lq;             // rows of the chunk
+  int64_t q_pos0;         // position of the chunk's row 0
+  int h_idx;
+  int d_idx;
+  int r;
+  int n_sel;
+  uint64_t* lists;        // [lq][n_split][split_cap] ranks (score key << 24 | 0xffffff - id)
+  int32_t* counts;        // [lq][n_split]
+  int32_t* flags;         // [lq]: 1 where the fallback selects
+  int n_split;            // key-range pieces of a row tile (one workgroup each)
+  int split_cap;          // entries a (row, piece) list holds
+  int cap;                // entries a row's lists may hold in all (<= kFusedListCap)
+  int target;             // list entries a row aims at
+  int sample_k;           // the threshold is about the sample_k-th best sampled score
+  float* scores;          // fallback: [lq][ld]
+  int64_t ld;
+  int32_t* sel;           // the chunk's selection rows [lq][n_sel]
+};
+// Pieces per row tile for a chunk of lq rows (enough workgroups to fill the device).
+int fused_n_split(int64_t lq);
+hipError_t launch_select_fused(const FusedSelArgs& f, hipStream_t stream);
 
 // ---- stage 3 ----
 struct TopkArgs {

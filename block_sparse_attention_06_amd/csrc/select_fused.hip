@@ -1,0 +1,414 @@
+// Stages 2 and 3 of QSA fused for prefill rows: the block scores of a row never go to
+// memory whole; only the scores that can still be among the row's best do.
+//
+// Method ("On the Design of Qwen3.8-Next Architecture", item 2 QSA: the light indexer
+// scores micro-blocks of r = 4 tokens and the query keeps the best ones up to its token
+// budget; "Qwen3.8-Flash-Next开源", section GDN+QSA: finding the important context is
+// a cost of its own). The selection is the same as the two-kernel path's (the m best
+// earlier blocks by score, then block id; own block kept), on the very same fp32 scores
+// (score_of_heads), so the kept ids are identical.
+//
+// Per chunk of rows, four launches:
+//  1. score_list_kernel: a workgroup takes 64 rows and one piece of their block range.
+//     It first scores a strided sample of the rows' blocks (one in about
+//     lim * sample_k / target) and sets each row's threshold at about the sample_k-th
+//     best sampled score, which about `target` of the row's scores reach. It then
+//     scores the piece on MFMA as the plain GEMM does and appends every score at or
+//     above the threshold to the (row, piece) list as a rank (score key, then id): the
+//     16 lanes that hold a row's scores place their entries by ballot prefix counts,
+//     so a list is in ascending block-id order and no atomics are needed.
+//  2. list_select_kernel: one wave per row. A row whose candidates all fit keeps them;
+//     otherwise, if its lists hold at least m and at most the capacity in all, they
+//     hold the row's m best (every score that is not in them is below the threshold,
+//     below each of at least m listed ones); a radix select on the ranks finds the
+//     m-th and the listed ranks at or above it are written in list order (ascending
+//     ids). Other rows are flagged.
+//  3. The plain score GEMM, only on 64-row tiles that hold a flagged row.
+//  4. fallback_select_kernel: one wave per flagged row, an exact radix select streamed
+//     over its materialised scores.
+
+#include "qsa_device.h"
+#include "qsa_internal.h"
+#include "qsa_wave.h"
+
+namespace qsa {
+
+namespace {
+
+constexpr int kFsRows = 64;    // query rows per workgroup (4 waves x 16)
+constexpr int kFsTileN = 64;   // pooled keys per LDS tile
+constexpr int kFsTopR = 4;     // sampled keys a lane keeps per row
+constexpr int kFsIdBits = 24;  // block ids in a rank (ids < 2^24)
+constexpr int kFsRankBits = 32 + kFsIdBits;
+constexpr uint32_t kFsIdMask = (1u << kFsIdBits) - 1u;
+constexpr int kLsSlots = kFusedListCap / kWave;
+
+// Rank of a (score, id) pair: larger ranks earlier (score descending, then id
+// ascending); 0 is no entry.
+__device__ __forceinline__ uint64_t fs_rank(float v, int64_t id) {
+  return ((uint64_t)order_key(v) << kFsIdBits) | (uint64_t)(kFsIdMask - (uint32_t)id);
+}
+
+__device__ __forceinline__ int fs_rank_id(uint64_t rk) {
+  return (int)(kFsIdMask - (uint32_t)(rk & kFsIdMask));
+}
+
+// Sum over the 16 lanes of this lane's quad group (lanes 16q .. 16q + 15).
+__device__ __forceinline__ int group16_sum(int x) {
+  x += __shfl_xor(x, 1, kWave);
+  x += __shfl_xor(x, 2, kWave);
+  x += __shfl_xor(x, 4, kWave);
+  x += __shfl_xor(x, 8, kWave);
+  return x;
+}
+
+template <int DI>
+__global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
+  constexpr int NC = DI / 32;
+  constexpr int ROW = DI + 8;  // LDS row in bf16 elements, padded by 16 B
+  constexpr int VPR = DI / 8;
+  constexpr int LPT = kFsTileN * VPR / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kFsTileN * ROW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c16 = lane & 15;
+  const int quad = lane >> 4;
+  const int64_t n_tiles = (f.lq + kFsRows - 1) / kFsRows;
+  const int64_t i0 = (n_tiles - 1 - (int64_t)blockIdx.x) * kFsRows;  // longest rows first
+  const int split = blockIdx.y;
+  const int64_t t_last = f.q_pos0 + min(i0 + kFsRows - 1, f.lq - 1);
+  const int64_t nb_need = min(t_last / f.r, f.nblk);
+
+  // Per accumulator row of this lane: token (mt*4 + quad) of the wave's 16.
+  float W[4][4];
+  int lim[4];   // candidates of the token (blocks < 2^24)
+  int tokv[4];  // the token's row in the chunk, -1 past its end
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int64_t tok = i0 + wave * 16 + mt * 4 + quad;
+    const bool valid = tok < f.lq;
+    tokv[mt] = valid ? (int)tok : -1;
+    lim[mt] = valid ? (int)min((f.q_pos0 + tok) / f.r, f.nblk) : 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) W[mt][h] = (valid && h < f.h_idx) ? f.w[tok * f.h_idx + h] : 0.f;
+  }
+  int cnt[4] = {0, 0, 0, 0};
+  if (nb_need > 0) {
+    const int64_t n_begin = (nb_need * split / f.n_split) / kFsTileN * kFsTileN;
+    const int64_t n_end = split + 1 == f.n_split
+                              ? nb_need
+                              : (nb_need * (split + 1) / f.n_split) / kFsTileN * kFsTileN;
+    // A operands: this wave's 16 tokens as 4 M-tiles of (4 tokens x 4 heads).
+    uint4 A[4][NC];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int64_t tok = i0 + wave * 16 + mt * 4 + (c16 >> 2);
+      const int h = c16 & 3;
+      const bool ok = tok < f.lq && h < f.h_idx;
+      const uint16_t* p = f.q_idx + (tok * f.h_idx + h) * DI + quad * 8;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) A[mt][c] = ok ? ld16(p + c * 32) : make_uint4(0, 0, 0, 0);
+    }
+    uint4 stage[LPT];
+    // Tile rows from a map row -> block (< 0: zero row).
+    auto load_rows = [&](auto&& blk_of) {
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        const int v = threadIdx.x + 256 * u;
+        const int row = v / VPR, cv = v - row * VPR;
+        const int64_t blk = blk_of(row);
+        stage[u] = (blk >= 0 && blk < f.nblk) ? ld16(f.kp + blk * DI + cv * 8)
+                                              : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        const int v = threadIdx.x + 256 * u;
+        const int row = v / VPR, cv = v - row * VPR;
+        *reinterpret_cast<uint4*>(&tile[buf][row * ROW + cv * 8]) = stage[u];
+      }
+    };
+    // acc[mt][j]: token (mt, quad), tile row 4*c16 + j.
+    auto multiply = [&](const uint16_t* tb, f32x4 (&acc)[4][4]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint4 B[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          B[c] = *reinterpret_cast<const uint4*>(&tb[(4 * c16 + j) * ROW + c * 32 + quad * 8]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[mt][j] = mfma_16x16x32(A[mt][c], B[c], acc[mt][j]);
+        }
+      }
+    };
+
+    // 1. Thresholds from a strided sample (rows whose candidates all fit admit all).
+    float thr[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (nb_need > f.cap) {
+      const int64_t want = ((int64_t)f.sample_k * nb_need + f.target - 1) / f.target;
+      const int64_t S = min(nb_need, (want + kFsTileN - 1) / kFsTileN * kFsTileN);
+      const int n_st = (int)((S + kFsTileN - 1) / kFsTileN);
+      auto sample_blk = [&](int64_t i) -> int64_t { return i < S ? (i * nb_need) / S : -1; };
+      uint32_t top[4][kFsTopR];
+      int nv[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q = 0; q < kFsTopR; ++q) top[mt][q] = 0u;
+      load_rows([&](int row) { return sample_blk(row); });
+      store_tile(0);
+      __syncthreads();
+      for (int st = 0; st < n_st; ++st) {
+        const bool more = st + 1 < n_st;
+        if (more) load_rows([&](int row) { return sample_blk((int64_t)(st + 1) * kFsTileN + row); });
+        f32x4 acc[4][4];
+        multiply(tile[st & 1], acc);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t b = sample_blk((int64_t)st * kFsTileN + 4 * c16 + j);
+            if (b >= 0 && b < lim[mt]) {
+              uint32_t x = order_key(score_of_heads(W[mt], acc[mt][j]));
+              ++nv[mt];
+#pragma unroll
+              for (int q = 0; q < kFsTopR; ++q) {  // keep the kFsTopR largest, sorted
+                const uint32_t hi = max(top[mt][q], x);
+                x = min(top[mt][q], x);
+                top[mt][q] = hi;
+              }
+            }
+          }
+        if (more) store_tile((st + 1) & 1);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int nvg = group16_sum(nv[mt]);
+        int kept = 0;
+#pragma unroll
+        for (int q = 0; q < kFsTopR; ++q) kept += top[mt][q] != 0u;
+        kept = group16_sum(kept);
+        if (lim[mt] > f.cap && kept > 0) {
+          // about `target` of the lim scores reach the k-th best of the nvg sampled
+          int64_t k = ((int64_t)nvg * f.target + lim[mt] - 1) / lim[mt];
+          k = k < 1 ? 1 : (k > kept ? kept : k);  // fewer kept: a lower threshold
+          uint32_t pre = 0u;
+          for (int b = 31; b >= 0; --b) {
+            const uint32_t cand = pre | (1u << b);
+            int c = 0;
+#pragma unroll
+            for (int q = 0; q < kFsTopR; ++q) c += top[mt][q] >= cand;
+            if (group16_sum(c) >= k) pre = cand;
+          }
+          thr[mt] = key_to_float(pre);  // the key of a sampled score
+        }
+      }
+    }
+
+    // 2. The piece's scores; those at or above the threshold go to the lists.
+    const int n_main = (int)((n_end - n_begin + kFsTileN - 1) / kFsTileN);
+    if (n_main > 0) {
+      load_rows([&](int row) { return n_begin + row < n_end ? n_begin + row : (int64_t)-1; });
+      store_tile(0);
+      __syncthreads();
+      for (int it = 0; it < n_main; ++it) {
+        const int64_t n0 = n_begin + (int64_t)it * kFsTileN;
+        const bool more = it + 1 < n_main;
+        if (more)
+          load_rows([&](int row) {
+            const int64_t b = n0 + kFsTileN + row;
+            return b < n_end ? b : (int64_t)-1;
+          });
+        f32x4 acc[4][4];
+        multiply(tile[it & 1], acc);
+        const int64_t blk0 = n0 + 4 * c16;
+        const uint64_t gm = 0xffffull << (16 * quad);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          float sv[4];
+          bool fl[4];
+          int k = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sv[j] = score_of_heads(W[mt], acc[mt][j]);
+            fl[j] = blk0 + j < lim[mt] && blk0 + j < n_end && sv[j] >= thr[mt];
+            k += fl[j];
+          }
+          if (__ballot(k > 0) == 0ull) continue;
+          const uint64_t b0 = __ballot(k & 1) & gm, b1 = __ballot(k & 2) & gm,
+                         b2 = __ballot(k & 4) & gm;
+          int p = cnt[mt] + lane_prefix(b0) + 2 * lane_prefix(b1) + 4 * lane_prefix(b2);
+          if (k > 0) {
+            uint64_t* lrow = f.lists + ((int64_t)tokv[mt] * f.n_split + split) * f.split_cap;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (fl[j]) {
+                if (p < f.split_cap) lrow[p] = fs_rank(sv[j], blk0 + j);
+                ++p;
+              }
+          }
+          cnt[mt] += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+        }
+        if (more) store_tile((it + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+    if (c16 == 0 && tokv[mt] >= 0) f.counts[(int64_t)tokv[mt] * f.n_split + split] = cnt[mt];
+}
+
+__global__ __launch_bounds__(256) void list_select_kernel(FusedSelArgs f) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= f.lq) return;
+  const int64_t own = (f.q_pos0 + row) / f.r;
+  const int64_t lim = min(own, f.nblk);
+  int32_t* srow = f.sel + row * f.n_sel;
+  const int m = f.n_sel - 1;
+  if (lim <= m) {  // every candidate is kept
+    for (int k = lane; k < f.n_sel; k += kWave) srow[k] = k < lim ? k : (k == lim ? (int)own : -1);
+    if (lane == 0) f.flags[row] = 0;
+    return;
+  }
+  int off[5];
+  off[0] = 0;
+  bool bad = false;
+  for (int sp = 0; sp < f.n_split; ++sp) {
+    const int c = f.counts[row * f.n_split + sp];
+    bad |= c > f.split_cap;
+    off[sp + 1] = off[sp] + c;
+  }
+  const int total = off[f.n_split];
+  if (bad || total < m || total > f.cap) {
+    if (lane == 0) f.flags[row] = 1;
+    return;
+  }
+  uint64_t rk[kLsSlots];
+#pragma unroll
+  for (int j = 0; j < kLsSlots; ++j) {
+    const int p = j * kWave + lane;
+    rk[j] = 0ull;
+    if (p < total) {
+      int sp = 0;
+      while (sp + 1 < f.n_split && p >= off[sp + 1]) ++sp;
+      rk[j] = f.lists[(row * f.n_split + sp) * f.split_cap + (p - off[sp])];
+    }
+  }
+  int pb;
+  const uint64_t pre = wave_radix_select<kFsRankBits>(
+      hist[wave], (uint32_t)m,
+      [&](auto&& fn) {
+#pragma unroll
+        for (int j = 0; j < kLsSlots; ++j)
+          if (rk[j]) fn(rk[j]);
+      },
+      pb);
+  uint32_t written = 0;
+#pragma unroll
+  for (int j = 0; j < kLsSlots; ++j) {
+    const bool kp = rk[j] != 0ull && (rk[j] >> (kFsRankBits - pb)) >= pre;
+    const uint64_t b = __ballot(kp);
+    const uint32_t p = written + (uint32_t)lane_prefix(b);
+    if (kp && p < (uint32_t)m) srow[p] = fs_rank_id(rk[j]);
+    written += (uint32_t)__popcll(b);
+  }
+  for (int k = m + lane; k < f.n_sel; k += kWave) srow[k] = k == m ? (int)own : -1;
+  if (lane == 0) f.flags[row] = 0;
+}
+
+__global__ __launch_bounds__(256) void fallback_select_kernel(FusedSelArgs f) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= f.lq || f.flags[row] == 0) return;
+  const int64_t own = (f.q_pos0 + row) / f.r;
+  const int n = (int)min(own, f.nblk);  // > m here
+  const int m = f.n_sel - 1;
+  const float* srow_s = f.scores + row * f.ld;
+  int32_t* srow = f.sel + row * f.n_sel;
+  // Lane's float4 of the 256 scores at base (clamped into the row; ids >= n absent).
+  auto load4 = [&](int base) {
+    const int i = min(base + 4 * lane, (n - 1) & ~3);
+    return *reinterpret_cast<const float4*>(srow_s + i);
+  };
+  int pb;
+  const uint64_t pre = wave_radix_select<kFsRankBits>(
+      hist[wave], (uint32_t)m,
+      [&](auto&& fn) {
+        for (int base = 0; base < n; base += 4 * kWave) {
+          const float4 v = load4(base);
+          const float xs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (base + 4 * lane + e < n) fn(fs_rank(xs[e], base + 4 * lane + e));
+        }
+      },
+      pb);
+  uint32_t written = 0;
+  for (int base = 0; base < n; base += 4 * kWave) {
+    const float4 v = load4(base);
+    const float xs[4] = {v.x, v.y, v.z, v.w};
+    bool fl[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int id = base + 4 * lane + e;
+      fl[e] = id < n && (fs_rank(xs[e], id) >> (kFsRankBits - pb)) >= pre;
+    }
+    written += wave_append4(fl, written, [&](uint32_t p, int e) {
+      if (p < (uint32_t)m) srow[p] = base + 4 * lane + e;
+    });
+  }
+  for (int k = m + lane; k < f.n_sel; k += kWave) srow[k] = k == m ? (int)own : -1;
+}
+
+}  // namespace
+
+int fused_n_split(int64_t lq) {
+  const int64_t tiles = (lq + kFsRows - 1) / kFsRows;
+  const int64_t ns = 512 / (tiles > 0 ? tiles : 1);
+  return (int)(ns < 1 ? 1 : (ns > 4 ? 4 : ns));
+}
+
+hipError_t launch_select_fused(const FusedSelArgs& f, hipStream_t stream) {
+  if (f.lq <= 0) return hipSuccess;
+  if (f.n_split < 1 || f.n_split > 4 || f.cap > kFusedListCap || f.nblk >= (1 << kFsIdBits) ||
+      f.target < 1 || f.sample_k < 1 || f.split_cap < 1)
+    return hipErrorInvalidValue;
+  const int64_t tiles = (f.lq + kFsRows - 1) / kFsRows;
+  const dim3 g1((unsigned)tiles, (unsigned)f.n_split);
+  if (f.d_idx == 128)
+    hipLaunchKernelGGL(score_list_kernel<128>, g1, dim3(256), 0, stream, f);
+  else
+    hipLaunchKernelGGL(score_list_kernel<64>, g1, dim3(256), 0, stream, f);
+  const dim3 gr((unsigned)((f.lq + 3) / 4));
+  hipLaunchKernelGGL(list_select_kernel, gr, dim3(256), 0, stream, f);
+  ScoreArgs sa{};
+  sa.q_idx = f.q_idx;
+  sa.w = f.w;
+  sa.kp = f.kp;
+  sa.nblk = f.nblk;
+  sa.lq = f.lq;
+  sa.h_idx = f.h_idx;
+  sa.d_idx = f.d_idx;
+  sa.r = f.r;
+  sa.q_pos0 = f.q_pos0;
+  sa.scores = f.scores;
+  sa.ld = f.ld;
+  sa.batch = 1;
+  sa.row_flags = f.flags;
+  const hipError_t e = launch_index_scores(sa, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fallback_select_kernel, gr, dim3(256), 0, stream, f);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

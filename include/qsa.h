@@ -296,6 +296,37 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
                               const qsa_pooled_pe* pe, void* stream);
 
 /*
+ * Stages 2 + 3 fused (prefill): the same selection as qsa_prefill_select, bit for
+ * bit (the same fp32 scores, the same exact top-k and tie rule), without writing the
+ * whole score matrix. Per row, a strided sample of its blocks' scores sets a threshold
+ * about `target` of the row's scores reach; the scoring pass appends only the scores
+ * at or above it to a short per-row list, and the m = K/r - 1 best are selected from
+ * the list. A list that came out shorter than m or longer than `cap` makes that row
+ * fall back to materialised scores and an exact select (the same result, slower).
+ * ("On the Design of Qwen3.8-Next Architecture", item 2 QSA: the indexer rates
+ * micro-blocks and each query keeps the best up to its budget; the release article's
+ * GDN+QSA section counts finding the important context as a cost of its own.)
+ * Arguments as qsa_prefill_select; blocks (lk / r) must be fewer than 2^24. tuning may
+ * be NULL (defaults: target 2 (K/r - 1), sample_k 32, cap 2048); a field <= 0 takes
+ * its default; cap <= 2048. The workspace holds one chunk's scores (for the fallback),
+ * its lists, counts and flags: qsa_prefill_fused_workspace_bytes().
+ */
+typedef struct qsa_fused_tuning {
+  int target;    /* list entries a row aims at */
+  int sample_k;  /* the threshold is about the sample_k-th best sampled score */
+  int cap;       /* most list entries a row may hold before it falls back */
+} qsa_fused_tuning;
+size_t qsa_prefill_fused_workspace_bytes(int64_t lq, int64_t lk, int r, int budget_tokens,
+                                         int64_t row_chunk);
+qsa_status qsa_prefill_select_fused(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
+                                    int d_idx, int r, int budget_tokens, const void* q_idx,
+                                    const float* w, const void* k_idx, int64_t first_raw_token,
+                                    const void* k_pooled_prefix, void* k_pooled, int32_t* sel,
+                                    int64_t row_chunk, void* workspace, size_t workspace_bytes,
+                                    const qsa_pooled_pe* pe, const qsa_fused_tuning* tuning,
+                                    void* stream);
+
+/*
  * Whole prefill path: qsa_prefill_select followed by qsa_sparse_attn_fwd on the same
  * stream. Arguments as in those two calls.
  */

@@ -269,3 +269,21 @@ def test_decode_noalloc_rejects_sizes_beyond_its_scratch(lib):
                                           *tail) == 2  # r = 3
     assert "r=3" in _err(lib)
 
+
+
+def test_fused_selection_validation(lib):
+    from block_sparse_attention_06_amd.ops import _FusedTuning
+
+    def call(lq=64, lk=64, tuning=None, ws_bytes=1 << 40, budget=256):
+        tp = None if tuning is None else ctypes.byref(tuning)
+        return lib.qsa_prefill_select_fused(lq, lk, 0, 4, 128, 4, budget, FAKE, FAKE, FAKE, 0,
+                                            None, FAKE, FAKE, 64, FAKE, ws_bytes, None, tp, None)
+
+    assert call(tuning=_FusedTuning(0, 0, 4096)) == 2 and "cap" in _err(lib)
+    assert call(lk=4 << 24) == 2 and "2^24" in _err(lib)
+    assert call(budget=258) == 1
+    need = lib.qsa_prefill_fused_workspace_bytes(64, 64, 4, 256, 64)
+    # one chunk of scores, lists of 2048 entries per row and piece, counts, flags
+    assert need >= 64 * 16 * 4 + 64 * 2048 * 8
+    assert call(ws_bytes=need - 1) == 3 and "workspace" in _err(lib)
+    assert lib.qsa_prefill_fused_workspace_bytes(0, 64, 4, 256, 64) == 0
