@@ -335,37 +335,51 @@ __global__ __launch_bounds__(256) void fallback_select_kernel(FusedSelArgs f) {
   const int m = f.n_sel - 1;
   const float* srow_s = f.scores + row * f.ld;
   int32_t* srow = f.sel + row * f.n_sel;
-  // Lane's float4 of the 256 scores at base (clamped into the row; ids >= n absent).
-  auto load4 = [&](int base) {
-    const int i = min(base + 4 * lane, (n - 1) & ~3);
-    return *reinterpret_cast<const float4*>(srow_s + i);
+  // The row streams in chunks of 8 float4 per lane (2048 scores), every load issued
+  // before any is used; loads are clamped into the row (ids >= n are absent).
+  constexpr int kVec = 8;
+  constexpr int kChunk = 4 * kWave * kVec;
+  auto load_chunk = [&](int c0, float4 (&v)[kVec]) {
+#pragma unroll
+    for (int q = 0; q < kVec; ++q) {
+      const int i = min(c0 + (q * kWave + lane) * 4, (n - 1) & ~3);
+      v[q] = *reinterpret_cast<const float4*>(srow_s + i);
+    }
   };
   int pb;
   const uint64_t pre = wave_radix_select<kFsRankBits>(
       hist[wave], (uint32_t)m,
       [&](auto&& fn) {
-        for (int base = 0; base < n; base += 4 * kWave) {
-          const float4 v = load4(base);
-          const float xs[4] = {v.x, v.y, v.z, v.w};
+        for (int c0 = 0; c0 < n; c0 += kChunk) {
+          float4 v[kVec];
+          load_chunk(c0, v);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (base + 4 * lane + e < n) fn(fs_rank(xs[e], base + 4 * lane + e));
+          for (int q = 0; q < kVec; ++q) {
+            const int i = c0 + (q * kWave + lane) * 4;
+            const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (i + e < n) fn(fs_rank(xs[e], i + e));
+          }
         }
       },
       pb);
   uint32_t written = 0;
-  for (int base = 0; base < n; base += 4 * kWave) {
-    const float4 v = load4(base);
-    const float xs[4] = {v.x, v.y, v.z, v.w};
-    bool fl[4];
+  for (int c0 = 0; c0 < n; c0 += kChunk) {
+    float4 v[kVec];
+    load_chunk(c0, v);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int id = base + 4 * lane + e;
-      fl[e] = id < n && (fs_rank(xs[e], id) >> (kFsRankBits - pb)) >= pre;
+    for (int q = 0; q < kVec; ++q) {
+      const int i = c0 + (q * kWave + lane) * 4;
+      const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+      bool fl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        fl[e] = i + e < n && (fs_rank(xs[e], i + e) >> (kFsRankBits - pb)) >= pre;
+      written += wave_append4(fl, written, [&](uint32_t p, int e) {
+        if (p < (uint32_t)m) srow[p] = i + e;
+      });
     }
-    written += wave_append4(fl, written, [&](uint32_t p, int e) {
-      if (p < (uint32_t)m) srow[p] = base + 4 * lane + e;
-    });
   }
   for (int k = m + lane; k < f.n_sel; k += kWave) srow[k] = k == m ? (int)own : -1;
 }
