@@ -697,7 +697,7 @@ size_t qsa_prefill_fused_workspace_bytes(int64_t lq, int64_t lk, int r, int budg
   if (lq <= 0 || lk <= 0 || r <= 0) return 0;
   const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
   return align256((size_t)rc * (size_t)score_ld(lk / r) * sizeof(float)) +
-         align256(fused_list_bytes(lq, rc)) + align256((size_t)rc * 4 * sizeof(int32_t)) +
+         align256(fused_list_bytes(lq, rc)) + align256((size_t)rc * 4 * 16 * sizeof(int32_t)) +
          align256((size_t)rc * sizeof(int32_t));
 }
 
@@ -734,7 +734,7 @@ qsa_status qsa_prefill_select_fused(int64_t lq, int64_t lk, int64_t q_pos0, int 
   uint64_t* lists = reinterpret_cast<uint64_t*>(ws);
   ws += align256(fused_list_bytes(lq, rc));
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
-  ws += align256((size_t)rc * 4 * sizeof(int32_t));
+  ws += align256((size_t)rc * 4 * 16 * sizeof(int32_t));
   int32_t* flags = reinterpret_cast<int32_t*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int64_t c0 = 0; c0 < lq; c0 += rc) {
@@ -754,7 +754,7 @@ qsa_status qsa_prefill_select_fused(int64_t lq, int64_t lk, int64_t q_pos0, int 
     f.counts = counts;
     f.flags = flags;
     f.n_split = qsa::fused_n_split(n);
-    f.split_cap = qsa::kFusedListCap;
+    f.lane_cap = qsa::kFusedListCap / 16;  // 16 lane lists of a (row, piece): 2048 in all
     f.cap = tn.cap;
     f.target = tn.target;
     f.sample_k = tn.sample_k;

@@ -107,11 +107,11 @@ struct FusedSelArgs {
   int d_idx;
   int r;
   int n_sel;
-  uint64_t* lists;        // [lq][n_split][split_cap] ranks (score key << 24 | 0xffffff - id)
-  int32_t* counts;        // [lq][n_split]
+  uint64_t* lists;        // [lq][n_split][16][lane_cap] ranks (score key << 24 | 0xffffff - id)
+  int32_t* counts;        // [lq][n_split][16]
   int32_t* flags;         // [lq]: 1 where the fallback selects
   int n_split;            // key-range pieces of a row tile (one workgroup each)
-  int split_cap;          // entries a (row, piece) list holds
+  int lane_cap;           // entries a (row, piece, lane) list holds
   int cap;                // entries a row's lists may hold in all (<= kFusedListCap)
   int target;             // list entries a row aims at
   int sample_k;           // the threshold is about the sample_k-th best sampled score

@@ -10,19 +10,19 @@
 //
 // Per chunk of rows, four launches:
 //  1. score_list_kernel: a workgroup takes 64 rows and one piece of their block range.
-//     It first scores a strided sample of the rows' blocks (one in about
+//     It first scores an evenly strided sample of the rows' blocks (one in about
 //     lim * sample_k / target) and sets each row's threshold at about the sample_k-th
 //     best sampled score, which about `target` of the row's scores reach. It then
-//     scores the piece on MFMA as the plain GEMM does and appends every score at or
-//     above the threshold to the (row, piece) list as a rank (score key, then id): the
-//     16 lanes that hold a row's scores place their entries by ballot prefix counts,
-//     so a list is in ascending block-id order and no atomics are needed.
+//     scores the piece on MFMA as the plain GEMM does, and each of the 16 lanes that
+//     hold a row's scores appends its own scores at or above the threshold to a list of
+//     its own as ranks (score key, then id): no cross-lane bookkeeping, no atomics
+//     (placing entries by ballot prefix counts cost as much as the products).
 //  2. list_select_kernel: one wave per row. A row whose candidates all fit keeps them;
-//     otherwise, if its lists hold at least m and at most the capacity in all, they
-//     hold the row's m best (every score that is not in them is below the threshold,
-//     below each of at least m listed ones); a radix select on the ranks finds the
-//     m-th and the listed ranks at or above it are written in list order (ascending
-//     ids). Other rows are flagged.
+//     otherwise, if its lane lists hold at least m and at most the capacity in all,
+//     they hold the row's m best (every score that is not in them is below the
+//     threshold, below each of at least m listed ones). A radix select on the listed
+//     ranks finds the m-th; the kept ids go out ascending through an LDS bitmap over
+//     the row's blocks. Other rows are flagged.
 //  3. The plain score GEMM, only on 64-row tiles that hold a flagged row.
 //  4. fallback_select_kernel: one wave per flagged row, an exact radix select streamed
 //     over its materialised scores.
@@ -42,6 +42,8 @@ constexpr int kFsIdBits = 24;  // block ids in a rank (ids < 2^24)
 constexpr int kFsRankBits = 32 + kFsIdBits;
 constexpr uint32_t kFsIdMask = (1u << kFsIdBits) - 1u;
 constexpr int kLsSlots = kFusedListCap / kWave;
+constexpr int kFsLanes = 16;  // lanes holding one row's scores: one list each
+constexpr int kLsMapWords = 2048;  // bitmap words of a list-select wave (65536 blocks)
 
 // Rank of a (score, id) pair: larger ranks earlier (score descending, then id
 // ascending); 0 is no entry.
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) W[mt][h] = (valid && h < f.h_idx) ? f.w[tok * f.h_idx + h] : 0.f;
   }
-  int cnt[4] = {0, 0, 0, 0};
+  int cnt[4] = {0, 0, 0, 0};  // entries in this lane's list of each of its rows
   if (nb_need > 0) {
     const int64_t n_begin = (nb_need * split / f.n_split) / kFsTileN * kFsTileN;
     const int64_t n_end = split + 1 == f.n_split
@@ -151,9 +153,13 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
     float thr[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (nb_need > f.cap) {
       const int64_t want = ((int64_t)f.sample_k * nb_need + f.target - 1) / f.target;
-      const int64_t S = min(nb_need, (want + kFsTileN - 1) / kFsTileN * kFsTileN);
-      const int n_st = (int)((S + kFsTileN - 1) / kFsTileN);
-      auto sample_blk = [&](int64_t i) -> int64_t { return i < S ? (i * nb_need) / S : -1; };
+      const int S = (int)min(nb_need, (want + kFsTileN - 1) / kFsTileN * kFsTileN);
+      const int n_st = (S + kFsTileN - 1) / kFsTileN;
+      // sample i is block i * stride: evenly spaced over the first S * stride blocks, in
+      // 32-bit arithmetic (blocks < 2^24; a 64-bit division per sample cost as much as
+      // the whole scoring pass)
+      const int stride = (int)(nb_need / S);
+      auto sample_blk = [&](int i) -> int64_t { return i < S ? (int64_t)(i * stride) : -1; };
       uint32_t top[4][kFsTopR];
       int nv[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -165,14 +171,14 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
       __syncthreads();
       for (int st = 0; st < n_st; ++st) {
         const bool more = st + 1 < n_st;
-        if (more) load_rows([&](int row) { return sample_blk((int64_t)(st + 1) * kFsTileN + row); });
+        if (more) load_rows([&](int row) { return sample_blk((st + 1) * kFsTileN + row); });
         f32x4 acc[4][4];
         multiply(tile[st & 1], acc);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int64_t b = sample_blk((int64_t)st * kFsTileN + 4 * c16 + j);
+            const int64_t b = sample_blk(st * kFsTileN + 4 * c16 + j);
             if (b >= 0 && b < lim[mt]) {
               uint32_t x = order_key(score_of_heads(W[mt], acc[mt][j]));
               ++nv[mt];
@@ -228,7 +234,6 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
         f32x4 acc[4][4];
         multiply(tile[it & 1], acc);
         const int64_t blk0 = n0 + 4 * c16;
-        const uint64_t gm = 0xffffull << (16 * quad);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           float sv[4];
@@ -240,20 +245,18 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
             fl[j] = blk0 + j < lim[mt] && blk0 + j < n_end && sv[j] >= thr[mt];
             k += fl[j];
           }
-          if (__ballot(k > 0) == 0ull) continue;
-          const uint64_t b0 = __ballot(k & 1) & gm, b1 = __ballot(k & 2) & gm,
-                         b2 = __ballot(k & 4) & gm;
-          int p = cnt[mt] + lane_prefix(b0) + 2 * lane_prefix(b1) + 4 * lane_prefix(b2);
-          if (k > 0) {
-            uint64_t* lrow = f.lists + ((int64_t)tokv[mt] * f.n_split + split) * f.split_cap;
+          if (k > 0) {  // this lane's own list: ascending ids, no other lane involved
+            uint64_t* ll = f.lists +
+                           (((int64_t)tokv[mt] * f.n_split + split) * kFsLanes + c16) * f.lane_cap;
+            int p = cnt[mt];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               if (fl[j]) {
-                if (p < f.split_cap) lrow[p] = fs_rank(sv[j], blk0 + j);
+                if (p < f.lane_cap) ll[p] = fs_rank(sv[j], blk0 + j);
                 ++p;
               }
+            cnt[mt] = p;
           }
-          cnt[mt] += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
         }
         if (more) store_tile((it + 1) & 1);
         __syncthreads();
@@ -262,16 +265,18 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
   }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
-    if (c16 == 0 && tokv[mt] >= 0) f.counts[(int64_t)tokv[mt] * f.n_split + split] = cnt[mt];
+    if (tokv[mt] >= 0) f.counts[((int64_t)tokv[mt] * f.n_split + split) * kFsLanes + c16] = cnt[mt];
 }
 
 __global__ __launch_bounds__(256) void list_select_kernel(FusedSelArgs f) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[4][256];
+  // A wave's LDS area: the radix histogram, then a bitmap of the kept ids.
+  __shared__ __attribute__((aligned(16))) uint32_t area[4][kLsMapWords];
+  __shared__ int off_lds[4][kWave + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= f.lq) return;
   const int64_t own = (f.q_pos0 + row) / f.r;
-  const int64_t lim = min(own, f.nblk);
+  const int lim = (int)min(own, f.nblk);  // blocks < 2^24
   int32_t* srow = f.sel + row * f.n_sel;
   const int m = f.n_sel - 1;
   if (lim <= m) {  // every candidate is kept
@@ -279,47 +284,91 @@ __global__ __launch_bounds__(256) void list_select_kernel(FusedSelArgs f) {
     if (lane == 0) f.flags[row] = 0;
     return;
   }
-  int off[5];
-  off[0] = 0;
-  bool bad = false;
-  for (int sp = 0; sp < f.n_split; ++sp) {
-    const int c = f.counts[row * f.n_split + sp];
-    bad |= c > f.split_cap;
-    off[sp + 1] = off[sp] + c;
+  // Lane l holds the count of list l (lists: pieces x 16 lanes, <= 64).
+  const int n_lists = f.n_split * kFsLanes;
+  const int c = lane < n_lists ? f.counts[row * n_lists + lane] : 0;
+  int incl = c;  // inclusive prefix over the lanes
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
   }
-  const int total = off[f.n_split];
+  const int total = __shfl(incl, kWave - 1, kWave);
+  const bool bad = __ballot(c > f.lane_cap) != 0ull;
   if (bad || total < m || total > f.cap) {
     if (lane == 0) f.flags[row] = 1;
     return;
   }
+  int* off = off_lds[wave];
+  off[lane + 1] = incl;
+  if (lane == 0) off[0] = 0;
+  wave_lds_sync();
+  // Entry p (slot p / 64 of lane p % 64) comes from the last list l with off[l] <= p:
+  // a branchless search per slot, all slots' searches and loads independent.
+  const uint64_t* lrow = f.lists + row * n_lists * (int64_t)f.lane_cap;
   uint64_t rk[kLsSlots];
 #pragma unroll
   for (int j = 0; j < kLsSlots; ++j) {
     const int p = j * kWave + lane;
-    rk[j] = 0ull;
-    if (p < total) {
-      int sp = 0;
-      while (sp + 1 < f.n_split && p >= off[sp + 1]) ++sp;
-      rk[j] = f.lists[(row * f.n_split + sp) * f.split_cap + (p - off[sp])];
-    }
+    int l = 0;
+#pragma unroll
+    for (int s = kWave / 2; s > 0; s >>= 1)
+      if (l + s < n_lists && off[l + s] <= p) l += s;
+    rk[j] = p < total ? lrow[(int64_t)l * f.lane_cap + (p - off[l])] : 0ull;
   }
+  uint32_t* hist = area[wave];
   int pb;
   const uint64_t pre = wave_radix_select<kFsRankBits>(
-      hist[wave], (uint32_t)m,
+      hist, (uint32_t)m,
       [&](auto&& fn) {
 #pragma unroll
         for (int j = 0; j < kLsSlots; ++j)
           if (rk[j]) fn(rk[j]);
       },
       pb);
-  uint32_t written = 0;
+  uint32_t kept_mask = 0u;  // bit j: slot j holds one of the m kept
 #pragma unroll
-  for (int j = 0; j < kLsSlots; ++j) {
-    const bool kp = rk[j] != 0ull && (rk[j] >> (kFsRankBits - pb)) >= pre;
-    const uint64_t b = __ballot(kp);
-    const uint32_t p = written + (uint32_t)lane_prefix(b);
-    if (kp && p < (uint32_t)m) srow[p] = fs_rank_id(rk[j]);
-    written += (uint32_t)__popcll(b);
+  for (int j = 0; j < kLsSlots; ++j)
+    if (rk[j] != 0ull && (rk[j] >> (kFsRankBits - pb)) >= pre) kept_mask |= 1u << j;
+  // Ascending order: the kept ids set bits of a bitmap over the row's blocks, one
+  // window of kLsMapWords * 32 blocks at a time; each lane owns a run of words,
+  // counts their bits, and writes its ids after those of the lanes before it.
+  uint32_t* bm = area[wave];
+  const int n_words = (lim + 31) >> 5;
+  int written = 0;
+  for (int w0 = 0; w0 < n_words; w0 += kLsMapWords) {
+    const int nw = min(n_words - w0, kLsMapWords);
+    const int wpl = (nw + kWave - 1) / kWave;  // words per lane
+    wave_lds_sync();  // the histogram, or the last window, is no longer read
+    for (int i = lane; i < nw; i += kWave) bm[i] = 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < kLsSlots; ++j)
+      if (kept_mask & (1u << j)) {
+        const int rel = fs_rank_id(rk[j]) - (w0 << 5);
+        if (rel >= 0 && rel < (nw << 5)) atomicOr(&bm[rel >> 5], 1u << (rel & 31));
+      }
+    wave_lds_sync();
+    const int q0 = lane * wpl, q1 = min(q0 + wpl, nw);
+    int cl = 0;
+    for (int q = q0; q < q1; ++q) cl += __popc(bm[q]);
+    int ci = cl;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(ci, o, kWave);
+      if (lane >= o) ci += y;
+    }
+    int pos = written + ci - cl;
+    for (int q = q0; q < q1; ++q) {
+      uint32_t x = bm[q];
+      while (x) {
+        const int b = __ffs(x) - 1;
+        if (pos < m) srow[pos] = ((w0 + q) << 5) + b;
+        ++pos;
+        x &= x - 1u;
+      }
+    }
+    written += __shfl(ci, kWave - 1, kWave);
   }
   for (int k = m + lane; k < f.n_sel; k += kWave) srow[k] = k == m ? (int)own : -1;
   if (lane == 0) f.flags[row] = 0;
@@ -395,7 +444,7 @@ int fused_n_split(int64_t lq) {
 hipError_t launch_select_fused(const FusedSelArgs& f, hipStream_t stream) {
   if (f.lq <= 0) return hipSuccess;
   if (f.n_split < 1 || f.n_split > 4 || f.cap > kFusedListCap || f.nblk >= (1 << kFsIdBits) ||
-      f.target < 1 || f.sample_k < 1 || f.split_cap < 1)
+      f.target < 1 || f.sample_k < 1 || f.lane_cap < 1)
     return hipErrorInvalidValue;
   const int64_t tiles = (f.lq + kFsRows - 1) / kFsRows;
   const dim3 g1((unsigned)tiles, (unsigned)f.n_split);
