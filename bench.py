@@ -127,6 +127,34 @@ def gather_ceiling(torch, Q, dev, mib, sequential, n_waves=65536, steps=32):
     return n_waves * steps * 16384 / (ms * 1e-3) / 1e9
 
 
+def write_ceiling(torch, dev, nbytes, nontemporal, reps=3):
+    """GB/s of the probe library's write stream (16-byte stores, 1 KiB per wave
+    instruction: the score GEMM's store pattern) over a buffer of nbytes."""
+    from block_sparse_attention_06_amd.probe import probe_write
+    buf = torch.empty(nbytes // 16 * 16, dtype=torch.uint8, device=dev)
+    probe_write(buf, nontemporal)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        probe_write(buf, nontemporal)
+        b.record()
+    torch.cuda.synchronize()
+    ms = min(a.elapsed_time(b) for a, b in evs)
+    n = buf.numel()
+    del buf
+    return n / (ms * 1e-3) / 1e9
+
+
+def score_write_bytes(wl):
+    """fp32 scores the score GEMM stores in a step: each row its min(own block, n_blocks)
+    candidates, rounded up to the 4 of one 16-byte store."""
+    import numpy as np
+    t = wl.q_pos0 + np.arange(wl.lq, dtype=np.int64)
+    lim = np.minimum(t // wl.r, wl.lk // wl.r)
+    return int(((lim + 3) // 4 * 16).sum())
+
+
 def kept_tokens(t, n_sel, r=4):
     """Tokens attended by a query at position t (array) under a full selection."""
     own = t // r
@@ -649,6 +677,20 @@ def main():
         "random_gather_ceiling_GBs": ceil_rand, "random_buffer_MiB": kv_mib,
         "sequential_stream_GBs": ceil_seq, "sequential_buffer_MiB": 2048,
         "beyond_l2_frac_of_random_ceiling": beyond / ceil_rand if beyond else None}
+    # The score GEMM's output stream against the write ceiling (a chunk-sized buffer).
+    w_bytes = score_write_bytes(wl)
+    chunk_bytes = min(args.row_chunk, wl.lq) * Q.score_ld(wl.lk // wl.r) * 4
+    w_plain = write_ceiling(torch, dev, chunk_bytes, nontemporal=False)
+    w_nt = write_ceiling(torch, dev, chunk_bytes, nontemporal=True)
+    progress(f"write ceiling: {w_plain:.0f} GB/s plain, {w_nt:.0f} GB/s non-temporal")
+    w_best = max(w_plain, w_nt)
+    line["score_writes"] = {
+        "bytes_per_step": w_bytes, "GBs": w_bytes / (score_ms * 1e-3) / 1e9,
+        "write_ceiling_GBs": {"plain": w_plain, "nontemporal": w_nt},
+        "ceiling_buffer_MiB": chunk_bytes >> 20,
+        "frac_of_write_ceiling": w_bytes / (score_ms * 1e-3) / 1e9 / w_best,
+        "floor_ms_at_ceiling": w_bytes / (w_best * 1e9) * 1e3,
+        "note": "the score GEMM stores non-temporal; its time cannot fall below the floor"}
     if not args.no_backward:
         b_ms = bench_backward(torch, Q, wl, inp, plan)
         b_bytes = backward_bytes(wl, t)

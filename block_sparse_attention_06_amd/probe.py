@@ -1,7 +1,8 @@
-"""Binding of the benchmark's gather probe (libqsa_probe.so, include/qsa_probe.h).
+"""Binding of the benchmark's probes (libqsa_probe.so, include/qsa_probe.h).
 
-A measurement aid, not part of the QSA path: it reads 4 KiB blocks of a buffer in the
-attention stage's access pattern, to measure the memory system's gather ceiling.
+Measurement aids, not part of the QSA path: a gather of 4 KiB blocks in the attention
+stage's access pattern (the memory system's gather ceiling) and a write stream in the
+score GEMM's store pattern (the ceiling of its output stream).
 """
 from __future__ import annotations
 
@@ -18,6 +19,8 @@ SIGNATURES = {
     "qsa_probe_gather": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                         ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    "qsa_probe_write": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p]),
 }
 _lib = None
 
@@ -52,3 +55,14 @@ def probe_gather(buf: torch.Tensor, block_ids: torch.Tensor, steps: int, sink: t
                                  block_ids.data_ptr(), n_waves, steps, sink.data_ptr(), st)
     if rc != 0:
         raise RuntimeError(f"qsa_probe_gather failed with status {rc}")
+
+
+def probe_write(buf: torch.Tensor, nontemporal: bool = False):
+    """Fill the whole of `buf` (contiguous, on the GPU, a multiple of 16 bytes)."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_contiguous() or nbytes % 16:
+        raise ValueError("a contiguous buffer of a multiple of 16 bytes expected")
+    st = torch.cuda.current_stream(buf.device).cuda_stream
+    rc = load().qsa_probe_write(buf.data_ptr(), nbytes, int(bool(nontemporal)), st)
+    if rc != 0:
+        raise RuntimeError(f"qsa_probe_write failed with status {rc}")

@@ -14,6 +14,13 @@
  *   stream     hipStream_t the launch is enqueued on
  * Bytes read per call: n_waves * steps * 16384. Returns 0 on success, 1 for a bad
  * argument (null or misaligned pointer, negative size), 4 when the launch fails.
+ *
+ * The write-stream ceiling for the score GEMM's output: qsa_probe_write fills the
+ * first `bytes` bytes of buf with 16-byte float values, each wave instruction writing
+ * 1 KiB of consecutive bytes, with the non-temporal hint when nontemporal != 0.
+ *   buf     device buffer, 16-byte aligned; bytes a multiple of 16
+ *   stream  hipStream_t the launch is enqueued on
+ * Returns 0 on success, 1 for a bad argument, 4 when the launch fails.
  */
 #ifndef QSA_PROBE_H
 #define QSA_PROBE_H
@@ -27,6 +34,8 @@ extern "C" {
 
 int qsa_probe_gather(const void* buf, size_t buf_bytes, const int32_t* block_ids,
                      int64_t n_waves, int steps, uint32_t* sink, void* stream);
+
+int qsa_probe_write(void* buf, size_t bytes, int nontemporal, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,18 +28,23 @@ def test_every_header_function_is_exported_and_declared(lib):
 
 
 def test_probe_library_is_separate():
-    # The benchmark's gather probe lives in its own library and header; libqsa.so
-    # exports only the QSA calls.
+    # The benchmark's probes live in their own library and header; libqsa.so exports
+    # only the QSA calls.
     from block_sparse_attention_06_amd import probe
     if not os.path.exists(probe.PROBE_LIB_PATH):
         from block_sparse_attention_06_amd import build
         build.build()
     assert _lib.header_functions(probe.HEADER_PATH) == sorted(probe.SIGNATURES)
     plib = probe.load()
-    assert hasattr(plib, "qsa_probe_gather")
     qlib = _lib.load()
-    assert not hasattr(qlib, "qsa_probe_gather")
+    for name in ("qsa_probe_gather", "qsa_probe_write"):
+        assert hasattr(plib, name)
+        assert not hasattr(qlib, name)
     assert plib.qsa_probe_gather(None, 4096, None, 1, 1, None, None) == 1
+    assert plib.qsa_probe_write(None, 4096, 0, None) == 1
+    # rejected on the host before any launch: a misaligned pointer, a ragged size
+    assert plib.qsa_probe_write(8, 4096, 0, None) == 1
+    assert plib.qsa_probe_write(16, 4095, 0, None) == 1
 
 
 P = ctypes.c_void_p
