@@ -43,6 +43,10 @@ def _both(wl, inp, row_chunk, tuning=None):
     ("prefill32k", 16384, dict(smooth=100)),                      # correlated rows
     ("prefill128k", 16384, {}),
     ("chunked1m", 8192, {}),                                      # 262K candidates a row
+    ("prefill32k", 32768, {}),                                    # one key-range piece
+    ("prefill32k", 9000, {}),                                     # three pieces
+    # rows whose candidates cross the 65536-block window of the list select's bitmap
+    ("prefill32k", 1000, dict(lq=1000, lk=263000, q_pos0=262000, pooled_prefix_blocks=65500)),
 ])
 def test_fused_selection_equals_two_kernel_selection(name, row_chunk, over):
     wl = workload(name, **over)
