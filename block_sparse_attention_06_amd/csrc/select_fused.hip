@@ -47,7 +47,7 @@ constexpr int kLsMapWords = 2048;  // bitmap words of a list-select wave (65536 
 
 // Rank of a (score, id) pair: larger ranks earlier (score descending, then id
 // ascending); 0 is no entry.
-__device__ __forceinline__ uint64_t fs_rank(float v, int64_t id) {
+__device__ __forceinline__ uint64_t fs_rank(float v, int id) {
   return ((uint64_t)order_key(v) << kFsIdBits) | (uint64_t)(kFsIdMask - (uint32_t)id);
 }
 
@@ -217,7 +217,16 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
       }
     }
 
-    // 2. The piece's scores; those at or above the threshold go to the lists.
+    // 2. The piece's scores; those at or above the threshold go to the lists. Per row:
+    // the end of its candidates in this piece and its lane list (block ids < 2^24).
+    int lim_p[4];
+    uint64_t* lbase[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      lim_p[mt] = (int)min((int64_t)lim[mt], n_end);
+      lbase[mt] = f.lists + ((int64_t)max(tokv[mt], 0) * f.n_split + split) * kFsLanes * f.lane_cap +
+                  (int64_t)c16 * f.lane_cap;
+    }
     const int n_main = (int)((n_end - n_begin + kFsTileN - 1) / kFsTileN);
     if (n_main > 0) {
       load_rows([&](int row) { return n_begin + row < n_end ? n_begin + row : (int64_t)-1; });
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
           });
         f32x4 acc[4][4];
         multiply(tile[it & 1], acc);
-        const int64_t blk0 = n0 + 4 * c16;
+        const int blk0 = (int)n0 + 4 * c16;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           float sv[4];
@@ -242,17 +251,17 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             sv[j] = score_of_heads(W[mt], acc[mt][j]);
-            fl[j] = blk0 + j < lim[mt] && blk0 + j < n_end && sv[j] >= thr[mt];
+            fl[j] = blk0 + j < lim_p[mt] && sv[j] >= thr[mt];
             k += fl[j];
           }
           if (k > 0) {  // this lane's own list: ascending ids, no other lane involved
-            uint64_t* ll = f.lists +
-                           (((int64_t)tokv[mt] * f.n_split + split) * kFsLanes + c16) * f.lane_cap;
             int p = cnt[mt];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               if (fl[j]) {
-                if (p < f.lane_cap) ll[p] = fs_rank(sv[j], blk0 + j);
+                // past the capacity the count still grows (the row then takes the exact
+                // fallback) while the entry lands on the last slot
+                lbase[mt][min(p, f.lane_cap - 1)] = fs_rank(sv[j], blk0 + j);
                 ++p;
               }
             cnt[mt] = p;
