@@ -696,9 +696,12 @@ size_t qsa_prefill_fused_workspace_bytes(int64_t lq, int64_t lk, int r, int budg
                                          int64_t row_chunk) {
   if (lq <= 0 || lk <= 0 || r <= 0) return 0;
   const int64_t rc = row_chunk > 0 ? (row_chunk < lq ? row_chunk : lq) : lq;
+  // scores, lists, list counts, row flags, sampled keys and sample counts per
+  // (row, piece, lane)
   return align256((size_t)rc * (size_t)score_ld(lk / r) * sizeof(float)) +
          align256(fused_list_bytes(lq, rc)) + align256((size_t)rc * 4 * 16 * sizeof(int32_t)) +
-         align256((size_t)rc * sizeof(int32_t));
+         align256((size_t)rc * sizeof(int32_t)) + align256((size_t)rc * 4 * 16 * 16) +
+         align256((size_t)rc * 4 * 16 * sizeof(int32_t));
 }
 
 qsa_status qsa_prefill_select_fused(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
@@ -736,6 +739,10 @@ qsa_status qsa_prefill_select_fused(int64_t lq, int64_t lk, int64_t q_pos0, int 
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   ws += align256((size_t)rc * 4 * 16 * sizeof(int32_t));
   int32_t* flags = reinterpret_cast<int32_t*>(ws);
+  ws += align256((size_t)rc * sizeof(int32_t));
+  uint4* s_top = reinterpret_cast<uint4*>(ws);
+  ws += align256((size_t)rc * 4 * 16 * 16);
+  int32_t* s_nv = reinterpret_cast<int32_t*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int64_t c0 = 0; c0 < lq; c0 += rc) {
     const int64_t n = (lq - c0) < rc ? (lq - c0) : rc;
@@ -753,6 +760,8 @@ qsa_status qsa_prefill_select_fused(int64_t lq, int64_t lk, int64_t q_pos0, int 
     f.lists = lists;
     f.counts = counts;
     f.flags = flags;
+    f.s_top = s_top;
+    f.s_nv = s_nv;
     f.n_split = qsa::fused_n_split(n);
     f.lane_cap = qsa::kFusedListCap / 16;  // 16 lane lists of a (row, piece): 2048 in all
     f.cap = tn.cap;

@@ -64,7 +64,10 @@ __device__ __forceinline__ int group16_sum(int x) {
   return x;
 }
 
-template <int DI>
+// SAMPLE: score this piece's share of the rows' strided sample and store, per row and
+// lane, its kFsTopR best sampled keys and its sample count (no lists). Otherwise: take
+// the row thresholds from all pieces' sample shares, then score the piece and append.
+template <int DI, bool SAMPLE>
 __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
   constexpr int NC = DI / 32;
   constexpr int ROW = DI + 8;  // LDS row in bf16 elements, padded by 16 B
@@ -150,72 +153,114 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
     };
 
     // 1. Thresholds from a strided sample (rows whose candidates all fit admit all).
+    // The sample is scored once per row tile: each piece scores its share of it.
     float thr[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (nb_need > f.cap) {
       const int64_t want = ((int64_t)f.sample_k * nb_need + f.target - 1) / f.target;
       const int S = (int)min(nb_need, (want + kFsTileN - 1) / kFsTileN * kFsTileN);
       const int n_st = (S + kFsTileN - 1) / kFsTileN;
-      // sample i is block i * stride: evenly spaced over the first S * stride blocks, in
-      // 32-bit arithmetic (blocks < 2^24; a 64-bit division per sample cost as much as
-      // the whole scoring pass)
-      const int stride = (int)(nb_need / S);
-      auto sample_blk = [&](int i) -> int64_t { return i < S ? (int64_t)(i * stride) : -1; };
-      uint32_t top[4][kFsTopR];
-      int nv[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int q = 0; q < kFsTopR; ++q) top[mt][q] = 0u;
-      load_rows([&](int row) { return sample_blk(row); });
-      store_tile(0);
-      __syncthreads();
-      for (int st = 0; st < n_st; ++st) {
-        const bool more = st + 1 < n_st;
-        if (more) load_rows([&](int row) { return sample_blk((st + 1) * kFsTileN + row); });
-        f32x4 acc[4][4];
-        multiply(tile[st & 1], acc);
+      if constexpr (SAMPLE) {
+        // sample i is block i * stride: evenly spaced over the first S * stride blocks,
+        // in 32-bit arithmetic (blocks < 2^24; a 64-bit division per sample cost as much
+        // as the whole scoring pass)
+        const int stride = (int)(nb_need / S);
+        auto sample_blk = [&](int i) -> int64_t { return i < S ? (int64_t)(i * stride) : -1; };
+        const int st0 = n_st * split / f.n_split, st1 = n_st * (split + 1) / f.n_split;
+        uint32_t top[4][kFsTopR];
+        int nv[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int64_t b = sample_blk(st * kFsTileN + 4 * c16 + j);
-            if (b >= 0 && b < lim[mt]) {
-              uint32_t x = order_key(score_of_heads(W[mt], acc[mt][j]));
-              ++nv[mt];
+          for (int q = 0; q < kFsTopR; ++q) top[mt][q] = 0u;
+        if (st0 < st1) {
+          load_rows([&](int row) { return sample_blk(st0 * kFsTileN + row); });
+          store_tile(0);
+          __syncthreads();
+        }
+        for (int st = st0; st < st1; ++st) {
+          const bool more = st + 1 < st1;
+          if (more) load_rows([&](int row) { return sample_blk((st + 1) * kFsTileN + row); });
+          f32x4 acc[4][4];
+          multiply(tile[(st - st0) & 1], acc);
 #pragma unroll
-              for (int q = 0; q < kFsTopR; ++q) {  // keep the kFsTopR largest, sorted
-                const uint32_t hi = max(top[mt][q], x);
-                x = min(top[mt][q], x);
-                top[mt][q] = hi;
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int64_t b = sample_blk(st * kFsTileN + 4 * c16 + j);
+              if (b >= 0 && b < lim[mt]) {
+                uint32_t x = order_key(score_of_heads(W[mt], acc[mt][j]));
+                ++nv[mt];
+#pragma unroll
+                for (int q = 0; q < kFsTopR; ++q) {  // keep the kFsTopR largest, sorted
+                  const uint32_t hi = max(top[mt][q], x);
+                  x = min(top[mt][q], x);
+                  top[mt][q] = hi;
+                }
+              }
+            }
+          if (more) store_tile((st + 1 - st0) & 1);
+          __syncthreads();
+        }
+        static_assert(kFsTopR == 4, "one uint4 of sampled keys per lane and row");
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          if (tokv[mt] >= 0) {
+            const int64_t at = ((int64_t)tokv[mt] * f.n_split + split) * kFsLanes + c16;
+            f.s_top[at] = make_uint4(top[mt][0], top[mt][1], top[mt][2], top[mt][3]);
+            f.s_nv[at] = nv[mt];
+          }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          // This lane's kFsTopR best sampled keys over every piece's share (0: none):
+          // the same keys as one pass over the whole sample would keep. Keeping only a
+          // lane's best few lowers the threshold a little where a lane holds more of
+          // the row's best samples; the target is set with that margin, which keeps
+          // rows with fewer than m entries (each an exact fallback) rare.
+          uint32_t top[kFsTopR] = {0u, 0u, 0u, 0u};
+          int nv = 0;
+#pragma unroll
+          for (int sp = 0; sp < 4; ++sp) {
+            if (sp < f.n_split && tokv[mt] >= 0) {
+              const int64_t at = ((int64_t)tokv[mt] * f.n_split + sp) * kFsLanes + c16;
+              const uint4 tp = f.s_top[at];
+              nv += f.s_nv[at];
+              const uint32_t ks[4] = {tp.x, tp.y, tp.z, tp.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                uint32_t x = ks[e];
+#pragma unroll
+                for (int q = 0; q < kFsTopR; ++q) {  // insert into the sorted kFsTopR best
+                  const uint32_t hi = max(top[q], x);
+                  x = min(top[q], x);
+                  top[q] = hi;
+                }
               }
             }
           }
-        if (more) store_tile((st + 1) & 1);
-        __syncthreads();
-      }
+          const int nvg = group16_sum(nv);
+          int kept = 0;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int nvg = group16_sum(nv[mt]);
-        int kept = 0;
+          for (int q = 0; q < kFsTopR; ++q) kept += top[q] != 0u;
+          kept = group16_sum(kept);
+          if (lim[mt] > f.cap && kept > 0) {
+            // about `target` of the lim scores reach the k-th best of the nvg sampled
+            int64_t k = ((int64_t)nvg * f.target + lim[mt] - 1) / lim[mt];
+            k = k < 1 ? 1 : (k > kept ? kept : k);  // fewer kept: a lower threshold
+            uint32_t pre = 0u;
+            for (int b = 31; b >= 0; --b) {
+              const uint32_t cand = pre | (1u << b);
+              int c = 0;
 #pragma unroll
-        for (int q = 0; q < kFsTopR; ++q) kept += top[mt][q] != 0u;
-        kept = group16_sum(kept);
-        if (lim[mt] > f.cap && kept > 0) {
-          // about `target` of the lim scores reach the k-th best of the nvg sampled
-          int64_t k = ((int64_t)nvg * f.target + lim[mt] - 1) / lim[mt];
-          k = k < 1 ? 1 : (k > kept ? kept : k);  // fewer kept: a lower threshold
-          uint32_t pre = 0u;
-          for (int b = 31; b >= 0; --b) {
-            const uint32_t cand = pre | (1u << b);
-            int c = 0;
-#pragma unroll
-            for (int q = 0; q < kFsTopR; ++q) c += top[mt][q] >= cand;
-            if (group16_sum(c) >= k) pre = cand;
+              for (int q = 0; q < kFsTopR; ++q) c += top[q] >= cand;
+              if (group16_sum(c) >= k) pre = cand;
+            }
+            thr[mt] = key_to_float(pre);  // the key of a sampled score
           }
-          thr[mt] = key_to_float(pre);  // the key of a sampled score
         }
       }
     }
+    if constexpr (SAMPLE) return;
 
     // 2. The piece's scores; those at or above the threshold go to the lists. Per row:
     // the end of its candidates in this piece and its lane list (block ids < 2^24).
@@ -272,9 +317,11 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
       }
     }
   }
+  if constexpr (!SAMPLE) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-    if (tokv[mt] >= 0) f.counts[((int64_t)tokv[mt] * f.n_split + split) * kFsLanes + c16] = cnt[mt];
+    for (int mt = 0; mt < 4; ++mt)
+      if (tokv[mt] >= 0) f.counts[((int64_t)tokv[mt] * f.n_split + split) * kFsLanes + c16] = cnt[mt];
+  }
 }
 
 __global__ __launch_bounds__(256) void list_select_kernel(FusedSelArgs f) {
@@ -457,10 +504,13 @@ hipError_t launch_select_fused(const FusedSelArgs& f, hipStream_t stream) {
     return hipErrorInvalidValue;
   const int64_t tiles = (f.lq + kFsRows - 1) / kFsRows;
   const dim3 g1((unsigned)tiles, (unsigned)f.n_split);
-  if (f.d_idx == 128)
-    hipLaunchKernelGGL(score_list_kernel<128>, g1, dim3(256), 0, stream, f);
-  else
-    hipLaunchKernelGGL(score_list_kernel<64>, g1, dim3(256), 0, stream, f);
+  if (f.d_idx == 128) {
+    hipLaunchKernelGGL((score_list_kernel<128, true>), g1, dim3(256), 0, stream, f);
+    hipLaunchKernelGGL((score_list_kernel<128, false>), g1, dim3(256), 0, stream, f);
+  } else {
+    hipLaunchKernelGGL((score_list_kernel<64, true>), g1, dim3(256), 0, stream, f);
+    hipLaunchKernelGGL((score_list_kernel<64, false>), g1, dim3(256), 0, stream, f);
+  }
   const dim3 gr((unsigned)((f.lq + 3) / 4));
   hipLaunchKernelGGL(list_select_kernel, gr, dim3(256), 0, stream, f);
   ScoreArgs sa{};

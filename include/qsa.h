@@ -309,7 +309,7 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
  * Arguments as qsa_prefill_select; blocks (lk / r) must be fewer than 2^24. tuning may
  * be NULL (defaults: target 2 (K/r - 1), sample_k 32, cap 2048); a field <= 0 takes
  * its default; cap <= 2048. The workspace holds one chunk's scores (for the fallback),
- * its lists, counts and flags: qsa_prefill_fused_workspace_bytes().
+ * its lists, counts, flags and sampled keys: qsa_prefill_fused_workspace_bytes().
  */
 typedef struct qsa_fused_tuning {
   int target;    /* list entries a row aims at */
