@@ -700,7 +700,7 @@ size_t qsa_prefill_fused_workspace_bytes(int64_t lq, int64_t lk, int r, int budg
   // (row, piece, lane)
   return align256((size_t)rc * (size_t)score_ld(lk / r) * sizeof(float)) +
          align256(fused_list_bytes(lq, rc)) + align256((size_t)rc * 4 * 16 * sizeof(int32_t)) +
-         align256((size_t)rc * sizeof(int32_t)) + align256((size_t)rc * 4 * 16 * 16) +
+         align256((size_t)rc * sizeof(int32_t)) + align256((size_t)rc * 4 * 16 * 32) +
          align256((size_t)rc * 4 * 16 * sizeof(int32_t));
 }
 
@@ -715,7 +715,7 @@ qsa_status qsa_prefill_select_fused(int64_t lq, int64_t lk, int64_t q_pos0, int 
   QSA_REQUIRE(nblk < ((int64_t)1 << 24), QSA_ERR_UNSUPPORTED,
               "%lld blocks: the fused selection takes fewer than 2^24", (long long)nblk);
   const int n_sel = r > 0 ? budget_tokens / r : 0;
-  qsa_fused_tuning tn{2 * (n_sel > 1 ? n_sel - 1 : 1), 32, qsa::kFusedListCap};
+  qsa_fused_tuning tn{2 * (n_sel > 1 ? n_sel - 1 : 1), 64, qsa::kFusedListCap};
   if (tuning) {
     if (tuning->target > 0) tn.target = tuning->target;
     if (tuning->sample_k > 0) tn.sample_k = tuning->sample_k;
@@ -741,7 +741,7 @@ qsa_status qsa_prefill_select_fused(int64_t lq, int64_t lk, int64_t q_pos0, int 
   int32_t* flags = reinterpret_cast<int32_t*>(ws);
   ws += align256((size_t)rc * sizeof(int32_t));
   uint4* s_top = reinterpret_cast<uint4*>(ws);
-  ws += align256((size_t)rc * 4 * 16 * 16);
+  ws += align256((size_t)rc * 4 * 16 * 32);
   int32_t* s_nv = reinterpret_cast<int32_t*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int64_t c0 = 0; c0 < lq; c0 += rc) {

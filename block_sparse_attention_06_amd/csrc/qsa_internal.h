@@ -110,7 +110,7 @@ struct FusedSelArgs {
   uint64_t* lists;        // [lq][n_split][16][lane_cap] ranks (score key << 24 | 0xffffff - id)
   int32_t* counts;        // [lq][n_split][16]
   int32_t* flags;         // [lq]: 1 where the fallback selects
-  uint4* s_top;           // [lq][n_split][16]: a lane's best sampled keys of one piece's share
+  uint4* s_top;           // [lq][n_split][16][2]: a lane's 8 best sampled keys of a piece's share
   int32_t* s_nv;          // [lq][n_split][16]: its sampled candidates
   int n_split;            // key-range pieces of a row tile (one workgroup each)
   int lane_cap;           // entries a (row, piece, lane) list holds

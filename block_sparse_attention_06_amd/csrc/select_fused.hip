@@ -12,7 +12,8 @@
 //  1. score_list_kernel: a workgroup takes 64 rows and one piece of their block range.
 //     It first scores an evenly strided sample of the rows' blocks (one in about
 //     lim * sample_k / target) and sets each row's threshold at about the sample_k-th
-//     best sampled score, which about `target` of the row's scores reach. It then
+//     best sampled score, which about `target` of the row's scores reach. The sample is
+//     scored once per row tile, a share per piece, by a sample-only launch before. It then
 //     scores the piece on MFMA as the plain GEMM does, and each of the 16 lanes that
 //     hold a row's scores appends its own scores at or above the threshold to a list of
 //     its own as ranks (score key, then id): no cross-lane bookkeeping, no atomics
@@ -37,7 +38,7 @@ namespace {
 
 constexpr int kFsRows = 64;    // query rows per workgroup (4 waves x 16)
 constexpr int kFsTileN = 64;   // pooled keys per LDS tile
-constexpr int kFsTopR = 4;     // sampled keys a lane keeps per row
+constexpr int kFsTopR = 8;     // sampled keys a lane keeps per row (two uint4)
 constexpr int kFsIdBits = 24;  // block ids in a rank (ids < 2^24)
 constexpr int kFsRankBits = 32 + kFsIdBits;
 constexpr uint32_t kFsIdMask = (1u << kFsIdBits) - 1u;
@@ -201,12 +202,13 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
           if (more) store_tile((st + 1 - st0) & 1);
           __syncthreads();
         }
-        static_assert(kFsTopR == 4, "one uint4 of sampled keys per lane and row");
+        static_assert(kFsTopR == 8, "two uint4 of sampled keys per lane and row");
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           if (tokv[mt] >= 0) {
             const int64_t at = ((int64_t)tokv[mt] * f.n_split + split) * kFsLanes + c16;
-            f.s_top[at] = make_uint4(top[mt][0], top[mt][1], top[mt][2], top[mt][3]);
+            f.s_top[2 * at] = make_uint4(top[mt][0], top[mt][1], top[mt][2], top[mt][3]);
+            f.s_top[2 * at + 1] = make_uint4(top[mt][4], top[mt][5], top[mt][6], top[mt][7]);
             f.s_nv[at] = nv[mt];
           }
       } else {
@@ -217,17 +219,17 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
           // lane's best few lowers the threshold a little where a lane holds more of
           // the row's best samples; the target is set with that margin, which keeps
           // rows with fewer than m entries (each an exact fallback) rare.
-          uint32_t top[kFsTopR] = {0u, 0u, 0u, 0u};
+          uint32_t top[kFsTopR] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
           int nv = 0;
 #pragma unroll
           for (int sp = 0; sp < 4; ++sp) {
             if (sp < f.n_split && tokv[mt] >= 0) {
               const int64_t at = ((int64_t)tokv[mt] * f.n_split + sp) * kFsLanes + c16;
-              const uint4 tp = f.s_top[at];
+              const uint4 t0 = f.s_top[2 * at], t1 = f.s_top[2 * at + 1];
               nv += f.s_nv[at];
-              const uint32_t ks[4] = {tp.x, tp.y, tp.z, tp.w};
+              const uint32_t ks[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
+              for (int e = 0; e < 8; ++e) {
                 uint32_t x = ks[e];
 #pragma unroll
                 for (int q = 0; q < kFsTopR; ++q) {  // insert into the sorted kFsTopR best

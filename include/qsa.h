@@ -307,7 +307,7 @@ qsa_status qsa_prefill_select(int64_t lq, int64_t lk, int64_t q_pos0, int h_idx,
  * micro-blocks and each query keeps the best up to its budget; the release article's
  * GDN+QSA section counts finding the important context as a cost of its own.)
  * Arguments as qsa_prefill_select; blocks (lk / r) must be fewer than 2^24. tuning may
- * be NULL (defaults: target 2 (K/r - 1), sample_k 32, cap 2048); a field <= 0 takes
+ * be NULL (defaults: target 2 (K/r - 1), sample_k 64, cap 2048); a field <= 0 takes
  * its default; cap <= 2048. The workspace holds one chunk's scores (for the fallback),
  * its lists, counts, flags and sampled keys: qsa_prefill_fused_workspace_bytes().
  */
