@@ -8,24 +8,25 @@
 // earlier blocks by score, then block id; own block kept), on the very same fp32 scores
 // (score_of_heads), so the kept ids are identical.
 //
-// Per chunk of rows, four launches:
-//  1. score_list_kernel: a workgroup takes 64 rows and one piece of their block range.
-//     It first scores an evenly strided sample of the rows' blocks (one in about
-//     lim * sample_k / target) and sets each row's threshold at about the sample_k-th
-//     best sampled score, which about `target` of the row's scores reach. The sample is
-//     scored once per row tile, a share per piece, by a sample-only launch before. It then
-//     scores the piece on MFMA as the plain GEMM does, and each of the 16 lanes that
-//     hold a row's scores appends its own scores at or above the threshold to a list of
-//     its own as ranks (score key, then id): no cross-lane bookkeeping, no atomics
-//     (placing entries by ballot prefix counts cost as much as the products).
-//  2. list_select_kernel: one wave per row. A row whose candidates all fit keeps them;
+// Per chunk of rows, five launches:
+//  1. score_list_kernel<SAMPLE>: a workgroup takes 64 rows and one piece of their block
+//     range, and scores its share of an evenly strided sample of the rows' blocks (one
+//     in about lim * sample_k / target), keeping each lane's 8 best sampled keys per row.
+//  2. score_list_kernel: the same workgroups merge the pieces' sampled keys and set each
+//     row's threshold at about the sample_k-th best sampled score, which about `target`
+//     of the row's scores reach. They then score their piece on MFMA as the plain GEMM
+//     does, and each of the 16 lanes that hold a row's scores appends its own scores at
+//     or above the threshold to a list of its own as ranks (score key, then id): no
+//     cross-lane bookkeeping, no atomics (placing entries by ballot prefix counts cost
+//     as much as the products).
+//  3. list_select_kernel: one wave per row. A row whose candidates all fit keeps them;
 //     otherwise, if its lane lists hold at least m and at most the capacity in all,
 //     they hold the row's m best (every score that is not in them is below the
 //     threshold, below each of at least m listed ones). A radix select on the listed
 //     ranks finds the m-th; the kept ids go out ascending through an LDS bitmap over
 //     the row's blocks. Other rows are flagged.
-//  3. The plain score GEMM, only on 64-row tiles that hold a flagged row.
-//  4. fallback_select_kernel: one wave per flagged row, an exact radix select streamed
+//  4. The plain score GEMM, only on 64-row tiles that hold a flagged row.
+//  5. fallback_select_kernel: one wave per flagged row, an exact radix select streamed
 //     over its materialised scores.
 
 #include "qsa_device.h"
