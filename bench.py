@@ -666,7 +666,9 @@ def main():
     kv_mib = (2 * wl.lk * wl.hkv * wl.d * 2) >> 20
     ceil_rand = gather_ceiling(torch, Q, dev, kv_mib, sequential=False)
     ceil_seq = gather_ceiling(torch, Q, dev, 2048, sequential=True)
-    progress(f"gather ceiling: {ceil_rand:.0f} GB/s random, {ceil_seq:.0f} GB/s sequential")
+    ceil_l2 = gather_ceiling(torch, Q, dev, 2, sequential=False)  # L2-resident on every XCD
+    progress(f"gather ceiling: {ceil_rand:.0f} GB/s random, {ceil_seq:.0f} GB/s sequential, "
+             f"{ceil_l2:.0f} GB/s from L2")
     beyond = traffic / (attn_ms * 1e-3) / 1e9 if traffic else None
     line["gather"] = {
         "algorithmic_bytes_per_call": a_bytes,
@@ -676,6 +678,11 @@ def main():
         "beyond_l2_bytes_per_call": traffic, "beyond_l2_GBs": beyond,
         "random_gather_ceiling_GBs": ceil_rand, "random_buffer_MiB": kv_mib,
         "sequential_stream_GBs": ceil_seq, "sequential_buffer_MiB": 2048,
+        "l2_resident_gather_GBs": ceil_l2, "l2_resident_buffer_MiB": 2,
+        # time if the L2 hits and the fetches beyond L2 were served one after the other,
+        # each at its measured ceiling
+        "serial_model_ms": ((a_bytes - traffic) / ceil_l2 + traffic / ceil_rand) / 1e6
+        if traffic else None,
         "beyond_l2_frac_of_random_ceiling": beyond / ceil_rand if beyond else None}
     # The score GEMM's output stream against the write ceiling (a chunk-sized buffer).
     w_bytes = score_write_bytes(wl)
