@@ -43,9 +43,10 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(const uint2& a, const uint2& b, f
 // lanes): sum_h w_h * max(0, dot_h), always in this order, so that every kernel that
 // scores blocks produces the same fp32 value.
 __device__ __forceinline__ float score_of_heads(const float (&W)[4], const f32x4& acc) {
-  // ReLU as an integer max on the bits: a finite float is negative exactly when its
-  // bits are as an int32 (-0 included, which becomes +0), so max(bits, 0) is max(x, 0)
-  // in one v_max_i32, where fmaxf costs a canonicalising max before the max.
+  // ReLU as an integer max on the bits: a finite float has its sign bit set exactly
+  // when its bits, read as an int32, are negative (-0 included, which becomes +0), so
+  // max(bits, 0) is max(x, 0) in one v_max_i32, where fmaxf costs a canonicalising max
+  // before the max.
   auto relu = [](float x) { return __int_as_float(max(__float_as_int(x), 0)); };
   float s = W[0] * relu(acc[0]);
   s = fmaf(W[1], relu(acc[1]), s);
