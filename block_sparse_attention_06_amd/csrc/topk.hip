@@ -1082,6 +1082,23 @@ __device__ void wave_select_row(const WrLds L, const float* row, int n, int m, E
           },
           pb);
       tau = (uint32_t)(pre << (32 - pb));
+      // A threshold on a value the row's scores tie at in numbers (exact zeros after
+      // the ReLU) admits every tie: when the sample says that overflows the list while
+      // the scores above it still fill m, admit only those above.
+      uint32_t above = 0, atleast = 0;
+#pragma unroll
+      for (int j = 0; j < kWrSampleSlots; ++j) {
+        above += sk[j] > tau;
+        atleast += sk[j] >= tau;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        above += __shfl_xor(above, o, kWave);
+        atleast += __shfl_xor(atleast, o, kWave);
+      }
+      if ((int64_t)atleast * n > (int64_t)cap * nv && (int64_t)above * n >= (int64_t)m * nv &&
+          tau < 0xffffffffu)
+        ++tau;
     }
     wave_lds_sync();
   }
