@@ -399,8 +399,10 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
   __syncthreads();
   for (int it = 0; it < n_tiles; ++it) {
     const int64_t n0 = n_begin + (int64_t)it * kScoreTileN;
-    const bool more = it + 1 < n_tiles;
-    if (more) load_tile(n0 + kScoreTileN);
+    // The next tile's loads and LDS writes run on every pass, the last one's going
+    // to a buffer nothing reads: with both under one condition the compiler could not
+    // tell that the writes had waited for the loads and waited again at the top.
+    load_tile(n0 + kScoreTileN);
     const uint16_t* tb = tile[it & 1];
     f32x4 acc[4][4];
 #pragma unroll
@@ -417,14 +419,18 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
       }
     }
     const int64_t blk0 = n0 + 4 * c16;
+    float s[4][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      float s[4];
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[j] = score_of_heads(W[mt], acc[mt][j]);
-      if (blk0 < lim[mt]) st16_stream(orow[mt] + blk0, s[0], s[1], s[2], s[3]);
-    }
-    if (more) store_tile((it + 1) & 1);
+      for (int j = 0; j < 4; ++j) s[mt][j] = score_of_heads(W[mt], acc[mt][j]);
+    // The next tile goes to LDS (the other buffer, read by no wave until the barrier)
+    // before the score stores: loads and stores share one counter, so a wait for the
+    // tile's loads placed after the stores would wait for the stores too.
+    store_tile((it + 1) & 1);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      if (blk0 < lim[mt]) st16_stream(orow[mt] + blk0, s[mt][0], s[mt][1], s[mt][2], s[mt][3]);
     __syncthreads();
   }
 }

@@ -734,7 +734,7 @@ qsa_status qsa_prefill_select_fused(int64_t lq, int64_t lk, int64_t q_pos0, int 
   char* ws = static_cast<char*>(workspace);
   float* sc = reinterpret_cast<float*>(ws);
   ws += align256((size_t)rc * (size_t)ld * sizeof(float));
-  uint64_t* lists = reinterpret_cast<uint64_t*>(ws);
+  uint2* lists = reinterpret_cast<uint2*>(ws);
   ws += align256(fused_list_bytes(lq, rc));
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   ws += align256((size_t)rc * 4 * 16 * sizeof(int32_t));

@@ -107,7 +107,7 @@ struct FusedSelArgs {
   int d_idx;
   int r;
   int n_sel;
-  uint64_t* lists;        // [lq][n_split][16][lane_cap] ranks (score key << 24 | 0xffffff - id)
+  uint2* lists;           // [lq][n_split][16][lane_cap] entries (fp32 score bits, block id)
   int32_t* counts;        // [lq][n_split][16]
   int32_t* flags;         // [lq]: 1 where the fallback selects
   uint4* s_top;           // [lq][n_split][16][2]: a lane's 8 best sampled keys of a piece's share

@@ -16,9 +16,9 @@
 //     row's threshold at about the sample_k-th best sampled score, which about `target`
 //     of the row's scores reach. They then score their piece on MFMA as the plain GEMM
 //     does, and each of the 16 lanes that hold a row's scores appends its own scores at
-//     or above the threshold to a list of its own as ranks (score key, then id): no
-//     cross-lane bookkeeping, no atomics (placing entries by ballot prefix counts cost
-//     as much as the products).
+//     or above the threshold, with their block ids, to a list of its own: no cross-lane
+//     bookkeeping, no atomics (placing entries by ballot prefix counts cost as much as
+//     the products).
 //  3. list_select_kernel: one wave per row. A row whose candidates all fit keeps them;
 //     otherwise, if its lane lists hold at least m and at most the capacity in all,
 //     they hold the row's m best (every score that is not in them is below the
@@ -28,6 +28,8 @@
 //  4. The plain score GEMM, only on 64-row tiles that hold a flagged row.
 //  5. fallback_select_kernel: one wave per flagged row, an exact radix select streamed
 //     over its materialised scores.
+
+#include <type_traits>
 
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -268,13 +270,20 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
     // 2. The piece's scores; those at or above the threshold go to the lists. Per row:
     // the end of its candidates in this piece and its lane list (block ids < 2^24).
     int lim_p[4];
-    uint64_t* lbase[4];
+    uint2* lbase[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       lim_p[mt] = (int)min((int64_t)lim[mt], n_end);
       lbase[mt] = f.lists + ((int64_t)max(tokv[mt], 0) * f.n_split + split) * kFsLanes * f.lane_cap +
                   (int64_t)c16 * f.lane_cap;
     }
+    // The smallest end over the wave's 16 rows (0 if one is past the chunk): a tile
+    // below it needs no per-score range test.
+    int lim_lo = min(min(lim_p[0], lim_p[1]), min(lim_p[2], lim_p[3]));
+    lim_lo = min(lim_lo, __shfl_xor(lim_lo, 16, kWave));
+    lim_lo = min(lim_lo, __shfl_xor(lim_lo, 32, kWave));
+    lim_lo = __builtin_amdgcn_readfirstlane(lim_lo);
+    const unsigned slot_max = (unsigned)f.lane_cap - 1u;
     const int n_main = (int)((n_end - n_begin + kFsTileN - 1) / kFsTileN);
     if (n_main > 0) {
       load_rows([&](int row) { return n_begin + row < n_end ? n_begin + row : (int64_t)-1; });
@@ -282,40 +291,54 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
       __syncthreads();
       for (int it = 0; it < n_main; ++it) {
         const int64_t n0 = n_begin + (int64_t)it * kFsTileN;
-        const bool more = it + 1 < n_main;
-        if (more)
-          load_rows([&](int row) {
-            const int64_t b = n0 + kFsTileN + row;
-            return b < n_end ? b : (int64_t)-1;
-          });
+        // The next tile's loads and LDS writes run on every pass (the last one's are
+        // zero rows into a buffer nothing reads): with both under one condition the
+        // compiler could not tell that the writes had waited for the loads.
+        load_rows([&](int row) {
+          const int64_t b = n0 + kFsTileN + row;
+          return b < n_end ? b : (int64_t)-1;
+        });
         f32x4 acc[4][4];
         multiply(tile[it & 1], acc);
         const int blk0 = (int)n0 + 4 * c16;
+        float sv[4][4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          float sv[4];
-          bool fl[4];
-          int k = 0;
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            sv[j] = score_of_heads(W[mt], acc[mt][j]);
-            fl[j] = blk0 + j < lim_p[mt] && sv[j] >= thr[mt];
-            k += fl[j];
-          }
-          if (k > 0) {  // this lane's own list: ascending ids, no other lane involved
-            int p = cnt[mt];
+          for (int j = 0; j < 4; ++j) sv[mt][j] = score_of_heads(W[mt], acc[mt][j]);
+        // The next tile goes to LDS (the other buffer, read by no wave until the
+        // barrier) before the appends: loads and stores share one counter, so a wait
+        // for the tile's loads placed after the appends would wait for them too.
+        store_tile((it + 1) & 1);
+        // An entry is the score's bits and its block id; the rank is formed when the
+        // list is read, which keeps the appends (executed for nearly every slot, with
+        // a few lanes active) short.
+        auto append = [&](auto ranged) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            bool fl[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              if (fl[j]) {
-                // past the capacity the count still grows (the row then takes the exact
-                // fallback) while the entry lands on the last slot
-                lbase[mt][min(p, f.lane_cap - 1)] = fs_rank(sv[j], blk0 + j);
-                ++p;
-              }
-            cnt[mt] = p;
+              fl[j] = sv[mt][j] >= thr[mt] && (!decltype(ranged)::value || blk0 + j < lim_p[mt]);
+            if (fl[0] | fl[1] | fl[2] | fl[3]) {  // this lane's own list, ascending ids
+              unsigned p = (unsigned)cnt[mt];
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (fl[j]) {
+                  // past the capacity the count still grows (the row then takes the
+                  // exact fallback) while the entry lands on the last slot
+                  lbase[mt][min(p, slot_max)] =
+                      make_uint2(__float_as_uint(sv[mt][j]), (unsigned)(blk0 + j));
+                  ++p;
+                }
+              cnt[mt] = (int)p;
+            }
           }
-        }
-        if (more) store_tile((it + 1) & 1);
+        };
+        if (n0 + kFsTileN <= lim_lo)
+          append(std::false_type{});
+        else
+          append(std::true_type{});
         __syncthreads();
       }
     }
@@ -330,7 +353,6 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
 __global__ __launch_bounds__(256) void list_select_kernel(FusedSelArgs f) {
   // A wave's LDS area: the radix histogram, then a bitmap of the kept ids.
   __shared__ __attribute__((aligned(16))) uint32_t area[4][kLsMapWords];
-  __shared__ int off_lds[4][kWave + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= f.lq) return;
@@ -358,23 +380,32 @@ __global__ __launch_bounds__(256) void list_select_kernel(FusedSelArgs f) {
     if (lane == 0) f.flags[row] = 1;
     return;
   }
-  int* off = off_lds[wave];
-  off[lane + 1] = incl;
-  if (lane == 0) off[0] = 0;
+  // Entry p of the row (slot p / 64 of lane p % 64) is entry p - start(l) of list l.
+  // Each lane writes the places of its own list's entries into an LDS map (the wave's
+  // area, free until the radix select), so a slot finds its entry with one LDS read;
+  // every slot's load is then issued before any is used, all in flight at once.
+  // Slots past the last entry hold nothing in every lane: the wave skips them.
+  uint16_t* place = reinterpret_cast<uint16_t*>(area[wave]);  // < 64 * 128 places
+  int cmax = c;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cmax = max(cmax, __shfl_xor(cmax, o, kWave));
+  for (int i = 0; i < cmax; ++i)
+    if (i < c) place[incl - c + i] = (uint16_t)(lane * f.lane_cap + i);
   wave_lds_sync();
-  // Entry p (slot p / 64 of lane p % 64) comes from the last list l with off[l] <= p:
-  // a branchless search per slot, all slots' searches and loads independent.
-  const uint64_t* lrow = f.lists + row * n_lists * (int64_t)f.lane_cap;
-  uint64_t rk[kLsSlots];
+  const uint2* lrow = f.lists + row * n_lists * (int64_t)f.lane_cap;
+  const int n_slots = (total + kWave - 1) / kWave;
+  uint2 ent[kLsSlots];
 #pragma unroll
   for (int j = 0; j < kLsSlots; ++j) {
+    ent[j] = make_uint2(0u, 0u);
     const int p = j * kWave + lane;
-    int l = 0;
-#pragma unroll
-    for (int s = kWave / 2; s > 0; s >>= 1)
-      if (l + s < n_lists && off[l + s] <= p) l += s;
-    rk[j] = p < total ? lrow[(int64_t)l * f.lane_cap + (p - off[l])] : 0ull;
+    if (j < n_slots && p < total) ent[j] = lrow[place[p]];
   }
+  wave_lds_sync();  // the map is read before the histogram reuses the area
+  uint64_t rk[kLsSlots];
+#pragma unroll
+  for (int j = 0; j < kLsSlots; ++j)
+    rk[j] = j * kWave + lane < total ? fs_rank(__uint_as_float(ent[j].x), (int)ent[j].y) : 0ull;
   uint32_t* hist = area[wave];
   int pb;
   const uint64_t pre = wave_radix_select<kFsRankBits>(
@@ -382,13 +413,13 @@ __global__ __launch_bounds__(256) void list_select_kernel(FusedSelArgs f) {
       [&](auto&& fn) {
 #pragma unroll
         for (int j = 0; j < kLsSlots; ++j)
-          if (rk[j]) fn(rk[j]);
+          if (j < n_slots && rk[j]) fn(rk[j]);
       },
       pb);
   uint32_t kept_mask = 0u;  // bit j: slot j holds one of the m kept
 #pragma unroll
   for (int j = 0; j < kLsSlots; ++j)
-    if (rk[j] != 0ull && (rk[j] >> (kFsRankBits - pb)) >= pre) kept_mask |= 1u << j;
+    if (j < n_slots && rk[j] != 0ull && (rk[j] >> (kFsRankBits - pb)) >= pre) kept_mask |= 1u << j;
   // Ascending order: the kept ids set bits of a bitmap over the row's blocks, one
   // window of kLsMapWords * 32 blocks at a time; each lane owns a run of words,
   // counts their bits, and writes its ids after those of the lanes before it.
@@ -403,7 +434,7 @@ __global__ __launch_bounds__(256) void list_select_kernel(FusedSelArgs f) {
     wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < kLsSlots; ++j)
-      if (kept_mask & (1u << j)) {
+      if (j < n_slots && (kept_mask & (1u << j))) {
         const int rel = fs_rank_id(rk[j]) - (w0 << 5);
         if (rel >= 0 && rel < (nw << 5)) atomicOr(&bm[rel >> 5], 1u << (rel & 31));
       }
@@ -503,7 +534,8 @@ int fused_n_split(int64_t lq) {
 hipError_t launch_select_fused(const FusedSelArgs& f, hipStream_t stream) {
   if (f.lq <= 0) return hipSuccess;
   if (f.n_split < 1 || f.n_split > 4 || f.cap > kFusedListCap || f.nblk >= (1 << kFsIdBits) ||
-      f.target < 1 || f.sample_k < 1 || f.lane_cap < 1)
+      f.target < 1 || f.sample_k < 1 || f.lane_cap < 1 ||
+      (int64_t)f.n_split * kFsLanes * f.lane_cap > 65536)  // list places in 16 bits
     return hipErrorInvalidValue;
   const int64_t tiles = (f.lq + kFsRows - 1) / kFsRows;
   const dim3 g1((unsigned)tiles, (unsigned)f.n_split);
