@@ -303,10 +303,11 @@ def qsa_sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
 # ------------------------------------------------------------------------------------
 
 
-# Rows with more candidate blocks than this take the fused selection by default: there
-# it is faster (measured on MI355X: 8192 rows over 1M keys, 3.7 against 4.7 ms), while
-# shorter rows are selected faster by the two-kernel path (128K: 5.4 against 5.7 ms).
-FUSED_MIN_BLOCKS = 65536
+# Sequences with more blocks than this take the fused selection by default: there it
+# is faster (measured on MI355X, per 128K prefill step: 4.7 against 5.1 ms of
+# selection; 8192 rows over 1M keys: 2.8 against 4.2 ms), while shorter ones are
+# selected faster by the two-kernel path (32K: 9.83 against 9.70 ms a whole step).
+FUSED_MIN_BLOCKS = 16384
 
 
 def prefer_fused_select(lk: int, r: int = 4) -> bool:
