@@ -697,7 +697,9 @@ def main():
         "ceiling_buffer_MiB": chunk_bytes >> 20,
         "frac_of_write_ceiling": w_bytes / (score_ms * 1e-3) / 1e9 / w_best,
         "floor_ms_at_ceiling": w_bytes / (w_best * 1e9) * 1e3,
-        "note": "the score GEMM stores non-temporal; its time cannot fall below the floor"}
+        "note": ("the two-kernel selection's score GEMM (score_gemm_ms) stores every fp32 score "
+                 "non-temporal; its time cannot fall below the floor. The fused "
+                 "selection stores only list entries.")}
     if not args.no_backward:
         b_ms = bench_backward(torch, Q, wl, inp, plan)
         b_bytes = backward_bytes(wl, t)
