@@ -48,6 +48,8 @@ def parse_args():
                    help="skip the packed variable-length prefill batch")
     p.add_argument("--no-other", action="store_true",
                    help="skip the 32K and chunked-1M prefill steps")
+    p.add_argument("--no-tile", action="store_true",
+                   help="skip the multi-row attention tile measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -68,7 +70,7 @@ def copy_calibration(torch, mib):
 ROOT = os.path.dirname(os.path.abspath(__file__))
 COUNTERS = os.path.join(ROOT, "profiles", "sparse_attn_prefill128k_counters.md")
 ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_06_amd", "csrc", f)
-                for f in ("attention.hip", "qsa_device.h")]
+                for f in ("attention.hip", "attn_step.h", "qsa_device.h")]
 
 
 def attention_source_hash():
@@ -340,6 +342,41 @@ def time_calls(torch, f, reps):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps * 1e-3
+
+
+def bench_attention_tile(torch, Q, wl, inp, sel, reps=3):
+    """The multi-row attention tile (qsa_sparse_attn_fwd_tiled) against the per-row
+    kernel, on the step's own selections (random rows: neighbours share few blocks) and
+    on the same workload with token-correlated indexer inputs (smooth 100: neighbours
+    share most blocks): ms per call over all rows, the union always and chosen by the
+    sampled overlap (32 of 64)."""
+    import math
+    from synth import generate, workload
+    scale = 1.0 / math.sqrt(wl.d)
+    res = {"what": "attention over all rows of the workload, ms per call"}
+
+    def run(name, q, k, v, s):
+        out = torch.empty_like(q)
+        lse = torch.empty((q.shape[0], wl.hq), dtype=torch.float32, device=q.device)
+        r = {"per_row_ms": 1e3 * time_calls(torch, lambda: Q.qsa_sparse_attn_fwd(
+            q, k, v, s, q_pos0=wl.q_pos0, scale=scale, out=out, lse=lse), reps)}
+        for key, ms in (("tile_union_ms", 0), ("tile_by_overlap_ms", 32)):
+            r[key] = 1e3 * time_calls(torch, lambda: Q.qsa_sparse_attn_fwd_tiled(
+                q, k, v, s, q_pos0=wl.q_pos0, scale=scale, min_shared=ms, out=out, lse=lse), reps)
+        res[name] = r
+        progress(f"attention tile ({name}): per row {r['per_row_ms']:.1f} ms, union "
+                 f"{r['tile_union_ms']:.1f} ms, by overlap {r['tile_by_overlap_ms']:.1f} ms")
+
+    run("random", inp["q"], inp["k"], inp["v"], sel)
+    swl = workload(wl.name, smooth=100)
+    sinp = generate(swl, device="cuda")
+    ssel, _ = Q.qsa_prefill_select(sinp["q_idx"], sinp["w"], sinp["k_idx"], lk=swl.lk,
+                                   budget=swl.budget, q_pos0=swl.q_pos0,
+                                   k_pooled_prefix=sinp["k_pooled_prefix"], row_chunk=16384)
+    run("correlated (smooth 100)", sinp["q"], sinp["k"], sinp["v"], ssel)
+    del sinp, ssel
+    torch.cuda.empty_cache()
+    return res
 
 
 def paged_copy(torch, kc, vc, page_size, seed=1):
@@ -700,6 +737,8 @@ def main():
         "note": ("the two-kernel selection's score GEMM (score_gemm_ms) stores every fp32 score "
                  "non-temporal; its time cannot fall below the floor. The fused "
                  "selection stores only list entries.")}
+    if not args.no_tile and wl.n_sel <= 512:
+        line["attention_tile"] = bench_attention_tile(torch, Q, wl, inp, plan.sel)
     if not args.no_backward:
         b_ms = bench_backward(torch, Q, wl, inp, plan)
         b_bytes = backward_bytes(wl, t)

@@ -27,6 +27,7 @@ from .ops import (  # noqa: F401
     qsa_sparse_attn_fwd,
     qsa_sparse_attn_fwd_launches,
     qsa_sparse_attn_fwd_rows_per_launch,
+    qsa_sparse_attn_fwd_tiled,
     qsa_sparse_attn_varlen_fwd,
     qsa_topk_blocks,
     score_ld,

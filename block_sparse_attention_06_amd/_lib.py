@@ -27,6 +27,8 @@ SIGNATURES = {
     "qsa_topk_blocks": (_I, [_I, _L, _I, _I, _P, _L, _L, _L, _L, _P, _P, _P, _Z, _P]),
     "qsa_sparse_attn_fwd": (_I, [_L, _L, _I, _I, _I, _I, _I, _P, _P, _P, _P, _L, _F, _P, _P,
                                  _P]),
+    "qsa_sparse_attn_fwd_tiled": (_I, [_L, _L, _I, _I, _I, _I, _I, _P, _P, _P, _P, _L, _F, _I,
+                                       _P, _P, _P]),
     "qsa_sparse_attn_fwd_rows_per_launch": (_L, [_I, _I]),
     "qsa_sparse_attn_bwd_workspace_bytes": (_Z, [_L, _L, _I, _I, _I]),
     "qsa_sparse_attn_bwd": (_I, [_L, _L, _I, _I, _I, _I, _I, _P, _P, _P, _P, _L, _F, _P, _P, _P,

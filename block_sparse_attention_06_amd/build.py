@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 PROBE_LIB_PATH = os.path.join(PKG_DIR, "libqsa_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 
-SOURCES = ["indexer.hip", "topk.hip", "select_fused.hip", "attention.hip", "backward.hip",
-           "warmup.hip", "qsa_abi.hip"]
+SOURCES = ["indexer.hip", "topk.hip", "select_fused.hip", "attention.hip", "attention_tile.hip",
+           "backward.hip", "warmup.hip", "qsa_abi.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code (the hipcc host pass warns
 # that it does not know the feature; that warning is harmless).

@@ -330,6 +330,37 @@ qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, i
                     "qsa_sparse_attn_fwd launch");
 }
 
+qsa_status qsa_sparse_attn_fwd_tiled(int64_t lq, int64_t lk, int hq, int hkv, int d, int r,
+                                     int n_sel, const void* q, const void* k, const void* v,
+                                     const int32_t* sel, int64_t q_pos0, float softmax_scale,
+                                     int min_shared, void* out, float* lse, void* stream) {
+  QSA_TRY(check_attn_fwd(lq, lk, hq, hkv, d, r, n_sel, q, k, v, sel, q_pos0, softmax_scale,
+                         out));
+  QSA_REQUIRE(n_sel <= qsa::kTileMaxSel, QSA_ERR_UNSUPPORTED,
+              "n_sel=%d: the tiled attention holds kept lists of up to %d blocks", n_sel,
+              qsa::kTileMaxSel);
+  QSA_REQUIRE(min_shared >= 0 && min_shared <= 65, QSA_ERR_INVALID_ARGUMENT,
+              "min_shared=%d: 0..64 of 64 sampled blocks, or 65 for never", min_shared);
+  if (lq == 0) return QSA_OK;
+  qsa::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sel = sel;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.lq = lq;
+  a.lk = lk;
+  a.q_pos0 = q_pos0;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.n_sel = n_sel;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return hip_status(qsa::launch_sparse_attn_fwd_tiled(a, min_shared, static_cast<hipStream_t>(stream)),
+                    "qsa_sparse_attn_fwd_tiled launch");
+}
+
 int64_t qsa_sparse_attn_fwd_rows_per_launch(int hkv, int d) {
   if (hkv < 1 || (d != 128 && d != 256)) return 0;
   return qsa::sparse_attn_fwd_rows_per_launch(hkv, d);

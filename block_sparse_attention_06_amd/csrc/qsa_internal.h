@@ -190,6 +190,16 @@ struct AttnArgs {
   int num_pages;
 };
 hipError_t launch_sparse_attn_fwd(const AttnArgs& a, hipStream_t stream);
+// Workgroups of `kernel` (block_threads threads) the current device holds at once; 0
+// when the runtime cannot say.
+int resident_workgroups(const void* kernel, int block_threads);
+// Multi-row tile (four neighbouring rows of one KV group per workgroup, the union of
+// their kept blocks staged in LDS): kept lists of at most kTileMaxSel entries; the
+// union is used where a sample of row 0's blocks finds at least min_shared of 64 in
+// row 1's list (0: always, 65: never).
+constexpr int kTileMaxSel = 512;
+hipError_t launch_sparse_attn_fwd_tiled(const AttnArgs& a, int min_shared, hipStream_t stream);
+int64_t sparse_attn_tiled_rows_per_launch(int d);
 // Rows per launch of launch_sparse_attn_fwd on the current device; -1 if unknown.
 int64_t sparse_attn_fwd_rows_per_launch(int hkv, int d);
 // Kernel launches of one launch_sparse_attn_fwd call over lq rows whose longest

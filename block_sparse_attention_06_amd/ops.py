@@ -176,6 +176,29 @@ def qsa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: 
     return out, lse
 
 
+def qsa_sparse_attn_fwd_tiled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              sel: torch.Tensor, *, q_pos0: int = 0, scale: Optional[float] = None,
+                              r: int = 4, min_shared: int = 0, out: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """qsa_sparse_attn_fwd as four-row tiles that stage the union of their kept blocks
+    in LDS (min_shared: 0 always, 1..64 when that many of 64 sampled blocks are shared,
+    65 never). n_sel <= 512."""
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, q.device)
+    _need(v, "v", torch.bfloat16, q.device)
+    _need(sel, "sel", torch.int32, q.device)
+    lq, hq, d = q.shape
+    lk, hkv, _ = k.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((lq, hq), dtype=torch.float32, device=q.device)
+    _call("qsa_sparse_attn_fwd_tiled", lq, lk, hq, hkv, d, r, sel.shape[1], _ptr(q), _ptr(k),
+          _ptr(v), _ptr(sel), q_pos0, scale, min_shared, _ptr(out), _ptr(lse), _stream(q))
+    return out, lse
+
+
 def qsa_sparse_attn_fwd_rows_per_launch(hkv: int, d: int, device=None) -> int:
     """Rows per GPU launch of qsa_sparse_attn_fwd on `device` (the current device by
     default); -1 when the runtime cannot report the occupancy, 0 for unsupported

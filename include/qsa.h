@@ -169,6 +169,26 @@ qsa_status qsa_sparse_attn_fwd(int64_t lq, int64_t lk, int hq, int hkv, int d, i
                                const int32_t* sel, int64_t q_pos0, float softmax_scale,
                                void* out, float* lse, void* stream);
 /*
+ * Stage 4 as a multi-row tile [MR], [DR] (MTP reuse of the kept blocks): the same
+ * outputs as qsa_sparse_attn_fwd up to the order of the online softmax (fp32 rounding).
+ * A workgroup takes four neighbouring rows of one KV group; where they share enough
+ * kept blocks it stages the sorted union of their blocks in LDS once, 16 keys at a
+ * time, and each row attends over it with the blocks it did not keep masked, so a block
+ * kept by several of the rows is read once. Where they share too little, each row
+ * walks its own blocks as in qsa_sparse_attn_fwd.
+ *   arguments as for qsa_sparse_attn_fwd, with n_sel <= 512 (QSA_ERR_UNSUPPORTED above)
+ *   min_shared  0: always the union; 1..64: the union when at least min_shared of 64
+ *               evenly spaced kept blocks of the tile's first row are kept by its second
+ *               row too; 65: never
+ * Launches: one KV group and one resident generation of tiles at a time. On random
+ * selections the rows share few blocks and the per-row kernel is faster; the tile is
+ * for inputs whose neighbouring rows keep mostly the same blocks.
+ */
+qsa_status qsa_sparse_attn_fwd_tiled(int64_t lq, int64_t lk, int hq, int hkv, int d, int r,
+                                     int n_sel, const void* q, const void* k, const void* v,
+                                     const int32_t* sel, int64_t q_pos0, float softmax_scale,
+                                     int min_shared, void* out, float* lse, void* stream);
+/*
  * Rows per launch of qsa_sparse_attn_fwd on the current device when each launch takes
  * one KV group of its rows (hkv KV heads, head dim d = 128 or 256); 0 when the
  * arguments are unsupported, -1 when the runtime cannot report the device's occupancy

@@ -105,6 +105,24 @@ def test_topk_and_attention_validation(lib):
                                    ctypes.c_float(float("nan")), FAKE, None, None) == 1
 
 
+def test_tiled_attention_validation(lib):
+    f = ctypes.c_float(0.1)
+    # the shared checks of the per-row entry point
+    assert lib.qsa_sparse_attn_fwd_tiled(10, 100, 24, 5, 256, 4, 512, FAKE, FAKE, FAKE, FAKE, 0,
+                                         f, 0, FAKE, None, None) == 1  # 24 % 5
+    assert lib.qsa_sparse_attn_fwd_tiled(10, 100, 24, 2, 256, 4, 512, FAKE, FAKE, FAKE, FAKE, 95,
+                                         f, 0, FAKE, None, None) == 1  # rows past Lk
+    # kept lists beyond the tile's LDS (512 blocks), and a bad sharing threshold
+    assert lib.qsa_sparse_attn_fwd_tiled(10, 100, 24, 2, 256, 4, 513, FAKE, FAKE, FAKE, FAKE, 0,
+                                         f, 0, FAKE, None, None) == 2
+    assert lib.qsa_sparse_attn_fwd_tiled(10, 100, 24, 2, 256, 4, 512, FAKE, FAKE, FAKE, FAKE, 0,
+                                         f, 66, FAKE, None, None) == 1
+    assert lib.qsa_sparse_attn_fwd_tiled(10, 100, 24, 2, 256, 4, 512, FAKE, FAKE, FAKE, FAKE, 0,
+                                         f, -1, FAKE, None, None) == 1
+    assert lib.qsa_sparse_attn_fwd_tiled(0, 100, 24, 2, 256, 4, 512, None, None, None, None, 0,
+                                         f, 65, None, None, None) == 0  # nothing to do
+
+
 def test_attention_rows_per_launch_query(lib):
     assert lib.qsa_sparse_attn_fwd_rows_per_launch(2, 192) == 0   # d unsupported
     assert lib.qsa_sparse_attn_fwd_rows_per_launch(0, 256) == 0
