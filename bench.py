@@ -50,6 +50,11 @@ def parse_args():
                    help="skip the 32K and chunked-1M prefill steps")
     p.add_argument("--no-tile", action="store_true",
                    help="skip the multi-row attention tile measurement")
+    p.add_argument("--tile-only", choices=["random", "correlated"], default=None,
+                   help="only select and run the attention on the workload (correlated: "
+                        "smooth 100 indexer inputs), one per-row call and one tile call with "
+                        "the union always taken, each after one warm-up call (a short run "
+                        "for the profiler's counters) and exit")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -379,6 +384,28 @@ def bench_attention_tile(torch, Q, wl, inp, sel, reps=3):
     return res
 
 
+def tile_only(torch, Q, name, kind):
+    """--tile-only: the attention of one 128K-style workload, per row and as the tile
+    (union always), one call each after a warm-up call; prints one JSON line."""
+    import math
+    from synth import generate, workload
+    wl = workload(name, smooth=100) if kind == "correlated" else workload(name)
+    inp = generate(wl, device="cuda")
+    sel, _ = Q.qsa_prefill_select(inp["q_idx"], inp["w"], inp["k_idx"], lk=wl.lk,
+                                  budget=wl.budget, q_pos0=wl.q_pos0,
+                                  k_pooled_prefix=inp["k_pooled_prefix"], row_chunk=16384)
+    scale = 1.0 / math.sqrt(wl.d)
+    out = torch.empty_like(inp["q"])
+    lse = torch.empty((wl.lq, wl.hq), dtype=torch.float32, device="cuda")
+    per_row = time_calls(torch, lambda: Q.qsa_sparse_attn_fwd(
+        inp["q"], inp["k"], inp["v"], sel, q_pos0=wl.q_pos0, scale=scale, out=out, lse=lse), 1)
+    tile = time_calls(torch, lambda: Q.qsa_sparse_attn_fwd_tiled(
+        inp["q"], inp["k"], inp["v"], sel, q_pos0=wl.q_pos0, scale=scale, min_shared=0,
+        out=out, lse=lse), 1)
+    print(json.dumps({"workload": wl.name, "selections": kind, "per_row_ms": per_row * 1e3,
+                      "tile_union_ms": tile * 1e3}), flush=True)
+
+
 def paged_copy(torch, kc, vc, page_size, seed=1):
     """The caches [B, L, Hkv, d] scattered into pools of shuffled pages (the layout a
     serving engine's page allocator leaves), and the block table."""
@@ -626,6 +653,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
+        return
+    if args.tile_only:
+        tile_only(torch, Q, args.workload, args.tile_only)
         return
 
     wl = workload(args.workload)
