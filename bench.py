@@ -31,7 +31,7 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="prefill128k",
                    choices=["prefill128k", "prefill32k", "chunked1m", "tiny"])
-    p.add_argument("--row-chunk", type=int, default=16384)
+    p.add_argument("--row-chunk", type=int, default=65536)
     p.add_argument("--select", choices=["auto", "fused", "plain"], default="auto",
                    help="selection path of the step: the fused score/top-k, the two-kernel "
                         "one (scores materialised, then top-k), or the library's default for "
@@ -272,7 +272,7 @@ def bench_other_prefill(torch, Q, name, select, steps=5):
     select = select_path(Q, owl, select)
     res = {"query_tokens": owl.lq, "context": owl.lk, "q_pos0": owl.q_pos0, "select": select}
     for path in (select, "plain" if select == "fused" else "fused"):
-        args = types.SimpleNamespace(row_chunk=min(16384, owl.lq), warmup=1, steps=steps,
+        args = types.SimpleNamespace(row_chunk=min(65536, owl.lq), warmup=1, steps=steps,
                                      select=path)
         wall, attn_ms, plan = bench_prefill(args, torch, Q, owl, oinp)
         step_ms = bench_prefill.step_ms

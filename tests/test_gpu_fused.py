@@ -42,6 +42,7 @@ def _both(wl, inp, row_chunk, tuning=None):
     ("prefill32k", 2500, dict(lq=12000, lk=40000, q_pos0=28000, pooled_prefix_blocks=5000)),
     ("prefill32k", 16384, dict(smooth=100)),                      # correlated rows
     ("prefill128k", 16384, {}),
+    ("prefill128k", 65536, {}),                                   # the bench's chunks: 1024 tiles, one piece
     ("chunked1m", 8192, {}),                                      # 262K candidates a row
     ("prefill32k", 32768, {}),                                    # one key-range piece
     ("prefill32k", 9000, {}),                                     # three pieces
