@@ -327,9 +327,10 @@ def qsa_sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
 
 
 # Sequences with more blocks than this take the fused selection by default: there it
-# is faster (measured on MI355X, per 128K prefill step: 4.7 against 5.1 ms of
-# selection; 8192 rows over 1M keys: 2.8 against 4.2 ms), while shorter ones are
-# selected faster by the two-kernel path (32K: 9.83 against 9.70 ms a whole step).
+# is faster (measured on MI355X, per 128K prefill step: 4.2 against 4.5 ms of
+# selection in 65536-row chunks, 4.7 against 5.1 ms in 16384-row chunks; 8192 rows
+# over 1M keys: 2.8 against 4.2 ms), while shorter ones are selected faster by the
+# two-kernel path (32K: 9.73 against 9.50 ms a whole step).
 FUSED_MIN_BLOCKS = 16384
 
 
