@@ -11,6 +11,7 @@ from .ops import (  # noqa: F401
     prefer_fused_select,
     QSAError,
     abi_version,
+    default_row_chunk,
     qsa_decode_forward,
     qsa_decode_forward_noalloc,
     qsa_decode_forward_paged,

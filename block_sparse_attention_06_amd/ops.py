@@ -58,6 +58,21 @@ def score_ld(nblk: int) -> int:
     return (nblk + 3) // 4 * 4
 
 
+# Selection chunk when the caller gives none: as many rows as keep the chunk's fp32
+# score rows within 8 GiB, from 4096 up to 65536. At 128K (32768 blocks) that is 65536
+# rows, where a prefill step on MI355X takes 42.9 ms against 43.4 at 16384 and 44.1 at
+# 8192 (fewer launches; for the fused selection, more workgroups than the GPU holds,
+# so the long row tiles' CUs are refilled); at 1M it is 8192.
+SCORE_CHUNK_BYTES = 8 << 30
+
+
+def default_row_chunk(lq: int, lk: int, r: int = 4) -> int:
+    """Rows per selection chunk for lq query rows over lk keys (see SCORE_CHUNK_BYTES)."""
+    per_row = score_ld(lk // r) * 4
+    rc = max(4096, min(65536, SCORE_CHUNK_BYTES // max(per_row, 1)))
+    return int(max(1, min(rc, lq)))
+
+
 def abi_version() -> int:
     return _lib.load().qsa_abi_version()
 
@@ -343,9 +358,10 @@ class PrefillPlan:
     """Preallocated outputs and workspace for repeated prefill calls of one shape.
     fused: the selection path the plan is sized for (None: prefer_fused_select)."""
 
-    def __init__(self, lq, lk, hq, hkv, d, h_idx, d_idx, budget, *, r=4, row_chunk=4096,
+    def __init__(self, lq, lk, hq, hkv, d, h_idx, d_idx, budget, *, r=4, row_chunk=None,
                  device="cuda", with_attention=True, fused=None):
         self.shape = (lq, lk, hq, hkv, d, h_idx, d_idx, budget, r)
+        row_chunk = default_row_chunk(lq, lk, r) if row_chunk is None else row_chunk
         self.row_chunk = row_chunk
         fused = prefer_fused_select(lk, r) if fused is None else fused
         self.fused = fused
@@ -381,12 +397,13 @@ class _FusedTuning(ctypes.Structure):
 
 def qsa_prefill_select(q_idx, w, k_idx, *, lk: int, budget: int, q_pos0: int = 0,
                        k_pooled_prefix: Optional[torch.Tensor] = None, r: int = 4,
-                       row_chunk: int = 4096, plan: Optional[PrefillPlan] = None, pe=None,
-                       fused: Optional[bool] = None, tuning=None):
-    """Selection half of prefill: pool the new blocks, score + top-k in row chunks.
-    fused (default: the plan's choice, else False) takes the fused score/top-k path,
-    whose selection is identical; tuning = (target, sample_k, cap) adjusts it (0 keeps a
-    default). Returns (sel, k_pooled)."""
+                       row_chunk: Optional[int] = None, plan: Optional[PrefillPlan] = None,
+                       pe=None, fused: Optional[bool] = None, tuning=None):
+    """Selection half of prefill: pool the new blocks, score + top-k in row chunks
+    (row_chunk rows each; default_row_chunk when not given, the plan's when a plan is).
+    fused (default: the plan's choice, else prefer_fused_select) takes the fused
+    score/top-k path, whose selection is identical; tuning = (target, sample_k, cap)
+    adjusts it (0 keeps a default). Returns (sel, k_pooled)."""
     lq, h_idx, d_idx = q_idx.shape
     prefix_blocks = _prefill_args(q_idx, w, k_idx, k_pooled_prefix, r, lk)
     if fused is None:
@@ -416,8 +433,9 @@ def qsa_prefill_select(q_idx, w, k_idx, *, lk: int, budget: int, q_pos0: int = 0
 
 def qsa_prefill_forward(q, k, v, q_idx, w, k_idx, *, budget: int, q_pos0: int = 0,
                         k_pooled_prefix: Optional[torch.Tensor] = None,
-                        scale: Optional[float] = None, r: int = 4, row_chunk: int = 4096,
-                        plan: Optional[PrefillPlan] = None, pe=None):
+                        scale: Optional[float] = None, r: int = 4,
+                        row_chunk: Optional[int] = None, plan: Optional[PrefillPlan] = None,
+                        pe=None):
     """Whole prefill: pool the new blocks, score + top-k in row chunks, attention.
 
     q [Lq,Hq,d], k/v [Lk,Hkv,d], q_idx [Lq,H_I,d_I], w [Lq,H_I]; k_idx holds the raw

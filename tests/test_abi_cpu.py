@@ -310,3 +310,20 @@ def test_fused_selection_validation(lib):
     assert need >= 64 * 16 * 4 + 64 * 2048 * 8
     assert call(ws_bytes=need - 1) == 3 and "workspace" in _err(lib)
     assert lib.qsa_prefill_fused_workspace_bytes(0, 64, 4, 256, 64) == 0
+
+
+def test_binding_defaults_for_the_selection():
+    # Host logic of the binding: the default selection chunk keeps its fp32 score rows
+    # within 8 GiB (65536 rows at 128K, 8192 at 1M, whole short prefills), and the fused
+    # selection is the default above 16384 blocks.
+    from block_sparse_attention_06_amd import ops
+    assert ops.default_row_chunk(131072, 131072) == 65536
+    assert ops.default_row_chunk(8192, 1048576) == 8192
+    assert ops.default_row_chunk(32768, 32768) == 32768
+    assert ops.default_row_chunk(100, 100) == 100
+    assert ops.default_row_chunk(1 << 20, 1 << 22) == 4096  # never below 4096 rows
+    for lq, lk in ((131072, 131072), (8192, 1048576), (70000, 1 << 22)):
+        rc = ops.default_row_chunk(lq, lk)
+        assert rc * ops.score_ld(lk // 4) * 4 <= max(ops.SCORE_CHUNK_BYTES, 4096 * ops.score_ld(lk // 4) * 4)
+    assert not ops.prefer_fused_select(32768 * 2)    # 16384 blocks: the two-kernel path
+    assert ops.prefer_fused_select(131072)           # 32768 blocks: fused
