@@ -28,6 +28,11 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# Per-source device flags. attention.hip keeps its MFMA accumulators in VGPRs: with
+# them in AGPRs the compiler copies all of them out and back around every step's
+# conditional rescale, and needs 264 registers where the VGPR form needs 198 (two
+# waves per SIMD; the decode kernels go from 304 to 180-238 registers).
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 _NOISE = "is not a recognized feature for this target"
 
 
@@ -55,8 +60,8 @@ def build_library(sources, out_path, verbose=False, extra_flags=()):
     jobs = max(1, min(len(sources), int(os.environ.get("MAX_JOBS", "8"))))
     with tempfile.TemporaryDirectory(prefix="qsa_build_") as tmpd:
         objs = [os.path.join(tmpd, os.path.splitext(s)[0] + ".o") for s in sources]
-        cmds = [[cc, *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c",
-                 os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
+        cmds = [[cc, *HIP_FLAGS, *SOURCE_FLAGS.get(s, []), *extra_flags, "-I", INCLUDE, "-I",
+                 CSRC, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
         with ThreadPoolExecutor(jobs) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()

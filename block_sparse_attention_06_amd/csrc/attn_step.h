@@ -50,6 +50,23 @@ __device__ __forceinline__ int64_t attn_row(int b, int p, int i, int64_t t, bool
   return (int64_t)p * 4 + (off < 0 ? 0 : off);
 }
 
+// V rows of one step: this lane's 4 keys are the 4 tokens of block slot `quad`, 16
+// contiguous bytes (8 dims) of each per 128-dim half.
+template <int D>
+__device__ __forceinline__ void attn_load_v(AttnStep<D>& st, const int (&b4)[4], const int (&p4)[4],
+                                            bool paged, const uint16_t* vb, int64_t kstride, int g,
+                                            int64_t t, int c16, int quad) {
+  const int bv = pick4(b4[0], b4[1], b4[2], b4[3], quad);
+  const int pv = pick4(p4[0], p4[1], p4[2], p4[3], quad);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int64_t tv = attn_row(bv, pv, kk, t, paged);
+    const uint16_t* vp = vb + tv * kstride + g * D + c16 * 8;
+#pragma unroll
+    for (int hf = 0; hf < AttnStep<D>::NH; ++hf) st.Vr[kk][hf] = ld16(vp + hf * 128);
+  }
+}
+
 // Issues the loads of one step. Block ids < 0 (padding) and keys after position t
 // read an in-bounds row that the softmax masks. b4 holds the kept blocks' ids (token
 // positions); with a paged pool, p4 holds their places in it (units of 4 rows).
@@ -66,16 +83,7 @@ __device__ __forceinline__ void attn_load_step(AttnStep<D>& st, const int (&b4)[
   const uint16_t* kp = kb + tk * kstride + g * D + quad * 8;
 #pragma unroll
   for (int c = 0; c < AttnStep<D>::NC; ++c) st.Kc[c] = ld16(kp + c * 32);
-  // V rows: this lane's 4 keys are the 4 tokens of block slot `quad`.
-  const int bv = pick4(b4[0], b4[1], b4[2], b4[3], quad);
-  const int pv = pick4(p4[0], p4[1], p4[2], p4[3], quad);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int64_t tv = attn_row(bv, pv, kk, t, paged);
-    const uint16_t* vp = vb + tv * kstride + g * D + c16 * 8;
-#pragma unroll
-    for (int hf = 0; hf < AttnStep<D>::NH; ++hf) st.Vr[kk][hf] = ld16(vp + hf * 128);
-  }
+  attn_load_v<D>(st, b4, p4, paged, vb, kstride, g, t, c16, quad);
 }
 
 // S^T = K.Q^T, online softmax update of (m_run, l_run), O = O*alpha + P.V.

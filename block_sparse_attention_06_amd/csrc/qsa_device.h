@@ -173,11 +173,33 @@ __device__ __forceinline__ uint64_t wave_extract_top(uint64_t (&rk)[SLOTS], int 
   return readlane_u64(v, __builtin_ctzll(at));
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// The value of lane l and that of lane l ^ mask (mask 16 or 32, a constant), in some
+// order, without a trip through LDS: gfx950's lane-swap instructions exchange odd
+// 16-lane rows of one operand with even rows of the other (permlane16) or the upper
+// half of one with the lower half of the other (permlane32), so with the same value
+// as both operands the two results hold, lane by lane, the value and its partner's.
+__device__ __forceinline__ u32x2 xor_pair(float x, int mask) {
+  const uint32_t u = __float_as_uint(x);
+  return mask == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                    : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+}
+
 __device__ __forceinline__ float wave_xor_max(float x, int mask) {
+  if (mask == 16 || mask == 32) {
+    const u32x2 r = xor_pair(x, mask);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
   return fmaxf(x, __shfl_xor(x, mask, kWave));
 }
 
+// (Addition is commutative, so the order of the pair does not change the sum.)
 __device__ __forceinline__ float wave_xor_sum(float x, int mask) {
+  if (mask == 16 || mask == 32) {
+    const u32x2 r = xor_pair(x, mask);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   return x + __shfl_xor(x, mask, kWave);
 }
 
