@@ -363,7 +363,8 @@ def test_topk_merge_short_and_tied_rows(budget):
 # ------------------------------------------------------------------------------------
 
 
-def _attn_case(lq, lk, q_pos0, hq, hkv, d, budget, seed, unscaled=False, rows=None):
+def _attn_case(lq, lk, q_pos0, hq, hkv, d, budget, seed, unscaled=False, rows=None,
+               sel_offset=0):
     sc = 1.0 if unscaled else 1 / math.sqrt(d)
     q = _randn_bf16((lq, hq, d), seed, sc)
     k = _randn_bf16((lk, hkv, d), seed + 1, sc)
@@ -371,7 +372,13 @@ def _attn_case(lq, lk, q_pos0, hq, hkv, d, budget, seed, unscaled=False, rows=No
     pos = q_pos0 + np.arange(lq)
     n_sel = budget // 4
     sel_np = _random_selection(pos, n_sel, 4, seed)
-    sel = torch.from_numpy(sel_np).to(DEV)
+    if sel_offset:
+        # A contiguous view that starts sel_offset int32s into its allocation.
+        buf = torch.full((lq * n_sel + sel_offset,), -1, dtype=torch.int32, device=DEV)
+        sel = buf[sel_offset:].view(lq, n_sel)
+        sel.copy_(torch.from_numpy(sel_np))
+    else:
+        sel = torch.from_numpy(sel_np).to(DEV)
     out, lse = Q.qsa_sparse_attn_fwd(q, k, v, sel, q_pos0=q_pos0)
     torch.cuda.synchronize()
     rows = np.arange(lq) if rows is None else np.asarray(rows)
@@ -396,6 +403,19 @@ def _attn_case(lq, lk, q_pos0, hq, hkv, d, budget, seed, unscaled=False, rows=No
 def test_sparse_attn_fwd(lq, lk, q_pos0, hq, hkv, d, budget):
     _say(f"attn lq={lq} lk={lk} q_pos0={q_pos0} hq={hq} hkv={hkv} d={d} K={budget}")
     _attn_case(lq, lk, q_pos0, hq, hkv, d, budget, seed=lq)
+
+
+@pytest.mark.parametrize("budget,sel_offset", [
+    (52, 0),    # 13 blocks a row: rows are not a whole number of 16-byte id groups
+    (28, 1),    # 7 blocks a row, rows start 4 bytes past a 16-byte boundary
+    (256, 1),   # 64 blocks a row, every row start off a 16-byte boundary
+])
+def test_sparse_attn_fwd_unaligned_selection_rows(budget, sel_offset):
+    # The attention reads a step's four block ids 16 bytes at once only when every row
+    # starts on a 16-byte boundary; other selection layouts take the id-by-id reads.
+    _say(f"attn selection rows K={budget} offset={sel_offset}")
+    _attn_case(400, 1500, 1100, 24, 2, 256, budget, seed=budget + sel_offset,
+               sel_offset=sel_offset)
 
 
 @pytest.mark.parametrize("lq,lk,q_pos0,hq,hkv,d", [
