@@ -308,10 +308,9 @@ constexpr int kScoreTileN = 64;  // pooled keys per LDS tile
 template <int DI>
 __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64_t n_per_wg) {
   constexpr int NC = DI / 32;      // 32-dim MFMA k-chunks
-  constexpr int ROW = DI + 8;      // LDS row in bf16 elements, padded by 16 B
   constexpr int VPR = DI / 8;      // 16-byte vectors per pooled key
   constexpr int LPT = kScoreTileN * VPR / 256;  // 16-byte loads per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kScoreTileN * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kScoreTileN * DI];  // key_tile_off layout
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -363,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
     for (int u = 0; u < LPT; ++u) {
       const int v = threadIdx.x + 256 * u;
       const int row = v / VPR, cv = v - row * VPR;
-      *reinterpret_cast<uint4*>(&tile[buf][row * ROW + cv * 8]) = stage[u];
+      *reinterpret_cast<uint4*>(&tile[buf][key_tile_off<DI>(row, cv)]) = stage[u];
     }
   };
 
@@ -410,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(ScoreArgs a, int64
       uint4 B[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        B[c] = *reinterpret_cast<const uint4*>(&tb[(4 * c16 + j) * ROW + c * 32 + quad * 8]);
+        B[c] = *reinterpret_cast<const uint4*>(&tb[key_tile_off<DI>(4 * c16 + j, 4 * c + quad)]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -173,6 +173,18 @@ __device__ __forceinline__ uint64_t wave_extract_top(uint64_t (&rk)[SLOTS], int 
   return readlane_u64(v, __builtin_ctzll(at));
 }
 
+// Element offset of 16-byte chunk `ch` of row `row` in an LDS tile of pooled keys
+// (DI bf16 a row, no padding). The score kernels read B operands with lane c16 taking
+// row 4*c16 + j and one chunk per instruction, so with plain rows every fourth lane
+// would hit the same banks; XOR-ing the chunk with the row's group of four, (row / 4)
+// mod (chunks a row), gives the 16 lanes distinct chunk positions, while the 16-byte
+// writes of one row still cover each position once.
+template <int DI>
+__device__ __forceinline__ int key_tile_off(int row, int ch) {
+  constexpr int CPR = DI / 8;
+  return row * DI + ((ch ^ ((row >> 2) & (CPR - 1))) << 3);
+}
+
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // The value of lane l and that of lane l ^ mask (mask 16 or 32, a constant), in some

@@ -74,10 +74,9 @@ __device__ __forceinline__ int group16_sum(int x) {
 template <int DI, bool SAMPLE>
 __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
   constexpr int NC = DI / 32;
-  constexpr int ROW = DI + 8;  // LDS row in bf16 elements, padded by 16 B
   constexpr int VPR = DI / 8;
   constexpr int LPT = kFsTileN * VPR / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kFsTileN * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kFsTileN * DI];  // key_tile_off layout
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -136,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
       for (int u = 0; u < LPT; ++u) {
         const int v = threadIdx.x + 256 * u;
         const int row = v / VPR, cv = v - row * VPR;
-        *reinterpret_cast<uint4*>(&tile[buf][row * ROW + cv * 8]) = stage[u];
+        *reinterpret_cast<uint4*>(&tile[buf][key_tile_off<DI>(row, cv)]) = stage[u];
       }
     };
     // acc[mt][j]: token (mt, quad), tile row 4*c16 + j.
@@ -146,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void score_list_kernel(FusedSelArgs f) {
         uint4 B[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          B[c] = *reinterpret_cast<const uint4*>(&tb[(4 * c16 + j) * ROW + c * 32 + quad * 8]);
+          B[c] = *reinterpret_cast<const uint4*>(&tb[key_tile_off<DI>(4 * c16 + j, 4 * c + quad)]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
