@@ -135,9 +135,9 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
   // A step's four block ids are read one step ahead (uniform: scalar loads), 16 bytes
   // at once when the rows are 16-byte aligned, so no id load waits at the top of a
   // step. With the K operands read from LDS in one batch (attn_k_from_lds), at 128K on
-  // MI355X: 29.6 -> 27.2 ms on token-correlated selections, 32K 7.5 -> 7.2 ms, 8192
-  // rows over 1M keys 4.24 -> 4.18 ms; random selections unchanged (38.4 ms), bound by
-  // the fetches beyond L2. Outputs are bit-identical.
+  // MI355X: 38.4 -> 37.8 ms on random selections, 29.6 -> 27.2 ms on token-correlated
+  // ones, 32K 7.5 -> 7.2 ms, 8192 rows over 1M keys 4.24 -> 4.18 ms. Outputs are
+  // bit-identical.
   const bool ids4 = (a.n_sel & 3) == 0 && (reinterpret_cast<uintptr_t>(a.sel) & 15) == 0;
   auto read_ids = [&](int s, int (&b)[4]) {
     if (ids4 && s < n_steps) {
